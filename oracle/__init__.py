@@ -1,0 +1,14 @@
+"""CPU oracle for BSR block-sparse attention (test infrastructure only).
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package; the HIP library and its Python binding never do.
+"""
+from .bsr_attention import (  # noqa: F401
+    validate_bsr,
+    bsr_mask,
+    e4m3fn_decode,
+    bf16_bits_decode,
+    masked_attention,
+    bsr_attention,
+    merge_states,
+)

@@ -1,0 +1,287 @@
+"""Seeded synthetic workloads for BSR block-sparse attention.
+
+This module only draws inputs: sparsity structures (indptr / indices /
+per-block valid lengths) and value tensors.  It holds none of the attention
+arithmetic, so both the oracle-based tests and the GPU path can consume the
+same bytes without sharing any code of the method itself.
+
+Structures are drawn with ``numpy.random.default_rng(seed)``; values with
+``torch.Generator().manual_seed(seed)`` as float32 standard normals, then
+rounded (round-to-nearest-even) to the storage dtype.  Everything is made on
+the host, so the device copy and the oracle's copy are the same bytes.
+
+The five workloads follow the shapes the flashinfer.sparse documentation
+(BlockSparseAttentionWrapper: worked example and plan parameters) and the
+MATE sparse-MLA decode documentation describe:
+
+1. ``worked_example``  -- the 3x3 mask of the BlockSparseAttentionWrapper
+   example (R = C = 1, 32 qo / 8 kv heads, head_dim 128).
+2. ``paged_decode``    -- paged batch decode written as BSR with R = 1 and
+   C = page size 16: one query token per request, each request owning a run
+   of pages drawn from a randomly permuted shared pool, last page partial.
+3. ``bsr_prefill``     -- 64x64 blocks, all diagonal blocks plus Bernoulli
+   lower blocks, causal.
+4. ``window_prefill``  -- 128x128 blocks, a local window of preceding blocks
+   plus a stride-16 set of global column blocks, causal.
+5. ``sparse_mla``      -- R = C = 1, one shared latent KV head (576 = 512 +
+   64), fp8 e4m3 KV cache with a per-tensor scale, 2048 selected rows per
+   query token.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+__all__ = [
+    "Workload",
+    "worked_example",
+    "paged_decode",
+    "bsr_prefill",
+    "window_prefill",
+    "sparse_mla",
+    "random_bsr",
+    "by_name",
+    "WORKLOAD_NAMES",
+]
+
+
+@dataclasses.dataclass
+class Workload:
+    """A BSR attention problem: structure, parameters and host tensors."""
+
+    name: str
+    indptr: np.ndarray            # int32 (MB + 1,)
+    indices: np.ndarray           # int32 (nnz,)
+    M: int
+    N: int
+    R: int
+    C: int
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int                 # q/k head dim
+    head_dim_vo: int              # v/o head dim
+    causal: bool
+    sm_scale: float
+    kv_block_lens: Optional[np.ndarray] = None   # int32 (NB,) or None
+    q_dtype: torch.dtype = torch.float16
+    kv_dtype: torch.dtype = torch.float16
+    o_dtype: torch.dtype = torch.float16
+    q: Optional[torch.Tensor] = None      # (M, Hq, D)
+    k: Optional[torch.Tensor] = None      # (N, Hkv, D) or (N, D) for MLA
+    v: Optional[torch.Tensor] = None      # (N, Hkv, Dv) or None (v aliases k)
+    k_descale: float = 1.0
+    v_descale: float = 1.0
+    v_aliases_k: bool = False     # MLA: V = first head_dim_vo components of K
+    k_token_stride: int = 0       # elements; 0 = contiguous
+    v_token_stride: int = 0
+    meta: dict = dataclasses.field(default_factory=dict)
+
+    @property
+    def nnz(self) -> int:
+        return int(self.indptr[-1])
+
+    @property
+    def MB(self) -> int:
+        return -(-self.M // self.R)
+
+    @property
+    def NB(self) -> int:
+        return self.N // self.C
+
+
+def _randn(gen: torch.Generator, shape, dtype: torch.dtype) -> torch.Tensor:
+    return torch.randn(*shape, generator=gen, dtype=torch.float32).to(dtype)
+
+
+def _csr_from_rows(rows) -> tuple[np.ndarray, np.ndarray]:
+    indptr = np.zeros(len(rows) + 1, dtype=np.int64)
+    for i, r in enumerate(rows):
+        indptr[i + 1] = indptr[i] + len(r)
+    indices = np.concatenate([np.asarray(r, dtype=np.int64) for r in rows]) if rows else np.zeros(0)
+    return indptr.astype(np.int32), indices.astype(np.int32)
+
+
+def worked_example(seed: int = 1, dtype: torch.dtype = torch.float16,
+                   values: bool = True) -> Workload:
+    """The 3x3 BSR example of BlockSparseAttentionWrapper (R = C = 1)."""
+    M = N = 3
+    Hq, Hkv, D = 32, 8, 128
+    w = Workload("worked_example", np.array([0, 1, 3, 5], np.int32),
+                 np.array([2, 0, 2, 1, 2], np.int32), M, N, 1, 1, Hq, Hkv, D, D,
+                 False, 1.0 / np.sqrt(D), q_dtype=dtype, kv_dtype=dtype, o_dtype=dtype)
+    if values:
+        g = torch.Generator().manual_seed(seed)
+        w.q = _randn(g, (M, Hq, D), dtype)
+        w.k = _randn(g, (N, Hkv, D), dtype)
+        w.v = _randn(g, (N, Hkv, D), dtype)
+    return w
+
+
+def paged_decode(seed: int = 2, batch: int = 64, min_len: int = 512, max_len: int = 4096,
+                 page: int = 16, num_qo_heads: int = 32, num_kv_heads: int = 8,
+                 head_dim: int = 128, dtype: torch.dtype = torch.float16,
+                 values: bool = True) -> Workload:
+    """Paged batch decode as BSR: R = 1, C = page size, last page partial.
+
+    Request lengths are uniform in [min_len, max_len]; request i owns
+    ceil(len_i / page) pages taken, in order, from one random permutation of
+    the shared pool; its last page holds len_i - page * (pages_i - 1) tokens.
+    Unused slots of partial pages hold random values like every other slot.
+    """
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(min_len, max_len + 1, size=batch)
+    pages = -(-lens // page)
+    P = int(pages.sum())
+    perm = rng.permutation(P)
+    rows, pos = [], 0
+    block_lens = np.full(P, page, dtype=np.int32)
+    for i in range(batch):
+        own = perm[pos:pos + pages[i]]
+        pos += pages[i]
+        rows.append(own)
+        block_lens[own[-1]] = lens[i] - page * (pages[i] - 1)
+    indptr, indices = _csr_from_rows(rows)
+    N = P * page
+    w = Workload("paged_decode", indptr, indices, batch, N, 1, page, num_qo_heads,
+                 num_kv_heads, head_dim, head_dim, False, 1.0 / np.sqrt(head_dim),
+                 kv_block_lens=block_lens, q_dtype=dtype, kv_dtype=dtype, o_dtype=dtype,
+                 meta={"seq_lens": lens.astype(np.int64)})
+    if values:
+        g = torch.Generator().manual_seed(seed)
+        w.q = _randn(g, (batch, num_qo_heads, head_dim), dtype)
+        w.k = _randn(g, (N, num_kv_heads, head_dim), dtype)
+        w.v = _randn(g, (N, num_kv_heads, head_dim), dtype)
+    return w
+
+
+def bsr_prefill(seed: int = 3, M: int = 8192, block: int = 64, density: float = 0.10,
+                num_qo_heads: int = 32, num_kv_heads: int = 8, head_dim: int = 128,
+                dtype: torch.dtype = torch.float16, values: bool = True) -> Workload:
+    """All diagonal blocks plus i.i.d. Bernoulli(density) strictly-lower blocks; causal."""
+    rng = np.random.default_rng(seed)
+    MB = M // block
+    rows = []
+    for i in range(MB):
+        lower = np.nonzero(rng.random(i) < density)[0]
+        rows.append(np.concatenate([lower, [i]]))
+    indptr, indices = _csr_from_rows(rows)
+    w = Workload("bsr_prefill", indptr, indices, M, M, block, block, num_qo_heads,
+                 num_kv_heads, head_dim, head_dim, True, 1.0 / np.sqrt(head_dim),
+                 q_dtype=dtype, kv_dtype=dtype, o_dtype=dtype)
+    if values:
+        g = torch.Generator().manual_seed(seed)
+        w.q = _randn(g, (M, num_qo_heads, head_dim), dtype)
+        w.k = _randn(g, (M, num_kv_heads, head_dim), dtype)
+        w.v = _randn(g, (M, num_kv_heads, head_dim), dtype)
+    return w
+
+
+def window_prefill(seed: int = 4, M: int = 32768, block: int = 128, window: int = 8,
+                   stride: int = 16, num_qo_heads: int = 64, num_kv_heads: int = 8,
+                   head_dim: int = 128, dtype: torch.dtype = torch.float16,
+                   values: bool = True) -> Workload:
+    """Row block i attends to {max(0, i - window) .. i} and {j <= i : j % stride == 0}; causal."""
+    MB = M // block
+    rows = []
+    for i in range(MB):
+        cols = set(range(max(0, i - window), i + 1))
+        cols.update(range(0, i + 1, stride))
+        rows.append(sorted(cols))
+    indptr, indices = _csr_from_rows(rows)
+    w = Workload("window_prefill", indptr, indices, M, M, block, block, num_qo_heads,
+                 num_kv_heads, head_dim, head_dim, True, 1.0 / np.sqrt(head_dim),
+                 q_dtype=dtype, kv_dtype=dtype, o_dtype=dtype)
+    if values:
+        g = torch.Generator().manual_seed(seed)
+        w.q = _randn(g, (M, num_qo_heads, head_dim), dtype)
+        w.k = _randn(g, (M, num_kv_heads, head_dim), dtype)
+        w.v = _randn(g, (M, num_kv_heads, head_dim), dtype)
+    return w
+
+
+def sparse_mla(seed: int = 5, num_tokens: int = 128, num_heads: int = 128,
+               cache_rows: int = 65536, topk: int = 2048, min_ctx: int = 4096,
+               max_ctx: int = 65536, latent: int = 512, rope: int = 64,
+               values: bool = True) -> Workload:
+    """Index-selected sparse MLA decode as BSR with R = C = 1 and one KV head.
+
+    Query token t attends to ``topk`` cache rows drawn without replacement
+    from [0, ctx_t), ctx_t uniform in [min_ctx, max_ctx], kept in drawn
+    order.  The cache is float32 normals quantised with one per-tensor
+    scale s = max|kv| / 448 to OCP fp8 e4m3 (torch.float8_e4m3fn); the
+    dequant scale handed to the kernel is s for both K and V.
+    """
+    rng = np.random.default_rng(seed)
+    D = latent + rope
+    ctx = rng.integers(min_ctx, max_ctx + 1, size=num_tokens)
+    rows = [rng.choice(int(c), size=topk, replace=False) for c in ctx]
+    indptr, indices = _csr_from_rows(rows)
+    w = Workload("sparse_mla", indptr, indices, num_tokens, cache_rows, 1, 1, num_heads, 1,
+                 D, latent, False, 1.0 / np.sqrt(D), q_dtype=torch.bfloat16,
+                 kv_dtype=torch.float8_e4m3fn, o_dtype=torch.bfloat16, v_aliases_k=True,
+                 meta={"ctx_lens": ctx.astype(np.int64)})
+    if values:
+        g = torch.Generator().manual_seed(seed)
+        w.q = _randn(g, (num_tokens, num_heads, D), torch.bfloat16)
+        kv32 = torch.randn(cache_rows, D, generator=g, dtype=torch.float32)
+        s = float(kv32.abs().max()) / 448.0
+        w.k = (kv32 / s).to(torch.float8_e4m3fn)
+        w.v = None
+        w.k_descale = s
+        w.v_descale = s
+    return w
+
+
+def random_bsr(seed: int, M: int, N: int, R: int, C: int, num_qo_heads: int,
+               num_kv_heads: int, head_dim: int = 128, density: float = 0.5,
+               causal: bool = False, partial_lens: bool = False, empty_rows: bool = True,
+               shuffle: bool = True, dtype: torch.dtype = torch.float16,
+               garbage: float = 0.0, values: bool = True) -> Workload:
+    """A small random BSR problem for parity and edge cases.
+
+    ``partial_lens`` draws per-block valid lengths in [1, C];
+    ``garbage`` > 0 overwrites the unused slots of partial blocks with
+    +-garbage (finite) so that masking them is exercised; ``shuffle`` leaves
+    the column indices of a row in random order.
+    """
+    assert N % C == 0
+    rng = np.random.default_rng(seed)
+    MB, NB = -(-M // R), N // C
+    rows = []
+    for i in range(MB):
+        sel = np.nonzero(rng.random(NB) < density)[0]
+        if empty_rows is False and sel.size == 0:
+            sel = np.array([rng.integers(NB)])
+        if shuffle:
+            sel = rng.permutation(sel)
+        rows.append(sel)
+    indptr, indices = _csr_from_rows(rows)
+    lens = rng.integers(1, C + 1, size=NB).astype(np.int32) if partial_lens else None
+    w = Workload("random_bsr", indptr, indices, M, N, R, C, num_qo_heads, num_kv_heads,
+                 head_dim, head_dim, causal, 1.0 / np.sqrt(head_dim), kv_block_lens=lens,
+                 q_dtype=dtype, kv_dtype=dtype, o_dtype=dtype)
+    if values:
+        g = torch.Generator().manual_seed(seed)
+        w.q = _randn(g, (M, num_qo_heads, head_dim), dtype)
+        w.k = _randn(g, (N, num_kv_heads, head_dim), dtype)
+        w.v = _randn(g, (N, num_kv_heads, head_dim), dtype)
+        if lens is not None and garbage > 0:
+            for J in range(NB):
+                if lens[J] < C:
+                    sl = slice(J * C + int(lens[J]), (J + 1) * C)
+                    sign = torch.where(torch.rand(w.k[sl].shape, generator=g) < 0.5, -1.0, 1.0)
+                    w.k[sl] = (sign * garbage).to(dtype)
+                    w.v[sl] = (-sign * garbage).to(dtype)
+    return w
+
+
+WORKLOAD_NAMES = ["worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla"]
+
+
+def by_name(name: str, **kw) -> Workload:
+    return {"worked_example": worked_example, "paged_decode": paged_decode,
+            "bsr_prefill": bsr_prefill, "window_prefill": window_prefill,
+            "sparse_mla": sparse_mla}[name](**kw)
