@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of BSR block-sparse attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one run of the planned attention (attention kernel, plus the LSE
+merge kernel when the plan splits rows) over one batch of synthetic inputs
+already resident in HBM.  Planning (host) and the one-time table upload are
+done before the timed region and reported separately (plan_ms).
+
+Prints ONE JSON line.  For the decode workloads the metric is KV GB/s
+(algorithmic bytes: K and V of every unmasked key once per kv head, plus q,
+o, lse and the index structure); for the block-sparse prefill workloads it
+is TFLOP/s (algorithmic flops: 4 * head_dim * qo heads * unmasked query-key
+pairs).  ``roofline`` is measured live with HIP events around the attention
+kernel alone (bsa_run_phase); ``cpu_baseline`` times the CPU oracle on a
+bounded sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "KV GB/s (decode) & TFLOP/s (sparse prefill), % of MI355X HBM/MFMA peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}
+DECODE = {"paged_decode", "sparse_mla", "worked_example"}
+KERNEL_SOURCES = ["attn_tile.hip", "attn_mla.hip", "merge.hip", "device_common.h", "kernels.h"]
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_attention_bsr_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def unmasked_pairs(w, rows=None):
+    """Unmasked (query row, key) pairs (the same for every head), counted block by block."""
+    import numpy as np
+    lens = w.kv_block_lens
+    off = w.N - w.M
+    row_set = None if rows is None else np.asarray(sorted(rows))
+    total = 0
+    for I in range(len(w.indptr) - 1):
+        r0, r1 = I * w.R, min(w.M, (I + 1) * w.R)
+        rr = np.arange(r0, r1)
+        if row_set is not None:
+            rr = rr[np.isin(rr, row_set)]
+            if rr.size == 0:
+                continue
+        for J in w.indices[w.indptr[I]:w.indptr[I + 1]]:
+            n = w.C if lens is None else int(lens[J])
+            if not w.causal:
+                total += n * rr.size
+            else:
+                allowed = np.clip(rr + off - int(J) * w.C + 1, 0, n)
+                total += int(allowed.sum())
+    return total
+
+
+def algorithmic_work(w, rows=None):
+    """(bytes, flops) the method itself must move / compute for one run (or for `rows` only).
+
+    bytes: K and V of every unmasked key once per (query row, kv head) -- for
+    the decode shapes (R = 1) that is each selected cache row once -- (for
+    the latent MLA cache one 576-value row per key, V being its prefix),
+    plus q, o, lse and the int32 index structure.
+    flops: 2 * (head_dim + head_dim_vo) per unmasked pair and qo head
+    (QK^T and PV).
+    """
+    pairs = unmasked_pairs(w, rows)
+    m = w.M if rows is None else len(rows)
+    e_kv = w.kv_dtype.itemsize
+    if w.v_aliases_k:
+        kv_bytes = pairs * w.num_kv_heads * w.head_dim * e_kv
+    else:
+        kv_bytes = pairs * w.num_kv_heads * (w.head_dim + w.head_dim_vo) * e_kv
+    qo = m * w.num_qo_heads * (w.head_dim * w.q_dtype.itemsize + w.head_dim_vo * w.o_dtype.itemsize + 4)
+    nnz_rows = w.nnz if rows is None else sum(int(w.indptr[r // w.R + 1] - w.indptr[r // w.R]) for r in rows)
+    idx = 4 * (m + 1 + nnz_rows)
+    if w.kv_block_lens is not None:
+        idx += 4 * nnz_rows
+    flops = 2 * pairs * w.num_qo_heads * (w.head_dim + w.head_dim_vo)
+    return kv_bytes + qo + idx, flops
+
+
+def cpu_baseline(w, budget_s: float):
+    """Time the CPU oracle, as it stands, on a bounded sample of query rows of the same workload."""
+    import numpy as np
+    import oracle
+    import torch
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    if w.kv_dtype == torch.float8_e4m3fn:
+        kf = oracle.e4m3fn_decode(w.k.view(torch.uint8).numpy())
+        k = (kf * w.k_descale)[:, None, :]
+        v = (kf[:, :w.head_dim_vo] * w.v_descale)[:, None, :]
+    else:
+        k, v = w.k.double().numpy(), w.v.double().numpy()
+    q = w.q.double().numpy()
+    order = np.random.default_rng(0).permutation(w.M)
+    done, t_used, batch = 0, 0.0, 1
+    while done < w.M and t_used < budget_s:
+        rows = order[done:done + batch].tolist()
+        t0 = time.perf_counter()
+        oracle.bsr_attention(w.indptr, w.indices, w.M, w.N, w.R, w.C, q, k, v, sm_scale=w.sm_scale,
+                             causal=w.causal, kv_block_lens=w.kv_block_lens, rows=rows)
+        t_used += time.perf_counter() - t0
+        done += len(rows)
+        batch = min(batch * 2, 64)
+    b, f = algorithmic_work(w, order[:done].tolist())
+    return {"seconds": t_used, "rows": done, "bytes": b, "flops": f, "cores": threads}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="paged_decode",
+                    choices=["worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla"])
+    ap.add_argument("--kv-splits", type=int, default=None, help="override the workload's split-KV setting")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
+              "the attention shards by kv head or request with no exchange, see DESIGN.md.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    sys.path.insert(0, ROOT)
+    from paged_attention_bsr_amd import Plan
+    from paged_attention_bsr_amd import _lib as L
+    from paged_attention_bsr_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"[bench] device {props.name} CUs={props.multi_processor_count} workload={args.workload}")
+
+    w = W.by_name(args.workload)
+    kv_splits = W.BENCH_KV_SPLITS[args.workload] if args.kv_splits is None else args.kv_splits
+    t0 = time.perf_counter()
+    plan = Plan(w.indptr, w.indices, w.M, w.N, w.R, w.C, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                head_dim_vo=w.head_dim_vo, causal=w.causal, sm_scale=w.sm_scale, kv_splits=kv_splits,
+                kv_block_lens=w.kv_block_lens, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, o_dtype=w.o_dtype,
+                k_descale=w.k_descale, v_descale=w.v_descale, k_token_stride=w.k_token_stride,
+                v_token_stride=w.v_token_stride)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    info = plan.info()
+    q = w.q.to(dev)
+    k = w.k.to(dev)
+    v = None if w.v_aliases_k else w.v.to(dev)
+    out = torch.empty((w.M, w.num_qo_heads, w.head_dim_vo), dtype=w.o_dtype, device=dev)
+    lse = torch.empty((w.M, w.num_qo_heads), dtype=torch.float32, device=dev)
+    ws = plan.workspace(dev)
+    plan.upload(ws)
+    torch.cuda.synchronize()
+    log(f"[bench] plan {plan_ms:.1f} ms: {info}")
+
+    def step(evs=None):
+        if evs is None:
+            plan.run(q, k, v, out=out, lse=lse, workspace=ws)
+            return
+        evs[0].record()
+        plan.run(q, k, v, out=out, lse=lse, workspace=ws, phase=L.BSA_PHASE_ATTENTION)
+        evs[1].record()
+        plan.run(q, k, v, out=out, lse=lse, workspace=ws, phase=L.BSA_PHASE_MERGE)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    attn_ms = [e[0].elapsed_time(e[1]) for e in events]
+    attn_avg_ms = float(np.mean(attn_ms))
+    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step; attention kernel avg {attn_avg_ms:.4f} ms "
+        f"(min {min(attn_ms):.4f}, max {max(attn_ms):.4f})")
+
+    alg_bytes, alg_flops = algorithmic_work(w)
+    dtype = {torch.float16: "f16", torch.bfloat16: "bf16"}[w.q_dtype]
+    if w.kv_dtype == torch.float8_e4m3fn:
+        dtype = "bf16 (fp8 e4m3 KV storage)"
+    decode = args.workload in DECODE
+    if decode:
+        value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+        achieved = alg_bytes / (attn_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS}
+    else:
+        value = alg_flops / (ms_per_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        achieved = alg_flops / (attn_avg_ms * 1e-3) / 1e12
+        peak = MFMA_PEAK_TFLOPS["f16" if w.q_dtype == torch.float16 else "bf16"]
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
+    if args.workload == "sparse_mla":
+        # exact bf16 MFMA arithmetic bounds this shape too; report its MFMA fraction beside HBM
+        mfma_tf = alg_flops / (attn_avg_ms * 1e-3) / 1e12
+        roof["mfma_frac_bf16"] = mfma_tf / MFMA_PEAK_TFLOPS["bf16"]
+    roof["traffic"] = measured_traffic(args.workload, kernel_source_hash())
+    roof["kernel"] = "attn_mla_kernel" if info["kernel"] == L.BSA_KERNEL_MLA else "attn_tile_kernel"
+    roof["alg_bytes_per_launch"] = alg_bytes
+    roof["alg_flops_per_launch"] = alg_flops
+    roof["avg_launch_ms"] = attn_avg_ms
+
+    cpu = None
+    if args.cpu_budget > 0:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s budget)")
+        cb = cpu_baseline(w, args.cpu_budget)
+        if decode:
+            cval = cb["bytes"] / cb["seconds"] / 1e9
+        else:
+            cval = cb["flops"] / cb["seconds"] / 1e12
+        cpu = {"value": cval, "unit": unit, "cores": cb["cores"], "kind": "oracle",
+               "sample": f"{cb['rows']} of {w.M} query rows (all heads), float64 dense-mask oracle, "
+                         f"{cb['seconds']:.1f} s"}
+
+    cfg = {"workload": args.workload, "M": w.M, "N": w.N, "R": w.R, "C": w.C,
+           "num_qo_heads": w.num_qo_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+           "head_dim_vo": w.head_dim_vo, "causal": w.causal, "nnz_blocks": w.nnz, "kv_splits": kv_splits,
+           "tiles": info["num_tiles"], "merges": info["num_merges"], "plan_ms": plan_ms,
+           "alg_bytes": alg_bytes, "alg_flops": alg_flops}
+    line = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": dtype, "data": "synthetic", "config": cfg,
+            "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def measured_traffic(workload: str, src_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(workload)
+    if not ent or ent.get("kernel_source_hash") != src_hash:
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+if __name__ == "__main__":
+    sys.exit(main())

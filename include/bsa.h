@@ -1,0 +1,248 @@
+/*
+ * bsa.h -- block-sparse (BSR) attention over a KV cache on AMD MI355X (gfx950).
+ *
+ * C ABI of libbsa.so.  Plain pointers and sizes only; device pointers are
+ * HIP device addresses on the current device, streams are hipStream_t
+ * passed as void*.
+ *
+ * The operation (flashinfer.sparse, BlockSparseAttentionWrapper: class
+ * description, the worked example and plan()/run() parameters):
+ *   A BSR matrix in the SciPy bsr_matrix convention -- indptr over
+ *   MB = ceil_div(M, R) row blocks, indices of column blocks below
+ *   NB = N / C -- is an attention mask over M query rows and N key rows.
+ *   Query row i attends to key j iff the row block i / R lists a column
+ *   block J with J*C <= j < J*C + len_J (len_J = kv_block_lens[J], or C),
+ *   and, if causal, j <= i + (N - M).  For every qo head h (kv head
+ *   h / (num_qo_heads / num_kv_heads)):
+ *       o[i,h,:]  = sum_j softmax_j(sm_scale * q[i,h,:] . k[j,kvh,:]) v[j,kvh,:]
+ *       lse[i,h]  = ln sum_j exp(sm_scale * q[i,h,:] . k[j,kvh,:])
+ *   over the unmasked keys; a row with no unmasked key gets o = 0 and
+ *   lse = -inf.  Paged batch decode is the case R = 1, C = page size;
+ *   index-selected sparse MLA decode (MATE sparse_mla_fp8_decode) is the
+ *   case R = C = 1, one KV head of 576 = 512 latent + 64 rope values stored
+ *   as fp8 e4m3, V = the first 512 values of each K row.
+ *
+ * Plan / run split (BlockSparseAttentionWrapper.plan notes; MATE decode
+ * "metadata reuse"): bsa_plan* turns the structure into work tiles once,
+ * on the host; bsa_run launches the kernels for one set of q/k/v and may
+ * be called many times per plan.  A plan must not be shared by overlapping
+ * runs on the same workspace.
+ *
+ * Errors: every call returns a bsa_status_t; bsa_last_error() gives the
+ * calling thread's text for the last failure.  Nothing aborts, throws or
+ * prints.  A failed bsa_run launches nothing and writes no output.
+ */
+#ifndef BSA_H_
+#define BSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSA_VERSION_MAJOR 0
+#define BSA_VERSION_MINOR 1
+
+typedef struct bsa_plan_s* bsa_plan_t;
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_ERR_INVALID_ARGUMENT = 1,   /* malformed structure, bad sizes, null/misaligned pointer */
+  BSA_ERR_UNSUPPORTED = 2,        /* valid request this build has no kernel for */
+  BSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  BSA_ERR_HIP = 4,                /* a HIP runtime call or kernel launch failed */
+  BSA_ERR_HOST_ALLOC = 5          /* host memory allocation failed */
+} bsa_status_t;
+
+typedef enum { BSA_F16 = 0, BSA_BF16 = 1, BSA_FP8_E4M3 = 2 } bsa_dtype_t;
+
+/* Kernel family a plan selected (informational). */
+typedef enum {
+  BSA_KERNEL_TILE = 0,    /* MFMA tile kernel: head_dim 128, fp16/bf16, any R, C */
+  BSA_KERNEL_MLA = 1      /* MFMA sparse-MLA kernel: Dqk 576 / Dv 512, bf16 q/o, fp8 e4m3 kv, R = 1 */
+} bsa_kernel_t;
+
+/*
+ * Full plan description.  Fill with bsa_plan_desc_init() first, then set
+ * fields.  All arrays are HOST memory, read only during the call.
+ *
+ *   indptr         int32[MB + 1]; indptr[0] = 0, non-decreasing, indptr[MB] = nnz
+ *   indices        int32[nnz]; column block of each non-zero block, 0 <= J < NB,
+ *                  no duplicate within a row block; any order within a row
+ *   M, N           query rows / key rows; N % C == 0
+ *   R, C           block rows / block columns, >= 1
+ *   num_qo_heads   multiple of num_kv_heads (grouped-query attention)
+ *   head_dim_qk    q/k head dim; head_dim_vo: v/o head dim (0 = head_dim_qk)
+ *   causal         0/1: also mask key j > i + (N - M)
+ *   sm_scale       softmax scale; <= 0 selects 1/sqrt(head_dim_qk)
+ *   kv_splits      1 = no split-KV; k > 1 = at most k contiguous partitions of
+ *                  each row's blocks; 0 = automatic (from the sparsity and
+ *                  num_cus).  Split partials live in the workspace and are
+ *                  LSE-merged by a second kernel.
+ *   kv_block_lens  NULL, or int32[NB] valid tokens per key block, each in [1, C]
+ *   q/kv/o_dtype   storage types.  Supported: all BSA_F16, or all BSA_BF16
+ *                  (head_dim 128); or q/o BSA_BF16 with kv BSA_FP8_E4M3 and
+ *                  head_dim_qk 576 / head_dim_vo 512 / one kv head / R = 1.
+ *   q_descale etc. per-tensor dequant scales: real value = stored * descale
+ *                  (MATE scale folding: the logit scale becomes
+ *                  sm_scale * q_descale * k_descale, the output scale v_descale)
+ *   *_token_stride elements between consecutive tokens; 0 = dense
+ *                  (q: num_qo_heads*head_dim_qk, k: num_kv_heads*head_dim_qk,
+ *                  v: num_kv_heads*head_dim_vo, o: num_qo_heads*head_dim_vo).
+ *                  For the MLA shape v may alias k (v pointer == k pointer,
+ *                  v_token_stride == k_token_stride).
+ *   num_cus        0 = query the current device; > 0 = plan for that many CUs
+ *                  without touching the GPU (host-only planning)
+ */
+typedef struct {
+  const int32_t* indptr;
+  const int32_t* indices;
+  int64_t M, N;
+  int32_t R, C;
+  int32_t num_qo_heads, num_kv_heads;
+  int32_t head_dim_qk, head_dim_vo;
+  int32_t causal;
+  float sm_scale;
+  int32_t kv_splits;
+  const int32_t* kv_block_lens;
+  bsa_dtype_t q_dtype, kv_dtype, o_dtype;
+  float q_descale, k_descale, v_descale;
+  int64_t q_token_stride, k_token_stride, v_token_stride, o_token_stride;
+  int32_t num_cus;
+} bsa_plan_desc_t;
+
+/* Defaults: fp16 everywhere, head_dim_vo = head_dim_qk, non-causal, default
+ * sm_scale, kv_splits = 1, descales 1, dense strides, num_cus from device. */
+void bsa_plan_desc_init(bsa_plan_desc_t* desc);
+
+/* sizeof(bsa_plan_desc_t) as compiled into the library, so that foreign
+ * bindings can check their copy of the struct layout. */
+size_t bsa_plan_desc_sizeof(void);
+
+/* North-star form: fp16 q/k/v/o of shape (M, Hq, D) / (N, Hkv, D) / (N, Hkv, D)
+ * / (M, Hq, D), all blocks full, num_cus from the current device.
+ * sm_scale <= 0 selects 1/sqrt(head_dim).  On success *out_plan owns host
+ * memory only; release it with bsa_plan_destroy. */
+bsa_status_t bsa_plan(const int32_t* indptr, const int32_t* indices, int64_t M, int64_t N,
+                      int32_t R, int32_t C, int32_t num_qo_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t causal, float sm_scale, int32_t kv_splits,
+                      bsa_plan_t* out_plan);
+
+/* Extended form (partial blocks, other dtypes, fp8 scales, strides, CU count). */
+bsa_status_t bsa_plan_ex(const bsa_plan_desc_t* desc, bsa_plan_t* out_plan);
+
+/* Bytes of device workspace bsa_run needs for this plan (multiple of 256).
+ * The workspace holds the plan's tables (uploaded once) and the split-KV
+ * partials.  Returns 0 for a NULL plan. */
+size_t bsa_workspace_size(bsa_plan_t plan);
+
+/* Copy the plan's tables into `workspace` (device memory of at least
+ * bsa_workspace_size bytes, 256-byte aligned) on `stream`.  bsa_run does this
+ * by itself the first time it sees a workspace that does not hold this
+ * plan's tables, so calling it is only needed to keep the copy out of a
+ * later run (for example before capturing runs in a HIP graph).  The
+ * library remembers, per device and workspace address, which plan's tables
+ * it last wrote there; if anything else writes that memory afterwards, call
+ * bsa_upload again. */
+bsa_status_t bsa_upload(bsa_plan_t plan, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Run the planned attention on `stream` (hipStream_t; NULL = default stream).
+ *   q    device, q_dtype,  [M][q_token_stride] with head h at h*head_dim_qk
+ *   k    device, kv_dtype, [N][k_token_stride] with kv head h at h*head_dim_qk
+ *   v    device, kv_dtype, [N][v_token_stride] with kv head h at h*head_dim_vo
+ *   o    device, o_dtype,  [M][o_token_stride] with head h at h*head_dim_vo (written)
+ *   lse  device float32 [M][num_qo_heads] natural-log LSE (written), or NULL
+ *   workspace  device, >= bsa_workspace_size(plan) bytes, 256-byte aligned
+ * q, k, v, o must be 16-byte aligned and must not overlap the workspace.
+ * Every one of the M * num_qo_heads output rows is written; rows with no
+ * unmasked key get o = 0 and lse = -inf.  The call only enqueues work on
+ * `stream` (after the one-time table upload described at bsa_upload): it
+ * neither synchronises nor allocates device memory.
+ */
+bsa_status_t bsa_run(bsa_plan_t plan, const void* q, const void* k, const void* v, void* o,
+                     float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The two phases of bsa_run, for callers that schedule them separately (or
+ * time them separately).  phase = BSA_PHASE_ATTENTION launches the attention
+ * kernel only (tiles without a split write o/lse, split tiles write their
+ * partials into the workspace); BSA_PHASE_MERGE launches the LSE merge of the
+ * split partials only (it must follow an attention phase of the same plan on
+ * the same workspace, in stream order); BSA_PHASE_ALL is bsa_run.  Arguments
+ * and errors as for bsa_run.
+ */
+#define BSA_PHASE_ATTENTION 1
+#define BSA_PHASE_MERGE 2
+#define BSA_PHASE_ALL 3
+bsa_status_t bsa_run_phase(bsa_plan_t plan, int32_t phase, const void* q, const void* k, const void* v,
+                           void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * LSE merge of attention states (flashinfer.cascade merge_states): for each
+ * of seq_len * num_heads rows, combine num_states partial results computed
+ * over disjoint key sets:
+ *     s_out = ln sum_k exp(s_k),   v_out = sum_k exp(s_k - s_out) v_k
+ * States with s_k = -inf have weight 0; if all are -inf, v_out = 0 and
+ * s_out = -inf.
+ *   v      device float32 [seq_len][num_states][num_heads][head_dim]
+ *   s      device float32 [seq_len][num_states][num_heads]   (natural log)
+ *   v_out  device, out_dtype (BSA_F16, BSA_BF16 or float32 via BSA_FP32_OUT)
+ *          [seq_len][num_heads][head_dim]
+ *   s_out  device float32 [seq_len][num_heads], or NULL
+ * head_dim must be a multiple of 4; pointers 16-byte aligned.
+ */
+#define BSA_FP32_OUT 3
+bsa_status_t bsa_merge_states(const float* v, const float* s, void* v_out, float* s_out,
+                              int64_t seq_len, int32_t num_states, int32_t num_heads,
+                              int32_t head_dim, int32_t out_dtype, void* stream);
+
+/* Plan statistics, and the tables themselves, for inspection and tests. */
+typedef struct {
+  int32_t kernel;          /* bsa_kernel_t */
+  int32_t tile_rows;       /* query rows (token, head pairs) per work tile */
+  int32_t key_tile;        /* keys per inner step */
+  int32_t num_tiles;
+  int32_t num_merges;      /* row tiles split over > 1 partition */
+  int32_t num_cols;        /* entries of the column table */
+  int32_t max_splits;
+  int32_t num_cus;
+  int64_t table_bytes;     /* int tables at the start of the workspace */
+  int64_t partial_bytes;   /* split partials after the tables */
+  int64_t workspace_bytes;
+  int64_t valid_pairs;     /* block-level key positions x query rows, summed over tiles */
+} bsa_plan_info_t;
+
+bsa_status_t bsa_plan_info(bsa_plan_t plan, bsa_plan_info_t* info);
+
+/*
+ * Copy the plan's tables to caller-owned host arrays sized from
+ * bsa_plan_info (any pointer may be NULL to skip it):
+ *   tiles   int32[num_tiles][8]  = {row_block, kv_head, row0, nrows,
+ *                                   col_begin, col_end, partial_offset, key_count}
+ *           in launch order; row r of a tile (row0 <= r < row0 + nrows) is
+ *           query token row_block*R + r / g and qo head kv_head*g + r % g
+ *           (g = num_qo_heads / num_kv_heads); its keys are the blocks
+ *           cols[col_begin .. col_end); partial_offset is -1 when the tile
+ *           writes o/lse directly, else the float offset of its partial in
+ *           the workspace's partial region.
+ *   merges  int32[num_merges][8] = {row_block, kv_head, row0, nrows,
+ *                                   first_partial, num_splits, partial_stride, 0}
+ *   cols    int32[num_cols]: per row block, its column blocks in ascending
+ *           order, without blocks that the causal mask removes entirely.
+ */
+bsa_status_t bsa_plan_export(bsa_plan_t plan, int32_t* tiles, int32_t* merges, int32_t* cols);
+
+void bsa_plan_destroy(bsa_plan_t plan);
+
+/* Text of the calling thread's last error ("" if none).  Valid until the
+ * thread's next bsa_* call. */
+const char* bsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H_ */

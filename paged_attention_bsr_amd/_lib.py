@@ -1,0 +1,125 @@
+"""ctypes declarations of libbsa.so (include/bsa.h).  Loading fails loudly if
+the library has not been built; there is no fallback implementation."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsa.so")
+
+BSA_OK = 0
+BSA_ERR_INVALID_ARGUMENT = 1
+BSA_ERR_UNSUPPORTED = 2
+BSA_ERR_WORKSPACE_TOO_SMALL = 3
+BSA_ERR_HIP = 4
+BSA_ERR_HOST_ALLOC = 5
+
+BSA_F16, BSA_BF16, BSA_FP8_E4M3, BSA_FP32_OUT = 0, 1, 2, 3
+BSA_KERNEL_TILE, BSA_KERNEL_MLA = 0, 1
+BSA_PHASE_ATTENTION, BSA_PHASE_MERGE, BSA_PHASE_ALL = 1, 2, 3
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+
+class PlanDesc(ctypes.Structure):
+    _fields_ = [
+        ("indptr", _i32p),
+        ("indices", _i32p),
+        ("M", ctypes.c_int64),
+        ("N", ctypes.c_int64),
+        ("R", ctypes.c_int32),
+        ("C", ctypes.c_int32),
+        ("num_qo_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim_qk", ctypes.c_int32),
+        ("head_dim_vo", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("sm_scale", ctypes.c_float),
+        ("kv_splits", ctypes.c_int32),
+        ("kv_block_lens", _i32p),
+        ("q_dtype", ctypes.c_int),
+        ("kv_dtype", ctypes.c_int),
+        ("o_dtype", ctypes.c_int),
+        ("q_descale", ctypes.c_float),
+        ("k_descale", ctypes.c_float),
+        ("v_descale", ctypes.c_float),
+        ("q_token_stride", ctypes.c_int64),
+        ("k_token_stride", ctypes.c_int64),
+        ("v_token_stride", ctypes.c_int64),
+        ("o_token_stride", ctypes.c_int64),
+        ("num_cus", ctypes.c_int32),
+    ]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("kernel", ctypes.c_int32),
+        ("tile_rows", ctypes.c_int32),
+        ("key_tile", ctypes.c_int32),
+        ("num_tiles", ctypes.c_int32),
+        ("num_merges", ctypes.c_int32),
+        ("num_cols", ctypes.c_int32),
+        ("max_splits", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32),
+        ("table_bytes", ctypes.c_int64),
+        ("partial_bytes", ctypes.c_int64),
+        ("workspace_bytes", ctypes.c_int64),
+        ("valid_pairs", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libbsa.so, with argument/return types declared."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m paged_attention_bsr_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, st, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    L.bsa_plan_desc_init.argtypes = [ctypes.POINTER(PlanDesc)]
+    L.bsa_plan_desc_init.restype = None
+    L.bsa_plan_desc_sizeof.argtypes = []
+    L.bsa_plan_desc_sizeof.restype = sz
+    L.bsa_plan.argtypes = [_i32p, _i32p, i64, i64, i32, i32, i32, i32, i32, i32, f32, i32, ctypes.POINTER(vp)]
+    L.bsa_plan.restype = st
+    L.bsa_plan_ex.argtypes = [ctypes.POINTER(PlanDesc), ctypes.POINTER(vp)]
+    L.bsa_plan_ex.restype = st
+    L.bsa_workspace_size.argtypes = [vp]
+    L.bsa_workspace_size.restype = sz
+    L.bsa_upload.argtypes = [vp, vp, sz, vp]
+    L.bsa_upload.restype = st
+    L.bsa_run.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.bsa_run.restype = st
+    L.bsa_run_phase.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.bsa_run_phase.restype = st
+    L.bsa_merge_states.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, vp]
+    L.bsa_merge_states.restype = st
+    L.bsa_plan_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+    L.bsa_plan_info.restype = st
+    L.bsa_plan_export.argtypes = [vp, _i32p, _i32p, _i32p]
+    L.bsa_plan_export.restype = st
+    L.bsa_plan_destroy.argtypes = [vp]
+    L.bsa_plan_destroy.restype = None
+    L.bsa_last_error.argtypes = []
+    L.bsa_last_error.restype = ctypes.c_char_p
+    if L.bsa_plan_desc_sizeof() != ctypes.sizeof(PlanDesc):
+        raise RuntimeError("bsa_plan_desc_t layout mismatch between bsa.h and the Python binding")
+    _lib = L
+    return L
+
+
+class BsaError(RuntimeError):
+    """A libbsa call returned a status other than BSA_OK."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"bsa status {status}: {message}")
+        self.status = status
+
+
+def check(status: int) -> None:
+    if status != BSA_OK:
+        raise BsaError(status, lib().bsa_last_error().decode(errors="replace"))

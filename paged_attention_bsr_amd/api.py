@@ -1,0 +1,178 @@
+"""Python binding of libbsa: plan once, run many times.
+
+Argument marshalling only -- every step of the attention runs in the HIP
+library.  PyTorch supplies device memory and the current stream.  The call
+names follow the C ABI (bsa_plan / bsa_run) and, for the arguments, the
+flashinfer.sparse BlockSparseAttentionWrapper plan()/run() parameters.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+_DTYPE_CODES = {torch.float16: L.BSA_F16, torch.bfloat16: L.BSA_BF16, torch.float8_e4m3fn: L.BSA_FP8_E4M3}
+
+
+def _i32(a) -> np.ndarray:
+    if isinstance(a, torch.Tensor):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+class Plan:
+    """A planned BSR attention problem (bsa_plan_ex).
+
+    indptr / indices / kv_block_lens are host arrays (numpy or CPU tensors).
+    ``kv_splits``: 1 = none, k = at most k partitions per row tile, 0 or
+    "auto" = automatic.  ``num_cus`` = 0 asks the current device.
+    """
+
+    def __init__(self, indptr, indices, M: int, N: int, R: int, C: int, num_qo_heads: int,
+                 num_kv_heads: int, head_dim: int, *, head_dim_vo: Optional[int] = None,
+                 causal: bool = False, sm_scale: Optional[float] = None, kv_splits=1,
+                 kv_block_lens=None, q_dtype: torch.dtype = torch.float16,
+                 kv_dtype: Optional[torch.dtype] = None, o_dtype: Optional[torch.dtype] = None,
+                 q_descale: float = 1.0, k_descale: float = 1.0, v_descale: float = 1.0,
+                 q_token_stride: int = 0, k_token_stride: int = 0, v_token_stride: int = 0,
+                 o_token_stride: int = 0, num_cus: int = 0):
+        lib = L.lib()
+        self._handle = ctypes.c_void_p()
+        self._indptr = _i32(indptr)
+        self._indices = _i32(indices)
+        self._lens = None if kv_block_lens is None else _i32(kv_block_lens)
+        kv_dtype = q_dtype if kv_dtype is None else kv_dtype
+        o_dtype = q_dtype if o_dtype is None else o_dtype
+        for t in (q_dtype, kv_dtype, o_dtype):
+            if t not in _DTYPE_CODES:
+                raise ValueError(f"unsupported dtype {t}")
+        d = L.PlanDesc()
+        lib.bsa_plan_desc_init(ctypes.byref(d))
+        d.indptr = _ptr(self._indptr)
+        d.indices = _ptr(self._indices) if self._indices.size else None
+        d.M, d.N, d.R, d.C = int(M), int(N), int(R), int(C)
+        d.num_qo_heads, d.num_kv_heads = int(num_qo_heads), int(num_kv_heads)
+        d.head_dim_qk = int(head_dim)
+        d.head_dim_vo = int(head_dim if head_dim_vo is None else head_dim_vo)
+        d.causal = int(bool(causal))
+        d.sm_scale = float(sm_scale) if sm_scale is not None else 0.0
+        d.kv_splits = 0 if kv_splits == "auto" else (1 if kv_splits is None else int(kv_splits))
+        d.kv_block_lens = _ptr(self._lens) if self._lens is not None else None
+        d.q_dtype, d.kv_dtype, d.o_dtype = _DTYPE_CODES[q_dtype], _DTYPE_CODES[kv_dtype], _DTYPE_CODES[o_dtype]
+        d.q_descale, d.k_descale, d.v_descale = float(q_descale), float(k_descale), float(v_descale)
+        d.q_token_stride, d.k_token_stride = int(q_token_stride), int(k_token_stride)
+        d.v_token_stride, d.o_token_stride = int(v_token_stride), int(o_token_stride)
+        d.num_cus = int(num_cus)
+        L.check(lib.bsa_plan_ex(ctypes.byref(d), ctypes.byref(self._handle)))
+        self.M, self.N, self.R, self.C = int(M), int(N), int(R), int(C)
+        self.num_qo_heads, self.num_kv_heads = int(num_qo_heads), int(num_kv_heads)
+        self.head_dim, self.head_dim_vo = int(head_dim), int(d.head_dim_vo)
+        self.q_dtype, self.kv_dtype, self.o_dtype = q_dtype, kv_dtype, o_dtype
+        self.k_token_stride = int(k_token_stride) or self.num_kv_heads * self.head_dim
+        self.v_token_stride = int(v_token_stride) or self.num_kv_heads * self.head_dim_vo
+        self._workspace: Optional[torch.Tensor] = None
+
+    # ------------------------------------------------------------------ info
+    def info(self) -> dict:
+        inf = L.PlanInfo()
+        L.check(L.lib().bsa_plan_info(self._handle, ctypes.byref(inf)))
+        return {name: getattr(inf, name) for name, _ in inf._fields_}
+
+    @property
+    def workspace_size(self) -> int:
+        return int(L.lib().bsa_workspace_size(self._handle))
+
+    def tables(self) -> dict:
+        """The planner's tables (tiles (T, 8), merges (S, 8), cols) as int32 numpy arrays."""
+        inf = self.info()
+        tiles = np.zeros((inf["num_tiles"], 8), np.int32)
+        merges = np.zeros((inf["num_merges"], 8), np.int32)
+        cols = np.zeros(inf["num_cols"], np.int32)
+        L.check(L.lib().bsa_plan_export(self._handle, _ptr(tiles), _ptr(merges), _ptr(cols)))
+        return {"tiles": tiles, "merges": merges, "cols": cols}
+
+    # ------------------------------------------------------------------ run
+    def workspace(self, device=None) -> torch.Tensor:
+        """A device workspace owned by this plan (kept alive with it)."""
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        ws = self._workspace
+        if ws is None or ws.device != dev or ws.numel() < self.workspace_size:
+            self._workspace = torch.empty(max(self.workspace_size, 256), dtype=torch.uint8, device=dev)
+        return self._workspace
+
+    def upload(self, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+        ws = self.workspace() if workspace is None else workspace
+        st = torch.cuda.current_stream(ws.device).cuda_stream if stream is None else stream
+        L.check(L.lib().bsa_upload(self._handle, ws.data_ptr(), ws.numel() * ws.element_size(), st))
+
+    def run(self, q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+            return_lse: bool = True, workspace: Optional[torch.Tensor] = None, stream=None,
+            phase: int = L.BSA_PHASE_ALL):
+        """o (M, Hq, Dv) and, if requested, lse (M, Hq) float32.  v=None aliases k (MLA).
+
+        ``phase`` selects bsa_run_phase's attention-only / merge-only halves."""
+        if v is None:
+            v = k
+        for name, t, dt in (("q", q, self.q_dtype), ("k", k, self.kv_dtype), ("v", v, self.kv_dtype)):
+            if not t.is_cuda:
+                raise ValueError(f"{name} must be a device tensor")
+            if t.dtype != dt:
+                raise ValueError(f"{name} dtype {t.dtype} does not match the plan ({dt})")
+        if q.shape != (self.M, self.num_qo_heads, self.head_dim) or not q.is_contiguous():
+            raise ValueError(f"q must be a contiguous ({self.M}, {self.num_qo_heads}, {self.head_dim}) tensor")
+        if k.shape[0] != self.N or v.shape[0] != self.N:
+            raise ValueError(f"k and v need {self.N} rows")
+        if k.stride(-1) != 1 or v.stride(-1) != 1 or k.stride(0) != self.k_token_stride or \
+                v.stride(0) != self.v_token_stride:
+            raise ValueError(f"k/v token strides must be {self.k_token_stride}/{self.v_token_stride} "
+                             "elements with a contiguous last dimension")
+        if out is None:
+            out = torch.empty((self.M, self.num_qo_heads, self.head_dim_vo), dtype=self.o_dtype, device=q.device)
+        elif out.shape != (self.M, self.num_qo_heads, self.head_dim_vo) or out.dtype != self.o_dtype or not out.is_contiguous():
+            raise ValueError("out has the wrong shape, dtype or layout")
+        if lse is None and return_lse:
+            lse = torch.empty((self.M, self.num_qo_heads), dtype=torch.float32, device=q.device)
+        ws = self.workspace(q.device) if workspace is None else workspace
+        st = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+        L.check(L.lib().bsa_run_phase(self._handle, int(phase), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                      out.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                      ws.data_ptr(), ws.numel() * ws.element_size(), st))
+        return (out, lse) if return_lse else out
+
+    def __del__(self):
+        h = getattr(self, "_handle", None)
+        if h is not None and h.value:
+            try:
+                L.lib().bsa_plan_destroy(h)
+            except Exception:  # interpreter shutdown
+                pass
+            self._handle = None
+
+
+def merge_states(v: torch.Tensor, s: torch.Tensor, out_dtype: torch.dtype = torch.float32, stream=None):
+    """LSE merge of attention states (bsa_merge_states).
+
+    v: float32 (seq_len, num_states, num_heads, head_dim), s: float32
+    (seq_len, num_states, num_heads).  Returns (v_merged, s_merged).
+    """
+    if v.dtype != torch.float32 or s.dtype != torch.float32 or not v.is_contiguous() or not s.is_contiguous():
+        raise ValueError("v and s must be contiguous float32 device tensors")
+    seq, ns, heads, dim = v.shape
+    if s.shape != (seq, ns, heads):
+        raise ValueError("s must have shape (seq_len, num_states, num_heads)")
+    code = {torch.float16: L.BSA_F16, torch.bfloat16: L.BSA_BF16, torch.float32: L.BSA_FP32_OUT}[out_dtype]
+    v_out = torch.empty((seq, heads, dim), dtype=out_dtype, device=v.device)
+    s_out = torch.empty((seq, heads), dtype=torch.float32, device=v.device)
+    st = torch.cuda.current_stream(v.device).cuda_stream if stream is None else stream
+    L.check(L.lib().bsa_merge_states(v.data_ptr(), s.data_ptr(), v_out.data_ptr(), s_out.data_ptr(),
+                                     seq, ns, heads, dim, code, st))
+    return v_out, s_out

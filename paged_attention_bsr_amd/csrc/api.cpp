@@ -1,0 +1,307 @@
+// C ABI of libbsa.so: validation, plan lifetime, workspace tables, launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <string>
+#include <utility>
+
+#include "bsa.h"
+#include "kernels.h"
+#include "planner.h"
+
+struct bsa_plan_s {
+  bsa::Plan p;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+bsa_status_t set_err(bsa_status_t st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+// Which plan's tables each (device, workspace address) currently holds.
+std::mutex g_reg_mu;
+std::map<std::pair<int, uintptr_t>, uint64_t> g_registry;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elt_bytes(bsa_dtype_t t) { return t == BSA_FP8_E4M3 ? 1 : 2; }
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return an && bn && x < y + bn && y < x + an;
+}
+
+bsa_status_t hip_fail(hipError_t e, const char* what) {
+  return set_err(BSA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bsa_status_t do_upload(const bsa::Plan& P, void* ws, hipStream_t st) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  e = hipMemcpyAsync(ws, P.table_blob.data(), static_cast<size_t>(P.table_bytes), hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "table upload");
+  std::lock_guard<std::mutex> lk(g_reg_mu);
+  g_registry[{dev, reinterpret_cast<uintptr_t>(ws)}] = P.id;
+  return BSA_OK;
+}
+
+bool holds_tables(const bsa::Plan& P, void* ws) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> lk(g_reg_mu);
+  auto it = g_registry.find({dev, reinterpret_cast<uintptr_t>(ws)});
+  return it != g_registry.end() && it->second == P.id;
+}
+
+}  // namespace
+
+extern "C" {
+
+void bsa_plan_desc_init(bsa_plan_desc_t* d) {
+  if (!d) return;
+  std::memset(d, 0, sizeof(*d));
+  d->R = 1;
+  d->C = 1;
+  d->num_qo_heads = 1;
+  d->num_kv_heads = 1;
+  d->head_dim_qk = 128;
+  d->head_dim_vo = 0;
+  d->sm_scale = 0.f;
+  d->kv_splits = 1;
+  d->q_dtype = d->kv_dtype = d->o_dtype = BSA_F16;
+  d->q_descale = d->k_descale = d->v_descale = 1.f;
+}
+
+size_t bsa_plan_desc_sizeof(void) { return sizeof(bsa_plan_desc_t); }
+
+bsa_status_t bsa_plan_ex(const bsa_plan_desc_t* desc, bsa_plan_t* out_plan) {
+  g_err.clear();
+  if (!desc || !out_plan) return set_err(BSA_ERR_INVALID_ARGUMENT, "desc and out_plan must be non-NULL");
+  *out_plan = nullptr;
+  bsa_plan_desc_t d = *desc;
+  if (d.head_dim_vo == 0) d.head_dim_vo = d.head_dim_qk;
+  if (d.q_token_stride == 0) d.q_token_stride = static_cast<int64_t>(d.num_qo_heads) * d.head_dim_qk;
+  if (d.k_token_stride == 0) d.k_token_stride = static_cast<int64_t>(d.num_kv_heads) * d.head_dim_qk;
+  if (d.v_token_stride == 0) d.v_token_stride = static_cast<int64_t>(d.num_kv_heads) * d.head_dim_vo;
+  if (d.o_token_stride == 0) d.o_token_stride = static_cast<int64_t>(d.num_qo_heads) * d.head_dim_vo;
+  if (d.q_token_stride < static_cast<int64_t>(d.num_qo_heads) * d.head_dim_qk ||
+      d.k_token_stride < static_cast<int64_t>(d.num_kv_heads) * d.head_dim_qk ||
+      d.v_token_stride < static_cast<int64_t>(d.num_kv_heads) * d.head_dim_vo ||
+      d.o_token_stride < static_cast<int64_t>(d.num_qo_heads) * d.head_dim_vo)
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "token strides must cover all heads of a token");
+  const int vec = 16 / elt_bytes(d.kv_dtype);
+  if (d.k_token_stride % vec || d.v_token_stride % vec || d.q_token_stride % 8 || d.o_token_stride % 8)
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "token strides must keep every row 16-byte aligned");
+  int32_t cus = d.num_cus;
+  if (cus == 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "querying the CU count (pass num_cus > 0 to plan without a GPU)");
+  }
+  bsa_plan_s* plan = nullptr;
+  try {
+    plan = new bsa_plan_s();
+    std::string err;
+    const bsa_status_t st = bsa::build_plan(d, cus, plan->p, err);
+    if (st != BSA_OK) {
+      delete plan;
+      return set_err(st, err);
+    }
+  } catch (const std::bad_alloc&) {
+    delete plan;
+    return set_err(BSA_ERR_HOST_ALLOC, "host allocation failed while planning");
+  }
+  *out_plan = plan;
+  return BSA_OK;
+}
+
+bsa_status_t bsa_plan(const int32_t* indptr, const int32_t* indices, int64_t M, int64_t N, int32_t R,
+                      int32_t C, int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t causal, float sm_scale, int32_t kv_splits, bsa_plan_t* out_plan) {
+  bsa_plan_desc_t d;
+  bsa_plan_desc_init(&d);
+  d.indptr = indptr;
+  d.indices = indices;
+  d.M = M;
+  d.N = N;
+  d.R = R;
+  d.C = C;
+  d.num_qo_heads = num_qo_heads;
+  d.num_kv_heads = num_kv_heads;
+  d.head_dim_qk = head_dim;
+  d.head_dim_vo = head_dim;
+  d.causal = causal;
+  d.sm_scale = sm_scale;
+  d.kv_splits = kv_splits;
+  return bsa_plan_ex(&d, out_plan);
+}
+
+size_t bsa_workspace_size(bsa_plan_t plan) {
+  return plan ? static_cast<size_t>(plan->p.workspace_bytes) : 0;
+}
+
+bsa_status_t bsa_upload(bsa_plan_t plan, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!plan || !workspace) return set_err(BSA_ERR_INVALID_ARGUMENT, "plan and workspace must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (workspace_bytes < static_cast<size_t>(plan->p.workspace_bytes))
+    return set_err(BSA_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than bsa_workspace_size(plan)");
+  return do_upload(plan->p, workspace, static_cast<hipStream_t>(stream));
+}
+
+bsa_status_t bsa_run(bsa_plan_t plan, const void* q, const void* k, const void* v, void* o, float* lse,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  return bsa_run_phase(plan, BSA_PHASE_ALL, q, k, v, o, lse, workspace, workspace_bytes, stream);
+}
+
+bsa_status_t bsa_run_phase(bsa_plan_t plan, int32_t phase, const void* q, const void* k, const void* v, void* o,
+                           float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  if (!plan) return set_err(BSA_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (phase < BSA_PHASE_ATTENTION || phase > BSA_PHASE_ALL)
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "phase must be BSA_PHASE_ATTENTION, BSA_PHASE_MERGE or BSA_PHASE_ALL");
+  const bsa::Plan& P = plan->p;
+  const bsa_plan_desc_t& d = P.d;
+  if (!q || !k || !v || !o || !workspace)
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "q, k, v, o and workspace must be non-NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "q, k, v and o must be 16-byte aligned");
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "lse must be 4-byte aligned");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (workspace_bytes < static_cast<size_t>(P.workspace_bytes))
+    return set_err(BSA_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than bsa_workspace_size(plan)");
+  const size_t o_bytes = static_cast<size_t>(d.M) * d.o_token_stride * elt_bytes(d.o_dtype);
+  const size_t lse_bytes = lse ? static_cast<size_t>(d.M) * d.num_qo_heads * 4 : 0;
+  if (overlaps(o, o_bytes, workspace, P.workspace_bytes) || overlaps(lse, lse_bytes, workspace, P.workspace_bytes))
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "o and lse must not overlap the workspace");
+  if (overlaps(o, o_bytes, q, static_cast<size_t>(d.M) * d.q_token_stride * elt_bytes(d.q_dtype)))
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "o must not overlap q");
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!holds_tables(P, workspace)) {
+    const bsa_status_t s = do_upload(P, workspace, st);
+    if (s != BSA_OK) return s;
+  }
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  bsa::AttnArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.tiles = reinterpret_cast<const int32_t*>(ws + P.off_tiles);
+  a.cols = reinterpret_cast<const int32_t*>(ws + P.off_cols);
+  a.lens = P.lens.empty() ? nullptr : reinterpret_cast<const int32_t*>(ws + P.off_lens);
+  a.part = reinterpret_cast<float*>(ws + P.table_bytes);
+  a.q_stride = d.q_token_stride;
+  a.k_stride = d.k_token_stride;
+  a.v_stride = d.v_token_stride;
+  a.o_stride = d.o_token_stride;
+  a.R = d.R;
+  a.C = d.C;
+  a.group = P.group;
+  a.num_qo_heads = d.num_qo_heads;
+  a.causal_off = static_cast<int32_t>(d.N - d.M);
+  a.scale_log2 = static_cast<float>(static_cast<double>(P.sm_scale) * d.q_descale * d.k_descale * 1.4426950408889634);
+  a.out_scale = d.v_descale;
+  a.num_tiles = static_cast<int32_t>(P.tiles.size() / bsa::kTileInts);
+
+  hipError_t e;
+  if (phase & BSA_PHASE_ATTENTION) {
+    if (P.kernel == BSA_KERNEL_MLA) e = bsa::launch_attn_mla(a, d.causal != 0, a.lens != nullptr, st);
+    else e = bsa::launch_attn_tile(a, d.q_dtype == BSA_BF16, P.tile_rows, d.causal != 0, a.lens != nullptr, st);
+    if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
+  }
+  if (!(phase & BSA_PHASE_MERGE)) return BSA_OK;
+
+  bsa::MergeArgs m{};
+  m.merges = reinterpret_cast<const int32_t*>(ws + P.off_merges);
+  m.part = a.part;
+  m.o = o;
+  m.lse = lse;
+  m.o_stride = d.o_token_stride;
+  m.R = d.R;
+  m.group = P.group;
+  m.num_qo_heads = d.num_qo_heads;
+  m.dv = d.head_dim_vo;
+  m.num_merges = static_cast<int32_t>(P.merges.size() / bsa::kMergeInts);
+  e = bsa::launch_merge(m, d.o_dtype == BSA_BF16 ? 1 : 0, st);
+  if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  return BSA_OK;
+}
+
+bsa_status_t bsa_merge_states(const float* v, const float* s, void* v_out, float* s_out, int64_t seq_len,
+                              int32_t num_states, int32_t num_heads, int32_t head_dim, int32_t out_dtype,
+                              void* stream) {
+  g_err.clear();
+  if (seq_len < 0 || num_states < 1 || num_heads < 1 || head_dim < 4 || head_dim % 4)
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "need seq_len >= 0, num_states >= 1, num_heads >= 1, head_dim % 4 == 0");
+  if (out_dtype != BSA_F16 && out_dtype != BSA_BF16 && out_dtype != BSA_FP32_OUT)
+    return set_err(BSA_ERR_UNSUPPORTED, "out_dtype must be BSA_F16, BSA_BF16 or BSA_FP32_OUT");
+  if (seq_len == 0) return BSA_OK;
+  if (!v || !s || !v_out) return set_err(BSA_ERR_INVALID_ARGUMENT, "v, s and v_out must be non-NULL");
+  if (!aligned16(v) || !aligned16(v_out)) return set_err(BSA_ERR_INVALID_ARGUMENT, "v and v_out must be 16-byte aligned");
+  const hipError_t e = bsa::launch_merge_states(v, s, v_out, s_out, seq_len, num_states, num_heads, head_dim,
+                                                out_dtype == BSA_FP32_OUT ? 2 : out_dtype,
+                                                static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "merge_states launch");
+  return BSA_OK;
+}
+
+bsa_status_t bsa_plan_info(bsa_plan_t plan, bsa_plan_info_t* info) {
+  g_err.clear();
+  if (!plan || !info) return set_err(BSA_ERR_INVALID_ARGUMENT, "plan and info must be non-NULL");
+  const bsa::Plan& P = plan->p;
+  info->kernel = P.kernel;
+  info->tile_rows = P.tile_rows;
+  info->key_tile = P.key_tile;
+  info->num_tiles = static_cast<int32_t>(P.tiles.size() / bsa::kTileInts);
+  info->num_merges = static_cast<int32_t>(P.merges.size() / bsa::kMergeInts);
+  info->num_cols = static_cast<int32_t>(P.cols.size());
+  info->max_splits = P.max_splits;
+  info->num_cus = P.num_cus;
+  info->table_bytes = P.table_bytes;
+  info->partial_bytes = P.partial_bytes;
+  info->workspace_bytes = P.workspace_bytes;
+  info->valid_pairs = P.valid_pairs;
+  return BSA_OK;
+}
+
+bsa_status_t bsa_plan_export(bsa_plan_t plan, int32_t* tiles, int32_t* merges, int32_t* cols) {
+  g_err.clear();
+  if (!plan) return set_err(BSA_ERR_INVALID_ARGUMENT, "plan is NULL");
+  const bsa::Plan& P = plan->p;
+  if (tiles && !P.tiles.empty()) std::memcpy(tiles, P.tiles.data(), P.tiles.size() * 4);
+  if (merges && !P.merges.empty()) std::memcpy(merges, P.merges.data(), P.merges.size() * 4);
+  if (cols && !P.cols.empty()) std::memcpy(cols, P.cols.data(), P.cols.size() * 4);
+  return BSA_OK;
+}
+
+void bsa_plan_destroy(bsa_plan_t plan) {
+  if (!plan) return;
+  {
+    std::lock_guard<std::mutex> lk(g_reg_mu);
+    for (auto it = g_registry.begin(); it != g_registry.end();) {
+      if (it->second == plan->p.id) it = g_registry.erase(it);
+      else ++it;
+    }
+  }
+  delete plan;
+}
+
+const char* bsa_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,304 @@
+// Sparse-MLA attention kernel on gfx950: BSR with R = 1, one shared latent
+// KV head stored as OCP fp8 e4m3 rows of 576 values (512 latent + 64 rope),
+// V = the first 512 values of each row, bf16 queries and outputs
+// (MATE sparse_mla_fp8_decode / FlashInfer MLA decode conventions: 576-wide
+// query and cache rows, indices shared by all heads, bf16 out, fp32 lse;
+// per-tensor scales folded as bmm1 = sm_scale * q_descale * k_descale and
+// bmm2 = v_descale).
+//
+// One workgroup = one planner tile = 16 * NW heads of one query token.  The
+// heads are the MFMA row dimension, so every gathered cache row is used by
+// all heads of the tile.  Per key tile of 32 keys:
+//   * the workgroup gathers the 32 selected fp8 rows with 16-byte loads,
+//     widens them exactly to bf16 (every e4m3 value is a bf16 value; the
+//     dequant scale is applied to the logits and the output instead), and
+//     stores K row-major (chunk-swizzled, bf16) and V transposed (fp16) into LDS; two
+//     buffers let the next tile's loads overlap this tile's math;
+//   * each wave computes S^T = K Q^T for its 16 heads with
+//     v_mfma_f32_16x16x32_bf16 (Q^T resident in registers), runs the
+//     online softmax in the log2 domain, and accumulates O^T += V^T P^T with
+//     v_mfma_f32_16x16x32_f16: V is held as fp16 (exact for e4m3 values), so
+//     P keeps fp16's 11-bit precision instead of bf16's 8 bits.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace bsa {
+
+namespace {
+
+constexpr int kDqk = 576;
+constexpr int kDv = 512;
+constexpr int kKT = 32;
+
+struct MlaLds {
+  static constexpr int kKRow = kDqk * 2;                 // 1152 B of bf16 per key
+  static constexpr int kKBytes = kKT * kKRow;            // 36864
+  static constexpr int kVtStride = kKT * 2 + 8;          // 72 B per value dim
+  static constexpr int kVtBytes = kDv * kVtStride;       // 36864
+  static constexpr int kTokBytes = kKT * 4;
+  static constexpr int kBuf = kKBytes + kVtBytes + kTokBytes;
+};
+
+// Two OCP e4m3 bytes (the selected 16-bit half of `w`) -> two bf16 / two fp16
+// values packed in one dword, low value in the low half, with gfx950's direct
+// scaled conversions at scale 1.0.  Both are exact: every e4m3 value is a
+// bf16 value, and e4m3 magnitudes (2^-9 .. 448, 3 mantissa bits) are fp16
+// values too.  (Reinterpreting the second float of v_cvt_pk_f32_fp8's result
+// as bits was miscompiled by this toolchain -- element 1 came back as a copy
+// of element 0 -- so the f32 round trip is avoided.)
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
+#ifndef BSA_MLA_NBUF
+#define BSA_MLA_NBUF 2
+#endif
+
+template <int NW, bool CAUSAL, bool LENS>
+__global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
+  constexpr int NBUF = BSA_MLA_NBUF;
+  using L = MlaLds;
+  constexpr int NTHR = NW * 64;
+  constexpr int NCHUNK = kKT * (kDqk / 16);  // 16-byte fp8 chunks per key tile
+  constexpr int CH_PER_T = (NCHUNK + NTHR - 1) / NTHR;
+  static_assert(NTHR % kKT == 0, "loader maps one key per thread");
+
+  __shared__ __attribute__((aligned(16))) unsigned char lds[NBUF * L::kBuf];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int quad = lane >> 4;
+  const int col = lane & 15;
+
+  const int32_t* trec = a.tiles + static_cast<int64_t>(blockIdx.x) * 8;
+  const int I = trec[0];
+  const int row0 = trec[2];
+  const int nrows = trec[3];
+  const int cb = trec[4];
+  const int ce = trec[5];
+  const int part = trec[6];
+  const int C = a.C;
+  const int npos = (ce - cb) * C;
+  const int ntiles = (npos + kKT - 1) / kKT;
+
+  // rows of a unit are the g qo heads of token I (R = 1)
+  const int rloc = wave * 16 + col;
+  const bool row_ok = rloc < nrows;
+  const int head = row0 + rloc;
+  const int qtok = I;
+  const bool wave_active = wave * 16 < nrows;
+  int qlim = 0x7fffffff;
+  if (CAUSAL) {
+    const int64_t l = static_cast<int64_t>(qtok) + a.causal_off;
+    qlim = l > 0x7fffffff ? 0x7fffffff : (l < -1 ? -1 : static_cast<int>(l));
+  }
+
+  bf16x8 qf[kDqk / 32];
+  if (row_ok) {
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + static_cast<int64_t>(qtok) * a.q_stride +
+                       static_cast<int64_t>(head) * kDqk + quad * 8;
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 32; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 32);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < kDqk / 32; ++ks) qf[ks] = bf16x8{};
+  }
+
+  auto key_tok = [&](int t) -> int {
+    if (t >= npos) return -1;
+    const int blk = t / C;
+    const int off = t - blk * C;
+    const int J = a.cols[cb + blk];
+    if (LENS && off >= a.lens[J]) return -1;
+    return J * C + off;
+  };
+
+  const uint8_t* kv = static_cast<const uint8_t*>(a.k);
+  const int my_key = tid % kKT;
+  u32x4 creg[CH_PER_T];
+  int tok = -1;
+  auto load_tile = [&](int kt) {
+    tok = key_tok(kt * kKT + my_key);
+#pragma unroll
+    for (int i = 0; i < CH_PER_T; ++i) {
+      const int ci = tid + i * NTHR;
+      const int c = ci / kKT;  // 16-byte chunk of the fp8 row
+      creg[i] = (ci < NCHUNK && tok >= 0)
+                    ? *reinterpret_cast<const u32x4*>(kv + static_cast<int64_t>(tok) * a.k_stride + c * 16)
+                    : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto store_tile = [&](int buf) {
+    unsigned char* base = lds + buf * L::kBuf;
+    unsigned char* vt = base + L::kKBytes;
+#pragma unroll
+    for (int i = 0; i < CH_PER_T; ++i) {
+      const int ci = tid + i * NTHR;
+      if (ci >= NCHUNK) continue;
+      const int c = ci / kKT;
+      uint32_t b[8];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        b[2 * w] = fp8x2_to_bf16x2<false>(creg[i][w]);
+        b[2 * w + 1] = fp8x2_to_bf16x2<true>(creg[i][w]);
+      }
+      // K: bf16 chunks 2c and 2c + 1 of this key's row, XOR-swizzled by key
+      const int c0 = 2 * c, c1 = 2 * c + 1;
+      *reinterpret_cast<u32x4*>(base + my_key * L::kKRow + ((c0 ^ (my_key & 7)) << 4)) = u32x4{b[0], b[1], b[2], b[3]};
+      *reinterpret_cast<u32x4*>(base + my_key * L::kKRow + ((c1 ^ (my_key & 7)) << 4)) = u32x4{b[4], b[5], b[6], b[7]};
+      // V^T (fp16): the 16 values of this chunk, if they are latent (V) values
+      if (c * 16 < kDv) {
+        uint32_t hb[8];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          hb[2 * w] = fp8x2_to_f16x2<false>(creg[i][w]);
+          hb[2 * w + 1] = fp8x2_to_f16x2<true>(creg[i][w]);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const uint16_t hv = static_cast<uint16_t>(hb[e >> 1] >> ((e & 1) * 16));
+          *reinterpret_cast<uint16_t*>(vt + (c * 16 + e) * L::kVtStride + my_key * 2) = hv;
+        }
+      }
+    }
+    if (tid < kKT) reinterpret_cast<int*>(base + L::kKBytes + L::kVtBytes)[tid] = tok;
+  };
+
+  f32x4 oacc[kDv / 16];
+#pragma unroll
+  for (int db = 0; db < kDv / 16; ++db) oacc[db] = f32x4{};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  const float sl2 = a.scale_log2;
+
+  if (ntiles > 0) load_tile(0);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = NBUF == 1 ? 0 : (kt & 1);
+    if (NBUF == 1 && kt > 0) __syncthreads();  // single buffer: everyone is done reading it
+    store_tile(buf);
+    __syncthreads();
+    if (kt + 1 < ntiles) load_tile(kt + 1);
+    if (!wave_active) continue;
+
+    const int t0 = kt * kKT;
+    const int t1 = (t0 + kKT < npos ? t0 + kKT : npos) - 1;
+    const int blk0 = t0 / C, blk1 = t1 / C;
+    const int64_t tok_lo = static_cast<int64_t>(a.cols[cb + blk0]) * C + (t0 - blk0 * C);
+    const int64_t tok_hi = static_cast<int64_t>(a.cols[cb + blk1]) * C + (t1 - blk1 * C);
+    if (CAUSAL && tok_lo > static_cast<int64_t>(qtok) + a.causal_off) continue;
+    const bool need_mask = LENS || (t0 + kKT > npos) || (CAUSAL && tok_hi > static_cast<int64_t>(qtok) + a.causal_off);
+
+    const unsigned char* kl = lds + buf * L::kBuf;
+    const unsigned char* vt = kl + L::kKBytes;
+    const int* ktok = reinterpret_cast<const int*>(kl + L::kKBytes + L::kVtBytes);
+
+    f32x4 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x4{};
+      const int key = kb * 16 + col;
+#pragma unroll
+      for (int ks = 0; ks < kDqk / 32; ++ks) {
+        const int c = ks * 4 + quad;
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + key * L::kKRow + ((c ^ (key & 7)) << 4));
+        s[kb] = MfmaType<__bf16>::mfma16(kf, qf[ks], s[kb]);
+      }
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int4 tk = *reinterpret_cast<const int4*>(ktok + kb * 16 + 4 * quad);
+        const int tt[4] = {tk.x, tk.y, tk.z, tk.w};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const bool ok = tt[v] >= 0 && (!CAUSAL || tt[v] <= qlim);
+          if (!ok) s[kb][v] = -INFINITY;
+        }
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kb][v]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx * sl2);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float ls = 0.f;
+    f16x8 pf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p = fast_exp2(fmaf(s[kb][v], sl2, -m_use));
+        ls += p;
+        pf[kb * 4 + v] = static_cast<_Float16>(p);
+      }
+    l_run = l_run * alpha + ls;
+#pragma unroll
+    for (int db = 0; db < kDv / 16; ++db) oacc[db] *= alpha;
+    // O^T += V^T P^T: B element e of this lane is key (e / 4) * 16 + 4 * quad + e % 4
+#pragma unroll
+    for (int db = 0; db < kDv / 16; ++db) {
+      const unsigned char* row = vt + (db * 16 + col) * L::kVtStride;
+      const f16x4 lo = *reinterpret_cast<const f16x4*>(row + (4 * quad) * 2);
+      const f16x4 hi = *reinterpret_cast<const f16x4*>(row + (16 + 4 * quad) * 2);
+      const f16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      oacc[db] = MfmaType<_Float16>::mfma16(vf, pf, oacc[db]);
+    }
+  }
+
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  const float inv = l_tot > 0.f ? a.out_scale / l_tot : 0.f;
+  const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  if (!row_ok) return;
+  if (part < 0) {
+    __bf16* op = static_cast<__bf16*>(a.o) + static_cast<int64_t>(qtok) * a.o_stride + static_cast<int64_t>(head) * kDv;
+#pragma unroll
+    for (int db = 0; db < kDv / 16; ++db) {
+      bf16x4 out;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) out[v] = static_cast<__bf16>(oacc[db][v] * inv);
+      *reinterpret_cast<bf16x4*>(op + db * 16 + 4 * quad) = out;
+    }
+    if (quad == 0 && a.lse) a.lse[static_cast<int64_t>(qtok) * a.num_qo_heads + head] = lse_v;
+  } else {
+    float* pp = a.part + part;
+    float* po = pp + static_cast<int64_t>(rloc) * kDv;
+#pragma unroll
+    for (int db = 0; db < kDv / 16; ++db) {
+      f32x4 out = oacc[db] * inv;
+      *reinterpret_cast<f32x4*>(po + db * 16 + 4 * quad) = out;
+    }
+    if (quad == 0) pp[static_cast<int64_t>(nrows) * kDv + rloc] = lse_v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_mla(const AttnArgs& a, bool causal, bool has_lens, hipStream_t st) {
+  if (a.num_tiles == 0) return hipSuccess;
+  constexpr int NW = 4;
+  const dim3 grid(a.num_tiles), block(NW * 64);
+  if (causal) {
+    if (has_lens) attn_mla_kernel<NW, true, true><<<grid, block, 0, st>>>(a);
+    else attn_mla_kernel<NW, true, false><<<grid, block, 0, st>>>(a);
+  } else {
+    if (has_lens) attn_mla_kernel<NW, false, true><<<grid, block, 0, st>>>(a);
+    else attn_mla_kernel<NW, false, false><<<grid, block, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace bsa

@@ -1,0 +1,58 @@
+// Host planner: BSR structure -> work tiles, split-KV partitions, merge table.
+// Pure host code; never calls the HIP runtime.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "bsa.h"
+
+namespace bsa {
+
+// Record widths of the int32 tables (see bsa_plan_export in bsa.h).
+constexpr int kTileInts = 8;
+constexpr int kMergeInts = 8;
+
+// Tile record fields.
+enum TileField { T_ROWBLOCK = 0, T_KVHEAD, T_ROW0, T_NROWS, T_COLB, T_COLE, T_PART, T_KEYS };
+// Merge record fields.
+enum MergeField { MG_ROWBLOCK = 0, MG_KVHEAD, MG_ROW0, MG_NROWS, MG_PART0, MG_NSPLIT, MG_STRIDE };
+
+// Auto split-KV rule constants (kv_splits == 0).
+constexpr int kAutoTilesPerCu = 4;       // aim for this many tiles per CU
+constexpr int kAutoMinSplitKeys = 256;   // never cut a row tile into pieces below this many keys
+constexpr int kMaxSplits = 64;           // hard cap on partitions per row tile
+
+struct Plan {
+  // validated request
+  bsa_plan_desc_t d{};
+  int64_t MB = 0, NB = 0;
+  int32_t group = 1;
+  float sm_scale = 0.f;
+  // selected kernel
+  int32_t kernel = BSA_KERNEL_TILE;
+  int32_t tile_rows = 0;
+  int32_t key_tile = 0;
+  int32_t num_cus = 0;
+  // tables
+  std::vector<int32_t> tiles;    // kTileInts per tile, launch order
+  std::vector<int32_t> merges;   // kMergeInts per merge
+  std::vector<int32_t> cols;     // column blocks per row block, ascending, causally trimmed
+  std::vector<int32_t> lens;     // NB valid lengths, empty when every block is full
+  int32_t max_splits = 1;
+  int64_t partial_floats = 0;
+  int64_t valid_pairs = 0;
+  // workspace layout (bytes)
+  int64_t off_tiles = 0, off_merges = 0, off_cols = 0, off_lens = 0;
+  int64_t table_bytes = 0, partial_bytes = 0, workspace_bytes = 0;
+  std::vector<uint8_t> table_blob;  // exact image of the table region
+  uint64_t id = 0;                  // process-unique plan id
+};
+
+// Validates `desc` and builds every table.  `num_cus` must be > 0 here (the
+// C ABI layer resolves 0 from the device).  On failure returns a status and
+// sets `err`.
+bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& plan, std::string& err);
+
+}  // namespace bsa

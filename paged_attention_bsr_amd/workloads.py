@@ -222,7 +222,7 @@ def sparse_mla(seed: int = 5, num_tokens: int = 128, num_heads: int = 128,
     w = Workload("sparse_mla", indptr, indices, num_tokens, cache_rows, 1, 1, num_heads, 1,
                  D, latent, False, 1.0 / np.sqrt(D), q_dtype=torch.bfloat16,
                  kv_dtype=torch.float8_e4m3fn, o_dtype=torch.bfloat16, v_aliases_k=True,
-                 meta={"ctx_lens": ctx.astype(np.int64)})
+                 k_token_stride=D, v_token_stride=D, meta={"ctx_lens": ctx.astype(np.int64)})
     if values:
         g = torch.Generator().manual_seed(seed)
         w.q = _randn(g, (num_tokens, num_heads, D), torch.bfloat16)
@@ -277,6 +277,11 @@ def random_bsr(seed: int, M: int, N: int, R: int, C: int, num_qo_heads: int,
                     w.v[sl] = (-sign * garbage).to(dtype)
     return w
 
+
+# Split-KV setting each workload is timed (and parity-checked at full size) with:
+# 0 = automatic, 1 = no split.
+BENCH_KV_SPLITS = {"worked_example": 1, "paged_decode": 0, "bsr_prefill": 1, "window_prefill": 1,
+                   "sparse_mla": 1}
 
 WORKLOAD_NAMES = ["worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla"]
 

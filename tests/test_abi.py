@@ -1,0 +1,130 @@
+"""The C ABI library loads, exports every declared symbol, and validates
+its arguments on the host (no GPU work is started by these tests)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from paged_attention_bsr_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = L.lib()
+    names = _declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), f"{n} is declared in bsa.h but not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\b(bsa_[a-z0-9_]+)\b", out))
+    assert set(names) <= exported
+
+
+def test_desc_layout_matches_binding():
+    assert L.lib().bsa_plan_desc_sizeof() == ctypes.sizeof(L.PlanDesc)
+
+
+def _desc(**kw):
+    d = L.PlanDesc()
+    L.lib().bsa_plan_desc_init(ctypes.byref(d))
+    keep = []
+    for k, v in kw.items():
+        if isinstance(v, np.ndarray):
+            v = np.ascontiguousarray(v, dtype=np.int32)
+            keep.append(v)
+            v = v.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        setattr(d, k, v)
+    d._keep = keep
+    return d
+
+
+def _plan_status(**kw):
+    kw.setdefault("num_cus", 4)
+    d = _desc(**kw)
+    h = ctypes.c_void_p()
+    st = L.lib().bsa_plan_ex(ctypes.byref(d), ctypes.byref(h))
+    msg = L.lib().bsa_last_error().decode()
+    if st == 0:
+        L.lib().bsa_plan_destroy(h)
+    return st, msg
+
+
+GOOD = dict(indptr=np.array([0, 1, 3, 5]), indices=np.array([2, 0, 2, 1, 2]), M=3, N=3, R=1, C=1,
+            num_qo_heads=32, num_kv_heads=8, head_dim_qk=128)
+
+
+def test_plan_without_gpu_succeeds():
+    st, msg = _plan_status(**GOOD)
+    assert st == L.BSA_OK, msg
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(indptr=np.array([1, 1, 3, 5])), L.BSA_ERR_INVALID_ARGUMENT),
+    (dict(indptr=np.array([0, 3, 1, 5])), L.BSA_ERR_INVALID_ARGUMENT),
+    (dict(indices=np.array([2, 0, 3, 1, 2])), L.BSA_ERR_INVALID_ARGUMENT),
+    (dict(indices=np.array([2, 0, -1, 1, 2])), L.BSA_ERR_INVALID_ARGUMENT),
+    (dict(indices=np.array([2, 0, 0, 1, 2])), L.BSA_ERR_INVALID_ARGUMENT),   # duplicate in row 1
+    (dict(N=4, C=3), L.BSA_ERR_INVALID_ARGUMENT),                   # N % C
+    (dict(R=0), L.BSA_ERR_INVALID_ARGUMENT),
+    (dict(num_qo_heads=30), L.BSA_ERR_INVALID_ARGUMENT),            # not a multiple
+    (dict(head_dim_qk=64), L.BSA_ERR_UNSUPPORTED),
+    (dict(q_dtype=L.BSA_BF16), L.BSA_ERR_UNSUPPORTED),              # mixed dtypes
+    (dict(kv_dtype=L.BSA_FP8_E4M3), L.BSA_ERR_UNSUPPORTED),         # fp8 needs the MLA shape
+    (dict(kv_splits=-1), L.BSA_ERR_INVALID_ARGUMENT),
+    (dict(k_descale=0.0), L.BSA_ERR_INVALID_ARGUMENT),
+    (dict(kv_block_lens=np.array([1, 2, 1]), N=3), L.BSA_ERR_INVALID_ARGUMENT),  # len > C
+])
+def test_plan_rejects(change, status):
+    args = dict(GOOD)
+    args.update(change)
+    st, msg = _plan_status(**args)
+    assert st == status, msg
+    assert msg
+
+
+def test_run_validates_before_touching_the_gpu():
+    lib = L.lib()
+    d = _desc(num_cus=4, **GOOD)
+    h = ctypes.c_void_p()
+    assert lib.bsa_plan_ex(ctypes.byref(d), ctypes.byref(h)) == 0
+    ws_need = lib.bsa_workspace_size(h)
+    assert ws_need % 256 == 0 and ws_need > 0
+    fake = 1 << 40  # never dereferenced: every case below fails validation first
+    cases = [
+        ((None, fake, fake, fake, None, fake, ws_need), L.BSA_ERR_INVALID_ARGUMENT),     # null q
+        ((fake + 8, fake, fake, fake, None, fake, ws_need), L.BSA_ERR_INVALID_ARGUMENT),  # misaligned q
+        ((fake, fake, fake, fake, None, fake + 16, ws_need), L.BSA_ERR_INVALID_ARGUMENT),  # ws alignment
+        ((fake, fake, fake, fake, None, fake, ws_need - 256), L.BSA_ERR_WORKSPACE_TOO_SMALL),
+        ((fake, fake, fake, fake, fake + 2, fake, ws_need), L.BSA_ERR_INVALID_ARGUMENT),   # lse alignment
+    ]
+    for (q, k, v, o, lse, ws, n), want in cases:
+        st = lib.bsa_run(h, q, k, v, o, lse, ws, n, None)
+        assert st == want, lib.bsa_last_error()
+    # o overlapping the workspace (q, k, v far away)
+    ws = fake + (1 << 30)
+    st = lib.bsa_run(h, fake, fake, fake, ws + 256, None, ws, ws_need, None)
+    assert st == L.BSA_ERR_INVALID_ARGUMENT and "workspace" in lib.bsa_last_error().decode()
+    # o overlapping q
+    st = lib.bsa_run(h, fake, fake, fake, fake + 1024, None, ws, ws_need, None)
+    assert st == L.BSA_ERR_INVALID_ARGUMENT and "q" in lib.bsa_last_error().decode()
+    lib.bsa_plan_destroy(h)
+    assert lib.bsa_run(None, fake, fake, fake, fake, None, fake, 1 << 20, None) == L.BSA_ERR_INVALID_ARGUMENT
+
+
+def test_merge_states_validates():
+    lib = L.lib()
+    assert lib.bsa_merge_states(None, None, None, None, 4, 0, 2, 8, 0, None) == L.BSA_ERR_INVALID_ARGUMENT
+    assert lib.bsa_merge_states(None, None, None, None, 4, 2, 2, 6, 0, None) == L.BSA_ERR_INVALID_ARGUMENT
+    assert lib.bsa_merge_states(None, None, None, None, 4, 2, 2, 8, 9, None) == L.BSA_ERR_UNSUPPORTED
+    assert lib.bsa_merge_states(None, None, None, None, 0, 2, 2, 8, 0, None) == L.BSA_OK

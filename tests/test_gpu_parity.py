@@ -1,0 +1,178 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Small cases are compared on every output; the five full-size workloads are
+compared on sampled query rows that the oracle computes one by one, in the
+same launch configuration the benchmark times."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_attention_bsr_amd import workloads as W
+from paged_attention_bsr_amd import merge_states
+from tests.parity_util import (TOL_F16, compare, oracle_inputs, oracle_result, plan_for, run_gpu, say,
+                               to_device, tol_for)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(w, kv_splits=1, rows=None, what=None):
+    what = what or f"{w.name} M={w.M} N={w.N} R={w.R} C={w.C} splits={kv_splits}"
+    say(f"[parity] {what}")
+    o, lse = run_gpu(w, kv_splits)
+    o_ref, lse_ref = oracle_result(w, rows=rows)
+    if rows is not None:
+        o, lse = o[rows], lse[rows]
+    return compare(o, lse, o_ref, lse_ref, tol_for(w), what)
+
+
+def test_worked_example():
+    _check(W.worked_example())
+
+
+def test_worked_example_bf16():
+    _check(W.worked_example(dtype=torch.bfloat16))
+
+
+SMALL = [
+    # (seed, M, NB, R, C, Hq, Hkv, causal, partial_lens, density)
+    (1, 37, 9, 5, 7, 8, 2, False, False, 0.5),
+    (2, 64, 8, 64, 64, 32, 8, True, False, 0.6),
+    (3, 130, 6, 64, 64, 4, 1, True, False, 0.7),      # M % R != 0, g = 4, one kv head
+    (4, 256, 2, 128, 128, 16, 2, True, False, 1.0),   # R = C = 128, g = 8
+    (5, 9, 40, 1, 16, 32, 8, False, True, 0.4),       # paged decode shape, partial pages
+    (6, 50, 70, 3, 1, 8, 8, False, False, 0.3),       # C = 1, g = 1
+    (7, 33, 12, 11, 16, 12, 3, True, True, 0.5),      # odd everything, causal + lens
+    (8, 300, 10, 100, 30, 2, 1, False, False, 0.5),   # tile rows > 128 per unit
+    (9, 17, 5, 17, 48, 64, 8, True, False, 0.8),      # 136 rows per unit, C = 48
+    (10, 70, 30, 70, 3, 4, 4, False, True, 0.5),      # C = 3 with lens
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"s{c[0]}" for c in SMALL])
+@pytest.mark.parametrize("kv_splits", [1, 3, 0])
+def test_random_bsr(case, kv_splits):
+    seed, M, NB, R, C, Hq, Hkv, causal, lens, dens = case
+    w = W.random_bsr(seed, M, NB * C, R, C, Hq, Hkv, causal=causal, partial_lens=lens,
+                     density=dens, garbage=6e4 if lens else 0.0)
+    _check(w, kv_splits)
+
+
+@pytest.mark.parametrize("seed", [11, 12])
+def test_random_bsr_bf16(seed):
+    w = W.random_bsr(seed, 90, 12 * 32, 32, 32, 16, 4, causal=seed % 2 == 0, partial_lens=True,
+                     dtype=torch.bfloat16, garbage=3e4)
+    _check(w, 0)
+
+
+def test_empty_rows_and_empty_structure():
+    w = W.random_bsr(21, 40, 8 * 4, 4, 4, 8, 2, density=0.15)
+    assert (np.diff(w.indptr) == 0).any()
+    _check(w, 1)
+    w0 = W.random_bsr(22, 10, 4, 2, 2, 4, 2, density=0.0)
+    assert w0.nnz == 0
+    o, lse = run_gpu(w0)
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_causal_rows_before_the_key_window():
+    # M > N: early query rows have no allowed key at all (bottom-right alignment)
+    w = W.random_bsr(23, 48, 16, 8, 4, 8, 2, causal=True, density=1.0)
+    _check(w, 2)
+
+
+def test_reduced_paged_decode():
+    _check(W.paged_decode(seed=31, batch=12, min_len=1, max_len=700), 0)
+
+
+def test_reduced_bsr_prefill():
+    _check(W.bsr_prefill(seed=32, M=1024, density=0.3), 1)
+
+
+def test_reduced_window_prefill():
+    _check(W.window_prefill(seed=33, M=2048, num_qo_heads=16, num_kv_heads=2, window=3, stride=5), 1)
+
+
+def test_reduced_sparse_mla():
+    _check(W.sparse_mla(seed=34, num_tokens=6, num_heads=128, cache_rows=4096, topk=256, min_ctx=512,
+                        max_ctx=4096), 1)
+    _check(W.sparse_mla(seed=35, num_tokens=4, num_heads=64, cache_rows=2048, topk=200, min_ctx=300,
+                        max_ctx=2048), 3)
+
+
+def test_mla_every_fp8_code_decodes_exactly():
+    """One key per query: o must be that key's V row (every e4m3 code appears)."""
+    w = W.sparse_mla(seed=36, num_tokens=4, num_heads=16, cache_rows=64, topk=1, min_ctx=64, max_ctx=64)
+    codes = torch.arange(256, dtype=torch.int32).remainder(256).to(torch.uint8)
+    codes[codes == 0x7F] = 0x7E       # no NaN inputs
+    codes[codes == 0xFF] = 0xFE
+    kv = torch.zeros(64, 576, dtype=torch.uint8)
+    for r in range(64):
+        kv[r, :512] = codes.roll(r).repeat(2)
+        kv[r, 512:] = codes[:64]
+    w.k = kv.view(torch.float8_e4m3fn)
+    w.k_descale = w.v_descale = 1.0
+    _check(w, 1, what="mla fp8 codes")
+    o, _ = run_gpu(w)
+    q, k, v = oracle_inputs(w)
+    for t in range(w.M):
+        J = int(w.indices[t])
+        ref = torch.from_numpy(v[J, 0]).to(torch.bfloat16)
+        assert torch.equal(o[t].cpu(), ref.expand(w.num_qo_heads, -1)), f"token {t}"
+
+
+def test_permuted_indices_give_identical_bits():
+    w = W.random_bsr(41, 64, 20 * 16, 16, 16, 8, 2, causal=True, density=0.5, shuffle=False)
+    o1, l1 = run_gpu(w, 0)
+    rng = np.random.default_rng(0)
+    for I in range(len(w.indptr) - 1):
+        seg = w.indices[w.indptr[I]:w.indptr[I + 1]]
+        w.indices[w.indptr[I]:w.indptr[I + 1]] = seg[rng.permutation(seg.size)]
+    o2, l2 = run_gpu(w, 0)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_runs_are_deterministic_and_splits_agree():
+    w = W.paged_decode(seed=42, batch=16, min_len=100, max_len=3000)
+    p = plan_for(w, 0)
+    dev = to_device(w)
+    o1, l1 = run_gpu(w, plan=p, dev=dev)
+    o2, l2 = run_gpu(w, plan=p, dev=dev)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o3, l3 = run_gpu(w, 1, dev=dev)
+    assert (o1.float() - o3.float()).abs().max().item() < 4e-3
+    assert (l1 - l3).abs().max().item() < 1e-4
+
+
+def test_merge_states_matches_oracle():
+    g = torch.Generator().manual_seed(5)
+    seq, ns, heads, dim = 7, 5, 3, 64
+    v = torch.randn(seq, ns, heads, dim, generator=g)
+    s = torch.randn(seq, ns, heads, generator=g) * 3
+    s[0, :, 0] = -float("inf")          # all states empty
+    s[1, 2, 1] = -float("inf")          # one empty state
+    v[1, 2, 1] = float("nan")           # its values must not leak
+    o_ref, s_ref = oracle.merge_states(v.double().numpy().transpose(1, 0, 2, 3), s.double().numpy().transpose(1, 0, 2))
+    for dt in (torch.float32, torch.float16, torch.bfloat16):
+        say(f"[parity] merge_states {dt}")
+        vo, so = merge_states(v.cuda(), s.cuda(), out_dtype=dt)
+        torch.cuda.synchronize()
+        tol = (1e-6, 1e-5) if dt == torch.float32 else TOL_F16
+        compare(vo, so, o_ref, s_ref, tol, f"merge_states {dt}")
+
+
+# ---------------------------------------------------------------- full-size workloads
+FULL_ROWS = {
+    "worked_example": None,
+    "paged_decode": None,                                       # all 64 requests
+    "bsr_prefill": [0, 1, 63, 64, 127, 4095, 4096, 6000, 8190, 8191],
+    "window_prefill": [0, 1, 127, 128, 1100, 1151, 2048, 16383, 30000, 32767],
+    "sparse_mla": [0, 1, 17, 64, 100, 127],
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_ROWS))
+def test_full_size_workload(name):
+    kv_splits, rows = W.BENCH_KV_SPLITS[name], FULL_ROWS[name]
+    w = W.by_name(name)
+    _check(w, kv_splits, rows=rows, what=f"full {name} splits={kv_splits}")
