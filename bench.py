@@ -30,7 +30,7 @@ METRIC = "KV GB/s (decode) & TFLOP/s (sparse prefill), % of MI355X HBM/MFMA peak
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}
 DECODE = {"paged_decode", "sparse_mla", "worked_example"}
-KERNEL_SOURCES = ["attn_tile.hip", "attn_mla.hip", "merge.hip", "device_common.h", "kernels.h"]
+KERNEL_SOURCES = ["attn_tile.hip", "attn_decode.hip", "attn_mla.hip", "merge.hip", "device_common.h", "kernels.h"]
 
 
 def log(msg: str) -> None:
@@ -135,6 +135,9 @@ def main() -> int:
                     choices=["worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla"])
     ap.add_argument("--kv-splits", type=int, default=None, help="override the workload's split-KV setting")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
+    ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
+                    help="after the timed region, copy MIB MiB device-to-device once (a known-size "
+                         "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -202,6 +205,16 @@ def main() -> int:
     log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step; attention kernel avg {attn_avg_ms:.4f} ms "
         f"(min {min(attn_ms):.4f}, max {max(attn_ms):.4f})")
 
+    if args.calibration_copy > 0:
+        n = args.calibration_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {n} bytes read, {n} bytes written")
+        del src, dst
+
     alg_bytes, alg_flops = algorithmic_work(w)
     dtype = {torch.float16: "f16", torch.bfloat16: "bf16"}[w.q_dtype]
     if w.kv_dtype == torch.float8_e4m3fn:
@@ -224,7 +237,8 @@ def main() -> int:
         mfma_tf = alg_flops / (attn_avg_ms * 1e-3) / 1e12
         roof["mfma_frac_bf16"] = mfma_tf / MFMA_PEAK_TFLOPS["bf16"]
     roof["traffic"] = measured_traffic(args.workload, kernel_source_hash())
-    roof["kernel"] = "attn_mla_kernel" if info["kernel"] == L.BSA_KERNEL_MLA else "attn_tile_kernel"
+    roof["kernel"] = {L.BSA_KERNEL_MLA: "attn_mla_kernel", L.BSA_KERNEL_DECODE: "attn_decode_kernel"}.get(
+        info["kernel"], "attn_tile_kernel")
     roof["alg_bytes_per_launch"] = alg_bytes
     roof["alg_flops_per_launch"] = alg_flops
     roof["avg_launch_ms"] = attn_avg_ms

@@ -61,7 +61,8 @@ typedef enum { BSA_F16 = 0, BSA_BF16 = 1, BSA_FP8_E4M3 = 2 } bsa_dtype_t;
 /* Kernel family a plan selected (informational). */
 typedef enum {
   BSA_KERNEL_TILE = 0,    /* MFMA tile kernel: head_dim 128, fp16/bf16, any R, C */
-  BSA_KERNEL_MLA = 1      /* MFMA sparse-MLA kernel: Dqk 576 / Dv 512, bf16 q/o, fp8 e4m3 kv, R = 1 */
+  BSA_KERNEL_MLA = 1,     /* MFMA sparse-MLA kernel: Dqk 576 / Dv 512, bf16 q/o, fp8 e4m3 kv, R = 1 */
+  BSA_KERNEL_DECODE = 2   /* paged-decode kernel: R = 1, C >= 16, head_dim 128, fp16/bf16, <= 16 qo heads per kv head */
 } bsa_kernel_t;
 
 /*

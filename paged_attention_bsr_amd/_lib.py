@@ -15,7 +15,7 @@ BSA_ERR_HIP = 4
 BSA_ERR_HOST_ALLOC = 5
 
 BSA_F16, BSA_BF16, BSA_FP8_E4M3, BSA_FP32_OUT = 0, 1, 2, 3
-BSA_KERNEL_TILE, BSA_KERNEL_MLA = 0, 1
+BSA_KERNEL_TILE, BSA_KERNEL_MLA, BSA_KERNEL_DECODE = 0, 1, 2
 BSA_PHASE_ATTENTION, BSA_PHASE_MERGE, BSA_PHASE_ALL = 1, 2, 3
 
 _i32p = ctypes.POINTER(ctypes.c_int32)

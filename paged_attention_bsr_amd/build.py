@@ -28,8 +28,10 @@ HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-ffp-contract=fast", "-munsafe-fp-atomics"]
+# Extra -D definitions for tuning builds (e.g. "-DBSA_DECODE_NW=2"); empty for the product build.
+EXTRA = os.environ.get("BSA_EXTRA_CFLAGS", "").split()
 
-HIP_SOURCES = ["attn_tile.hip", "attn_mla.hip", "merge.hip", "api.cpp"]
+HIP_SOURCES = ["attn_tile.hip", "attn_decode.hip", "attn_mla.hip", "merge.hip", "api.cpp"]
 HOST_SOURCES = ["planner.cpp"]
 
 
@@ -49,10 +51,10 @@ def build(verbose: bool = False) -> str:
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        jobs.append([HIPCC, *COMMON, *HIP_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([HIPCC, *COMMON, *HIP_FLAGS, *EXTRA, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(BUILD_DIR, src + ".o")
-        jobs.append(["g++", *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append(["g++", *COMMON, *EXTRA, "-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
         outs = list(ex.map(_run, jobs))
     if verbose:

@@ -206,6 +206,7 @@ bsa_status_t bsa_run_phase(bsa_plan_t plan, int32_t phase, const void* q, const 
   a.cols = reinterpret_cast<const int32_t*>(ws + P.off_cols);
   a.lens = P.lens.empty() ? nullptr : reinterpret_cast<const int32_t*>(ws + P.off_lens);
   a.part = reinterpret_cast<float*>(ws + P.table_bytes);
+  a.zero_row = ws + P.off_zero;
   a.q_stride = d.q_token_stride;
   a.k_stride = d.k_token_stride;
   a.v_stride = d.v_token_stride;
@@ -222,6 +223,8 @@ bsa_status_t bsa_run_phase(bsa_plan_t plan, int32_t phase, const void* q, const 
   hipError_t e;
   if (phase & BSA_PHASE_ATTENTION) {
     if (P.kernel == BSA_KERNEL_MLA) e = bsa::launch_attn_mla(a, d.causal != 0, a.lens != nullptr, st);
+    else if (P.kernel == BSA_KERNEL_DECODE)
+      e = bsa::launch_attn_decode(a, d.q_dtype == BSA_BF16, d.causal != 0, a.lens != nullptr, st);
     else e = bsa::launch_attn_tile(a, d.q_dtype == BSA_BF16, P.tile_rows, d.causal != 0, a.lens != nullptr, st);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   }

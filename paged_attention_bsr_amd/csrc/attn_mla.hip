@@ -116,7 +116,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
     const int blk = t / C;
     const int off = t - blk * C;
     const int J = a.cols[cb + blk];
-    if (LENS && off >= a.lens[J]) return -1;
+    if (LENS && off >= a.lens[cb + blk]) return -1;
     return J * C + off;
   };
 

@@ -16,8 +16,9 @@ struct AttnArgs {
   float* lse;              // may be null
   const int32_t* tiles;    // 8 ints per tile (planner layout)
   const int32_t* cols;     // column blocks per row block
-  const int32_t* lens;     // NB valid lengths, or null
+  const int32_t* lens;     // valid length of each cols entry, or null (all blocks full)
   float* part;             // split partial region
+  const void* zero_row;    // >= 1 KB of zeros in the workspace (loads of masked keys)
   int64_t q_stride, k_stride, v_stride, o_stride;  // elements per token
   int32_t R, C, group, num_qo_heads;
   int32_t causal_off;      // N - M
@@ -40,6 +41,9 @@ struct MergeArgs {
 // tile_rows in {32, 128, 256}.
 hipError_t launch_attn_tile(const AttnArgs& a, bool bf16, int tile_rows, bool causal, bool has_lens,
                             hipStream_t stream);
+
+// Paged-decode kernel: R = 1, C >= 16, head_dim 128, fp16 or bf16, g <= 16.
+hipError_t launch_attn_decode(const AttnArgs& a, bool bf16, bool causal, bool has_lens, hipStream_t stream);
 
 // Sparse-MLA kernel: bf16 q/o, fp8 e4m3 kv, Dqk 576, Dv 512, one kv head.
 hipError_t launch_attn_mla(const AttnArgs& a, bool causal, bool has_lens, hipStream_t stream);

@@ -25,6 +25,10 @@
 //     leaving at least one block per later split.
 //  6. Tiles are emitted in (I, row tile, h, split) order, then stably sorted
 //     by descending work (longest processing time first).
+// Kernel choice: sparse-MLA shape -> MLA kernel (64-row tiles); R = 1 with
+// g <= 16 and C >= 16 -> decode kernel (16-row tiles, i.e. one per unit);
+// otherwise the generic tile kernel with 32, 128 or 256-row tiles for units
+// of <= 32, <= 128 or more rows.
 #include "planner.h"
 
 #include <algorithm>
@@ -119,10 +123,16 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
       return fail(err, BSA_ERR_UNSUPPORTED, "head_dim 128 (q/k and v/o) is the supported size");
     if (d.q_descale != 1.f || d.k_descale != 1.f || d.v_descale != 1.f)
       return fail(err, BSA_ERR_UNSUPPORTED, "dequant scales apply to fp8 KV only");
-    kernel = BSA_KERNEL_TILE;
-    const int64_t umax = std::min<int64_t>(d.R, std::max<int64_t>(d.M, 1)) * g;
-    tile_rows = umax <= 32 ? 32 : (umax <= 128 ? 128 : 256);
-    key_tile = tile_rows == 32 ? 32 : 64;
+    if (d.R == 1 && g <= 16 && d.C >= 16) {
+      kernel = BSA_KERNEL_DECODE;
+      tile_rows = 16;
+      key_tile = 32;
+    } else {
+      kernel = BSA_KERNEL_TILE;
+      const int64_t umax = std::min<int64_t>(d.R, std::max<int64_t>(d.M, 1)) * g;
+      tile_rows = umax <= 32 ? 32 : (umax <= 128 ? 128 : 256);
+      key_tile = tile_rows == 32 ? 32 : 64;
+    }
   }
 
   P.d = d;
@@ -153,8 +163,13 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
     }
     bptr[I + 1] = static_cast<int64_t>(P.cols.size());
   }
-  if (d.kv_block_lens) P.lens.assign(d.kv_block_lens, d.kv_block_lens + NB);
-  else P.lens.clear();
+  // valid length of each column-list entry (parallel to cols), so kernels
+  // read a block's length with the same index as the block itself
+  P.lens.clear();
+  if (d.kv_block_lens) {
+    P.lens.resize(P.cols.size());
+    for (size_t p = 0; p < P.cols.size(); ++p) P.lens[p] = d.kv_block_lens[P.cols[p]];
+  }
 
   // ---- 2./3. row tiles with their (prefix) column ranges and work
   struct RowTile {
@@ -273,6 +288,8 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
   o = round_up(o + (int64_t)P.cols.size() * 4, 256);
   P.off_lens = o;
   o = round_up(o + (int64_t)P.lens.size() * 4, 256);
+  P.off_zero = o;  // zero row: masked keys load from here
+  o = round_up(o + 1024, 256);
   P.table_bytes = std::max<int64_t>(o, 256);
   P.partial_bytes = round_up(P.partial_floats * 4, 256);
   P.workspace_bytes = P.table_bytes + P.partial_bytes;

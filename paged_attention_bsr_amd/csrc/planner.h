@@ -20,7 +20,10 @@ enum TileField { T_ROWBLOCK = 0, T_KVHEAD, T_ROW0, T_NROWS, T_COLB, T_COLE, T_PA
 enum MergeField { MG_ROWBLOCK = 0, MG_KVHEAD, MG_ROW0, MG_NROWS, MG_PART0, MG_NSPLIT, MG_STRIDE };
 
 // Auto split-KV rule constants (kv_splits == 0).
-constexpr int kAutoTilesPerCu = 4;       // aim for this many tiles per CU
+#ifndef BSA_AUTO_TILES_PER_CU
+#define BSA_AUTO_TILES_PER_CU 4
+#endif
+constexpr int kAutoTilesPerCu = BSA_AUTO_TILES_PER_CU;  // aim for this many tiles per CU
 constexpr int kAutoMinSplitKeys = 256;   // never cut a row tile into pieces below this many keys
 constexpr int kMaxSplits = 64;           // hard cap on partitions per row tile
 
@@ -39,12 +42,12 @@ struct Plan {
   std::vector<int32_t> tiles;    // kTileInts per tile, launch order
   std::vector<int32_t> merges;   // kMergeInts per merge
   std::vector<int32_t> cols;     // column blocks per row block, ascending, causally trimmed
-  std::vector<int32_t> lens;     // NB valid lengths, empty when every block is full
+  std::vector<int32_t> lens;     // valid length of each cols entry, empty when every block is full
   int32_t max_splits = 1;
   int64_t partial_floats = 0;
   int64_t valid_pairs = 0;
   // workspace layout (bytes)
-  int64_t off_tiles = 0, off_merges = 0, off_cols = 0, off_lens = 0;
+  int64_t off_tiles = 0, off_merges = 0, off_cols = 0, off_lens = 0, off_zero = 0;
   int64_t table_bytes = 0, partial_bytes = 0, workspace_bytes = 0;
   std::vector<uint8_t> table_blob;  // exact image of the table region
   uint64_t id = 0;                  // process-unique plan id
