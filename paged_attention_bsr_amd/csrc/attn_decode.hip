@@ -43,6 +43,11 @@ constexpr int kVBytes = kKT * kD * 2;   // wave-private V tile
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+template <typename T>
+__device__ __forceinline__ u32x4 load_kv(const T* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
 // LDS byte offset of 16-byte chunk `c` of key row `k` in a V tile.
 __device__ __forceinline__ int v_chunk_off(int k, int c) {
   return k * (kD * 2) + ((c ^ (((k & 3) << 1) | (((k >> 3) & 1) << 3))) << 4);
@@ -106,7 +111,8 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
   auto tile_blocks = [&](int kt) {
     TileBlocks b;
     const int t0 = kt * kKT;
-    const int blk0 = POW2C ? (t0 >> cshift) : t0 / C;
+    int blk0 = POW2C ? (t0 >> cshift) : t0 / C;
+    blk0 = blk0 < nblk ? blk0 : nblk - 1;  // tiles past the end only feed dummy loads
     const int b1 = blk0 + 1 < nblk ? blk0 + 1 : nblk - 1;
     const int b2 = blk0 + 2 < nblk ? blk0 + 2 : nblk - 1;
     b.base = blk0 * C;
@@ -118,8 +124,9 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
     b.L2 = LENS ? a.lens[cb + b2] : C;
     return b;
   };
+  // branch-free, so every stage issues the same loads and the compiler can
+  // wait for exactly the older stage
   auto key_token = [&](const TileBlocks& b, int t) -> int {
-    if (t >= npos) return -1;
     const int r = t - b.base;                      // < 32 + C, so at most two block steps
     // select block 0, 1 or 2 with masks (a plain ?: chain of these uniform
     // values was lowered to an indexed load from a stack copy)
@@ -130,16 +137,18 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
     J ^= (J ^ b.J2) & s2;
     int len = b.L0 ^ ((b.L0 ^ b.L1) & s1);
     len ^= (len ^ b.L2) & s2;
-    if (LENS && off >= len) return -1;
     const int tok = J * C + off;
-    if (CAUSAL && tok > qlim) return -1;
-    return tok;
+    bool ok = t < npos;
+    if (LENS) ok = ok && off < len;
+    if (CAUSAL) ok = ok && tok <= qlim;
+    return ok ? tok : -1;
   };
 
-  // per-tile registers: K fragments (kb, ks) and V chunks
+  // per-tile registers: K fragments and V chunks, both indexed (kb, ks):
+  // lane (col, quad) holds dims ks*32 + quad*8 .. +8 of key (kb, col)
   struct Stage {
     v8 k[2][4];
-    u32x4 v[8];
+    u32x4 v[2][4];
     uint32_t valid[2];  // bit m: key (kb, m) valid
   };
   // key of S^T row m in block kb: 8*(m/4) + 4*kb + m%4
@@ -149,18 +158,14 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
     for (int kb = 0; kb < 2; ++kb) {
       const int key = 8 * (col >> 2) + 4 * kb + (col & 3);
       const int tok = key_token(b, t0 + key);
-      const T* p = tok >= 0 ? kbase + static_cast<int64_t>(tok) * a.k_stride : zrow;
+      const T* pk = tok >= 0 ? kbase + static_cast<int64_t>(tok) * a.k_stride : zrow;
+      const T* pv = tok >= 0 ? vbase + static_cast<int64_t>(tok) * a.v_stride : zrow;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) s.k[kb][ks] = *reinterpret_cast<const v8*>(p + ks * 32 + quad * 8);
+      for (int ks = 0; ks < 4; ++ks) s.k[kb][ks] = bitcast<v8>(load_kv(pk + ks * 32 + quad * 8));
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) s.v[kb][ks] = load_kv(pv + ks * 32 + quad * 8);
       const uint64_t bal = __ballot(tok >= 0);
       s.valid[kb] = static_cast<uint32_t>(bal & 0xffffu);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int key = quad + 4 * i;
-      const int tok = key_token(b, t0 + key);
-      const T* p = tok >= 0 ? vbase + static_cast<int64_t>(tok) * a.v_stride : zrow;
-      s.v[i] = *reinterpret_cast<const u32x4*>(p + col * 8);
     }
   };
 
@@ -174,7 +179,11 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
   auto compute = [&](const Stage& s) {
     // stage V into this wave's LDS tile (row-major, swizzled chunks)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(vl + v_chunk_off(quad + 4 * i, col)) = s.v[i];
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = 8 * (col >> 2) + 4 * kb + (col & 3);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<u32x4*>(vl + v_chunk_off(key, ks * 4 + quad)) = s.v[kb][ks];
+    }
     // S^T = K Q^T
     f32x4 sc[2];
 #pragma unroll
@@ -227,25 +236,21 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
   // key loop: this wave's tiles wave, wave + NW, ...; the K/V loads of the
   // next tile and the block ids of the one after are in flight during each
   // tile's math
-  Stage s0, s1;
-  TileBlocks bA{}, bB{};
-  int kt = wave;
-  if (kt < ntiles) {
-    bA = tile_blocks(kt);
-    load_stage(s0, kt, bA);
-  }
-  if (kt + NW < ntiles) bB = tile_blocks(kt + NW);
-  while (kt < ntiles) {
-    const int k1 = kt + NW;
-    if (k1 < ntiles) load_stage(s1, k1, bB);
-    if (k1 + NW < ntiles) bA = tile_blocks(k1 + NW);
-    compute(s0);
-    if (k1 >= ntiles) break;
-    const int k2 = k1 + NW;
-    if (k2 < ntiles) load_stage(s0, k2, bA);
-    if (k2 + NW < ntiles) bB = tile_blocks(k2 + NW);
-    compute(s1);
-    kt = k2;
+  // Every stage issues its loads unconditionally (tiles past the end read
+  // the zero row), so the wait before each tile's math covers exactly the
+  // older stage.
+  if (ntiles > 0) {
+    Stage s0, s1;
+    TileBlocks bA = tile_blocks(wave), bB = tile_blocks(wave + NW);
+    load_stage(s0, wave, bA);
+    for (int kt = wave; kt < ntiles; kt += 2 * NW) {
+      load_stage(s1, kt + NW, bB);
+      bA = tile_blocks(kt + 2 * NW);
+      compute(s0);
+      load_stage(s0, kt + 2 * NW, bA);
+      bB = tile_blocks(kt + 3 * NW);
+      if (kt + NW < ntiles) compute(s1);
+    }
   }
 
   // ---- merge the waves' states (all waves, every query column)
