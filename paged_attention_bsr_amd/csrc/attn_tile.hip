@@ -8,20 +8,26 @@
 // grouping; the key loop is ordinary flash-style online softmax).
 //
 // Per key tile of KT keys:
-//   * the whole workgroup gathers K and V rows by block index with 16-byte
-//     global loads (keys outside a block's valid length, or past the range,
-//     are loaded as zeros and masked), K into a row-major LDS tile whose
-//     16-byte chunks are XOR-swizzled by key, V transposed into a padded
-//     (head_dim x KT) LDS tile; loads for tile t+1 are in flight while tile t
-//     is computed (two LDS buffers, one barrier per tile);
+//   * the whole workgroup gathers the K and V rows of the tile by block index
+//     with coalesced 16-byte loads (16 lanes per 256-byte row; keys outside a
+//     block's valid length, or past the range, load from a zero row) into
+//     row-major LDS tiles whose 16-byte chunks are XOR-swizzled by key; loads
+//     for tile t+1 are in flight while tile t is computed (two LDS buffers,
+//     one barrier per tile);
 //   * each wave computes S^T = K Q^T for its 32 rows with
 //     v_mfma_f32_32x32x16 (K from LDS as the A operand, Q^T held in
 //     registers as B), so every lane owns one query row and its row max
-//     needs one cross-half exchange only;
-//   * causal / valid-length masking runs only on tiles that need it;
-//   * online softmax in the log2 domain (scale folded into one FMA);
-//   * O^T += V^T P^T with v_mfma_f32_32x32x16, P^T straight from the S^T
-//     accumulator registers, so the per-row rescale is a per-lane multiply.
+//     needs one cross-half exchange only; K rows enter in an order (bits 2
+//     and 3 of the row index swapped) that makes the S^T accumulators line
+//     up with the transposed V fragments below;
+//   * causal / valid-length masking runs only on tiles that need it, and a
+//     wave skips tiles that lie wholly above its causal diagonal;
+//   * online softmax in the log2 domain (scale folded into one FMA); the
+//     running max only moves when a tile exceeds it by more than 2^8, so
+//     the rescale of O is rare (probabilities stay below 256);
+//   * O^T += V^T P^T with v_mfma_f32_32x32x16: V^T fragments come straight
+//     from the row-major V tile through ds_read_b64_tr_b16, P^T straight
+//     from the S^T accumulator registers.
 // The result is o = O / l (rounded to the storage type) and
 // lse = (m + log2 l) ln 2, or, for a split tile, the fp32 partial (O / l,
 // lse) in the workspace for the merge kernel.
@@ -32,19 +38,33 @@ namespace bsa {
 
 namespace {
 
-constexpr int kD = 128;  // q/k and v/o head dim of this kernel
+constexpr int kD = 128;            // q/k and v/o head dim of this kernel
+constexpr float kRescaleSlack = 8.f;  // log2 units the running max may lag behind
+
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <int KT>
 struct TileLds {
-  static constexpr int kKBytes = KT * kD * 2;       // K: KT rows of 256 B, swizzled chunks
-  static constexpr int kVtStride = KT * 2 + 8;      // V^T: one padded row of KT keys per dim
-  static constexpr int kVtBytes = kD * kVtStride;
-  static constexpr int kTokBytes = KT * 4;          // token of each key slot, -1 = masked
-  static constexpr int kBuf = kKBytes + kVtBytes + kTokBytes;
+  static constexpr int kKBytes = KT * kD * 2;   // K: KT rows of 256 B
+  static constexpr int kVBytes = KT * kD * 2;   // V: KT rows of 256 B
+  static constexpr int kTokBytes = KT * 4;      // token of each key slot, -1 = masked
+  static constexpr int kBuf = kKBytes + kVBytes + kTokBytes;
 };
 
-template <typename T, int NW, int KT, bool CAUSAL, bool LENS>
-__global__ __launch_bounds__(NW * 64) void attn_tile_kernel(AttnArgs a) {
+// Chunk swizzles.  K is read 8 rows at a time as rows {0,1,2,3,8,9,10,11}
+// (and shifts of that set), so its swizzle separates those; V is read by the
+// transposing loads 4 consecutive rows x 2 chunks at a time.
+__device__ __forceinline__ int k_off(int key, int c) {
+  return key * 256 + ((c ^ ((key & 3) | (((key >> 3) & 1) << 2))) << 4);
+}
+__device__ __forceinline__ int v_off(int key, int c) { return key * 256 + ((c ^ ((key & 3) << 1)) << 4); }
+
+// S^T row m of a 32-key block holds key swap23(m) (bits 2 and 3 exchanged).
+__device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
+
+template <typename T, int NW, int KT, bool CAUSAL, bool LENS, bool BLOCKTILE>
+__global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   using Ops = MfmaType<T>;
   using v8 = typename Ops::v8;
   using v4 = typename Ops::v4;
@@ -52,10 +72,10 @@ __global__ __launch_bounds__(NW * 64) void attn_tile_kernel(AttnArgs a) {
   constexpr int NTHR = NW * 64;
   constexpr int KCH = KT * 16 / NTHR;  // 16-byte chunks per thread per tile, for K and for V
   static_assert(KCH >= 1 && KT * 16 % NTHR == 0, "loader shape");
-  static_assert(NTHR % KT == 0, "V loader assumes one key per thread");
   constexpr int NKB = KT / 32;
+  constexpr int NSTAGE = 2;
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds[2 * L::kBuf];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[NSTAGE * L::kBuf];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -73,7 +93,8 @@ __global__ __launch_bounds__(NW * 64) void attn_tile_kernel(AttnArgs a) {
   const int part = trec[6];
   const int C = a.C;
   const int g = a.group;
-  const int npos = (ce - cb) * C;
+  const int nblk = ce - cb;
+  const int npos = nblk * C;
   const int ntiles = (npos + KT - 1) / KT;
 
   // ---- this lane's query row
@@ -105,59 +126,99 @@ __global__ __launch_bounds__(NW * 64) void attn_tile_kernel(AttnArgs a) {
     for (int ks = 0; ks < 8; ++ks) qf[ks] = v8{};
   }
 
-  // ---- key-slot -> token (-1: masked / outside the range)
-  auto key_tok = [&](int t) -> int {
-    if (t >= npos) return -1;
-    const int blk = t / C;
-    const int off = t - blk * C;
-    const int J = a.cols[cb + blk];
-    if (LENS && off >= a.lens[cb + blk]) return -1;
-    return J * C + off;
+  // ---- key tokens.  BLOCKTILE (C a multiple of KT): a key tile lies inside one
+  // block, whose id and length are uniform scalar loads.  Otherwise each key
+  // looks its block up.  Tiles past the end (only ever loaded, never used)
+  // resolve to masked keys.
+  struct TileInfo {
+    int base;   // token of the tile's first key slot
+    int off0;   // offset of that slot inside its block
+    int len;    // valid length of the block
+  };
+  auto tile_info = [&](int kt) {
+    TileInfo ti;
+    const int t0 = kt * KT;
+    int blk = t0 / C;
+    blk = blk < nblk ? blk : nblk - 1;
+    ti.off0 = t0 - blk * C;
+    ti.base = a.cols[cb + blk] * C + ti.off0;
+    ti.len = LENS ? a.lens[cb + blk] : C;
+    return ti;
+  };
+  auto key_tok = [&](int kt, const TileInfo& ti, int key) -> int {
+    const int t = kt * KT + key;
+    if (BLOCKTILE) {
+      bool ok = t < npos;
+      if (LENS) ok = ok && ti.off0 + key < ti.len;
+      return ok ? ti.base + key : -1;
+    } else {
+      if (t >= npos) return -1;
+      const int blk = t / C;
+      const int off = t - blk * C;
+      if (LENS && off >= a.lens[cb + blk]) return -1;
+      return a.cols[cb + blk] * C + off;
+    }
   };
 
   const T* kbase = static_cast<const T*>(a.k) + static_cast<int64_t>(kvh) * kD;
   const T* vbase = static_cast<const T*>(a.v) + static_cast<int64_t>(kvh) * kD;
+  const T* zrow = static_cast<const T*>(a.zero_row);
+  const int lc = tid & 15;  // 16-byte chunk this thread moves within a row
   u32x4 kreg[KCH], vreg[KCH];
-  int vtok = -1;
-  const int vkey = tid % KT;
-  auto load_tile = [&](int kt) {
-    const int t0 = kt * KT;
+  int ktok_reg[KCH];
+  auto issue_loads = [&](int kt) {
+    const TileInfo ti = tile_info(kt < ntiles ? kt : ntiles - 1);
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int key = (tid >> 4) + i * (NTHR / 16);
-      const int c = tid & 15;
-      const int tok = key_tok(t0 + key);
-      kreg[i] = tok >= 0 ? *reinterpret_cast<const u32x4*>(kbase + static_cast<int64_t>(tok) * a.k_stride + c * 8)
-                         : u32x4{0, 0, 0, 0};
-    }
-    vtok = key_tok(t0 + vkey);
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid / KT + i * (NTHR / KT);
-      vreg[i] = vtok >= 0 ? *reinterpret_cast<const u32x4*>(vbase + static_cast<int64_t>(vtok) * a.v_stride + c * 8)
-                          : u32x4{0, 0, 0, 0};
+      const int tok = kt < ntiles ? key_tok(kt, ti, key) : -1;
+      ktok_reg[i] = tok;
+      const T* pk = tok >= 0 ? kbase + static_cast<int64_t>(tok) * a.k_stride : zrow;
+      const T* pv = tok >= 0 ? vbase + static_cast<int64_t>(tok) * a.v_stride : zrow;
+      kreg[i] = *reinterpret_cast<const u32x4*>(pk + lc * 8);
+      vreg[i] = *reinterpret_cast<const u32x4*>(pv + lc * 8);
     }
   };
-  auto store_tile = [&](int buf) {
-    unsigned char* base = lds + buf * L::kBuf;
+  auto commit = [&](int slot) {
+    unsigned char* base = lds + slot * L::kBuf;
+    int* ktok = reinterpret_cast<int*>(base + L::kKBytes + L::kVBytes);
 #pragma unroll
     for (int i = 0; i < KCH; ++i) {
       const int key = (tid >> 4) + i * (NTHR / 16);
-      const int c = tid & 15;
-      *reinterpret_cast<u32x4*>(base + key * 256 + ((c ^ (key & 7)) << 4)) = kreg[i];
+      *reinterpret_cast<u32x4*>(base + k_off(key, lc)) = kreg[i];
+      *reinterpret_cast<u32x4*>(base + L::kKBytes + v_off(key, lc)) = vreg[i];
+      if (lc == 0) ktok[key] = ktok_reg[i];
     }
-    unsigned char* vt = base + L::kKBytes;
+  };
+
+  // wave-uniform token range of key tile kt (the column list is ascending)
+  auto tile_tok_range = [&](int kt, int64_t& lo, int64_t& hi) {
+    const int t0 = kt * KT;
+    const int t1 = (t0 + KT < npos ? t0 + KT : npos) - 1;
+    const int blk0 = t0 / C, blk1 = t1 / C;
+    lo = static_cast<int64_t>(a.cols[cb + blk0]) * C + (t0 - blk0 * C);
+    hi = static_cast<int64_t>(a.cols[cb + blk1]) * C + (t1 - blk1 * C);
+  };
+  // the whole tile lies above this wave's causal diagonal
+  auto wave_skips = [&](int kt) -> bool {
+    if (!CAUSAL || kt >= ntiles) return kt >= ntiles;
+    int64_t lo, hi;
+    tile_tok_range(kt, lo, hi);
+    return lo > wave_lim;
+  };
+
+  auto qk = [&](int slot, f32x16 (&sacc)[NKB]) {
+    const unsigned char* kl = lds + slot * L::kBuf;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid / KT + i * (NTHR / KT);
-      const uint32_t w[4] = {vreg[i][0], vreg[i][1], vreg[i][2], vreg[i][3]};
+    for (int kb = 0; kb < NKB; ++kb) {
+      sacc[kb] = f32x16{};
+      const int key = kb * 32 + swap23(ql);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint16_t hv = static_cast<uint16_t>(w[e >> 1] >> ((e & 1) * 16));
-        *reinterpret_cast<uint16_t*>(vt + (c * 8 + e) * L::kVtStride + vkey * 2) = hv;
+      for (int ks = 0; ks < 8; ++ks) {
+        const v8 kf = *reinterpret_cast<const v8*>(kl + k_off(key, 2 * ks + half));
+        sacc[kb] = Ops::mfma32(kf, qf[ks], sacc[kb]);
       }
     }
-    if (tid < KT) reinterpret_cast<int*>(base + L::kKBytes + L::kVtBytes)[tid] = vtok;
   };
 
   f32x16 oacc[4];
@@ -167,95 +228,109 @@ __global__ __launch_bounds__(NW * 64) void attn_tile_kernel(AttnArgs a) {
   float l_run = 0.f;
   const float sl2 = a.scale_log2;
 
-  if (ntiles > 0) load_tile(0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    store_tile(buf);
-    __syncthreads();
-    if (kt + 1 < ntiles) load_tile(kt + 1);
-    if (!wave_active) continue;
-
-    // wave-uniform range of key tokens in this tile (columns are ascending)
-    const int t0 = kt * KT;
-    const int t1 = (t0 + KT < npos ? t0 + KT : npos) - 1;
-    const int blk0 = t0 / C, blk1 = t1 / C;
-    const int64_t tok_lo = static_cast<int64_t>(a.cols[cb + blk0]) * C + (t0 - blk0 * C);
-    const int64_t tok_hi = static_cast<int64_t>(a.cols[cb + blk1]) * C + (t1 - blk1 * C);
-    if (CAUSAL && tok_lo > wave_lim) continue;  // every key of the tile is above this wave's diagonal
-    const bool need_mask = LENS || (t0 + KT > npos) || (CAUSAL && tok_hi > wave_lim_lo);
-
-    const unsigned char* kl = lds + buf * L::kBuf;
-    const unsigned char* vt = kl + L::kKBytes;
-    const int* ktok = reinterpret_cast<const int*>(kl + L::kKBytes + L::kVtBytes);
-
-    f32x16 s[NKB];
+  // causal / length mask of S(kt) (only on tiles that need it)
+  auto mask_scores = [&](int kt, int slot, f32x16 (&sacc)[NKB]) {
+    int64_t lo, hi;
+    tile_tok_range(kt, lo, hi);
+    const bool need_mask = LENS || (kt * KT + KT > npos) || (CAUSAL && hi > wave_lim_lo);
+    if (!need_mask) return;
+    const int* ktok = reinterpret_cast<const int*>(lds + slot * L::kBuf + L::kKBytes + L::kVBytes);
+    // value 4*g4 + e of this lane is S^T row 8*g4 + 4*half + e, i.e. key
+    // 16*(g4/2) + 8*half + 4*(g4%2) + e of the block
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16{};
-      const int key = kb * 32 + ql;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int c = 2 * ks + half;
-        const v8 kf = *reinterpret_cast<const v8*>(kl + key * 256 + ((c ^ (key & 7)) << 4));
-        s[kb] = Ops::mfma32(kf, qf[ks], s[kb]);
-      }
-    }
-    if (need_mask) {
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int4 tk = *reinterpret_cast<const int4*>(ktok + kb * 32 + 16 * (g4 >> 1) + 8 * half + 4 * (g4 & 1));
+        const int tt[4] = {tk.x, tk.y, tk.z, tk.w};
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int4 tk = *reinterpret_cast<const int4*>(ktok + kb * 32 + 8 * g4 + 4 * half);
-          const int tt[4] = {tk.x, tk.y, tk.z, tk.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bool ok = tt[e] >= 0 && (!CAUSAL || tt[e] <= qlim);
-            if (!ok) s[kb][g4 * 4 + e] = -INFINITY;
-          }
+        for (int e = 0; e < 4; ++e) {
+          const bool ok = tt[e] >= 0 && (!CAUSAL || tt[e] <= qlim);
+          if (!ok) sacc[kb][g4 * 4 + e] = -INFINITY;
         }
       }
     }
-    // online softmax (log2 domain)
+  };
+  // scores -> probabilities with a lagging running max (branch-free, so it can
+  // be interleaved with the next tile's QK^T); `live` = false leaves the running
+  // state untouched.  Returns alpha; sets `upd` when the running max moved.
+  auto softmax_core = [&](f32x16 (&sacc)[NKB], bool live, bool& upd) -> float {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
     mx = fmaxf(mx, xor_lane32(mx));
-    const float m_new = fmaxf(m_run, mx * sl2);
+    const float mt = mx * sl2;
+    upd = live && mt > m_run + kRescaleSlack;
+    const float m_new = upd ? mt : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
     float ls = 0.f;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = fast_exp2(fmaf(s[kb][v], sl2, -m_use));
-        s[kb][v] = p;
+        const float p = fast_exp2(fmaf(sacc[kb][v], sl2, -m_use));
+        sacc[kb][v] = p;
         ls += p;
       }
-    l_run = l_run * alpha + ls;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+    m_run = m_new;
+    l_run = live ? l_run * alpha + ls : l_run;
+    return alpha;
+  };
 
-    // O^T += V^T P^T
+  // lane -> transposed-read coordinates (16-lane group G, lane L within it)
+  const int G = lane >> 4;
+  const int Lg = lane & 15;
+  const int vrow = 8 * half + (Lg >> 2);          // + ks*16 + 4*j
+  const int vdim = 16 * (G & 1) + 4 * (Lg & 3);   // + db*32
+  auto pv = [&](int slot, const f32x16 (&sacc)[NKB]) {
+    const unsigned char* vl = lds + slot * L::kBuf + L::kKBytes;
+    // k-step ks covers keys ks*16 .. +16: lane half h holds keys ks*16 + 8h + e
+    // (e = 0..7), from S^T values hv*8 + e of block ks/2
 #pragma unroll
     for (int ks = 0; ks < KT / 16; ++ks) {
       const int kb = ks >> 1;
       const int hv = ks & 1;
       v8 pf;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = static_cast<T>(s[kb][hv * 8 + e]);
-      const int kcol = kb * 32 + hv * 16 + 4 * half;
+      for (int e = 0; e < 8; ++e) pf[e] = static_cast<T>(sacc[kb][hv * 8 + e]);
+      const int row = ks * 16 + vrow;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
-        const unsigned char* row = vt + (db * 32 + ql) * L::kVtStride;
-        const v4 lo = *reinterpret_cast<const v4*>(row + kcol * 2);
-        const v4 hi = *reinterpret_cast<const v4*>(row + (kcol + 8) * 2);
-        const v8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const int d = db * 32 + vdim;
+        const int boff = (d & 7) * 2;
+        const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vl + v_off(row, d >> 3) + boff));
+        const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vl + v_off(row + 4, d >> 3) + boff));
+        const v8 vf = __builtin_shufflevector(bitcast<v4>(lo), bitcast<v4>(hi), 0, 1, 2, 3, 4, 5, 6, 7);
         oacc[db] = Ops::mfma32(vf, pf, oacc[db]);
       }
+    }
+  };
+
+  // ---- key loop: two LDS stages, one barrier per tile; the loads of tile t+1
+  // are in flight while tile t is computed
+  if (ntiles > 0) {
+    issue_loads(0);
+    for (int t = 0; t < ntiles; ++t) {
+      const int slot = t & 1;
+      commit(slot);
+      __syncthreads();
+      issue_loads(t + 1);
+      if (!wave_active || wave_skips(t)) continue;
+      f32x16 sc[NKB];
+      qk(slot, sc);
+      mask_scores(t, slot, sc);
+      bool upd;
+      const float alpha = softmax_core(sc, true, upd);
+      if (__ballot(upd) != 0) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      }
+      pv(slot, sc);
     }
   }
 
@@ -295,13 +370,16 @@ __global__ __launch_bounds__(NW * 64) void attn_tile_kernel(AttnArgs a) {
 template <typename T, int NW, int KT>
 hipError_t launch_variant(const AttnArgs& a, bool causal, bool lens, hipStream_t st) {
   const dim3 grid(a.num_tiles), block(NW * 64);
+  const bool bt = a.C % KT == 0;
+#define BSA_TILE_LAUNCH(CA, LE)                                                              \
+  if (bt) attn_tile_kernel<T, NW, KT, CA, LE, true><<<grid, block, 0, st>>>(a);              \
+  else attn_tile_kernel<T, NW, KT, CA, LE, false><<<grid, block, 0, st>>>(a);
   if (causal) {
-    if (lens) attn_tile_kernel<T, NW, KT, true, true><<<grid, block, 0, st>>>(a);
-    else attn_tile_kernel<T, NW, KT, true, false><<<grid, block, 0, st>>>(a);
+    if (lens) { BSA_TILE_LAUNCH(true, true) } else { BSA_TILE_LAUNCH(true, false) }
   } else {
-    if (lens) attn_tile_kernel<T, NW, KT, false, true><<<grid, block, 0, st>>>(a);
-    else attn_tile_kernel<T, NW, KT, false, false><<<grid, block, 0, st>>>(a);
+    if (lens) { BSA_TILE_LAUNCH(false, true) } else { BSA_TILE_LAUNCH(false, false) }
   }
+#undef BSA_TILE_LAUNCH
   return hipGetLastError();
 }
 

@@ -130,7 +130,7 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
     } else {
       kernel = BSA_KERNEL_TILE;
       const int64_t umax = std::min<int64_t>(d.R, std::max<int64_t>(d.M, 1)) * g;
-      tile_rows = umax <= 32 ? 32 : (umax <= 128 ? 128 : 256);
+      tile_rows = umax <= 32 ? 32 : (umax <= 128 || kTileMaxRows == 128 ? 128 : 256);
       key_tile = tile_rows == 32 ? 32 : 64;
     }
   }

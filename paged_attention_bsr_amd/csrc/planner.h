@@ -26,6 +26,10 @@ enum MergeField { MG_ROWBLOCK = 0, MG_KVHEAD, MG_ROW0, MG_NROWS, MG_PART0, MG_NS
 constexpr int kAutoTilesPerCu = BSA_AUTO_TILES_PER_CU;  // aim for this many tiles per CU
 constexpr int kAutoMinSplitKeys = 256;   // never cut a row tile into pieces below this many keys
 constexpr int kMaxSplits = 64;           // hard cap on partitions per row tile
+#ifndef BSA_TILE_MAX_ROWS
+#define BSA_TILE_MAX_ROWS 256
+#endif
+constexpr int kTileMaxRows = BSA_TILE_MAX_ROWS;  // largest row tile of the generic kernel (128 or 256)
 
 struct Plan {
   // validated request
