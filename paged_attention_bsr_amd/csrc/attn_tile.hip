@@ -52,13 +52,14 @@ struct TileLds {
   static constexpr int kBuf = kKBytes + kVBytes + kTokBytes;
 };
 
-// Chunk swizzles.  K is read 8 rows at a time as rows {0,1,2,3,8,9,10,11}
-// (and shifts of that set), so its swizzle separates those; V is read by the
-// transposing loads 4 consecutive rows x 2 chunks at a time.
-__device__ __forceinline__ int k_off(int key, int c) {
-  return key * 256 + ((c ^ ((key & 3) | (((key >> 3) & 1) << 2))) << 4);
-}
-__device__ __forceinline__ int v_off(int key, int c) { return key * 256 + ((c ^ ((key & 3) << 1)) << 4); }
+// Chunk swizzles for 64 banks x 4 B (a 16-byte-per-lane access is served
+// 16 lanes at a time, an 8-byte one up to 32 lanes at a time).  K: the 16
+// lanes of a phase read 16 different rows at one chunk, so the chunk is
+// XORed with the row's low 4 bits.  V: a transposing read touches 4
+// consecutive rows x 2 chunks per 16-lane group and a neighbouring group the
+// next 2 chunks of the same rows, so the chunk is XORed with 4 * (row % 4).
+__device__ __forceinline__ int k_off(int key, int c) { return key * 256 + ((c ^ (key & 15)) << 4); }
+__device__ __forceinline__ int v_off(int key, int c) { return key * 256 + ((c ^ ((key & 3) << 2)) << 4); }
 
 // S^T row m of a 32-key block holds key swap23(m) (bits 2 and 3 exchanged).
 __device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
