@@ -80,10 +80,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps per-wave branches scalar
   const int half = lane >> 5;
   const int ql = lane & 31;
 
+  // read-only tables through the constant address space: their wave-uniform
+  // lookups inside the key loop become scalar loads
+  const cint32_t* cols = (const cint32_t*)(a.cols);
+  const cint32_t* lens = (const cint32_t*)(a.lens);
   const int32_t* trec = a.tiles + static_cast<int64_t>(blockIdx.x) * 8;
   const int I = trec[0];
   const int kvh = trec[1];
@@ -108,10 +112,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   const bool wave_active = wave_rows > 0;
   const int wave_min_tok = I * a.R + (row0 + wave * 32) / g;
   const int wave_max_tok = I * a.R + (row0 + wave * 32 + (wave_rows < 32 ? wave_rows : 32) - 1) / g;
-  int qlim = 0x7fffffff;
+  // key token t is visible to this row iff (unsigned)t < qbound: masked slots
+  // carry t = -1, and causal rows see t <= qtok + N - M
+  uint32_t qbound = 0x80000000u;
   if (CAUSAL) {
     const int64_t l = static_cast<int64_t>(qtok) + a.causal_off;
-    qlim = l > 0x7fffffff ? 0x7fffffff : (l < -1 ? -1 : static_cast<int>(l));
+    qbound = l >= 0x7fffffff ? 0x80000000u : (l < -1 ? 0u : static_cast<uint32_t>(l + 1));
   }
   const int64_t wave_lim = static_cast<int64_t>(wave_max_tok) + a.causal_off;
   const int64_t wave_lim_lo = static_cast<int64_t>(wave_min_tok) + a.causal_off;
@@ -142,8 +148,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     int blk = t0 / C;
     blk = blk < nblk ? blk : nblk - 1;
     ti.off0 = t0 - blk * C;
-    ti.base = a.cols[cb + blk] * C + ti.off0;
-    ti.len = LENS ? a.lens[cb + blk] : C;
+    ti.base = cols[cb + blk] * C + ti.off0;
+    ti.len = LENS ? lens[cb + blk] : C;
     return ti;
   };
   auto key_tok = [&](int kt, const TileInfo& ti, int key) -> int {
@@ -156,8 +162,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
       if (t >= npos) return -1;
       const int blk = t / C;
       const int off = t - blk * C;
-      if (LENS && off >= a.lens[cb + blk]) return -1;
-      return a.cols[cb + blk] * C + off;
+      if (LENS && off >= lens[cb + blk]) return -1;
+      return cols[cb + blk] * C + off;
     }
   };
 
@@ -197,8 +203,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     const int t0 = kt * KT;
     const int t1 = (t0 + KT < npos ? t0 + KT : npos) - 1;
     const int blk0 = t0 / C, blk1 = t1 / C;
-    lo = static_cast<int64_t>(a.cols[cb + blk0]) * C + (t0 - blk0 * C);
-    hi = static_cast<int64_t>(a.cols[cb + blk1]) * C + (t1 - blk1 * C);
+    lo = static_cast<int64_t>(cols[cb + blk0]) * C + (t0 - blk0 * C);
+    hi = static_cast<int64_t>(cols[cb + blk1]) * C + (t1 - blk1 * C);
   };
   // the whole tile lies above this wave's causal diagonal
   auto wave_skips = [&](int kt) -> bool {
@@ -243,12 +249,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int4 tk = *reinterpret_cast<const int4*>(ktok + kb * 32 + 16 * (g4 >> 1) + 8 * half + 4 * (g4 & 1));
-        const int tt[4] = {tk.x, tk.y, tk.z, tk.w};
+        const uint32_t tt[4] = {static_cast<uint32_t>(tk.x), static_cast<uint32_t>(tk.y),
+                                static_cast<uint32_t>(tk.z), static_cast<uint32_t>(tk.w)};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool ok = tt[e] >= 0 && (!CAUSAL || tt[e] <= qlim);
-          if (!ok) sacc[kb][g4 * 4 + e] = -INFINITY;
-        }
+        for (int e = 0; e < 4; ++e) sacc[kb][g4 * 4 + e] = tt[e] < qbound ? sacc[kb][g4 * 4 + e] : -INFINITY;
       }
     }
   };
