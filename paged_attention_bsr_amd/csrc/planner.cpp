@@ -28,7 +28,8 @@
 // Kernel choice: sparse-MLA shape -> MLA kernel (64-row tiles); R = 1 with
 // g <= 16 and C >= 16 -> decode kernel (16-row tiles, i.e. one per unit);
 // otherwise the generic tile kernel with 32, 128 or 256-row tiles for units
-// of <= 32, <= 128 or more rows.
+// of <= 32, <= 128 or more rows; 128 also for larger units when 256-row tiles
+// would leave fewer than kTileSmallGridPerCu tiles per CU.
 #include "planner.h"
 
 #include <algorithm>
@@ -130,7 +131,16 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
     } else {
       kernel = BSA_KERNEL_TILE;
       const int64_t umax = std::min<int64_t>(d.R, std::max<int64_t>(d.M, 1)) * g;
-      tile_rows = umax <= 32 ? 32 : (umax <= 128 || kTileMaxRows == 128 ? 128 : 256);
+      if (umax <= 32) {
+        tile_rows = 32;
+      } else if (umax <= 128 || kTileMaxRows == 128) {
+        tile_rows = 128;
+      } else {
+        const int64_t rows_last = d.M - (MB - 1) * d.R;
+        const int64_t n256 = ((MB - 1) * ceil_div((int64_t)d.R * g, 256) + ceil_div(rows_last * g, 256)) *
+                             d.num_kv_heads;
+        tile_rows = n256 < (int64_t)kTileSmallGridPerCu * num_cus ? 128 : 256;
+      }
       key_tile = tile_rows == 32 ? 32 : 64;
     }
   }

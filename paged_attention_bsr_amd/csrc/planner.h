@@ -30,6 +30,12 @@ constexpr int kMaxSplits = 64;           // hard cap on partitions per row tile
 #define BSA_TILE_MAX_ROWS 256
 #endif
 constexpr int kTileMaxRows = BSA_TILE_MAX_ROWS;  // largest row tile of the generic kernel (128 or 256)
+// Generic kernel: 256-row tiles unless that gives fewer than this many tiles
+// per CU (then 128-row tiles, so that two workgroups share a CU).
+#ifndef BSA_TILE_SMALL_GRID_PER_CU
+#define BSA_TILE_SMALL_GRID_PER_CU 8
+#endif
+constexpr int kTileSmallGridPerCu = BSA_TILE_SMALL_GRID_PER_CU;
 
 struct Plan {
   // validated request

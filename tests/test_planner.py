@@ -200,3 +200,45 @@ def test_workspace_layout():
     assert inf["workspace_bytes"] % 256 == 0 and inf["table_bytes"] % 256 == 0
     assert p.workspace_size == inf["workspace_bytes"]
     assert inf["num_merges"] > 0 and inf["max_splits"] > 1
+
+
+TILE_SMALL_GRID_PER_CU = 8
+
+
+def model_kernel(w, num_cus):
+    """Python model of the planner's kernel / row-tile choice."""
+    g = w.num_qo_heads // w.num_kv_heads
+    if w.kv_dtype == torch.float8_e4m3fn:
+        return 1, 64
+    if w.R == 1 and g <= 16 and w.C >= 16:
+        return 2, 16
+    MB = _cdiv(w.M, w.R)
+    umax = min(w.R, max(w.M, 1)) * g
+    if umax <= 32:
+        return 0, 32
+    if umax <= 128:
+        return 0, 128
+    n256 = w.num_kv_heads * sum(_cdiv(min(w.R, w.M - I * w.R) * g, 256) for I in range(MB))
+    return 0, (128 if n256 < TILE_SMALL_GRID_PER_CU * num_cus else 256)
+
+
+@pytest.mark.parametrize("num_cus", [4, 64, 256])
+def test_kernel_and_tile_rows_rule(num_cus):
+    ws = [W.by_name(n, values=False) for n in W.WORKLOAD_NAMES] + _small_cases()
+    ws.append(W.random_bsr(11, 4096, 4096, 128, 128, 32, 4, causal=True, density=0.2, values=False))
+    seen = set()
+    for w in ws:
+        inf = _plan(w, 1, num_cus=num_cus).info()
+        want = model_kernel(w, num_cus)
+        assert (inf["kernel"], inf["tile_rows"]) == want
+        seen.add(want)
+    # the rule's branches are all exercised at some CU count
+    assert {(0, 32), (0, 128), (2, 16), (1, 64)} <= seen
+
+
+def test_small_grids_use_128_row_tiles():
+    w = W.by_name("bsr_prefill", values=False)   # 1024 tiles of 256 rows: 4 per CU at 256 CUs
+    assert _plan(w, 1, num_cus=256).info()["tile_rows"] == 128
+    assert _plan(w, 1, num_cus=64).info()["tile_rows"] == 256
+    w = W.by_name("window_prefill", values=False)  # 8192 tiles of 256 rows
+    assert _plan(w, 1, num_cus=256).info()["tile_rows"] == 256
