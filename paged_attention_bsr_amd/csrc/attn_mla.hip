@@ -12,7 +12,8 @@
 //   * the workgroup gathers the 32 selected fp8 rows with 16-byte loads,
 //     widens them exactly to bf16 (every e4m3 value is a bf16 value; the
 //     dequant scale is applied to the logits and the output instead), and
-//     stores K row-major (chunk-swizzled, bf16) and V transposed (fp16) into LDS; two
+//     stores K row-major (bf16, rows padded to an odd number of 16-byte
+//     units) and V transposed (fp16) into LDS; two
 //     buffers let the next tile's loads overlap this tile's math;
 //   * each wave computes S^T = K Q^T for its 16 heads with
 //     v_mfma_f32_16x16x32_bf16 (Q^T resident in registers), runs the
@@ -29,9 +30,13 @@ namespace {
 constexpr int kDqk = 576;
 constexpr int kDv = 512;
 constexpr int kKT = 32;
+constexpr float kRescaleSlack = 8.f;  // log2 units the running max may lag behind
 
 struct MlaLds {
-  static constexpr int kKRow = kDqk * 2;                 // 1152 B of bf16 per key
+  // 1152 B of bf16 per key, padded by one 16-byte unit: 73 units per row is
+  // odd, so 16 consecutive keys at one chunk fall on 16 different bank
+  // groups without a swizzle, and chunk offsets stay immediate
+  static constexpr int kKRow = kDqk * 2 + 16;
   static constexpr int kKBytes = kKT * kKRow;            // 36864
   static constexpr int kVtStride = kKT * 2 + 8;          // 72 B per value dim
   static constexpr int kVtBytes = kDv * kVtStride;       // 36864
@@ -73,10 +78,13 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int quad = lane >> 4;
   const int col = lane & 15;
 
+  // read-only tables through the constant address space (scalar loads)
+  const cint32_t* cols = (const cint32_t*)(a.cols);
+  const cint32_t* lens = (const cint32_t*)(a.lens);
   const int32_t* trec = a.tiles + static_cast<int64_t>(blockIdx.x) * 8;
   const int I = trec[0];
   const int row0 = trec[2];
@@ -115,8 +123,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
     if (t >= npos) return -1;
     const int blk = t / C;
     const int off = t - blk * C;
-    const int J = a.cols[cb + blk];
-    if (LENS && off >= a.lens[cb + blk]) return -1;
+    const int J = cols[cb + blk];
+    if (LENS && off >= lens[cb + blk]) return -1;
     return J * C + off;
   };
 
@@ -149,22 +157,23 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
         b[2 * w] = fp8x2_to_bf16x2<false>(creg[i][w]);
         b[2 * w + 1] = fp8x2_to_bf16x2<true>(creg[i][w]);
       }
-      // K: bf16 chunks 2c and 2c + 1 of this key's row, XOR-swizzled by key
+      // K: bf16 chunks 2c and 2c + 1 of this key's row
       const int c0 = 2 * c, c1 = 2 * c + 1;
-      *reinterpret_cast<u32x4*>(base + my_key * L::kKRow + ((c0 ^ (my_key & 7)) << 4)) = u32x4{b[0], b[1], b[2], b[3]};
-      *reinterpret_cast<u32x4*>(base + my_key * L::kKRow + ((c1 ^ (my_key & 7)) << 4)) = u32x4{b[4], b[5], b[6], b[7]};
-      // V^T (fp16): the 16 values of this chunk, if they are latent (V) values
+      *reinterpret_cast<u32x4*>(base + my_key * L::kKRow + (c0 << 4)) = u32x4{b[0], b[1], b[2], b[3]};
+      *reinterpret_cast<u32x4*>(base + my_key * L::kKRow + (c1 << 4)) = u32x4{b[4], b[5], b[6], b[7]};
+      // V^T (fp16): the 16 values of this chunk, if they are latent (V) values.
+      // Lanes 2m and 2m + 1 hold keys 2m and 2m + 1 of the same chunk; after
+      // a DPP swap each writes one dword (both keys) per value pair: the even
+      // lane the even values, the odd lane the odd ones.
       if (c * 16 < kDv) {
-        uint32_t hb[8];
+        const bool odd = my_key & 1;
+        const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+        unsigned char* vrow = vt + (c * 16 + (odd ? 1 : 0)) * L::kVtStride + (my_key & ~1) * 2;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          hb[2 * w] = fp8x2_to_f16x2<false>(creg[i][w]);
-          hb[2 * w + 1] = fp8x2_to_f16x2<true>(creg[i][w]);
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const uint16_t hv = static_cast<uint16_t>(hb[e >> 1] >> ((e & 1) * 16));
-          *reinterpret_cast<uint16_t*>(vt + (c * 16 + e) * L::kVtStride + my_key * 2) = hv;
+        for (int w = 0; w < 8; ++w) {
+          const uint32_t own = w & 1 ? fp8x2_to_f16x2<true>(creg[i][w >> 1]) : fp8x2_to_f16x2<false>(creg[i][w >> 1]);
+          const uint32_t other = __builtin_amdgcn_mov_dpp(own, 0xB1, 0xF, 0xF, true);  // lane ^ 1
+          *reinterpret_cast<uint32_t*>(vrow + 2 * w * L::kVtStride) = __builtin_amdgcn_perm(other, own, sel);
         }
       }
     }
@@ -190,8 +199,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
     const int t0 = kt * kKT;
     const int t1 = (t0 + kKT < npos ? t0 + kKT : npos) - 1;
     const int blk0 = t0 / C, blk1 = t1 / C;
-    const int64_t tok_lo = static_cast<int64_t>(a.cols[cb + blk0]) * C + (t0 - blk0 * C);
-    const int64_t tok_hi = static_cast<int64_t>(a.cols[cb + blk1]) * C + (t1 - blk1 * C);
+    const int64_t tok_lo = static_cast<int64_t>(cols[cb + blk0]) * C + (t0 - blk0 * C);
+    const int64_t tok_hi = static_cast<int64_t>(cols[cb + blk1]) * C + (t1 - blk1 * C);
     if (CAUSAL && tok_lo > static_cast<int64_t>(qtok) + a.causal_off) continue;
     const bool need_mask = LENS || (t0 + kKT > npos) || (CAUSAL && tok_hi > static_cast<int64_t>(qtok) + a.causal_off);
 
@@ -199,17 +208,24 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
     const unsigned char* vt = kl + L::kKBytes;
     const int* ktok = reinterpret_cast<const int*>(kl + L::kKBytes + L::kVtBytes);
 
-    f32x4 s[2];
+    // S^T = K Q^T: 2 key blocks x 18 k-steps, K fragments read through a ring
+    // of kRing registers so that kRing LDS reads are always in flight
+    constexpr int kSteps = kDqk / 32;
+    constexpr int kRing = 8;
+    auto kfrag = [&](int j) {
+      const int key = (j / kSteps) * 16 + col;
+      const int c = (j % kSteps) * 4 + quad;
+      return *reinterpret_cast<const bf16x8*>(kl + key * L::kKRow + (c << 4));
+    };
+    f32x4 s[2] = {f32x4{}, f32x4{}};
+    bf16x8 kr[kRing];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x4{};
-      const int key = kb * 16 + col;
+    for (int j = 0; j < kRing; ++j) kr[j] = kfrag(j);
 #pragma unroll
-      for (int ks = 0; ks < kDqk / 32; ++ks) {
-        const int c = ks * 4 + quad;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kl + key * L::kKRow + ((c ^ (key & 7)) << 4));
-        s[kb] = MfmaType<__bf16>::mfma16(kf, qf[ks], s[kb]);
-      }
+    for (int j = 0; j < 2 * kSteps; ++j) {
+      const bf16x8 kf = kr[j % kRing];
+      if (j + kRing < 2 * kSteps) kr[j % kRing] = kfrag(j + kRing);
+      s[j / kSteps] = MfmaType<__bf16>::mfma16(kf, qf[j % kSteps], s[j / kSteps]);
     }
     if (need_mask) {
 #pragma unroll
@@ -230,9 +246,13 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
       for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kb][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx * sl2);
+    // lagging running max: it only moves when the tile exceeds it by more
+    // than 2^kRescaleSlack, so the rescale of the 512-wide O is rare
+    const float mt = mx * sl2;
+    const bool upd = mt > m_run + kRescaleSlack;
+    const float m_new = upd ? mt : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
+    const float alpha = upd ? fast_exp2(m_run - m_new) : 1.f;
     m_run = m_new;
     float ls = 0.f;
     f16x8 pf;
@@ -245,15 +265,25 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
         pf[kb * 4 + v] = static_cast<_Float16>(p);
       }
     l_run = l_run * alpha + ls;
+    if (__ballot(upd) != 0) {
 #pragma unroll
-    for (int db = 0; db < kDv / 16; ++db) oacc[db] *= alpha;
-    // O^T += V^T P^T: B element e of this lane is key (e / 4) * 16 + 4 * quad + e % 4
-#pragma unroll
-    for (int db = 0; db < kDv / 16; ++db) {
+      for (int db = 0; db < kDv / 16; ++db) oacc[db] *= alpha;
+    }
+    // O^T += V^T P^T: B element e of this lane is key (e / 4) * 16 + 4 * quad + e % 4;
+    // V^T fragments through a ring as above
+    auto vfrag = [&](int db) {
       const unsigned char* row = vt + (db * 16 + col) * L::kVtStride;
       const f16x4 lo = *reinterpret_cast<const f16x4*>(row + (4 * quad) * 2);
       const f16x4 hi = *reinterpret_cast<const f16x4*>(row + (16 + 4 * quad) * 2);
-      const f16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    f16x8 vr[kRing];
+#pragma unroll
+    for (int j = 0; j < kRing; ++j) vr[j] = vfrag(j);
+#pragma unroll
+    for (int db = 0; db < kDv / 16; ++db) {
+      const f16x8 vf = vr[db % kRing];
+      if (db + kRing < kDv / 16) vr[db % kRing] = vfrag(db + kRing);
       oacc[db] = MfmaType<_Float16>::mfma16(vf, pf, oacc[db]);
     }
   }
