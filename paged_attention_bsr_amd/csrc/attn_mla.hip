@@ -37,11 +37,15 @@ struct MlaLds {
   // odd, so 16 consecutive keys at one chunk fall on 16 different bank
   // groups without a swizzle, and chunk offsets stay immediate
   static constexpr int kKRow = kDqk * 2 + 16;
-  static constexpr int kKBytes = kKT * kKRow;            // 36864
+  static constexpr int kKBytes = kKT * kKRow;
   static constexpr int kVtStride = kKT * 2 + 8;          // 72 B per value dim
   static constexpr int kVtBytes = kDv * kVtStride;       // 36864
   static constexpr int kTokBytes = kKT * 4;
   static constexpr int kBuf = kKBytes + kVtBytes + kTokBytes;
+  // score exchange of a wave pair: [16 heads][kXsRow] fp32, rows padded to
+  // 36 floats so that 16 heads at one key offset hit distinct banks
+  static constexpr int kXsRow = kKT + 4;
+  static constexpr int kXsBytes = 16 * kXsRow * 4;
 };
 
 // Two OCP e4m3 bytes (the selected 16-bit half of `w`) -> two bf16 / two fp16
@@ -72,13 +76,16 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
   constexpr int NTHR = NW * 64;
   constexpr int NCHUNK = kKT * (kDqk / 16);  // 16-byte fp8 chunks per key tile
   constexpr int CH_PER_T = (NCHUNK + NTHR - 1) / NTHR;
-  static_assert(NTHR % kKT == 0, "loader maps one key per thread");
+  constexpr int NGROUP = NW / 2;             // 16-head groups per tile
+  static_assert(NTHR % kKT == 0 && NW % 2 == 0, "loader maps one key per thread; waves pair up");
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds[NBUF * L::kBuf];
+  __shared__ __attribute__((aligned(16))) unsigned char lds[NBUF * L::kBuf + NGROUP * L::kXsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hg = wave >> 1;  // head group: 16 heads
+  const int hf = wave & 1;   // which half of the key tile (scores) and of dv (output)
   const int quad = lane >> 4;
   const int col = lane & 15;
 
@@ -96,16 +103,17 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
   const int npos = (ce - cb) * C;
   const int ntiles = (npos + kKT - 1) / kKT;
 
-  // rows of a unit are the g qo heads of token I (R = 1)
-  const int rloc = wave * 16 + col;
+  // rows of a unit are the g qo heads of token I (R = 1); lane column = head
+  const int rloc = hg * 16 + col;
   const bool row_ok = rloc < nrows;
   const int head = row0 + rloc;
   const int qtok = I;
-  const bool wave_active = wave * 16 < nrows;
-  int qlim = 0x7fffffff;
+  const bool group_active = hg * 16 < nrows;
+  // key token t is visible to this row iff (unsigned)t < qbound (masked slots carry -1)
+  uint32_t qbound = 0x80000000u;
   if (CAUSAL) {
     const int64_t l = static_cast<int64_t>(qtok) + a.causal_off;
-    qlim = l > 0x7fffffff ? 0x7fffffff : (l < -1 ? -1 : static_cast<int>(l));
+    qbound = l >= 0x7fffffff ? 0x80000000u : (l < -1 ? 0u : static_cast<uint32_t>(l + 1));
   }
 
   bf16x8 qf[kDqk / 32];
@@ -158,9 +166,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
         b[2 * w + 1] = fp8x2_to_bf16x2<true>(creg[i][w]);
       }
       // K: bf16 chunks 2c and 2c + 1 of this key's row
-      const int c0 = 2 * c, c1 = 2 * c + 1;
-      *reinterpret_cast<u32x4*>(base + my_key * L::kKRow + (c0 << 4)) = u32x4{b[0], b[1], b[2], b[3]};
-      *reinterpret_cast<u32x4*>(base + my_key * L::kKRow + (c1 << 4)) = u32x4{b[4], b[5], b[6], b[7]};
+      *reinterpret_cast<u32x4*>(base + my_key * L::kKRow + ((2 * c) << 4)) = u32x4{b[0], b[1], b[2], b[3]};
+      *reinterpret_cast<u32x4*>(base + my_key * L::kKRow + ((2 * c + 1) << 4)) = u32x4{b[4], b[5], b[6], b[7]};
       // V^T (fp16): the 16 values of this chunk, if they are latent (V) values.
       // Lanes 2m and 2m + 1 hold keys 2m and 2m + 1 of the same chunk; after
       // a DPP swap each writes one dword (both keys) per value pair: the even
@@ -180,12 +187,15 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
     if (tid < kKT) reinterpret_cast<int*>(base + L::kKBytes + L::kVtBytes)[tid] = tok;
   };
 
-  f32x4 oacc[kDv / 16];
+  // this wave's output: O^T for dv in [256 * hf, 256 * hf + 256), its 16 heads
+  constexpr int NDB = kDv / 2 / 16;
+  f32x4 oacc[NDB];
 #pragma unroll
-  for (int db = 0; db < kDv / 16; ++db) oacc[db] = f32x4{};
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x4{};
   float m_run = -INFINITY;
-  float l_run = 0.f;
+  float l_run = 0.f;  // this lane's share (keys 8 * quad .. + 8 of every tile)
   const float sl2 = a.scale_log2;
+  float* xs = reinterpret_cast<float*>(lds + NBUF * L::kBuf + hg * L::kXsBytes);  // [16 heads][kXsRow]
 
   if (ntiles > 0) load_tile(0);
   for (int kt = 0; kt < ntiles; ++kt) {
@@ -194,8 +204,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
     store_tile(buf);
     __syncthreads();
     if (kt + 1 < ntiles) load_tile(kt + 1);
-    if (!wave_active) continue;
 
+    // tile-level decisions are the same for every wave (one query token)
     const int t0 = kt * kKT;
     const int t1 = (t0 + kKT < npos ? t0 + kKT : npos) - 1;
     const int blk0 = t0 / C, blk1 = t1 / C;
@@ -208,46 +218,55 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
     const unsigned char* vt = kl + L::kKBytes;
     const int* ktok = reinterpret_cast<const int*>(kl + L::kKBytes + L::kVtBytes);
 
-    // S^T = K Q^T: 2 key blocks x 18 k-steps, K fragments read through a ring
-    // of kRing registers so that kRing LDS reads are always in flight
-    constexpr int kSteps = kDqk / 32;
-    constexpr int kRing = 8;
-    auto kfrag = [&](int j) {
-      const int key = (j / kSteps) * 16 + col;
-      const int c = (j % kSteps) * 4 + quad;
-      return *reinterpret_cast<const bf16x8*>(kl + key * L::kKRow + (c << 4));
-    };
-    f32x4 s[2] = {f32x4{}, f32x4{}};
-    bf16x8 kr[kRing];
+    // (1) S^T of this wave's 16 keys (16 * hf ..) x 16 heads over all 576
+    // dims, 18 k-steps; K fragments through a small register ring
+    if (group_active) {
+      constexpr int kSteps = kDqk / 32;
+      constexpr int kRing = 4;
+      const unsigned char* krow = kl + (hf * 16 + col) * L::kKRow + quad * 16;
+      auto kfrag = [&](int ks) { return *reinterpret_cast<const bf16x8*>(krow + ks * 64); };
+      f32x4 sacc = f32x4{};
+      bf16x8 kr[kRing];
 #pragma unroll
-    for (int j = 0; j < kRing; ++j) kr[j] = kfrag(j);
+      for (int j = 0; j < kRing; ++j) kr[j] = kfrag(j);
 #pragma unroll
-    for (int j = 0; j < 2 * kSteps; ++j) {
-      const bf16x8 kf = kr[j % kRing];
-      if (j + kRing < 2 * kSteps) kr[j % kRing] = kfrag(j + kRing);
-      s[j / kSteps] = MfmaType<__bf16>::mfma16(kf, qf[j % kSteps], s[j / kSteps]);
+      for (int ks = 0; ks < kSteps; ++ks) {
+        const bf16x8 kf = kr[ks % kRing];
+        if (ks + kRing < kSteps) kr[ks % kRing] = kfrag(ks + kRing);
+        sacc = MfmaType<__bf16>::mfma16(kf, qf[ks], sacc);
+      }
+      // lane holds head col, keys 16 * hf + 4 * quad + v
+      *reinterpret_cast<f32x4*>(xs + col * L::kXsRow + hf * 16 + 4 * quad) = sacc;
+    }
+    __syncthreads();
+    if (!group_active) continue;
+
+    // (2) both waves of the pair read all 32 scores of their heads in the
+    // P^T operand layout (head col, keys 8 * quad + e) and run the same softmax
+    float sv[8];
+    {
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(xs + col * L::kXsRow + 8 * quad);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(xs + col * L::kXsRow + 8 * quad + 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sv[e] = lo[e];
+        sv[e + 4] = hi[e];
+      }
     }
     if (need_mask) {
+      const int4 ta = *reinterpret_cast<const int4*>(ktok + 8 * quad);
+      const int4 tb = *reinterpret_cast<const int4*>(ktok + 8 * quad + 4);
+      const int tt[8] = {ta.x, ta.y, ta.z, ta.w, tb.x, tb.y, tb.z, tb.w};
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int4 tk = *reinterpret_cast<const int4*>(ktok + kb * 16 + 4 * quad);
-        const int tt[4] = {tk.x, tk.y, tk.z, tk.w};
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const bool ok = tt[v] >= 0 && (!CAUSAL || tt[v] <= qlim);
-          if (!ok) s[kb][v] = -INFINITY;
-        }
-      }
+      for (int e = 0; e < 8; ++e) sv[e] = static_cast<uint32_t>(tt[e]) < qbound ? sv[e] : -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) mx = fmaxf(mx, s[kb][v]);
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sv[e]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     // lagging running max: it only moves when the tile exceeds it by more
-    // than 2^kRescaleSlack, so the rescale of the 512-wide O is rare
+    // than 2^kRescaleSlack, so the rescale of O is rare
     const float mt = mx * sl2;
     const bool upd = mt > m_run + kRescaleSlack;
     const float m_new = upd ? mt : m_run;
@@ -257,33 +276,24 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
     float ls = 0.f;
     f16x8 pf;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float p = fast_exp2(fmaf(s[kb][v], sl2, -m_use));
-        ls += p;
-        pf[kb * 4 + v] = static_cast<_Float16>(p);
-      }
+    for (int e = 0; e < 8; ++e) {
+      const float p = fast_exp2(fmaf(sv[e], sl2, -m_use));
+      ls += p;
+      pf[e] = static_cast<_Float16>(p);
+    }
     l_run = l_run * alpha + ls;
     if (__ballot(upd) != 0) {
 #pragma unroll
-      for (int db = 0; db < kDv / 16; ++db) oacc[db] *= alpha;
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
     }
-    // O^T += V^T P^T: B element e of this lane is key (e / 4) * 16 + 4 * quad + e % 4;
-    // V^T fragments through a ring as above
-    auto vfrag = [&](int db) {
-      const unsigned char* row = vt + (db * 16 + col) * L::kVtStride;
-      const f16x4 lo = *reinterpret_cast<const f16x4*>(row + (4 * quad) * 2);
-      const f16x4 hi = *reinterpret_cast<const f16x4*>(row + (16 + 4 * quad) * 2);
-      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    };
-    f16x8 vr[kRing];
+    // (3) O^T += V^T P^T for this wave's dv half: A = V^T rows (dv), keys
+    // 8 * quad + e, contiguous in a V^T row
+    const unsigned char* vrow = vt + (hf * (kDv / 2) + col) * L::kVtStride + 16 * quad;
 #pragma unroll
-    for (int j = 0; j < kRing; ++j) vr[j] = vfrag(j);
-#pragma unroll
-    for (int db = 0; db < kDv / 16; ++db) {
-      const f16x8 vf = vr[db % kRing];
-      if (db + kRing < kDv / 16) vr[db % kRing] = vfrag(db + kRing);
+    for (int db = 0; db < NDB; ++db) {
+      const f16x4 lo = *reinterpret_cast<const f16x4*>(vrow + db * 16 * L::kVtStride);
+      const f16x4 hi = *reinterpret_cast<const f16x4*>(vrow + db * 16 * L::kVtStride + 8);
+      const f16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       oacc[db] = MfmaType<_Float16>::mfma16(vf, pf, oacc[db]);
     }
   }
@@ -293,25 +303,27 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
   const float inv = l_tot > 0.f ? a.out_scale / l_tot : 0.f;
   const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   if (!row_ok) return;
+  const int dv0 = hf * (kDv / 2);
   if (part < 0) {
-    __bf16* op = static_cast<__bf16*>(a.o) + static_cast<int64_t>(qtok) * a.o_stride + static_cast<int64_t>(head) * kDv;
+    __bf16* op = static_cast<__bf16*>(a.o) + static_cast<int64_t>(qtok) * a.o_stride +
+                 static_cast<int64_t>(head) * kDv + dv0;
 #pragma unroll
-    for (int db = 0; db < kDv / 16; ++db) {
+    for (int db = 0; db < NDB; ++db) {
       bf16x4 out;
 #pragma unroll
       for (int v = 0; v < 4; ++v) out[v] = static_cast<__bf16>(oacc[db][v] * inv);
       *reinterpret_cast<bf16x4*>(op + db * 16 + 4 * quad) = out;
     }
-    if (quad == 0 && a.lse) a.lse[static_cast<int64_t>(qtok) * a.num_qo_heads + head] = lse_v;
+    if (hf == 0 && quad == 0 && a.lse) a.lse[static_cast<int64_t>(qtok) * a.num_qo_heads + head] = lse_v;
   } else {
     float* pp = a.part + part;
-    float* po = pp + static_cast<int64_t>(rloc) * kDv;
+    float* po = pp + static_cast<int64_t>(rloc) * kDv + dv0;
 #pragma unroll
-    for (int db = 0; db < kDv / 16; ++db) {
+    for (int db = 0; db < NDB; ++db) {
       f32x4 out = oacc[db] * inv;
       *reinterpret_cast<f32x4*>(po + db * 16 + 4 * quad) = out;
     }
-    if (quad == 0) pp[static_cast<int64_t>(nrows) * kDv + rloc] = lse_v;
+    if (hf == 0 && quad == 0) pp[static_cast<int64_t>(nrows) * kDv + rloc] = lse_v;
   }
 }
 
@@ -319,7 +331,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
 
 hipError_t launch_attn_mla(const AttnArgs& a, bool causal, bool has_lens, hipStream_t st) {
   if (a.num_tiles == 0) return hipSuccess;
-  constexpr int NW = 4;
+  constexpr int NW = 8;
   const dim3 grid(a.num_tiles), block(NW * 64);
   if (causal) {
     if (has_lens) attn_mla_kernel<NW, true, true><<<grid, block, 0, st>>>(a);
