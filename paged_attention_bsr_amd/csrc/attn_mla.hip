@@ -38,8 +38,7 @@ struct MlaLds {
   // groups without a swizzle, and chunk offsets stay immediate
   static constexpr int kKRow = kDqk * 2 + 16;
   static constexpr int kKBytes = kKT * kKRow;
-  static constexpr int kVtStride = kKT * 2 + 8;          // 72 B per value dim
-  static constexpr int kVtBytes = kDv * kVtStride;       // 36864
+  static constexpr int kVtBytes = kDv * kKT * 2;         // V^T: 64 B per value dim
   static constexpr int kTokBytes = kKT * 4;
   static constexpr int kBuf = kKBytes + kVtBytes + kTokBytes;
   // score exchange of a wave pair: [16 heads][kXsRow] fp32, rows padded to
@@ -63,6 +62,13 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+}
+
+// V^T tile: row d (value dim) holds the 32 keys' fp16 values, 64 B = four
+// 16-byte units of 8 keys; the unit index is XORed with bits 2-3 of the row,
+// so that a read of 16 consecutive rows at one unit touches every bank once.
+__device__ __forceinline__ int vt_off(int d, int key) {
+  return d * 64 + (((key >> 3) ^ ((d >> 2) & 3)) << 4) + (key & 7) * 2;
 }
 
 #ifndef BSA_MLA_NBUF
@@ -175,12 +181,12 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
       if (c * 16 < kDv) {
         const bool odd = my_key & 1;
         const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
-        unsigned char* vrow = vt + (c * 16 + (odd ? 1 : 0)) * L::kVtStride + (my_key & ~1) * 2;
 #pragma unroll
         for (int w = 0; w < 8; ++w) {
           const uint32_t own = w & 1 ? fp8x2_to_f16x2<true>(creg[i][w >> 1]) : fp8x2_to_f16x2<false>(creg[i][w >> 1]);
           const uint32_t other = __builtin_amdgcn_mov_dpp(own, 0xB1, 0xF, 0xF, true);  // lane ^ 1
-          *reinterpret_cast<uint32_t*>(vrow + 2 * w * L::kVtStride) = __builtin_amdgcn_perm(other, own, sel);
+          *reinterpret_cast<uint32_t*>(vt + vt_off(c * 16 + 2 * w + (odd ? 1 : 0), my_key & ~1)) =
+              __builtin_amdgcn_perm(other, own, sel);
         }
       }
     }
@@ -287,13 +293,11 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
     }
     // (3) O^T += V^T P^T for this wave's dv half: A = V^T rows (dv), keys
-    // 8 * quad + e, contiguous in a V^T row
-    const unsigned char* vrow = vt + (hf * (kDv / 2) + col) * L::kVtStride + 16 * quad;
+    // 8 * quad + e, one 16-byte unit of a V^T row
+    const unsigned char* vrow = vt + vt_off(hf * (kDv / 2) + col, 8 * quad);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const f16x4 lo = *reinterpret_cast<const f16x4*>(vrow + db * 16 * L::kVtStride);
-      const f16x4 hi = *reinterpret_cast<const f16x4*>(vrow + db * 16 * L::kVtStride + 8);
-      const f16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      const f16x8 vf = *reinterpret_cast<const f16x8*>(vrow + db * 16 * 64);
       oacc[db] = MfmaType<_Float16>::mfma16(vf, pf, oacc[db]);
     }
   }
