@@ -133,31 +133,49 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
     for (int ks = 0; ks < kDqk / 32; ++ks) qf[ks] = bf16x8{};
   }
 
-  auto key_tok = [&](int t) -> int {
-    if (t >= npos) return -1;
-    const int blk = t / C;
-    const int off = t - blk * C;
-    const int J = cols[cb + blk];
-    if (LENS && off >= lens[cb + blk]) return -1;
-    return J * C + off;
+  // token of key position t (-1 past the range or past a block's valid
+  // length), in two steps: fetch_blk issues the (unconditional, clamped)
+  // table loads, finish_tok uses them -- a tile later for the prefetched
+  // index, so that waiting for it never drains the row loads in flight
+  struct BlkRef {
+    int J;    // column block
+    int len;  // its valid length (LENS)
   };
-
+  auto fetch_blk = [&](int t) -> BlkRef {
+    const int tc = t < npos ? t : npos - 1;
+    const int blk = tc / C;
+    BlkRef r;
+    r.J = cols[cb + blk];
+    r.len = LENS ? lens[cb + blk] : C;
+    return r;
+  };
+  auto finish_tok = [&](int t, const BlkRef& r) -> int {
+    const int off = t - (t / C) * C;
+    bool ok = t < npos;
+    if (LENS) ok = ok && off < r.len;
+    return ok ? r.J * C + off : -1;
+  };
+  auto key_tok = [&](int t) -> int { return finish_tok(t, fetch_blk(t)); };
   const uint8_t* kv = static_cast<const uint8_t*>(a.k);
   const int my_key = tid % kKT;
-  u32x4 creg[CH_PER_T];
-  int tok = -1;
-  auto load_tile = [&](int kt) {
-    tok = key_tok(kt * kKT + my_key);
+  // two register sets: the rows of tile kt + 2 are in flight while tile kt is
+  // stored and computed
+  u32x4 creg_a[CH_PER_T], creg_b[CH_PER_T];
+  int tok_a = -1, tok_b = -1;
+  BlkRef blk_next{};  // table entries of the next tile to be fetched
+  // unconditional loads (masked keys and idle lanes read the workspace's zero
+  // row), so the wait counters keep the prefetch in flight
+  const uint8_t* zrow = static_cast<const uint8_t*>(a.zero_row);
+  auto load_tile = [&](u32x4 (&creg)[CH_PER_T], int tok) {
 #pragma unroll
     for (int i = 0; i < CH_PER_T; ++i) {
       const int ci = tid + i * NTHR;
-      const int c = ci / kKT;  // 16-byte chunk of the fp8 row
-      creg[i] = (ci < NCHUNK && tok >= 0)
-                    ? *reinterpret_cast<const u32x4*>(kv + static_cast<int64_t>(tok) * a.k_stride + c * 16)
-                    : u32x4{0, 0, 0, 0};
+      const int c = ci / kKT;  // 16-byte chunk of the fp8 row (< 48, inside the 1 KB zero row)
+      const uint8_t* src = (ci < NCHUNK && tok >= 0) ? kv + static_cast<int64_t>(tok) * a.k_stride : zrow;
+      creg[i] = *reinterpret_cast<const u32x4*>(src + c * 16);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, const u32x4 (&creg)[CH_PER_T], int tok) {
     unsigned char* base = lds + buf * L::kBuf;
     unsigned char* vt = base + L::kKBytes;
 #pragma unroll
@@ -203,13 +221,22 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
   const float sl2 = a.scale_log2;
   float* xs = reinterpret_cast<float*>(lds + NBUF * L::kBuf + hg * L::kXsBytes);  // [16 heads][kXsRow]
 
-  if (ntiles > 0) load_tile(0);
-  for (int kt = 0; kt < ntiles; ++kt) {
+  auto tile_step = [&](int kt, u32x4 (&creg)[CH_PER_T], int& tok) {
     const int buf = NBUF == 1 ? 0 : (kt & 1);
     if (NBUF == 1 && kt > 0) __syncthreads();  // single buffer: everyone is done reading it
-    store_tile(buf);
+    store_tile(buf, creg, tok);
     __syncthreads();
-    if (kt + 1 < ntiles) load_tile(kt + 1);
+    {
+      // index of tile kt + 3 first, then the rows of tile kt + 2 (whose index
+      // arrived during the previous tile): waiting for the index next time
+      // leaves these row loads in flight.  Past the last tile both resolve
+      // to masked keys.
+      const int t2 = finish_tok((kt + 2) * kKT + my_key, blk_next);
+      blk_next = fetch_blk((kt + 3) * kKT + my_key);
+      load_tile(creg, t2);
+      tok = t2;
+    }
+    if (kt >= ntiles) return;  // the odd step after the last tile: loads only
 
     // tile-level decisions are the same for every wave (one query token)
     const int t0 = kt * kKT;
@@ -217,7 +244,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
     const int blk0 = t0 / C, blk1 = t1 / C;
     const int64_t tok_lo = static_cast<int64_t>(cols[cb + blk0]) * C + (t0 - blk0 * C);
     const int64_t tok_hi = static_cast<int64_t>(cols[cb + blk1]) * C + (t1 - blk1 * C);
-    if (CAUSAL && tok_lo > static_cast<int64_t>(qtok) + a.causal_off) continue;
+    if (CAUSAL && tok_lo > static_cast<int64_t>(qtok) + a.causal_off) return;
     const bool need_mask = LENS || (t0 + kKT > npos) || (CAUSAL && tok_hi > static_cast<int64_t>(qtok) + a.causal_off);
 
     const unsigned char* kl = lds + buf * L::kBuf;
@@ -245,7 +272,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
       *reinterpret_cast<f32x4*>(xs + col * L::kXsRow + hf * 16 + 4 * quad) = sacc;
     }
     __syncthreads();
-    if (!group_active) continue;
+    if (!group_active) return;
 
     // (2) both waves of the pair read all 32 scores of their heads in the
     // P^T operand layout (head col, keys 8 * quad + e) and run the same softmax
@@ -300,6 +327,17 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
       const f16x8 vf = *reinterpret_cast<const f16x8*>(vrow + db * 16 * 64);
       oacc[db] = MfmaType<_Float16>::mfma16(vf, pf, oacc[db]);
     }
+  };
+  if (ntiles > 0) {
+    tok_a = key_tok(my_key);
+    load_tile(creg_a, tok_a);
+    tok_b = key_tok(kKT + my_key);
+    load_tile(creg_b, tok_b);
+    blk_next = fetch_blk(2 * kKT + my_key);
+  }
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    tile_step(kt, creg_a, tok_a);
+    tile_step(kt + 1, creg_b, tok_b);
   }
 
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
