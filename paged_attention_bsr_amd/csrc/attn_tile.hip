@@ -46,19 +46,21 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <int KT>
 struct TileLds {
-  static constexpr int kKBytes = KT * kD * 2;   // K: KT rows of 256 B
+  static constexpr int kKBytes = KT * (kD * 2 + 16);  // K: KT rows of 256 B, padded to 272
   static constexpr int kVBytes = KT * kD * 2;   // V: KT rows of 256 B
   static constexpr int kTokBytes = KT * 4;      // token of each key slot, -1 = masked
   static constexpr int kBuf = kKBytes + kVBytes + kTokBytes;
 };
 
-// Chunk swizzles for 64 banks x 4 B (a 16-byte-per-lane access is served
-// 16 lanes at a time, an 8-byte one up to 32 lanes at a time).  K: the 16
-// lanes of a phase read 16 different rows at one chunk, so the chunk is
-// XORed with the row's low 4 bits.  V: a transposing read touches 4
-// consecutive rows x 2 chunks per 16-lane group and a neighbouring group the
-// next 2 chunks of the same rows, so the chunk is XORed with 4 * (row % 4).
-__device__ __forceinline__ int k_off(int key, int c) { return key * 256 + ((c ^ (key & 15)) << 4); }
+// LDS layouts for 64 banks x 4 B (a 16-byte-per-lane access is served 16
+// lanes at a time, an 8-byte one up to 32 lanes at a time).  K: the 16 lanes
+// of a phase read 16 different rows at one chunk; rows are padded to 272 B
+// (17 units of 16 bytes, an odd count), so those rows fall on 16 different
+// bank groups and a k-step's chunk offset stays an immediate.  V: a
+// transposing read touches 4 consecutive rows x 2 chunks per 16-lane group
+// and a neighbouring group the next 2 chunks of the same rows, so the chunk
+// is XORed with 4 * (row % 4).
+__device__ __forceinline__ int k_off(int key, int c) { return key * (kD * 2 + 16) + (c << 4); }
 __device__ __forceinline__ int v_off(int key, int c) { return key * 256 + ((c ^ ((key & 3) << 2)) << 4); }
 
 // S^T row m of a 32-key block holds key swap23(m) (bits 2 and 3 exchanged).
