@@ -46,22 +46,25 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 template <int KT>
 struct TileLds {
-  static constexpr int kKBytes = KT * (kD * 2 + 16);  // K: KT rows of 256 B, padded to 272
+  static constexpr int kKBytes = KT * kD * 2;   // K: KT rows of 256 B
   static constexpr int kVBytes = KT * kD * 2;   // V: KT rows of 256 B
   static constexpr int kTokBytes = KT * 4;      // token of each key slot, -1 = masked
   static constexpr int kBuf = kKBytes + kVBytes + kTokBytes;
 };
 
 // LDS layouts for 64 banks x 4 B (a 16-byte-per-lane access is served 16
-// lanes at a time, an 8-byte one up to 32 lanes at a time).  K: the 16 lanes
-// of a phase read 16 different rows at one chunk; rows are padded to 272 B
-// (17 units of 16 bytes, an odd count), so those rows fall on 16 different
-// bank groups and a k-step's chunk offset stays an immediate.  V: a
-// transposing read touches 4 consecutive rows x 2 chunks per 16-lane group
-// and a neighbouring group the next 2 chunks of the same rows, so the chunk
-// is XORed with 4 * (row % 4).
-__device__ __forceinline__ int k_off(int key, int c) { return key * (kD * 2 + 16) + (c << 4); }
-__device__ __forceinline__ int v_off(int key, int c) { return key * 256 + ((c ^ ((key & 3) << 2)) << 4); }
+// lanes at a time, an 8-byte one up to 32 lanes at a time).  Both tiles are
+// row-major, 256 B per key, with the 16-byte chunks of a row permuted by an
+// XOR (so a DMA that fills 1 KB = 4 rows per wave instruction can place them:
+// each lane fetches the chunk that belongs in its slot).  K: the 16 lanes of
+// a read phase fetch 16 different rows at one chunk, so the chunk is XORed
+// with the row's low 4 bits.  V: a transposing read touches 4 consecutive
+// rows x 2 chunks per 16-lane group and a neighbouring group the next 2
+// chunks of the same rows, so the chunk is XORed with 4 * (row % 4).
+__device__ __forceinline__ int k_swz(int key) { return key & 15; }
+__device__ __forceinline__ int v_swz(int key) { return (key & 3) << 2; }
+__device__ __forceinline__ int k_off(int key, int c) { return key * 256 + ((c ^ k_swz(key)) << 4); }
+__device__ __forceinline__ int v_off(int key, int c) { return key * 256 + ((c ^ v_swz(key)) << 4); }
 
 // S^T row m of a 32-key block holds key swap23(m) (bits 2 and 3 exchanged).
 __device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
@@ -73,12 +76,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   using v4 = typename Ops::v4;
   using L = TileLds<KT>;
   constexpr int NTHR = NW * 64;
-  constexpr int KCH = KT * 16 / NTHR;  // 16-byte chunks per thread per tile, for K and for V
-  static_assert(KCH >= 1 && KT * 16 % NTHR == 0, "loader shape");
   constexpr int NKB = KT / 32;
-  constexpr int NSTAGE = 2;
 
-  __shared__ __attribute__((aligned(16))) unsigned char lds[NSTAGE * L::kBuf];
+  // two LDS stages as separate arrays: the compiler then knows that reading
+  // one stage does not depend on the DMA in flight into the other
+  __shared__ __attribute__((aligned(16))) unsigned char st0[L::kKBytes + L::kVBytes];
+  __shared__ __attribute__((aligned(16))) unsigned char st1[L::kKBytes + L::kVBytes];
+  // the key tokens (written by ordinary stores) live apart from the DMA target
+  __shared__ __attribute__((aligned(16))) int tk0[KT];
+  __shared__ __attribute__((aligned(16))) int tk1[KT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -173,30 +179,29 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   const T* vbase = static_cast<const T*>(a.v) + static_cast<int64_t>(kvh) * kD;
   const T* zrow = static_cast<const T*>(a.zero_row);
   const int lc = tid & 15;  // 16-byte chunk this thread moves within a row
-  u32x4 kreg[KCH], vreg[KCH];
-  int ktok_reg[KCH];
-  auto issue_loads = [&](int kt) {
-    const TileInfo ti = tile_info(kt < ntiles ? kt : ntiles - 1);
+  // ---- global -> LDS by DMA (global_load_lds, 16 B per lane): a K or V tile
+  // is KT/4 blocks of 1 KB = 4 rows; wave w fills blocks w*BPW .. (w+1)*BPW-1
+  // of both.  Lane l of a block serves row 4b + l/16 and slot l%16, i.e. it
+  // fetches chunk (l%16) ^ swz(row) of that row.  Masked keys read the zero row.
+  constexpr int KBLK = KT / 4;
+  constexpr int BPW = KBLK / NW;
+  static_assert(KBLK % NW == 0, "DMA blocks per wave");
+  auto dma_tile = [&](int kt, unsigned char* st, int* ktok) {
+    const TileInfo ti = tile_info(kt);
+    const int u = lane & 15;
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int key = (tid >> 4) + i * (NTHR / 16);
-      const int tok = kt < ntiles ? key_tok(kt, ti, key) : -1;
-      ktok_reg[i] = tok;
+    for (int j = 0; j < BPW; ++j) {
+      const int b = wave * BPW + j;
+      const int row = 4 * b + (lane >> 4);
+      const int tok = key_tok(kt, ti, row);
       const T* pk = tok >= 0 ? kbase + static_cast<int64_t>(tok) * a.k_stride : zrow;
       const T* pv = tok >= 0 ? vbase + static_cast<int64_t>(tok) * a.v_stride : zrow;
-      kreg[i] = *reinterpret_cast<const u32x4*>(pk + lc * 8);
-      vreg[i] = *reinterpret_cast<const u32x4*>(pv + lc * 8);
-    }
-  };
-  auto commit = [&](int slot) {
-    unsigned char* base = lds + slot * L::kBuf;
-    int* ktok = reinterpret_cast<int*>(base + L::kKBytes + L::kVBytes);
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int key = (tid >> 4) + i * (NTHR / 16);
-      *reinterpret_cast<u32x4*>(base + k_off(key, lc)) = kreg[i];
-      *reinterpret_cast<u32x4*>(base + L::kKBytes + v_off(key, lc)) = vreg[i];
-      if (lc == 0) ktok[key] = ktok_reg[i];
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(pk + (u ^ k_swz(row)) * 8),
+                                       (__attribute__((address_space(3))) void*)(st + b * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(pv + (u ^ v_swz(row)) * 8),
+                                       (__attribute__((address_space(3))) void*)(st + L::kKBytes + b * 1024), 16, 0,
+                                       0);
+      if (u == 0) ktok[row] = tok;
     }
   };
 
@@ -208,25 +213,25 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     lo = static_cast<int64_t>(cols[cb + blk0]) * C + (t0 - blk0 * C);
     hi = static_cast<int64_t>(cols[cb + blk1]) * C + (t1 - blk1 * C);
   };
-  // the whole tile lies above this wave's causal diagonal
-  auto wave_skips = [&](int kt) -> bool {
-    if (!CAUSAL || kt >= ntiles) return kt >= ntiles;
-    int64_t lo, hi;
-    tile_tok_range(kt, lo, hi);
-    return lo > wave_lim;
-  };
 
-  auto qk = [&](int slot, f32x16 (&sacc)[NKB]) {
-    const unsigned char* kl = lds + slot * L::kBuf;
+  // all eight K fragments of a 32-key block are read before its products,
+  // so the LDS latency is paid once per block rather than per k-step
+  auto qk = [&](const unsigned char* kl, f32x16 (&sacc)[NKB]) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      sacc[kb] = f32x16{};
       const int key = kb * 32 + swap23(ql);
+      v8 kf[8];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const v8 kf = *reinterpret_cast<const v8*>(kl + k_off(key, 2 * ks + half));
-        sacc[kb] = Ops::mfma32(kf, qf[ks], sacc[kb]);
-      }
+      for (int ks = 0; ks < 8; ++ks) kf[ks] = *reinterpret_cast<const v8*>(kl + k_off(key, 2 * ks + half));
+      sacc[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) sacc[kb] = Ops::mfma32(kf[ks], qf[ks], sacc[kb]);
+    }
+    // keep that order: the scheduler would otherwise pair each read with its product
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // 8 LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // 8 MFMAs
     }
   };
 
@@ -237,13 +242,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   float l_run = 0.f;
   const float sl2 = a.scale_log2;
 
-  // causal / length mask of S(kt) (only on tiles that need it)
-  auto mask_scores = [&](int kt, int slot, f32x16 (&sacc)[NKB]) {
-    int64_t lo, hi;
-    tile_tok_range(kt, lo, hi);
-    const bool need_mask = LENS || (kt * KT + KT > npos) || (CAUSAL && hi > wave_lim_lo);
+  // causal / length mask of S (only on tiles that need it)
+  auto mask_scores = [&](bool need_mask, const int* ktok, f32x16 (&sacc)[NKB]) {
     if (!need_mask) return;
-    const int* ktok = reinterpret_cast<const int*>(lds + slot * L::kBuf + L::kKBytes + L::kVBytes);
     // value 4*g4 + e of this lane is S^T row 8*g4 + 4*half + e, i.e. key
     // 16*(g4/2) + 8*half + 4*(g4%2) + e of the block
 #pragma unroll
@@ -292,8 +293,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   const int Lg = lane & 15;
   const int vrow = 8 * half + (Lg >> 2);          // + ks*16 + 4*j
   const int vdim = 16 * (G & 1) + 4 * (Lg & 3);   // + db*32
-  auto pv = [&](int slot, const f32x16 (&sacc)[NKB]) {
-    const unsigned char* vl = lds + slot * L::kBuf + L::kKBytes;
+  auto pv = [&](const unsigned char* st, const f32x16 (&sacc)[NKB]) {
+    const unsigned char* vl = st + L::kKBytes;
     // k-step ks covers keys ks*16 .. +16: lane half h holds keys ks*16 + 8h + e
     // (e = 0..7), from S^T values hv*8 + e of block ks/2
 #pragma unroll
@@ -318,26 +319,35 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     }
   };
 
-  // ---- key loop: two LDS stages, one barrier per tile; the loads of tile t+1
-  // are in flight while tile t is computed
-  if (ntiles > 0) {
-    issue_loads(0);
-    for (int t = 0; t < ntiles; ++t) {
-      const int slot = t & 1;
-      commit(slot);
-      __syncthreads();
-      issue_loads(t + 1);
-      if (!wave_active || wave_skips(t)) continue;
-      f32x16 sc[NKB];
-      qk(slot, sc);
-      mask_scores(t, slot, sc);
-      bool upd;
-      const float alpha = softmax_core(sc, true, upd);
-      if (__ballot(upd) != 0) {
+  // ---- key loop: two LDS stages, one barrier per tile; the DMA of tile t+1
+  // is in flight while tile t is computed
+  auto step = [&](int t, unsigned char* cur, const int* curtok, unsigned char* nxt, int* nxttok) {
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's DMA into `cur` has landed
+    __syncthreads();                     // ... and every other wave's
+    // every scalar table read of the iteration happens here, before the LDS
+    // math: an outstanding scalar load would turn each LDS wait into a full
+    // drain (both share one counter)
+    int64_t lo = 0, hi = 0;
+    if (CAUSAL) tile_tok_range(t, lo, hi);
+    if (t + 1 < ntiles) dma_tile(t + 1, nxt, nxttok);
+    if (!wave_active || (CAUSAL && lo > wave_lim)) return;  // tile above this wave's diagonal
+    const bool need_mask = LENS || (t * KT + KT > npos) || (CAUSAL && hi > wave_lim_lo);
+    f32x16 sc[NKB];
+    qk(cur, sc);
+    mask_scores(need_mask, curtok, sc);
+    bool upd;
+    const float alpha = softmax_core(sc, true, upd);
+    if (__ballot(upd) != 0) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-      }
-      pv(slot, sc);
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+    }
+    pv(cur, sc);
+  };
+  if (ntiles > 0) {
+    dma_tile(0, st0, tk0);
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, st0, tk0, st1, tk1);
+      if (t + 1 < ntiles) step(t + 1, st1, tk1, st0, tk0);
     }
   }
 
