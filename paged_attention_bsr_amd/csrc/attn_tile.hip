@@ -405,7 +405,9 @@ hipError_t launch_typed(const AttnArgs& a, int tile_rows, bool causal, bool lens
   switch (tile_rows) {
     case 32: return launch_variant<T, 1, 32>(a, causal, lens, st);
     case 128: return launch_variant<T, 4, 64>(a, causal, lens, st);
-    case 256: return launch_variant<T, 8, 64>(a, causal, lens, st);
+    // 128-key tiles (two 64 KB LDS stages) when every tile lies in one block
+    case 256: return a.C % 128 == 0 ? launch_variant<T, 8, 128>(a, causal, lens, st)
+                                     : launch_variant<T, 8, 64>(a, causal, lens, st);
     default: return hipErrorInvalidValue;
   }
 }
