@@ -221,10 +221,15 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
   const float sl2 = a.scale_log2;
   float* xs = reinterpret_cast<float*>(lds + NBUF * L::kBuf + hg * L::kXsBytes);  // [16 heads][kXsRow]
 
-  auto tile_step = [&](int kt, u32x4 (&creg)[CH_PER_T], int& tok) {
-    const int buf = NBUF == 1 ? 0 : (kt & 1);
-    if (NBUF == 1 && kt > 0) __syncthreads();  // single buffer: everyone is done reading it
-    store_tile(buf, creg, tok);
+  // One tile.  `ld`: registers of tile kt (stored last iteration), refilled
+  // with the rows of tile kt + 2; `nx`: registers of tile kt + 1, widened and
+  // stored into the other LDS buffer while this tile's products run.  Barrier
+  // A: tile kt is in LDS and every wave is done with tile kt - 1 (its buffer
+  // and the score exchange area are free).  Barrier B: scores exchanged,
+  // tile kt + 1 stored.
+  auto tile_step = [&](int kt, u32x4 (&ld)[CH_PER_T], int& ld_tok, const u32x4 (&nx)[CH_PER_T], int nx_tok) {
+    static_assert(NBUF == 2, "the next tile is stored while this one is computed");
+    const int buf = kt & 1;
     __syncthreads();
     {
       // index of tile kt + 3 first, then the rows of tile kt + 2 (whose index
@@ -233,8 +238,8 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
       // to masked keys.
       const int t2 = finish_tok((kt + 2) * kKT + my_key, blk_next);
       blk_next = fetch_blk((kt + 3) * kKT + my_key);
-      load_tile(creg, t2);
-      tok = t2;
+      load_tile(ld, t2);
+      ld_tok = t2;
     }
     if (kt >= ntiles) return;  // the odd step after the last tile: loads only
 
@@ -244,7 +249,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
     const int blk0 = t0 / C, blk1 = t1 / C;
     const int64_t tok_lo = static_cast<int64_t>(cols[cb + blk0]) * C + (t0 - blk0 * C);
     const int64_t tok_hi = static_cast<int64_t>(cols[cb + blk1]) * C + (t1 - blk1 * C);
-    if (CAUSAL && tok_lo > static_cast<int64_t>(qtok) + a.causal_off) return;
+    const bool skip = CAUSAL && tok_lo > static_cast<int64_t>(qtok) + a.causal_off;
     const bool need_mask = LENS || (t0 + kKT > npos) || (CAUSAL && tok_hi > static_cast<int64_t>(qtok) + a.causal_off);
 
     const unsigned char* kl = lds + buf * L::kBuf;
@@ -253,7 +258,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
 
     // (1) S^T of this wave's 16 keys (16 * hf ..) x 16 heads over all 576
     // dims, 18 k-steps; K fragments through a small register ring
-    if (group_active) {
+    if (group_active && !skip) {
       constexpr int kSteps = kDqk / 32;
       constexpr int kRing = 4;
       const unsigned char* krow = kl + (hf * 16 + col) * L::kKRow + quad * 16;
@@ -271,8 +276,9 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
       // lane holds head col, keys 16 * hf + 4 * quad + v
       *reinterpret_cast<f32x4*>(xs + col * L::kXsRow + hf * 16 + 4 * quad) = sacc;
     }
+    if (kt + 1 < ntiles) store_tile(buf ^ 1, nx, nx_tok);
     __syncthreads();
-    if (!group_active) return;
+    if (!group_active || skip) return;
 
     // (2) both waves of the pair read all 32 scores of their heads in the
     // P^T operand layout (head col, keys 8 * quad + e) and run the same softmax
@@ -334,10 +340,11 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
     tok_b = key_tok(kKT + my_key);
     load_tile(creg_b, tok_b);
     blk_next = fetch_blk(2 * kKT + my_key);
+    store_tile(0, creg_a, tok_a);
   }
   for (int kt = 0; kt < ntiles; kt += 2) {
-    tile_step(kt, creg_a, tok_a);
-    tile_step(kt + 1, creg_b, tok_b);
+    tile_step(kt, creg_a, tok_a, creg_b, tok_b);
+    tile_step(kt + 1, creg_b, tok_b, creg_a, tok_a);
   }
 
   float l_tot = l_run + __shfl_xor(l_run, 16, 64);
