@@ -176,3 +176,32 @@ def test_full_size_workload(name):
     kv_splits, rows = W.BENCH_KV_SPLITS[name], FULL_ROWS[name]
     w = W.by_name(name)
     _check(w, kv_splits, rows=rows, what=f"full {name} splits={kv_splits}")
+
+
+# Every launch variant of the generic tile kernel: (rows per tile, keys per
+# tile, whole tiles inside one block or not, causal, valid lengths, dtype).
+# Planning for 1 CU keeps the planner from shrinking 256-row tiles to 128.
+TILE_VARIANTS = [
+    # (seed, M, NB, R, C, Hq, Hkv, causal, lens, dtype, expected tile_rows)
+    (31, 128, 6, 64, 64, 16, 4, True, False, torch.float16, 256),     # 64-key tiles, whole blocks
+    (32, 96, 20, 32, 48, 32, 4, False, True, torch.float16, 256),     # 64-key tiles over 48-key blocks
+    (33, 192, 4, 64, 256, 32, 4, True, True, torch.float16, 256),     # 128-key tiles, 2 per block, lens
+    (34, 256, 3, 128, 128, 16, 4, False, False, torch.bfloat16, 256), # 128-key tiles, bf16
+    (35, 96, 12, 32, 32, 16, 4, True, False, torch.float16, 128),     # 128-row tiles over 32-key blocks
+    (36, 40, 30, 8, 16, 16, 4, True, True, torch.float16, 32),        # 32-row tiles
+]
+
+
+@pytest.mark.parametrize("case", TILE_VARIANTS, ids=[f"v{c[0]}" for c in TILE_VARIANTS])
+@pytest.mark.parametrize("kv_splits", [1, 3])
+def test_tile_kernel_variants(case, kv_splits):
+    seed, M, NB, R, C, Hq, Hkv, causal, lens, dtype, rows = case
+    w = W.random_bsr(seed, M, NB * C, R, C, Hq, Hkv, causal=causal, partial_lens=lens, density=0.6,
+                     dtype=dtype, garbage=6e4 if lens else 0.0)
+    p = plan_for(w, kv_splits, num_cus=1)
+    assert p.info()["kernel"] == 0 and p.info()["tile_rows"] == rows
+    what = f"tile variant s{seed} rows={rows} C={C} splits={kv_splits}"
+    say(f"[parity] {what}")
+    o, lse = run_gpu(w, kv_splits, plan=p)
+    o_ref, lse_ref = oracle_result(w)
+    compare(o, lse, o_ref, lse_ref, tol_for(w), what)
