@@ -205,3 +205,20 @@ def test_tile_kernel_variants(case, kv_splits):
     o, lse = run_gpu(w, kv_splits, plan=p)
     o_ref, lse_ref = oracle_result(w)
     compare(o, lse, o_ref, lse_ref, tol_for(w), what)
+
+
+@pytest.mark.parametrize("causal,lens", [(True, False), (False, True), (True, True)])
+def test_mla_kernel_variants(causal, lens):
+    """Causal masking (early tokens lose the newest selected rows), per-block valid lengths
+    (all 1 for R = C = 1: the masked path with nothing to mask), 40 heads (a partial
+    16-head group) and 96 keys per token (an odd number of 32-key tiles)."""
+    w = W.sparse_mla(seed=37, num_tokens=64, num_heads=40, cache_rows=1024, topk=96, min_ctx=1024,
+                     max_ctx=1024)
+    w.causal = causal
+    if lens:
+        w.kv_block_lens = np.ones(w.N // w.C, np.int32)
+    if causal:  # make sure some selected rows lie above the diagonal of some token
+        off = w.N - w.M
+        assert any(int(j) > t + off for t in range(w.M) for j in w.indices[w.indptr[t]:w.indptr[t + 1]])
+    _check(w, 1, what=f"mla variant causal={causal} lens={lens}")
+    _check(w, 3, what=f"mla variant causal={causal} lens={lens} splits=3")
