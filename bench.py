@@ -142,7 +142,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
-              "the attention shards by kv head or request with no exchange, see DESIGN.md.", file=sys.stderr)
+              "the attention would shard by kv head or by request with no exchange between GPUs.", file=sys.stderr)
         return 2
 
     import numpy as np

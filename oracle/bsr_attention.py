@@ -24,7 +24,7 @@ the same boolean mask).  Every step is written out plainly in float64:
                                           (run(): o and the log-sum-exp of the logits)
   O7  merge of (o, lse) attention states  (flashinfer.cascade merge_state(s))
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   * lse is the natural log of sum(exp(sm_scale * q.k)) over unmasked keys;
   * a row with no unmasked key has o = 0 and lse = -inf;
   * causal masking keeps key j for query i iff j <= i + (N - M);
