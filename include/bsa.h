@@ -50,7 +50,7 @@ typedef struct bsa_plan_s* bsa_plan_t;
 typedef enum {
   BSA_OK = 0,
   BSA_ERR_INVALID_ARGUMENT = 1,   /* malformed structure, bad sizes, null/misaligned pointer */
-  BSA_ERR_UNSUPPORTED = 2,        /* valid request this build has no kernel for */
+  BSA_ERR_UNSUPPORTED = 2,        /* valid request the library has no kernel for */
   BSA_ERR_WORKSPACE_TOO_SMALL = 3,
   BSA_ERR_HIP = 4,                /* a HIP runtime call or kernel launch failed */
   BSA_ERR_HOST_ALLOC = 5          /* host memory allocation failed */
