@@ -6,18 +6,22 @@
 // per-tensor scales folded as bmm1 = sm_scale * q_descale * k_descale and
 // bmm2 = v_descale).
 //
-// One workgroup = one planner tile = 16 * NW heads of one query token.  The
-// heads are the MFMA row dimension, so every gathered cache row is used by
-// all heads of the tile.  Per key tile of 32 keys:
-//   * the workgroup gathers the 32 selected fp8 rows with 16-byte loads,
-//     widens them exactly to bf16 (every e4m3 value is a bf16 value; the
-//     dequant scale is applied to the logits and the output instead), and
-//     stores K row-major (bf16, rows padded to an odd number of 16-byte
-//     units) and V transposed (fp16) into LDS; two
-//     buffers let the next tile's loads overlap this tile's math;
-//   * each wave computes S^T = K Q^T for its 16 heads with
-//     v_mfma_f32_16x16x32_bf16 (Q^T resident in registers), runs the
-//     online softmax in the log2 domain, and accumulates O^T += V^T P^T with
+// One workgroup = one planner tile = 64 heads of one query token, 8 waves:
+// four groups of 16 heads, two waves per group.  The heads are the MFMA
+// column dimension, so every gathered cache row is used by all heads of the
+// tile.  Per key tile of 32 keys:
+//   * the selected fp8 rows are gathered with 16-byte loads two tiles ahead
+//     (the per-key index one tile ahead of its use), widened exactly to bf16
+//     (every e4m3 value is a bf16 value; the dequant scale is applied to the
+//     logits and the output instead) and stored as K rows (bf16, rows padded
+//     to an odd number of 16-byte units) and V^T (fp16, 64-byte rows with
+//     XOR-swizzled 16-byte units) into the LDS buffer of the next tile while
+//     this tile's scores are computed;
+//   * wave h of a pair computes S^T = K Q^T for keys 16h .. 16h+15 of the
+//     tile with v_mfma_f32_16x16x32_bf16 (Q^T resident in registers); the
+//     pair swaps its fp32 scores through LDS, both waves run the same online
+//     softmax (log2 domain, lagging running max) on all 32 keys, and wave h
+//     accumulates O^T += V^T P^T for value dims 256h .. 256h+255 with
 //     v_mfma_f32_16x16x32_f16: V is held as fp16 (exact for e4m3 values), so
 //     P keeps fp16's 11-bit precision instead of bf16's 8 bits.
 #include "device_common.h"
@@ -71,13 +75,10 @@ __device__ __forceinline__ int vt_off(int d, int key) {
   return d * 64 + (((key >> 3) ^ ((d >> 2) & 3)) << 4) + (key & 7) * 2;
 }
 
-#ifndef BSA_MLA_NBUF
-#define BSA_MLA_NBUF 2
-#endif
 
 template <int NW, bool CAUSAL, bool LENS>
 __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
-  constexpr int NBUF = BSA_MLA_NBUF;
+  constexpr int NBUF = 2;  // LDS tile buffers: tile kt + 1 is stored while tile kt is computed
   using L = MlaLds;
   constexpr int NTHR = NW * 64;
   constexpr int NCHUNK = kKT * (kDqk / 16);  // 16-byte fp8 chunks per key tile
@@ -228,7 +229,6 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
   // and the score exchange area are free).  Barrier B: scores exchanged,
   // tile kt + 1 stored.
   auto tile_step = [&](int kt, u32x4 (&ld)[CH_PER_T], int& ld_tok, const u32x4 (&nx)[CH_PER_T], int nx_tok) {
-    static_assert(NBUF == 2, "the next tile is stored while this one is computed");
     const int buf = kt & 1;
     __syncthreads();
     {

@@ -7,13 +7,15 @@
 // (flashinfer.sparse BlockSparseAttentionWrapper: BSR mask, GQA head
 // grouping; the key loop is ordinary flash-style online softmax).
 //
-// Per key tile of KT keys:
-//   * the whole workgroup gathers the K and V rows of the tile by block index
-//     with coalesced 16-byte loads (16 lanes per 256-byte row; keys outside a
-//     block's valid length, or past the range, load from a zero row) into
-//     row-major LDS tiles whose 16-byte chunks are XOR-swizzled by key; loads
-//     for tile t+1 are in flight while tile t is computed (two LDS buffers,
-//     one barrier per tile);
+// Per key tile of KT keys (64, or 128 for 256-row tiles over blocks of a
+// multiple of 128 keys):
+//   * the K and V rows of the tile are gathered by block index straight into
+//     LDS with global_load_lds (16 bytes per lane, each wave instruction
+//     filling 1 KB = 4 rows; keys outside a block's valid length, or past the
+//     range, read a zero row); the 16-byte chunks of each row are XOR-
+//     swizzled by key, each lane fetching the chunk that belongs in its slot.
+//     The DMA of tile t+1 lands in the other of two LDS stages while tile t
+//     is computed; one wait + barrier per tile;
 //   * each wave computes S^T = K Q^T for its 32 rows with
 //     v_mfma_f32_32x32x16 (K from LDS as the A operand, Q^T held in
 //     registers as B), so every lane owns one query row and its row max
@@ -48,8 +50,6 @@ template <int KT>
 struct TileLds {
   static constexpr int kKBytes = KT * kD * 2;   // K: KT rows of 256 B
   static constexpr int kVBytes = KT * kD * 2;   // V: KT rows of 256 B
-  static constexpr int kTokBytes = KT * 4;      // token of each key slot, -1 = masked
-  static constexpr int kBuf = kKBytes + kVBytes + kTokBytes;
 };
 
 // LDS layouts for 64 banks x 4 B (a 16-byte-per-lane access is served 16
@@ -178,7 +178,6 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   const T* kbase = static_cast<const T*>(a.k) + static_cast<int64_t>(kvh) * kD;
   const T* vbase = static_cast<const T*>(a.v) + static_cast<int64_t>(kvh) * kD;
   const T* zrow = static_cast<const T*>(a.zero_row);
-  const int lc = tid & 15;  // 16-byte chunk this thread moves within a row
   // ---- global -> LDS by DMA (global_load_lds, 16 B per lane): a K or V tile
   // is KT/4 blocks of 1 KB = 4 rows; wave w fills blocks w*BPW .. (w+1)*BPW-1
   // of both.  Lane l of a block serves row 4b + l/16 and slot l%16, i.e. it
