@@ -80,8 +80,10 @@ typedef enum {
  *   sm_scale       softmax scale; <= 0 selects 1/sqrt(head_dim_qk)
  *   kv_splits      1 = no split-KV; k > 1 = at most k contiguous partitions of
  *                  each row's blocks; 0 = automatic (from the sparsity and
- *                  num_cus).  Split partials live in the workspace and are
- *                  LSE-merged by a second kernel.
+ *                  num_cus; for the decode kernel an equal share of all keys
+ *                  per resident workgroup, see bsa_plan_export_workgroups).
+ *                  Split partials live in the workspace and are LSE-merged by
+ *                  a second kernel.
  *   kv_block_lens  NULL, or int32[NB] valid tokens per key block, each in [1, C]
  *   q/kv/o_dtype   storage types.  Supported: all BSA_F16, or all BSA_BF16
  *                  (head_dim 128); or q/o BSA_BF16 with kv BSA_FP8_E4M3 and
@@ -210,6 +212,8 @@ typedef struct {
   int32_t num_cols;        /* entries of the column table */
   int32_t max_splits;
   int32_t num_cus;
+  int32_t num_workgroups;  /* workgroups of the attention launch */
+  int32_t heads_per_wg;    /* kv heads per tile group (1 except for the decode kernel) */
   int64_t table_bytes;     /* int tables at the start of the workspace */
   int64_t partial_bytes;   /* split partials after the tables */
   int64_t workspace_bytes;
@@ -223,7 +227,7 @@ bsa_status_t bsa_plan_info(bsa_plan_t plan, bsa_plan_info_t* info);
  * bsa_plan_info (any pointer may be NULL to skip it):
  *   tiles   int32[num_tiles][8]  = {row_block, kv_head, row0, nrows,
  *                                   col_begin, col_end, partial_offset, key_count}
- *           in launch order; row r of a tile (row0 <= r < row0 + nrows) is
+ *           in launch order (see bsa_plan_export_workgroups); row r of a tile (row0 <= r < row0 + nrows) is
  *           query token row_block*R + r / g and qo head kv_head*g + r % g
  *           (g = num_qo_heads / num_kv_heads); its keys are the blocks
  *           cols[col_begin .. col_end); partial_offset is -1 when the tile
@@ -235,6 +239,21 @@ bsa_status_t bsa_plan_info(bsa_plan_t plan, bsa_plan_info_t* info);
  *           order, without blocks that the causal mask removes entirely.
  */
 bsa_status_t bsa_plan_export(bsa_plan_t plan, int32_t* tiles, int32_t* merges, int32_t* cols);
+
+/*
+ * Copy the workgroup table, int32[num_workgroups + 1], to a caller-owned host
+ * array: workgroup w of the attention launch runs tiles wg_ptr[w] ..
+ * wg_ptr[w+1]-1 in that order.  Tiles come in groups of heads_per_wg tiles
+ * (same row block and blocks, consecutive kv heads: the decode kernel gives
+ * each kv head of a group its own waves); each workgroup runs one group (the
+ * hardware handing out groups longest first), except for the decode kernel
+ * with kv_splits = 0: there the automatic split-KV partition
+ * (BlockSparseAttentionWrapper.plan, kv_splits "auto") gives each of a fixed
+ * number of resident workgroups an equal share of all keys, cutting rows
+ * where the shares end.  Returns BSA_ERR_INVALID_ARGUMENT for a NULL plan or
+ * array.
+ */
+bsa_status_t bsa_plan_export_workgroups(bsa_plan_t plan, int32_t* wg_ptr);
 
 void bsa_plan_destroy(bsa_plan_t plan);
 

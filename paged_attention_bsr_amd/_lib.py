@@ -61,6 +61,8 @@ class PlanInfo(ctypes.Structure):
         ("num_cols", ctypes.c_int32),
         ("max_splits", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
+        ("num_workgroups", ctypes.c_int32),
+        ("heads_per_wg", ctypes.c_int32),
         ("table_bytes", ctypes.c_int64),
         ("partial_bytes", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_int64),
@@ -102,6 +104,8 @@ def lib() -> ctypes.CDLL:
     L.bsa_plan_info.restype = st
     L.bsa_plan_export.argtypes = [vp, _i32p, _i32p, _i32p]
     L.bsa_plan_export.restype = st
+    L.bsa_plan_export_workgroups.argtypes = [vp, _i32p]
+    L.bsa_plan_export_workgroups.restype = st
     L.bsa_plan_destroy.argtypes = [vp]
     L.bsa_plan_destroy.restype = None
     L.bsa_last_error.argtypes = []

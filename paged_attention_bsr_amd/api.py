@@ -91,13 +91,15 @@ class Plan:
         return int(L.lib().bsa_workspace_size(self._handle))
 
     def tables(self) -> dict:
-        """The planner's tables (tiles (T, 8), merges (S, 8), cols) as int32 numpy arrays."""
+        """The planner's tables (tiles (T, 8), merges (S, 8), cols, wg_ptr (W + 1)) as int32 numpy arrays."""
         inf = self.info()
         tiles = np.zeros((inf["num_tiles"], 8), np.int32)
         merges = np.zeros((inf["num_merges"], 8), np.int32)
         cols = np.zeros(inf["num_cols"], np.int32)
+        wg_ptr = np.zeros(inf["num_workgroups"] + 1, np.int32)
         L.check(L.lib().bsa_plan_export(self._handle, _ptr(tiles), _ptr(merges), _ptr(cols)))
-        return {"tiles": tiles, "merges": merges, "cols": cols}
+        L.check(L.lib().bsa_plan_export_workgroups(self._handle, _ptr(wg_ptr)))
+        return {"tiles": tiles, "merges": merges, "cols": cols, "wg_ptr": wg_ptr}
 
     # ------------------------------------------------------------------ run
     def workspace(self, device=None) -> torch.Tensor:

@@ -203,6 +203,7 @@ bsa_status_t bsa_run_phase(bsa_plan_t plan, int32_t phase, const void* q, const 
   a.o = o;
   a.lse = lse;
   a.tiles = reinterpret_cast<const int32_t*>(ws + P.off_tiles);
+  a.wg_ptr = reinterpret_cast<const int32_t*>(ws + P.off_wg);
   a.cols = reinterpret_cast<const int32_t*>(ws + P.off_cols);
   a.lens = P.lens.empty() ? nullptr : reinterpret_cast<const int32_t*>(ws + P.off_lens);
   a.part = reinterpret_cast<float*>(ws + P.table_bytes);
@@ -219,6 +220,8 @@ bsa_status_t bsa_run_phase(bsa_plan_t plan, int32_t phase, const void* q, const 
   a.scale_log2 = static_cast<float>(static_cast<double>(P.sm_scale) * d.q_descale * d.k_descale * 1.4426950408889634);
   a.out_scale = d.v_descale;
   a.num_tiles = static_cast<int32_t>(P.tiles.size() / bsa::kTileInts);
+  a.num_wgs = static_cast<int32_t>(P.wg_ptr.size()) - 1;
+  a.heads_per_wg = P.heads_per_wg;
 
   hipError_t e;
   if (phase & BSA_PHASE_ATTENTION) {
@@ -276,6 +279,8 @@ bsa_status_t bsa_plan_info(bsa_plan_t plan, bsa_plan_info_t* info) {
   info->num_cols = static_cast<int32_t>(P.cols.size());
   info->max_splits = P.max_splits;
   info->num_cus = P.num_cus;
+  info->num_workgroups = static_cast<int32_t>(P.wg_ptr.size()) - 1;
+  info->heads_per_wg = P.heads_per_wg;
   info->table_bytes = P.table_bytes;
   info->partial_bytes = P.partial_bytes;
   info->workspace_bytes = P.workspace_bytes;
@@ -290,6 +295,14 @@ bsa_status_t bsa_plan_export(bsa_plan_t plan, int32_t* tiles, int32_t* merges, i
   if (tiles && !P.tiles.empty()) std::memcpy(tiles, P.tiles.data(), P.tiles.size() * 4);
   if (merges && !P.merges.empty()) std::memcpy(merges, P.merges.data(), P.merges.size() * 4);
   if (cols && !P.cols.empty()) std::memcpy(cols, P.cols.data(), P.cols.size() * 4);
+  return BSA_OK;
+}
+
+bsa_status_t bsa_plan_export_workgroups(bsa_plan_t plan, int32_t* wg_ptr) {
+  g_err.clear();
+  if (!plan || !wg_ptr) return set_err(BSA_ERR_INVALID_ARGUMENT, "plan and wg_ptr must be non-NULL");
+  const bsa::Plan& P = plan->p;
+  std::memcpy(wg_ptr, P.wg_ptr.data(), P.wg_ptr.size() * 4);
   return BSA_OK;
 }
 

@@ -6,9 +6,16 @@
 //
 // Decode reads every unmasked K/V row exactly once and does ~4 flops per
 // byte, so the kernel is built around bytes in flight, not arithmetic:
-//   * one workgroup = one planner tile = the g query heads of one token
-//     and one kv head, over a range of pages; its NW waves take 32-key
-//     tiles in turn and merge their softmax states through LDS at the end;
+//   * a workgroup of NW = 8 waves takes groups of HG tiles (the planner's
+//     head groups: same token and pages, HG consecutive kv heads, HG a power
+//     of two up to 8); wave w serves kv head w % HG of the group and takes
+//     its 32-key tiles w / HG, w / HG + NW / HG, ...  With 8 kv heads each
+//     wave owns one head, so one workgroup reads whole token rows of K and V
+//     (all heads of a page) at once: pages read in lockstep by workgroups on
+//     different XCDs stream markedly slower;
+//   * the workgroups stay resident and run their groups back to back, the
+//     next group's first keys loading while the current group's waves merge
+//     their softmax states through LDS;
 //   * K goes from HBM straight into MFMA A-operand registers (16-byte loads,
 //     no LDS); S^T = K Q^T runs on v_mfma_f32_16x16x32 with the g heads as
 //     the (zero-padded) 16 columns;
@@ -17,7 +24,7 @@
 //     the A operand of O^T += V^T P^T; the key order of S^T's rows is chosen
 //     so that P^T comes straight from the S^T accumulators in the order the
 //     transposed reads deliver V;
-//   * the next tile's K and V loads are issued before the current tile's
+//   * the next key tile's K and V loads are issued before the current one's
 //     math (register double buffering), and no workgroup barrier is needed
 //     inside the key loop;
 //   * keys outside a page's valid length (or past the range) load from a
@@ -31,7 +38,7 @@ namespace bsa {
 namespace {
 
 #ifndef BSA_DECODE_NW
-#define BSA_DECODE_NW 4            // waves per workgroup
+#define BSA_DECODE_NW 8            // waves per workgroup
 #endif
 #ifndef BSA_DECODE_MIN_WAVES
 #define BSA_DECODE_MIN_WAVES 2     // occupancy target (waves per SIMD) given to the register allocator
@@ -61,72 +68,97 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
 
   __shared__ __attribute__((aligned(16))) unsigned char lds[NW * kVBytes];
   __shared__ float red_m[NW][16], red_l[NW][16];
+  __shared__ int head_kvh[NW], head_part[NW];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int quad = lane >> 4;
   const int col = lane & 15;
-
-  const int32_t* trec = a.tiles + static_cast<int64_t>(blockIdx.x) * 8;
-  const int I = trec[0];
-  const int kvh = trec[1];
-  const int row0 = trec[2];
-  const int nrows = trec[3];
-  const int cb = trec[4];
-  const int ce = trec[5];
-  const int part = trec[6];
+  // head slot hw of the group and key-tile phase sub of this wave; WPH waves share a head
+  const int HG = a.heads_per_wg;
+  const int lg_hg = __builtin_ctz(HG);
+  const int WPH = NW >> lg_hg;
+  const int lg_wph = __builtin_ctz(WPH);
+  const int hw = wave & (HG - 1);
+  const int sub = wave >> lg_hg;
   const int C = a.C;
   const int cshift = POW2C ? __builtin_ctz(C) : 0;  // C = 1 << cshift when POW2C
-  const int npos = (ce - cb) * C;
-  const int ntiles = (npos + kKT - 1) / kKT;
   const int g = a.group;
-  const int qtok = I;                     // R = 1
-  int64_t lim64 = CAUSAL ? static_cast<int64_t>(qtok) + a.causal_off : 0;
-  const int qlim = CAUSAL ? (lim64 > 0x7fffffff ? 0x7fffffff : (lim64 < -1 ? -1 : static_cast<int>(lim64))) : 0;
-
-  // Q^T as the B operand: column `col` is qo head kvh*g + row0 + col (zero beyond nrows)
-  const bool col_ok = col < nrows;
-  v8 qf[4];
-  {
-    const T* qp = static_cast<const T*>(a.q) + static_cast<int64_t>(qtok) * a.q_stride +
-                  static_cast<int64_t>(kvh * g + row0 + col) * kD + quad * 8;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ks] = col_ok ? *reinterpret_cast<const v8*>(qp + ks * 32) : v8{};
-  }
-
-  const T* kbase = static_cast<const T*>(a.k) + static_cast<int64_t>(kvh) * kD;
-  const T* vbase = static_cast<const T*>(a.v) + static_cast<int64_t>(kvh) * kD;
   const T* zrow = static_cast<const T*>(a.zero_row);
+  const cint32_t* cols = (const cint32_t*)(a.cols);
+  const cint32_t* lens = (const cint32_t*)(a.lens);
+  const cint32_t* zints = (const cint32_t*)(a.zero_row);
 
-  // Token of key position t of this tile range (-1 = masked), from the
-  // tile's (uniform, scalar-loaded) column blocks and their valid lengths:
-  // a 32-key tile spans at most 3 blocks when C >= 16.
-  struct TileBlocks {
-    int base;              // first key position of the tile's first block
-    int J0, J1, J2;        // its first three column blocks (clamped to the range)
-    int L0, L1, L2;        // their valid lengths
+  // One planner tile as scalars (R = 1: the query token is the row block).
+  // A tile index past the end gives an empty context: no keys, and every
+  // load it leads to reads the zero row.
+  struct Ctx {
+    int I, kvh, row0, nrows, cb, nblk, part, ntiles, qlim;
   };
-  const int nblk = ce - cb;
-  auto tile_blocks = [&](int kt) {
-    TileBlocks b;
-    const int t0 = kt * kKT;
-    int blk0 = POW2C ? (t0 >> cshift) : t0 / C;
-    blk0 = blk0 < nblk ? blk0 : nblk - 1;  // tiles past the end only feed dummy loads
-    const int b1 = blk0 + 1 < nblk ? blk0 + 1 : nblk - 1;
-    const int b2 = blk0 + 2 < nblk ? blk0 + 2 : nblk - 1;
-    b.base = blk0 * C;
-    b.J0 = a.cols[cb + blk0];
-    b.J1 = a.cols[cb + b1];
-    b.J2 = a.cols[cb + b2];
-    b.L0 = LENS ? a.lens[cb + blk0] : C;
-    b.L1 = LENS ? a.lens[cb + b1] : C;
-    b.L2 = LENS ? a.lens[cb + b2] : C;
-    return b;
+  // this workgroup's tiles: t_begin .. t_end-1 of the plan's tile list, in
+  // groups of HG; this wave's tile of the group starting at g0 is g0 + hw
+  const cint32_t* wgp = (const cint32_t*)(a.wg_ptr) + blockIdx.x;
+  const int t_begin = wgp[0], t_end = wgp[1];
+  if (t_begin >= t_end) return;
+  auto read_ctx = [&](int g0) {
+    Ctx c{0, 0, 0, 0, 0, 0, -1, 0, -1};
+    if (g0 < t_end) {
+      const cint32_t* tr = (const cint32_t*)(a.tiles) + static_cast<int64_t>(g0 + hw) * 8;
+      c.I = tr[0];
+      c.kvh = tr[1];
+      c.row0 = tr[2];
+      c.nrows = tr[3];
+      c.cb = tr[4];
+      c.nblk = tr[5] - c.cb;
+      c.part = tr[6];
+      c.ntiles = (c.nblk * C + kKT - 1) / kKT;
+      if (CAUSAL) {
+        const int64_t lim64 = static_cast<int64_t>(c.I) + a.causal_off;
+        c.qlim = lim64 > 0x7fffffff ? 0x7fffffff : (lim64 < -1 ? -1 : static_cast<int>(lim64));
+      }
+    }
+    return c;
+  };
+
+  // Key tile kt of a tile context with its (uniform, scalar-loaded) column
+  // blocks and their valid lengths: a 32-key tile spans at most 3 blocks
+  // when C >= 16.  Tiles past the end of the range only feed dummy loads.
+  struct Src {
+    int t0, npos, qlim, kvh;
+    int base;            // first key position of the key tile's first block
+    int J0, J1, J2;      // its first three column blocks (clamped to the range)
+    int L0, L1, L2;      // their valid lengths
+  };
+  auto make_src = [&](const Ctx& c, int kt) {
+    Src s;
+    s.t0 = kt * kKT;
+    s.npos = c.nblk * C;
+    s.qlim = c.qlim;
+    s.kvh = c.kvh;
+    const int last = c.nblk > 0 ? c.nblk - 1 : 0;
+    const cint32_t* cp = c.nblk > 0 ? cols + c.cb : zints;
+    int blk0 = POW2C ? (s.t0 >> cshift) : s.t0 / C;
+    blk0 = blk0 < last ? blk0 : last;
+    const int b1 = blk0 + 1 < last ? blk0 + 1 : last;
+    const int b2 = blk0 + 2 < last ? blk0 + 2 : last;
+    s.base = blk0 * C;
+    s.J0 = cp[blk0];
+    s.J1 = cp[b1];
+    s.J2 = cp[b2];
+    if (LENS) {
+      const cint32_t* lp = c.nblk > 0 ? lens + c.cb : zints;
+      s.L0 = lp[blk0];
+      s.L1 = lp[b1];
+      s.L2 = lp[b2];
+    } else {
+      s.L0 = s.L1 = s.L2 = C;
+    }
+    return s;
   };
   // branch-free, so every stage issues the same loads and the compiler can
   // wait for exactly the older stage
-  auto key_token = [&](const TileBlocks& b, int t) -> int {
+  auto key_token = [&](const Src& b, int t) -> int {
     const int r = t - b.base;                      // < 32 + C, so at most two block steps
     // select block 0, 1 or 2 with masks (a plain ?: chain of these uniform
     // values was lowered to an indexed load from a stack copy)
@@ -138,13 +170,13 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
     int len = b.L0 ^ ((b.L0 ^ b.L1) & s1);
     len ^= (len ^ b.L2) & s2;
     const int tok = J * C + off;
-    bool ok = t < npos;
+    bool ok = t < b.npos;
     if (LENS) ok = ok && off < len;
-    if (CAUSAL) ok = ok && tok <= qlim;
+    if (CAUSAL) ok = ok && tok <= b.qlim;
     return ok ? tok : -1;
   };
 
-  // per-tile registers: K fragments and V chunks, both indexed (kb, ks):
+  // per-key-tile registers: K fragments and V chunks, both indexed (kb, ks):
   // lane (col, quad) holds dims ks*32 + quad*8 .. +8 of key (kb, col)
   struct Stage {
     v8 k[2][4];
@@ -152,12 +184,13 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
     uint32_t valid[2];  // bit m: key (kb, m) valid
   };
   // key of S^T row m in block kb: 8*(m/4) + 4*kb + m%4
-  auto load_stage = [&](Stage& s, int kt, const TileBlocks& b) {
-    const int t0 = kt * kKT;
+  auto load_stage = [&](Stage& s, const Src& b) {
+    const T* kbase = static_cast<const T*>(a.k) + static_cast<int64_t>(b.kvh) * kD;
+    const T* vbase = static_cast<const T*>(a.v) + static_cast<int64_t>(b.kvh) * kD;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key = 8 * (col >> 2) + 4 * kb + (col & 3);
-      const int tok = key_token(b, t0 + key);
+      const int tok = key_token(b, b.t0 + key);
       const T* pk = tok >= 0 ? kbase + static_cast<int64_t>(tok) * a.k_stride : zrow;
       const T* pv = tok >= 0 ? vbase + static_cast<int64_t>(tok) * a.v_stride : zrow;
 #pragma unroll
@@ -169,23 +202,33 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
     }
   };
 
+  // Q^T as the B operand: column `col` is qo head kvh*g + row0 + col.  Columns
+  // at or beyond nrows load the tile's last row instead (a plain, unconditional
+  // load): columns never mix, and those columns are never written.
+  v8 qf[4], qn[4];  // this group's Q and the next group's (loaded one group ahead)
+  auto load_q = [&](const Ctx& c, v8 (&q)[4]) {
+    const int cc = col < c.nrows ? col : (c.nrows > 0 ? c.nrows - 1 : 0);
+    const T* qp = static_cast<const T*>(a.q) + static_cast<int64_t>(c.I) * a.q_stride +
+                  static_cast<int64_t>(c.kvh * g + c.row0 + cc) * kD + quad * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) q[ks] = *reinterpret_cast<const v8*>(qp + ks * 32);
+  };
+
   unsigned char* vl = lds + wave * kVBytes;
   f32x4 oacc[8];
-#pragma unroll
-  for (int db = 0; db < 8; ++db) oacc[db] = f32x4{};
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_run, l_run;
   const float sl2 = a.scale_log2;
 
-  auto compute = [&](const Stage& s) {
-    // stage V into this wave's LDS tile (row-major, swizzled chunks)
+  // First half of a key tile's math: stage V into this wave's LDS tile
+  // (row-major, swizzled chunks) and form the masked scores S^T = K Q^T.
+  // After it the stage's registers are free for the next loads.
+  auto scores = [&](const Stage& s, f32x4 (&sc)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key = 8 * (col >> 2) + 4 * kb + (col & 3);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<u32x4*>(vl + v_chunk_off(key, ks * 4 + quad)) = s.v[kb][ks];
     }
-    // S^T = K Q^T
-    f32x4 sc[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sc[kb] = f32x4{};
@@ -195,6 +238,9 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
       for (int v = 0; v < 4; ++v)
         if (!((s.valid[kb] >> (4 * quad + v)) & 1u)) sc[kb][v] = -INFINITY;
     }
+  };
+  // Second half: online softmax update and O^T += V^T P^T.
+  auto accumulate = [&](const f32x4 (&sc)[2]) {
     float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
@@ -214,8 +260,8 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
         pf[4 * kb + v] = static_cast<T>(p);
       }
     l_run = l_run * alpha + ls;
-    // O^T += V^T P^T; transposed reads: lane L of this quad reads key row
-    // 8*quad + 4*j + L/4 at dims d0 + 4*(L%4) .. +3.
+    // transposed reads: lane L of this quad reads key row 8*quad + 4*j + L/4
+    // at dims d0 + 4*(L%4) .. +3
     const int rrow = 8 * quad + (col >> 2);
     const int dsub = 4 * (col & 3);
 #pragma unroll
@@ -233,86 +279,156 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
     }
   };
 
-  // key loop: this wave's tiles wave, wave + NW, ...; the K/V loads of the
-  // next tile and the block ids of the one after are in flight during each
-  // tile's math
-  // Every stage issues its loads unconditionally (tiles past the end read
-  // the zero row), so the wait before each tile's math covers exactly the
-  // older stage.
-  if (ntiles > 0) {
-    Stage s0, s1;
-    TileBlocks bA = tile_blocks(wave), bB = tile_blocks(wave + NW);
-    load_stage(s0, wave, bA);
-    for (int kt = wave; kt < ntiles; kt += 2 * NW) {
-      load_stage(s1, kt + NW, bB);
-      bA = tile_blocks(kt + 2 * NW);
-      compute(s0);
-      load_stage(s0, kt + 2 * NW, bA);
-      bB = tile_blocks(kt + 3 * NW);
-      if (kt + NW < ntiles) compute(s1);
+  // Merge the softmax states of the waves that share a head (WPH of them)
+  // for the finished group and write each head's output (or split partial);
+  // c is this wave's tile of the group.
+  auto finish_tile = [&](const Ctx& c) {
+    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+    l_tot += __shfl_xor(l_tot, 32, 64);
+    if (WPH == 1) {
+      // the wave owns its head: normalise and store straight from the
+      // accumulators (lane (col, quad) holds dims db*16 + 4*quad .. +3 of
+      // column col).  Columns at or beyond nrows replicate column nrows - 1
+      // bit for bit (same Q), so every lane stores, to that column's place,
+      // the same bytes: no predicated stores.
+      const int cc = col < c.nrows ? col : c.nrows - 1;
+      const int head = c.kvh * g + c.row0 + cc;
+      const float inv = l_tot > 0.f ? a.out_scale / l_tot : 0.f;
+      const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+      if (c.part < 0) {
+        T* op = static_cast<T*>(a.o) + static_cast<int64_t>(c.I) * a.o_stride + static_cast<int64_t>(head) * kD + 4 * quad;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+          v4 out;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[e] = static_cast<T>(oacc[db][e] * inv);
+          *reinterpret_cast<v4*>(op + db * 16) = out;
+        }
+        if (a.lse) a.lse[static_cast<int64_t>(c.I) * a.num_qo_heads + head] = lse_v;
+      } else {
+        float* pp = a.part + c.part;
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+          *reinterpret_cast<f32x4*>(pp + static_cast<int64_t>(cc) * kD + db * 16 + 4 * quad) = oacc[db] * inv;
+        pp[static_cast<int64_t>(c.nrows) * kD + cc] = lse_v;
+      }
+      return;
     }
-  }
+    __syncthreads();  // every wave is done with its V tile: reuse LDS for the merge
+    float* ob = reinterpret_cast<float*>(lds);  // [NW][16 cols][128 d]
+    if (quad == 0) {
+      red_m[wave][col] = m_run;
+      red_l[wave][col] = l_tot;
+    }
+    if (sub == 0 && lane == 0) {
+      head_kvh[hw] = c.kvh;
+      head_part[hw] = c.part;
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      *reinterpret_cast<f32x4*>(ob + (wave * 16 + col) * kD + db * 16 + 4 * quad) = oacc[db];
+    __syncthreads();
+    // thread -> (head slot, column, 4 dims): HG * 16 * 32 items over NW * 64 threads
+    for (int item = tid; item < HG * 16 * (kD / 4); item += NW * 64) {
+      const int hs = item >> 9;
+      const int cq = (item >> 5) & 15;
+      const int d4 = (item & 31) * 4;
+      if (cq >= c.nrows) continue;
+      float M = -INFINITY;
+      for (int s2 = 0; s2 < WPH; ++s2) M = fmaxf(M, red_m[hs + (s2 << lg_hg)][cq]);
+      const float Mu = M == -INFINITY ? 0.f : M;
+      float L = 0.f;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int s2 = 0; s2 < WPH; ++s2) {
+        const int w2 = hs + (s2 << lg_hg);
+        const float sc = fast_exp2(red_m[w2][cq] - Mu);
+        L += red_l[w2][cq] * sc;
+        acc += sc * *reinterpret_cast<const f32x4*>(ob + (w2 * 16 + cq) * kD + d4);
+      }
+      const float inv = L > 0.f ? a.out_scale / L : 0.f;
+      const float lse_v = L > 0.f ? (Mu + __log2f(L)) * kLn2 : -INFINITY;
+      const int head = head_kvh[hs] * g + c.row0 + cq;
+      const int part = head_part[hs];
+      acc *= inv;
+      if (part < 0) {
+        v4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = static_cast<T>(acc[e]);
+        *reinterpret_cast<v4*>(static_cast<T*>(a.o) + static_cast<int64_t>(c.I) * a.o_stride +
+                               static_cast<int64_t>(head) * kD + d4) = out;
+        if (d4 == 0 && a.lse) a.lse[static_cast<int64_t>(c.I) * a.num_qo_heads + head] = lse_v;
+      } else {
+        float* pp = a.part + part;
+        *reinterpret_cast<f32x4*>(pp + static_cast<int64_t>(cq) * kD + d4) = acc;
+        if (d4 == 0) pp[static_cast<int64_t>(c.nrows) * kD + cq] = lse_v;
+      }
+    }
+    __syncthreads();  // the merge buffer is the next group's V staging area
+  };
 
-  // ---- merge the waves' states (all waves, every query column)
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  __syncthreads();  // every wave is done with its V tile: reuse LDS for the merge
-  float* ob = reinterpret_cast<float*>(lds);  // [NW][16 cols][128 d]
-  if (quad == 0) {
-    red_m[wave][col] = m_run;
-    red_l[wave][col] = l_tot;
+  // The workgroup runs its groups in order.  Within a group the WPH waves of
+  // a head take its 32-key tiles sub, sub+WPH, ...; each wave's sequence is
+  // padded to an even length (at least 2) with key tiles past the end, which
+  // load the zero row and are fully masked (so computing them leaves the
+  // softmax state unchanged), and the loads run two items ahead across tile
+  // boundaries, so the next group's first keys are in flight during the
+  // current group's merge.  Every load and every use is unconditional, so each
+  // wait covers exactly the older stage.
+  Ctx cur = read_ctx(t_begin);
+  load_q(cur, qf);
+  Stage s0, s1;
+  Src sA = make_src(cur, sub), sB = make_src(cur, sub + WPH);
+  load_stage(s0, sA);
+  load_stage(s1, sB);
+  for (int gn = t_begin + HG;; gn += HG) {
+    const Ctx nxt = read_ctx(gn);
+    load_q(nxt, qn);
+    const int nT = cur.ntiles > sub ? (cur.ntiles - sub + WPH - 1) >> lg_wph : 0;
+    const int nTe = nT < 2 ? 2 : (nT + 1) & ~1;
+    // key tile loaded for item q: item q of this group for q < nTe, else item
+    // q - nTe of the next one
+    auto src_of = [&](int q) {
+      const bool in = q < nTe;
+      const Ctx c = in ? cur : nxt;
+      return make_src(c, sub + ((in ? q : q - nTe) << lg_wph));
+    };
+#pragma unroll
+    for (int db = 0; db < 8; ++db) oacc[db] = f32x4{};
+    m_run = -INFINITY;
+    l_run = 0.f;
+    // s0 and s1 hold items p and p + 1 at the top of each pass; a stage is
+    // reloaded (item p + 2, p + 3) as soon as its scores are formed
+    int p = 0;
+    do {  // nTe >= 2: at least one pair, so the waits never see a skipped body
+      f32x4 sc[2];
+      sA = src_of(p + 2);
+      scores(s0, sc);
+      load_stage(s0, sA);
+      accumulate(sc);
+      sB = src_of(p + 3);
+      scores(s1, sc);
+      load_stage(s1, sB);
+      accumulate(sc);
+      p += 2;
+    } while (p < nTe);
+    finish_tile(cur);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = qn[ks];
+    if (gn >= t_end) break;
+    cur = nxt;
   }
-#pragma unroll
-  for (int db = 0; db < 8; ++db)
-    *reinterpret_cast<f32x4*>(ob + (wave * 16 + col) * kD + db * 16 + 4 * quad) = oacc[db];
-  __syncthreads();
-  // thread -> (column, 4 dims): 16 * 32 items over NW * 64 threads
-  for (int item = tid; item < 16 * (kD / 4); item += NW * 64) {
-    const int cq = item / (kD / 4);
-    const int d4 = (item - cq * (kD / 4)) * 4;
-    if (cq >= nrows) continue;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, red_m[w][cq]);
-    const float Mu = M == -INFINITY ? 0.f : M;
-    float L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float sc = fast_exp2(red_m[w][cq] - Mu);
-      L += red_l[w][cq] * sc;
-      acc += sc * *reinterpret_cast<const f32x4*>(ob + (w * 16 + cq) * kD + d4);
-    }
-    const float inv = L > 0.f ? a.out_scale / L : 0.f;
-    const float lse_v = L > 0.f ? (Mu + __log2f(L)) * kLn2 : -INFINITY;
-    const int head = kvh * g + row0 + cq;
-    acc *= inv;
-    if (part < 0) {
-      v4 out;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) out[e] = static_cast<T>(acc[e]);
-      *reinterpret_cast<v4*>(static_cast<T*>(a.o) + static_cast<int64_t>(qtok) * a.o_stride +
-                             static_cast<int64_t>(head) * kD + d4) = out;
-      if (d4 == 0 && a.lse) a.lse[static_cast<int64_t>(qtok) * a.num_qo_heads + head] = lse_v;
-    } else {
-      float* pp = a.part + part;
-      *reinterpret_cast<f32x4*>(pp + static_cast<int64_t>(cq) * kD + d4) = acc;
-      if (d4 == 0) pp[static_cast<int64_t>(nrows) * kD + cq] = lse_v;
-    }
-  }
+}
+
+template <typename T, int NW, bool CAUSAL, bool LENS, bool POW2C>
+hipError_t launch_variant(const AttnArgs& a, hipStream_t st) {
+  attn_decode_kernel<T, NW, CAUSAL, LENS, POW2C><<<dim3(a.num_wgs), dim3(NW * 64), 0, st>>>(a);
+  return hipGetLastError();
 }
 
 template <typename T, int NW, bool POW2C>
 hipError_t launch_nw(const AttnArgs& a, bool causal, bool lens, hipStream_t st) {
-  const dim3 grid(a.num_tiles), block(NW * 64);
-  if (causal) {
-    if (lens) attn_decode_kernel<T, NW, true, true, POW2C><<<grid, block, 0, st>>>(a);
-    else attn_decode_kernel<T, NW, true, false, POW2C><<<grid, block, 0, st>>>(a);
-  } else {
-    if (lens) attn_decode_kernel<T, NW, false, true, POW2C><<<grid, block, 0, st>>>(a);
-    else attn_decode_kernel<T, NW, false, false, POW2C><<<grid, block, 0, st>>>(a);
-  }
-  return hipGetLastError();
+  if (causal) return lens ? launch_variant<T, NW, true, true, POW2C>(a, st) : launch_variant<T, NW, true, false, POW2C>(a, st);
+  return lens ? launch_variant<T, NW, false, true, POW2C>(a, st) : launch_variant<T, NW, false, false, POW2C>(a, st);
 }
 
 template <typename T>
@@ -324,7 +440,7 @@ hipError_t launch_typed(const AttnArgs& a, bool causal, bool lens, hipStream_t s
 }  // namespace
 
 hipError_t launch_attn_decode(const AttnArgs& a, bool bf16, bool causal, bool has_lens, hipStream_t stream) {
-  if (a.num_tiles == 0) return hipSuccess;
+  if (a.num_tiles == 0 || a.num_wgs <= 0) return hipSuccess;
   return bf16 ? launch_typed<__bf16>(a, causal, has_lens, stream)
               : launch_typed<_Float16>(a, causal, has_lens, stream);
 }

@@ -15,6 +15,7 @@ struct AttnArgs {
   void* o;
   float* lse;              // may be null
   const int32_t* tiles;    // 8 ints per tile (planner layout)
+  const int32_t* wg_ptr;   // workgroup w runs tiles wg_ptr[w] .. wg_ptr[w+1]-1 (decode kernel)
   const int32_t* cols;     // column blocks per row block
   const int32_t* lens;     // valid length of each cols entry, or null (all blocks full)
   float* part;             // split partial region
@@ -25,6 +26,8 @@ struct AttnArgs {
   float scale_log2;        // sm_scale * q_descale * k_descale * log2(e)
   float out_scale;         // v_descale
   int32_t num_tiles;
+  int32_t num_wgs;         // workgroups of the launch (decode kernel)
+  int32_t heads_per_wg;    // decode kernel: kv heads of one workgroup (a power of two <= 8)
 };
 
 struct MergeArgs {
@@ -42,7 +45,8 @@ struct MergeArgs {
 hipError_t launch_attn_tile(const AttnArgs& a, bool bf16, int tile_rows, bool causal, bool has_lens,
                             hipStream_t stream);
 
-// Paged-decode kernel: R = 1, C >= 16, head_dim 128, fp16 or bf16, g <= 16.
+// Paged-decode kernel: R = 1, C >= 16, head_dim 128, fp16 or bf16, g <= 16;
+// workgroup w runs the tile groups wg_ptr[w] .. wg_ptr[w+1]-1 (heads_per_wg tiles each).
 hipError_t launch_attn_decode(const AttnArgs& a, bool bf16, bool causal, bool has_lens, hipStream_t stream);
 
 // Sparse-MLA kernel: bf16 q/o, fp8 e4m3 kv, Dqk 576, Dv 512, one kv head.

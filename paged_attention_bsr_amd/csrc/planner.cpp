@@ -24,7 +24,20 @@
 //     prefix_keys[p] * s >= j * keys, then forced strictly increasing and
 //     leaving at least one block per later split.
 //  6. Tiles are emitted in (I, row tile, h, split) order, then stably sorted
-//     by descending work (longest processing time first).
+//     by descending work (longest processing time first); workgroup t runs
+//     tile t.
+//  Decode kernel: a workgroup takes G = decode_heads_per_wg(Hkv) kv heads at
+//     once, so the unit of steps 4-6 is (I, head group gi) and every piece
+//     emits G tiles (heads gi*G .. gi*G+G-1, same blocks) as one group; head
+//     i's partial of piece j of s is at base + (i*s + j) * psize.  Groups are
+//     sorted as in 6 and workgroup t runs group t, except with kv_splits = 0:
+//     then the partition is balanced over W = min(kDecodeWgPerCu * num_cus,
+//     max(1, K / kBalancedMinKeys)) resident workgroups, K = total keys over
+//     all units taken in (I, gi) order.  The block starting at key position X
+//     of that sequence goes to workgroup floor(X * W / K), a unit without keys
+//     to the workgroup of its position (at most W - 1); a unit's maximal runs
+//     of blocks with one workgroup are its pieces, emitted in order, which is
+//     workgroup order.
 // Kernel choice: sparse-MLA shape -> MLA kernel (64-row tiles); R = 1 with
 // g <= 16 and C >= 16 -> decode kernel (16-row tiles, i.e. one per unit);
 // otherwise the generic tile kernel with 32, 128 or 256-row tiles for units
@@ -205,90 +218,149 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
     }
   }
 
-  // ---- 4. split counts
-  int64_t total_work = 0;
-  for (const auto& rt : rts) total_work += rt.work * d.num_kv_heads;
-  const int64_t chunk = std::max<int64_t>(1, ceil_div(total_work, (int64_t)kAutoTilesPerCu * num_cus));
-  std::vector<int64_t> splits(rts.size(), 1);
-  for (size_t t = 0; t < rts.size(); ++t) {
-    const auto& rt = rts[t];
-    int64_t s = 1;
-    if (d.kv_splits > 1) {
-      s = std::min<int64_t>(d.kv_splits, rt.n);
-    } else if (d.kv_splits == 0) {
-      const int64_t cap = std::min<int64_t>({rt.n, (int64_t)kMaxSplits,
-                                             std::max<int64_t>(1, rt.keys / kAutoMinSplitKeys)});
-      s = std::min<int64_t>(ceil_div(rt.work, chunk), cap);
-    }
-    splits[t] = std::max<int64_t>(1, s);
-  }
-
-  // ---- 5./6. emit tiles and merges
+  // Tiles come in groups: one group per (row tile, head group, key range)
+  // holds the tiles of G consecutive kv heads (G = 1 except for the decode
+  // kernel, whose workgroup gives each of its waves one kv head of the group).
+  const int32_t G = kernel == BSA_KERNEL_DECODE ? decode_heads_per_wg(d.num_kv_heads) : 1;
+  const int32_t NG = d.num_kv_heads / G;
   struct TileRec {
     int32_t f[kTileInts];
-    int64_t work;
+  };
+  struct GroupRec {
+    size_t first;   // its G tiles are recs[first .. first + G)
+    int64_t work;   // keys x ceil(rows / 32)
+    int64_t wg;     // workgroup (balanced partition)
   };
   std::vector<TileRec> recs;
+  std::vector<GroupRec> groups;
   P.merges.clear();
   int64_t part = 0;
   int32_t max_s = 1;
   const int64_t dv = d.head_dim_vo;
   P.valid_pairs = 0;
-  for (size_t t = 0; t < rts.size(); ++t) {
-    const auto& rt = rts[t];
-    const int64_t s = splits[t];
-    max_s = std::max<int32_t>(max_s, static_cast<int32_t>(s));
-    // prefix key counts over the row tile's blocks
-    pref.assign(static_cast<size_t>(rt.n + 1), 0);
-    for (int64_t k = 0; k < rt.n; ++k) pref[k + 1] = pref[k] + blen(P.cols[rt.cb + k]);
-    std::vector<int64_t> b(static_cast<size_t>(s + 1), 0);
-    b[s] = rt.n;
-    for (int64_t j = 1; j < s; ++j) {
-      int64_t p = 0;
-      while (p < rt.n && pref[p] * s < j * rt.keys) ++p;
-      p = std::max<int64_t>(p, b[j - 1] + 1);
-      p = std::min<int64_t>(p, rt.n - (s - j));
-      b[j] = p;
-    }
+  // Tiles of head group gi of row tile rt cut at blocks b[0] < ... < b[s]
+  // (pref = the row tile's prefix key counts).  Head i's partial of piece j
+  // sits at base + (i * s + j) * psize; false if the partials overflow.
+  auto emit_unit = [&](const RowTile& rt, int32_t gi, const int64_t* b, const int64_t* wg, int64_t s) {
     const int64_t psize = round_up(rt.nrows * (dv + 1), 64);
-    for (int32_t h = 0; h < d.num_kv_heads; ++h) {
-      const int64_t first = part;
-      for (int64_t j = 0; j < s; ++j) {
+    const int64_t base = part;
+    for (int64_t j = 0; j < s; ++j) {
+      const int64_t keys_j = pref[b[j + 1]] - pref[b[j]];
+      groups.push_back({recs.size(), keys_j * ceil_div(rt.nrows, 32), wg ? wg[j] : 0});
+      for (int32_t i = 0; i < G; ++i) {
         TileRec r{};
-        const int64_t keys_j = pref[b[j + 1]] - pref[b[j]];
         r.f[T_ROWBLOCK] = static_cast<int32_t>(rt.I);
-        r.f[T_KVHEAD] = h;
+        r.f[T_KVHEAD] = gi * G + i;
         r.f[T_ROW0] = static_cast<int32_t>(rt.row0);
         r.f[T_NROWS] = static_cast<int32_t>(rt.nrows);
         r.f[T_COLB] = static_cast<int32_t>(rt.cb + b[j]);
         r.f[T_COLE] = static_cast<int32_t>(rt.cb + b[j + 1]);
-        r.f[T_PART] = s > 1 ? static_cast<int32_t>(part) : -1;
+        r.f[T_PART] = s > 1 ? static_cast<int32_t>(base + (i * s + j) * psize) : -1;
         r.f[T_KEYS] = static_cast<int32_t>(keys_j);
-        r.work = keys_j * ceil_div(rt.nrows, 32);
-        P.valid_pairs += keys_j * rt.nrows;
-        if (s > 1) part += psize;
-        if (part > INT32_MAX) return fail(err, BSA_ERR_UNSUPPORTED, "split partials exceed 2^31 floats");
         recs.push_back(r);
+        P.valid_pairs += keys_j * rt.nrows;
       }
-      if (s > 1) {
-        int32_t m[kMergeInts] = {static_cast<int32_t>(rt.I), h, static_cast<int32_t>(rt.row0),
-                                 static_cast<int32_t>(rt.nrows), static_cast<int32_t>(first),
+    }
+    max_s = std::max<int32_t>(max_s, static_cast<int32_t>(s));
+    if (s > 1) {
+      part += G * s * psize;
+      if (part > INT32_MAX) return false;
+      for (int32_t i = 0; i < G; ++i) {
+        int32_t m[kMergeInts] = {static_cast<int32_t>(rt.I), gi * G + i, static_cast<int32_t>(rt.row0),
+                                 static_cast<int32_t>(rt.nrows), static_cast<int32_t>(base + i * s * psize),
                                  static_cast<int32_t>(s), static_cast<int32_t>(psize), 0};
         P.merges.insert(P.merges.end(), m, m + kMergeInts);
       }
     }
+    return true;
+  };
+  auto row_prefix = [&](const RowTile& rt) {
+    pref.assign(static_cast<size_t>(rt.n + 1), 0);
+    for (int64_t k = 0; k < rt.n; ++k) pref[k + 1] = pref[k] + blen(P.cols[rt.cb + k]);
+  };
+  std::vector<int64_t> cut, cut_wg;
+  int64_t W = 0;
+  if (kernel == BSA_KERNEL_DECODE && d.kv_splits == 0) {
+    // ---- 4.-6. balanced partition over resident workgroups
+    int64_t K = 0;
+    for (const auto& rt : rts) K += rt.keys * NG;
+    W = std::max<int64_t>(1, std::min<int64_t>((int64_t)kDecodeWgPerCu * num_cus, K / kBalancedMinKeys));
+    auto wg_of = [&](int64_t X) -> int64_t {
+      if (K == 0) return 0;
+      const int64_t w = static_cast<int64_t>((static_cast<__int128>(X) * W) / K);
+      return std::min<int64_t>(w, W - 1);
+    };
+    int64_t X = 0;
+    for (const auto& rt : rts) {
+      row_prefix(rt);
+      for (int32_t gi = 0; gi < NG; ++gi) {
+        // maximal runs of blocks with one workgroup
+        cut.assign(1, 0);
+        cut_wg.assign(1, wg_of(X));
+        for (int64_t k = 1; k < rt.n; ++k) {
+          const int64_t wk = wg_of(X + pref[k]);
+          if (wk != cut_wg.back()) {
+            cut.push_back(k);
+            cut_wg.push_back(wk);
+          }
+        }
+        cut.push_back(rt.n);
+        if (!emit_unit(rt, gi, cut.data(), cut_wg.data(), static_cast<int64_t>(cut_wg.size())))
+          return fail(err, BSA_ERR_UNSUPPORTED, "split partials exceed 2^31 floats");
+        X += rt.keys;
+      }
+    }
+  } else {
+    // ---- 4. split counts
+    int64_t total_work = 0;
+    for (const auto& rt : rts) total_work += rt.work * d.num_kv_heads;
+    const int64_t chunk = std::max<int64_t>(1, ceil_div(total_work, (int64_t)kAutoTilesPerCu * num_cus));
+    for (const auto& rt : rts) {
+      int64_t s = 1;
+      if (d.kv_splits > 1) {
+        s = std::min<int64_t>(d.kv_splits, rt.n);
+      } else if (d.kv_splits == 0) {
+        const int64_t cap = std::min<int64_t>({rt.n, (int64_t)kMaxSplits,
+                                               std::max<int64_t>(1, rt.keys / kAutoMinSplitKeys)});
+        s = std::min<int64_t>(ceil_div(rt.work, chunk), cap);
+      }
+      s = std::max<int64_t>(1, s);
+      // ---- 5. boundaries
+      row_prefix(rt);
+      cut.assign(static_cast<size_t>(s + 1), 0);
+      cut[s] = rt.n;
+      for (int64_t j = 1; j < s; ++j) {
+        int64_t p = 0;
+        while (p < rt.n && pref[p] * s < j * rt.keys) ++p;
+        p = std::max<int64_t>(p, cut[j - 1] + 1);
+        p = std::min<int64_t>(p, rt.n - (s - j));
+        cut[j] = p;
+      }
+      for (int32_t gi = 0; gi < NG; ++gi)
+        if (!emit_unit(rt, gi, cut.data(), nullptr, s))
+          return fail(err, BSA_ERR_UNSUPPORTED, "split partials exceed 2^31 floats");
+    }
+    // ---- 6. longest first, one group per workgroup
+    std::stable_sort(groups.begin(), groups.end(),
+                     [](const GroupRec& a, const GroupRec& b) { return a.work > b.work; });
+    W = static_cast<int64_t>(groups.size());
+    for (int64_t w = 0; w < W; ++w) groups[static_cast<size_t>(w)].wg = w;
   }
-  std::stable_sort(recs.begin(), recs.end(),
-                   [](const TileRec& a, const TileRec& b) { return a.work > b.work; });
   if (recs.size() > static_cast<size_t>(INT32_MAX / kTileInts))
     return fail(err, BSA_ERR_UNSUPPORTED, "too many tiles");
   P.tiles.clear();
   P.tiles.reserve(recs.size() * kTileInts);
-  for (const auto& r : recs) P.tiles.insert(P.tiles.end(), r.f, r.f + kTileInts);
+  P.wg_ptr.assign(static_cast<size_t>(W + 1), 0);
+  for (const auto& gr : groups) {
+    for (int32_t i = 0; i < G; ++i) P.tiles.insert(P.tiles.end(), recs[gr.first + i].f, recs[gr.first + i].f + kTileInts);
+    P.wg_ptr[static_cast<size_t>(gr.wg + 1)] += G;
+  }
+  for (int64_t w = 0; w < W; ++w) P.wg_ptr[w + 1] += P.wg_ptr[w];
+  P.heads_per_wg = G;
   P.max_splits = max_s;
   P.partial_floats = part;
 
-  // ---- workspace layout: [tiles | merges | cols | lens] then partials
+  // ---- workspace layout: [tiles | merges | cols | lens | wg_ptr | zero row] then partials
   int64_t o = 0;
   P.off_tiles = o;
   o = round_up(o + (int64_t)P.tiles.size() * 4, 256);
@@ -298,6 +370,8 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
   o = round_up(o + (int64_t)P.cols.size() * 4, 256);
   P.off_lens = o;
   o = round_up(o + (int64_t)P.lens.size() * 4, 256);
+  P.off_wg = o;
+  o = round_up(o + (int64_t)P.wg_ptr.size() * 4, 256);
   P.off_zero = o;  // zero row: masked keys load from here
   o = round_up(o + 1024, 256);
   P.table_bytes = std::max<int64_t>(o, 256);
@@ -313,6 +387,7 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
   put(P.off_merges, P.merges);
   put(P.off_cols, P.cols);
   put(P.off_lens, P.lens);
+  put(P.off_wg, P.wg_ptr);
   return BSA_OK;
 }
 

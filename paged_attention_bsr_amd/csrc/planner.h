@@ -36,6 +36,19 @@ constexpr int kTileMaxRows = BSA_TILE_MAX_ROWS;  // largest row tile of the gene
 #define BSA_TILE_SMALL_GRID_PER_CU 8
 #endif
 constexpr int kTileSmallGridPerCu = BSA_TILE_SMALL_GRID_PER_CU;
+// Decode kernel: a workgroup of 8 waves takes a group of
+// decode_heads_per_wg(num_kv_heads) kv heads, the largest power of two up to
+// 8 that divides num_kv_heads (one head per wave when it is 8).  With
+// kv_splits == 0 the tiles are a balanced partition over the workgroups the
+// device holds at once (8 waves at 2 waves per SIMD: one per CU), each taking
+// at least kBalancedMinKeys keys.
+constexpr int kDecodeWaves = 8;
+constexpr int kDecodeWgPerCu = 1;
+constexpr int kBalancedMinKeys = 256;
+inline int32_t decode_heads_per_wg(int32_t num_kv_heads) {
+  const int32_t low = num_kv_heads & -num_kv_heads;
+  return low < kDecodeWaves ? low : kDecodeWaves;
+}
 
 struct Plan {
   // validated request
@@ -53,11 +66,13 @@ struct Plan {
   std::vector<int32_t> merges;   // kMergeInts per merge
   std::vector<int32_t> cols;     // column blocks per row block, ascending, causally trimmed
   std::vector<int32_t> lens;     // valid length of each cols entry, empty when every block is full
+  std::vector<int32_t> wg_ptr;   // workgroup w runs tiles wg_ptr[w] .. wg_ptr[w+1]-1, in order
   int32_t max_splits = 1;
+  int32_t heads_per_wg = 1;      // kv heads per tile group (decode kernel: one workgroup)
   int64_t partial_floats = 0;
   int64_t valid_pairs = 0;
   // workspace layout (bytes)
-  int64_t off_tiles = 0, off_merges = 0, off_cols = 0, off_lens = 0, off_zero = 0;
+  int64_t off_tiles = 0, off_merges = 0, off_cols = 0, off_lens = 0, off_wg = 0, off_zero = 0;
   int64_t table_bytes = 0, partial_bytes = 0, workspace_bytes = 0;
   std::vector<uint8_t> table_blob;  // exact image of the table region
   uint64_t id = 0;                  // process-unique plan id

@@ -207,6 +207,41 @@ def test_tile_kernel_variants(case, kv_splits):
     compare(o, lse, o_ref, lse_ref, tol_for(w), what)
 
 
+# The decode kernel for 1 to 16 kv heads (1, 2, 4 or 8 heads per workgroup),
+# under the balanced partition planned for a few CUs, so that each resident
+# workgroup runs many tile groups in a row (units cut at workgroup
+# boundaries, units without keys, the next group's keys prefetched across
+# every boundary), and with fixed splits (one group per workgroup).
+DECODE_VARIANTS = [
+    # (seed, M, NB, C, Hq, Hkv, causal, lens, density, dtype, num_cus)
+    (51, 30, 40, 16, 32, 8, False, True, 0.3, torch.float16, 1),   # 2 workgroups, partial pages
+    (52, 25, 30, 32, 16, 1, True, True, 0.5, torch.bfloat16, 2),   # g = 16, one kv head, causal
+    (53, 40, 50, 64, 3, 3, False, False, 0.2, torch.float16, 3),   # g = 1, three kv heads, C = 64
+    (54, 12, 80, 16, 8, 2, True, False, 0.9, torch.bfloat16, 5),
+    (55, 48, 1, 16, 8, 2, True, False, 1.0, torch.float16, 1),     # M > N: early rows see no key
+    (56, 9, 4, 16, 4, 1, False, True, 0.1, torch.float16, 2),      # nearly empty: one workgroup
+    (57, 20, 24, 16, 16, 4, True, True, 0.6, torch.float16, 2),    # 4 kv heads: two waves per head
+    (58, 10, 30, 32, 64, 16, False, True, 0.5, torch.bfloat16, 3), # 16 kv heads: two head groups
+]
+
+
+@pytest.mark.parametrize("case", DECODE_VARIANTS, ids=[f"d{c[0]}" for c in DECODE_VARIANTS])
+@pytest.mark.parametrize("kv_splits", [0, 3])
+def test_decode_balanced_partition(case, kv_splits):
+    seed, M, NB, C, Hq, Hkv, causal, lens, dens, dtype, num_cus = case
+    w = W.random_bsr(seed, M, NB * C, 1, C, Hq, Hkv, causal=causal, partial_lens=lens, density=dens,
+                     dtype=dtype, garbage=6e4 if lens else 0.0)
+    p = plan_for(w, kv_splits, num_cus=num_cus)
+    inf = p.info()
+    assert inf["kernel"] == 2
+    what = (f"decode s{seed} splits={kv_splits} C={C} g={Hq // Hkv} heads/wg={inf['heads_per_wg']} "
+            f"wgs={inf['num_workgroups']} tiles={inf['num_tiles']}")
+    say(f"[parity] {what}")
+    o, lse = run_gpu(w, kv_splits, plan=p)
+    o_ref, lse_ref = oracle_result(w)
+    compare(o, lse, o_ref, lse_ref, tol_for(w), what)
+
+
 @pytest.mark.parametrize("causal,lens", [(True, False), (False, True), (True, True)])
 def test_mla_kernel_variants(causal, lens):
     """Causal masking (early tokens lose the newest selected rows), per-block valid lengths

@@ -14,6 +14,8 @@ from paged_attention_bsr_amd import workloads as W
 AUTO_TILES_PER_CU = 4
 AUTO_MIN_SPLIT_KEYS = 256
 MAX_SPLITS = 64
+DECODE_WG_PER_CU = 1
+BALANCED_MIN_KEYS = 256
 
 
 def _cdiv(a, b):
@@ -21,7 +23,9 @@ def _cdiv(a, b):
 
 
 def model_plan(w, kv_splits, num_cus, tile_rows):
-    """Python model of the planner's partition rule (steps 1-6 of planner.cpp)."""
+    """Python model of the planner's partition rule (steps 1-6 of planner.cpp,
+    and the balanced partition of the decode kernel with kv_splits = 0).
+    Returns (tiles, merges, cols, wg_ptr)."""
     M, N, R, C = w.M, w.N, w.R, w.C
     g = w.num_qo_heads // w.num_kv_heads
     MB = _cdiv(M, R)
@@ -50,45 +54,85 @@ def model_plan(w, kv_splits, num_cus, tile_rows):
                 n = k
             keys = sum(blen(cols[bptr[I] + k]) for k in range(n))
             rts.append((I, r0, nr, bptr[I], n, keys, keys * _cdiv(nr, 32)))
-    total = sum(rt[6] for rt in rts) * w.num_kv_heads
-    chunk = max(1, _cdiv(total, AUTO_TILES_PER_CU * num_cus))
-    tiles, merges, part = [], [], 0
-    dv = w.head_dim_vo
-    for (I, r0, nr, cb, n, keys, work) in rts:
-        if kv_splits == 1:
-            s = 1
-        elif kv_splits > 1:
-            s = min(kv_splits, n)
-        else:
-            cap = min(n, MAX_SPLITS, max(1, keys // AUTO_MIN_SPLIT_KEYS))
-            s = min(_cdiv(work, chunk), cap)
-        s = max(1, s)
+    decode = model_kernel(w, num_cus)[0] == 2
+    G = min(8, w.num_kv_heads & -w.num_kv_heads) if decode else 1
+    NG = w.num_kv_heads // G
+    st = {"part": 0, "tiles": [], "merges": [], "groups": []}
+
+    def emit_unit(rt, gi, pref, b, wgs):
+        """Pieces b[j]..b[j+1] of head group gi; head i's partial of piece j at base + (i*s + j)*psize."""
+        (I, r0, nr, cb, n, keys, work) = rt
+        s = len(b) - 1
+        psize = _cdiv(nr * (w.head_dim_vo + 1), 64) * 64
+        base = st["part"]
+        for j in range(s):
+            kj = pref[b[j + 1]] - pref[b[j]]
+            grp = [[I, gi * G + i, r0, nr, cb + b[j], cb + b[j + 1],
+                    base + (i * s + j) * psize if s > 1 else -1, kj] for i in range(G)]
+            st["groups"].append((grp, kj * _cdiv(nr, 32), wgs[j] if wgs else 0))
+        if s > 1:
+            st["part"] += G * s * psize
+            for i in range(G):
+                st["merges"].append([I, gi * G + i, r0, nr, base + i * s * psize, s, psize, 0])
+
+    def prefix(rt):
         pref = [0]
-        for k in range(n):
-            pref.append(pref[-1] + blen(cols[cb + k]))
-        b = [0] * (s + 1)
-        b[s] = n
-        for j in range(1, s):
-            p = 0
-            while p < n and pref[p] * s < j * keys:
-                p += 1
-            p = max(p, b[j - 1] + 1)
-            p = min(p, n - (s - j))
-            b[j] = p
-        psize = _cdiv(nr * (dv + 1), 64) * 64
-        for h in range(w.num_kv_heads):
-            first = part
-            for j in range(s):
-                kj = pref[b[j + 1]] - pref[b[j]]
-                tiles.append(([I, h, r0, nr, cb + b[j], cb + b[j + 1], part if s > 1 else -1, kj],
-                              kj * _cdiv(nr, 32)))
-                if s > 1:
-                    part += psize
-            if s > 1:
-                merges.append([I, h, r0, nr, first, s, psize, 0])
-    order = sorted(range(len(tiles)), key=lambda t: -tiles[t][1])  # stable
-    return (np.array([tiles[t][0] for t in order], np.int32).reshape(-1, 8),
-            np.array(merges, np.int32).reshape(-1, 8), np.array(cols, np.int32))
+        for k in range(rt[4]):
+            pref.append(pref[-1] + blen(cols[rt[3] + k]))
+        return pref
+
+    if kv_splits == 0 and decode:
+        K = sum(rt[5] for rt in rts) * NG
+        Wn = max(1, min(DECODE_WG_PER_CU * num_cus, K // BALANCED_MIN_KEYS))
+        wg_of = (lambda X: min(Wn - 1, X * Wn // K)) if K > 0 else (lambda X: 0)
+        X = 0
+        for rt in rts:
+            pref = prefix(rt)
+            n = rt[4]
+            for gi in range(NG):
+                b, wgs = [0], [wg_of(X)]
+                for k in range(1, n):
+                    if wg_of(X + pref[k]) != wgs[-1]:
+                        b.append(k)
+                        wgs.append(wg_of(X + pref[k]))
+                b.append(n)
+                emit_unit(rt, gi, pref, b, wgs)
+                X += rt[5]
+        order = st["groups"]
+        count = [0] * Wn
+        for (_, _, wg) in order:
+            count[wg] += G
+        wg_ptr = np.concatenate([[0], np.cumsum(count)]).astype(np.int32)
+    else:
+        total = sum(rt[6] for rt in rts) * w.num_kv_heads
+        chunk = max(1, _cdiv(total, AUTO_TILES_PER_CU * num_cus))
+        for rt in rts:
+            (I, r0, nr, cb, n, keys, work) = rt
+            if kv_splits == 1:
+                s = 1
+            elif kv_splits > 1:
+                s = min(kv_splits, n)
+            else:
+                cap = min(n, MAX_SPLITS, max(1, keys // AUTO_MIN_SPLIT_KEYS))
+                s = min(_cdiv(work, chunk), cap)
+            s = max(1, s)
+            pref = prefix(rt)
+            b = [0] * (s + 1)
+            b[s] = n
+            for j in range(1, s):
+                p = 0
+                while p < n and pref[p] * s < j * keys:
+                    p += 1
+                p = max(p, b[j - 1] + 1)
+                p = min(p, n - (s - j))
+                b[j] = p
+            for gi in range(NG):
+                emit_unit(rt, gi, pref, b, None)
+        order = sorted(st["groups"], key=lambda gr: -gr[1])  # stable
+        wg_ptr = (np.arange(len(order) + 1) * G).astype(np.int32)
+    tiles = [t for (grp, _, _) in order for t in grp]
+    return (np.array(tiles, np.int32).reshape(-1, 8), np.array(st["merges"], np.int32).reshape(-1, 8),
+            np.array(cols, np.int32), wg_ptr)
 
 
 def _plan(w, kv_splits, num_cus=256):
@@ -118,10 +162,11 @@ def test_planner_matches_model_small(case, kv_splits):
     w = _small_cases()[case]
     p = _plan(w, kv_splits, num_cus=8)
     t = p.tables()
-    tiles, merges, cols = model_plan(w, kv_splits, 8, p.info()["tile_rows"])
+    tiles, merges, cols, wg_ptr = model_plan(w, kv_splits, 8, p.info()["tile_rows"])
     np.testing.assert_array_equal(t["cols"], cols)
     np.testing.assert_array_equal(t["tiles"], tiles)
     np.testing.assert_array_equal(t["merges"], merges)
+    np.testing.assert_array_equal(t["wg_ptr"], wg_ptr)
 
 
 @pytest.mark.parametrize("name", ["worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla"])
@@ -130,10 +175,11 @@ def test_planner_matches_model_full_workloads(name, kv_splits):
     w = W.by_name(name, values=False)
     p = _plan(w, kv_splits)
     t = p.tables()
-    tiles, merges, cols = model_plan(w, kv_splits, 256, p.info()["tile_rows"])
+    tiles, merges, cols, wg_ptr = model_plan(w, kv_splits, 256, p.info()["tile_rows"])
     np.testing.assert_array_equal(t["cols"], cols)
     np.testing.assert_array_equal(t["tiles"], tiles)
     np.testing.assert_array_equal(t["merges"], merges)
+    np.testing.assert_array_equal(t["wg_ptr"], wg_ptr)
 
 
 def _coverage(w, tables, g):
@@ -173,6 +219,73 @@ def test_every_unmasked_pair_is_covered_exactly_once(case, kv_splits):
     split = tiles[tiles[:, 6] >= 0]
     assert sum(int(m[5]) for m in t["merges"]) == len(split)
     assert set(split[:, 6].tolist()) == {int(m[4]) + j * int(m[6]) for m in t["merges"] for j in range(m[5])}
+
+
+def _decode_cases():
+    """R = 1, C >= 16 problems (decode kernel) with short and empty rows."""
+    cases = []
+    for seed in range(8):
+        rng = np.random.default_rng(100 + seed)
+        C = int(rng.choice([16, 32, 64]))
+        g = int(rng.choice([1, 4, 16]))
+        Hkv = int(rng.choice([1, 2, 3]))
+        M = int(rng.integers(1, 40))
+        NB = int(rng.integers(1, 60))
+        cases.append(W.random_bsr(200 + seed, M, NB * C, 1, C, Hkv * g, Hkv, causal=bool(seed % 2),
+                                  partial_lens=seed % 3 != 2, density=float(rng.choice([0.05, 0.3, 0.9])),
+                                  values=False))
+    return cases
+
+
+@pytest.mark.parametrize("num_cus", [1, 3, 8, 256])
+@pytest.mark.parametrize("case", range(8))
+def test_balanced_partition_matches_model(case, num_cus):
+    w = _decode_cases()[case]
+    p = _plan(w, 0, num_cus=num_cus)
+    assert p.info()["kernel"] == 2
+    t = p.tables()
+    tiles, merges, cols, wg_ptr = model_plan(w, 0, num_cus, 16)
+    np.testing.assert_array_equal(t["tiles"], tiles)
+    np.testing.assert_array_equal(t["merges"], merges)
+    np.testing.assert_array_equal(t["wg_ptr"], wg_ptr)
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_balanced_partition_shares_and_coverage(case):
+    """Every workgroup gets its share of all keys to within one block, each
+    workgroup's tiles are one contiguous run of the (I, h) key sequence, and
+    every unmasked pair is visited exactly once."""
+    w = _decode_cases()[case]
+    num_cus = 3
+    p = _plan(w, 0, num_cus=num_cus)
+    t, inf = p.tables(), p.info()
+    tiles, wg_ptr = t["tiles"], t["wg_ptr"]
+    G = inf["heads_per_wg"]
+    assert G == min(8, w.num_kv_heads & -w.num_kv_heads)
+    K = int(tiles[:, 7].sum()) // G          # keys of the (I, head group) sequence
+    Wn = inf["num_workgroups"]
+    assert Wn == max(1, min(DECODE_WG_PER_CU * num_cus, K // BALANCED_MIN_KEYS))
+    assert wg_ptr[0] == 0 and wg_ptr[-1] == len(tiles) and np.all(np.diff(wg_ptr) >= 0)
+    assert np.all(wg_ptr % G == 0)
+    # a group's G tiles share row block and blocks, heads gi*G .. gi*G+G-1
+    for q in range(0, len(tiles), G):
+        grp = tiles[q:q + G]
+        assert np.all(grp[:, [0, 2, 3, 4, 5, 7]] == grp[0, [0, 2, 3, 4, 5, 7]])
+        assert list(grp[:, 1]) == list(range(grp[0, 1], grp[0, 1] + G)) and grp[0, 1] % G == 0
+    share = [int(tiles[wg_ptr[i]:wg_ptr[i + 1], 7].sum()) // G for i in range(Wn)]
+    assert sum(share) == K
+    if K > 0:
+        assert max(share) <= -(-K // Wn) + w.C and min(share) >= K // Wn - w.C
+    # tiles follow the (I, head group) sequence: (row block, group, first block, head) never decreases
+    keyseq = [(int(r[0]), int(r[1]) // G, int(r[4]), int(r[1]) % G) for r in tiles]
+    assert keyseq == sorted(keyseq)
+    g = w.num_qo_heads // w.num_kv_heads
+    assert all(v == 1 for v in _coverage(w, t, g).values())
+    # every (token, kv head) unit has exactly one unsplit tile or one merge
+    split = tiles[tiles[:, 6] >= 0]
+    assert sum(int(m[5]) for m in t["merges"]) == len(split)
+    units = {(int(r[0]), int(r[1])) for r in tiles}
+    assert len(units) == w.M * w.num_kv_heads
 
 
 def test_plan_is_deterministic_and_order_free():
