@@ -30,23 +30,41 @@ __device__ __forceinline__ void store4<float>(float* p, f32x4 v) {
 
 // Merge `n` states of one row: lse of state s at lse_p[s * lse_step], its
 // 4-vector at o_p[s * o_step].  Returns the merged 4-vector, *lse_out the
-// merged lse.
+// merged lse.  One pass with a running maximum (the accumulator is rescaled
+// when it grows), four states per step so that their loads are in flight
+// together; a state with lse = -inf is skipped by a select, so whatever its
+// values hold never reaches the sum.
+__device__ __forceinline__ void merge_one(float l, f32x4 o, float& mx, float& tot, f32x4& acc) {
+  const bool live = l != -INFINITY;
+  const float m_new = live ? fmaxf(mx, l) : mx;
+  const float scale = m_new == mx ? 1.f : fast_exp2((mx - m_new) * kLog2e);  // mx = -inf: 0
+  const float w = live ? fast_exp2((l - m_new) * kLog2e) : 0.f;
+  tot = tot * scale + w;
+  acc = live ? acc * scale + w * o : acc;
+  mx = m_new;
+}
+
 __device__ __forceinline__ f32x4 merge_row4(const float* lse_p, int64_t lse_step, const float* o_p,
                                             int64_t o_step, int n, float* lse_out) {
-  float mx = -INFINITY;
-  for (int s = 0; s < n; ++s) mx = fmaxf(mx, lse_p[s * lse_step]);
+  float mx = -INFINITY, tot = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 4 <= n; s += 4) {
+    float l[4];
+    f32x4 o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      l[j] = lse_p[(s + j) * lse_step];
+      o[j] = *reinterpret_cast<const f32x4*>(o_p + (s + j) * o_step);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) merge_one(l[j], o[j], mx, tot, acc);
+  }
+  for (; s < n; ++s)
+    merge_one(lse_p[s * lse_step], *reinterpret_cast<const f32x4*>(o_p + s * o_step), mx, tot, acc);
   if (mx == -INFINITY) {
     *lse_out = -INFINITY;
-    return acc;
-  }
-  float tot = 0.f;
-  for (int s = 0; s < n; ++s) {
-    const float l = lse_p[s * lse_step];
-    if (l == -INFINITY) continue;
-    const float w = fast_exp2((l - mx) * kLog2e);
-    tot += w;
-    acc += w * *reinterpret_cast<const f32x4*>(o_p + s * o_step);
+    return f32x4{0.f, 0.f, 0.f, 0.f};
   }
   *lse_out = mx + __logf(tot);
   return acc * (1.f / tot);
