@@ -261,6 +261,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   // scores -> probabilities with a lagging running max (branch-free, so it can
   // be interleaved with the next tile's QK^T); `live` = false leaves the running
   // state untouched.  Returns alpha; sets `upd` when the running max moved.
+  // probabilities of the current tile, rounded to the storage type, in pairs
+  // (pair j of block kb = S^T values 2j, 2j+1 of this lane)
+  typedef T T2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  constexpr bool kIsHalf = sizeof(T) == 2 && static_cast<T>(1.0009765625f) != static_cast<T>(1.f);
+  T2 pp[NKB][8];
   auto softmax_core = [&](f32x16 (&sacc)[NKB], bool live, bool& upd) -> float {
     float mx = -INFINITY;
 #pragma unroll
@@ -277,10 +283,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = fast_exp2(fmaf(sacc[kb][v], sl2, -m_use));
-        sacc[kb][v] = p;
-        ls += p;
+      for (int v = 0; v < 16; v += 2) {
+        const float p0 = fast_exp2(fmaf(sacc[kb][v], sl2, -m_use));
+        const float p1 = fast_exp2(fmaf(sacc[kb][v + 1], sl2, -m_use));
+        T2 pr;
+        pr[0] = static_cast<T>(p0);
+        pr[1] = static_cast<T>(p1);
+        pp[kb][v >> 1] = pr;
+        // fp16: the row sum adds exactly the rounded probabilities the PV
+        // product uses (one dot2 per pair); bf16 rounding is too coarse for
+        // the sum, which stays in fp32
+        if (kIsHalf) ls = __builtin_amdgcn_fdot2(bitcast<h2>(pr), h2{1, 1}, ls, false);
+        else ls += p0 + p1;
       }
     m_run = m_new;
     l_run = live ? l_run * alpha + ls : l_run;
@@ -302,7 +316,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
       const int hv = ks & 1;
       v8 pf;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pf[e] = static_cast<T>(sacc[kb][hv * 8 + e]);
+      for (int j = 0; j < 4; ++j) {
+        pf[2 * j] = pp[kb][hv * 4 + j][0];
+        pf[2 * j + 1] = pp[kb][hv * 4 + j][1];
+      }
       const int row = ks * 16 + vrow;
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
