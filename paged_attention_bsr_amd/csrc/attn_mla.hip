@@ -13,17 +13,18 @@
 //   * the selected fp8 rows are gathered with 16-byte loads two tiles ahead
 //     (the per-key index one tile ahead of its use), widened exactly to bf16
 //     (every e4m3 value is a bf16 value; the dequant scale is applied to the
-//     logits and the output instead) and stored as K rows (bf16, rows padded
-//     to an odd number of 16-byte units) and V^T (fp16, 64-byte rows with
-//     XOR-swizzled 16-byte units) into the LDS buffer of the next tile while
-//     this tile's scores are computed;
+//     logits and the output instead) and stored as row-major bf16 rows with
+//     XOR-swizzled 16-byte units into the LDS buffer of the next tile while
+//     this tile's scores are computed.  The same rows serve as K and, through
+//     their first 512 values, as V: there is no separate V tile;
 //   * wave h of a pair computes S^T = K Q^T for keys 16h .. 16h+15 of the
 //     tile with v_mfma_f32_16x16x32_bf16 (Q^T resident in registers); the
 //     pair swaps its fp32 scores through LDS, both waves run the same online
 //     softmax (log2 domain, lagging running max) on all 32 keys, and wave h
 //     accumulates O^T += V^T P^T for value dims 256h .. 256h+255 with
-//     v_mfma_f32_16x16x32_f16: V is held as fp16 (exact for e4m3 values), so
-//     P keeps fp16's 11-bit precision instead of bf16's 8 bits.
+//     v_mfma_f32_16x16x32_bf16, the V^T fragments read from the row-major
+//     tile by ds_read_b64_tr_b16 and P rounded to bf16 (the row sum l keeps
+//     the unrounded fp32 probabilities).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -36,15 +37,14 @@ constexpr int kDv = 512;
 constexpr int kKT = 32;
 constexpr float kRescaleSlack = 8.f;  // log2 units the running max may lag behind
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
 struct MlaLds {
-  // 1152 B of bf16 per key, padded by one 16-byte unit: 73 units per row is
-  // odd, so 16 consecutive keys at one chunk fall on 16 different bank
-  // groups without a swizzle, and chunk offsets stay immediate
-  static constexpr int kKRow = kDqk * 2 + 16;
+  // 1152 B of bf16 per key (72 16-byte units, no padding)
+  static constexpr int kKRow = kDqk * 2;
   static constexpr int kKBytes = kKT * kKRow;
-  static constexpr int kVtBytes = kDv * kKT * 2;         // V^T: 64 B per value dim
   static constexpr int kTokBytes = kKT * 4;
-  static constexpr int kBuf = kKBytes + kVtBytes + kTokBytes;
+  static constexpr int kBuf = kKBytes + kTokBytes;
   // score exchange of a wave pair: [16 heads][kXsRow] fp32, rows padded to
   // 36 floats so that 16 heads at one key offset hit distinct banks
   static constexpr int kXsRow = kKT + 4;
@@ -63,17 +63,22 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-template <bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_f16x2(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+// Unit u of key k's row sits at unit u ^ kx(k), with kx(k) a permutation of
+// bits 1-3 of the key into the low three bits of the unit (bit 1 -> bit 1,
+// bit 2 -> bit 0, bit 3 -> bit 2), so the XOR stays inside an aligned group
+// of 8 units.  LDS has 64 banks of 4 B, 16 units per pass; a row is 72 units,
+// so even keys start at bank unit 0 and odd keys at 8.  Then
+//   * 16 consecutive keys at one unit (the QK reads and the tile stores, 16
+//     lanes x 16 B per pass) hit 16 different bank units: the key's bit 0
+//     picks the half, kx a distinct unit inside it;
+//   * a transposed read (32 lanes x 8 B per pass: keys 8q + {0..3} of two
+//     neighbouring q, or + {4..7}, two aligned units each) hits 8 different
+//     aligned unit pairs: bit 0 picks the half, bits 1 and 3 (kx bits 1 and 2)
+//     the pair.
+__device__ __forceinline__ int kx(int key) {
+  return (((key >> 1) & 1) << 1) | (((key >> 3) & 1) << 2) | ((key >> 2) & 1);
 }
-
-// V^T tile: row d (value dim) holds the 32 keys' fp16 values, 64 B = four
-// 16-byte units of 8 keys; the unit index is XORed with bits 2-3 of the row,
-// so that a read of 16 consecutive rows at one unit touches every bank once.
-__device__ __forceinline__ int vt_off(int d, int key) {
-  return d * 64 + (((key >> 3) ^ ((d >> 2) & 3)) << 4) + (key & 7) * 2;
-}
+__device__ __forceinline__ int k_off(int key, int u) { return key * MlaLds::kKRow + ((u ^ kx(key)) << 4); }
 
 
 template <int NW, bool CAUSAL, bool LENS>
@@ -178,7 +183,6 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
   };
   auto store_tile = [&](int buf, const u32x4 (&creg)[CH_PER_T], int tok) {
     unsigned char* base = lds + buf * L::kBuf;
-    unsigned char* vt = base + L::kKBytes;
 #pragma unroll
     for (int i = 0; i < CH_PER_T; ++i) {
       const int ci = tid + i * NTHR;
@@ -190,26 +194,11 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
         b[2 * w] = fp8x2_to_bf16x2<false>(creg[i][w]);
         b[2 * w + 1] = fp8x2_to_bf16x2<true>(creg[i][w]);
       }
-      // K: bf16 chunks 2c and 2c + 1 of this key's row
-      *reinterpret_cast<u32x4*>(base + my_key * L::kKRow + ((2 * c) << 4)) = u32x4{b[0], b[1], b[2], b[3]};
-      *reinterpret_cast<u32x4*>(base + my_key * L::kKRow + ((2 * c + 1) << 4)) = u32x4{b[4], b[5], b[6], b[7]};
-      // V^T (fp16): the 16 values of this chunk, if they are latent (V) values.
-      // Lanes 2m and 2m + 1 hold keys 2m and 2m + 1 of the same chunk; after
-      // a DPP swap each writes one dword (both keys) per value pair: the even
-      // lane the even values, the odd lane the odd ones.
-      if (c * 16 < kDv) {
-        const bool odd = my_key & 1;
-        const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) {
-          const uint32_t own = w & 1 ? fp8x2_to_f16x2<true>(creg[i][w >> 1]) : fp8x2_to_f16x2<false>(creg[i][w >> 1]);
-          const uint32_t other = __builtin_amdgcn_mov_dpp(own, 0xB1, 0xF, 0xF, true);  // lane ^ 1
-          *reinterpret_cast<uint32_t*>(vt + vt_off(c * 16 + 2 * w + (odd ? 1 : 0), my_key & ~1)) =
-              __builtin_amdgcn_perm(other, own, sel);
-        }
-      }
+      // bf16 units 2c and 2c + 1 of this key's row
+      *reinterpret_cast<u32x4*>(base + k_off(my_key, 2 * c)) = u32x4{b[0], b[1], b[2], b[3]};
+      *reinterpret_cast<u32x4*>(base + k_off(my_key, 2 * c + 1)) = u32x4{b[4], b[5], b[6], b[7]};
     }
-    if (tid < kKT) reinterpret_cast<int*>(base + L::kKBytes + L::kVtBytes)[tid] = tok;
+    if (tid < kKT) reinterpret_cast<int*>(base + L::kKBytes)[tid] = tok;
   };
 
   // this wave's output: O^T for dv in [256 * hf, 256 * hf + 256), its 16 heads
@@ -253,16 +242,22 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
     const bool need_mask = LENS || (t0 + kKT > npos) || (CAUSAL && tok_hi > static_cast<int64_t>(qtok) + a.causal_off);
 
     const unsigned char* kl = lds + buf * L::kBuf;
-    const unsigned char* vt = kl + L::kKBytes;
-    const int* ktok = reinterpret_cast<const int*>(kl + L::kKBytes + L::kVtBytes);
+    const int* ktok = reinterpret_cast<const int*>(kl + L::kKBytes);
 
     // (1) S^T of this wave's 16 keys (16 * hf ..) x 16 heads over all 576
     // dims, 18 k-steps; K fragments through a small register ring
     if (group_active && !skip) {
       constexpr int kSteps = kDqk / 32;
       constexpr int kRing = 4;
-      const unsigned char* krow = kl + (hf * 16 + col) * L::kKRow + quad * 16;
-      auto kfrag = [&](int ks) { return *reinterpret_cast<const bf16x8*>(krow + ks * 64); };
+      // unit quad + 4 ks of key 16 hf + col: the XOR touches the low three
+      // unit bits only, so even and odd ks each have one base and
+      // immediate offsets
+      const int key = hf * 16 + col;
+      const unsigned char* kev = kl + k_off(key, quad);
+      const unsigned char* kod = kl + k_off(key, quad + 4);
+      auto kfrag = [&](int ks) {
+        return *reinterpret_cast<const bf16x8*>((ks & 1 ? kod : kev) + (ks >> 1) * 128);
+      };
       f32x4 sacc = f32x4{};
       bf16x8 kr[kRing];
 #pragma unroll
@@ -313,25 +308,41 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
     const float alpha = upd ? fast_exp2(m_run - m_new) : 1.f;
     m_run = m_new;
     float ls = 0.f;
-    f16x8 pf;
+    bf16x8 pf;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float p = fast_exp2(fmaf(sv[e], sl2, -m_use));
       ls += p;
-      pf[e] = static_cast<_Float16>(p);
+      pf[e] = static_cast<__bf16>(p);
     }
     l_run = l_run * alpha + ls;
     if (__ballot(upd) != 0) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
     }
-    // (3) O^T += V^T P^T for this wave's dv half: A = V^T rows (dv), keys
-    // 8 * quad + e, one 16-byte unit of a V^T row
-    const unsigned char* vrow = vt + vt_off(hf * (kDv / 2) + col, 8 * quad);
+    // (3) O^T += V^T P^T for this wave's dv half.  A = V^T (16 dv x 32 keys):
+    // lane (col, quad) needs dv 16 db + col of keys 8 quad .. 8 quad + 7.  A
+    // transposed read of 16 lanes takes 4 keys x 16 dv (lane col addresses key
+    // col / 4, dv 4 (col % 4) .. + 3) and hands lane col that 4-key column of
+    // dv col; two reads cover keys 8 quad + 0..3 and + 4..7.
+    {
+      const int vr = 8 * quad + (col >> 2);
+      const int c1 = (col & 3) >> 1;
+      const int xa = kx(vr), xb = kx(vr + 4);
+      const unsigned char* va = kl + vr * L::kKRow + hf * (kDv / 2) * 2 + (col & 1) * 8;
+      const unsigned char* vb = va + 4 * L::kKRow;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const f16x8 vf = *reinterpret_cast<const f16x8*>(vrow + db * 16 * 64);
-      oacc[db] = MfmaType<_Float16>::mfma16(vf, pf, oacc[db]);
+      for (int db = 0; db < NDB; ++db) {
+        const int ul = 2 * (db & 3) + c1;  // low three unit bits before the XOR
+        const int hi = (db >> 2) * 128;
+        const auto lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(va + (((ul ^ xa)) << 4) + hi));
+        const auto hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vb + (((ul ^ xb)) << 4) + hi));
+        const bf16x8 vf = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
+        oacc[db] = MfmaType<__bf16>::mfma16(vf, pf, oacc[db]);
+      }
     }
   };
   if (ntiles > 0) {
