@@ -204,6 +204,46 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     }
   };
 
+  // Full blocks that each hold whole key tiles (BLOCKTILE without lengths):
+  // every key of a tile is valid and its tokens are consecutive, so the DMA
+  // needs one scalar base per tile plus per-lane byte offsets fixed for the
+  // whole loop, blocks advance without a division, and masks follow from the
+  // tile's first token (no token array).
+  constexpr bool FAST = BLOCKTILE && !LENS;
+  uint32_t koff[BPW], voff[BPW];
+  if (FAST) {
+    const int u = lane & 15;
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+      const int row = 4 * (wave * BPW + j) + (lane >> 4);
+      koff[j] = static_cast<uint32_t>(row) * static_cast<uint32_t>(a.k_stride * 2) + ((u ^ k_swz(row)) << 4);
+      voff[j] = static_cast<uint32_t>(row) * static_cast<uint32_t>(a.v_stride * 2) + ((u ^ v_swz(row)) << 4);
+    }
+  }
+  const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kbase);
+  const unsigned char* vbytes = reinterpret_cast<const unsigned char*>(vbase);
+  int dblk = 0, doff = 0;  // block and offset of the next tile to load (FAST)
+  auto dma_fast = [&](unsigned char* st) -> int {
+    const int lo = cols[cb + dblk] * C + doff;
+    doff += KT;
+    if (doff == C) {
+      doff = 0;
+      ++dblk;
+    }
+    const unsigned char* kt = kbytes + static_cast<int64_t>(lo) * (a.k_stride * 2);
+    const unsigned char* vt = vbytes + static_cast<int64_t>(lo) * (a.v_stride * 2);
+#pragma unroll
+    for (int j = 0; j < BPW; ++j) {
+      const int b = wave * BPW + j;
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(kt + koff[j]),
+                                       (__attribute__((address_space(3))) void*)(st + b * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(vt + voff[j]),
+                                       (__attribute__((address_space(3))) void*)(st + L::kKBytes + b * 1024), 16, 0,
+                                       0);
+    }
+    return lo;
+  };
+
   // wave-uniform token range of key tile kt (the column list is ascending)
   auto tile_tok_range = [&](int kt, int64_t& lo, int64_t& hi) {
     const int t0 = kt * KT;
@@ -257,6 +297,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
         for (int e = 0; e < 4; ++e) sacc[kb][g4 * 4 + e] = tt[e] < qbound ? sacc[kb][g4 * 4 + e] : -INFINITY;
       }
     }
+  };
+  // FAST causal mask: key idx of the tile is visible iff idx <= qtok + N - M - lo
+  auto mask_fast = [&](int lo, f32x16 (&sacc)[NKB]) {
+    const int limh = qtok + a.causal_off - lo - 8 * half;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = kb * 32 + 16 * (g4 >> 1) + 4 * (g4 & 1) + e;
+          sacc[kb][g4 * 4 + e] = c <= limh ? sacc[kb][g4 * 4 + e] : -INFINITY;
+        }
   };
   // scores -> probabilities with a lagging running max (branch-free, so it can
   // be interleaved with the next tile's QK^T); `live` = false leaves the running
@@ -359,11 +412,37 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     }
     pv(cur, sc);
   };
+  int lo_next = 0;  // first token of the tile in flight (FAST)
+  auto step_fast = [&](int t, unsigned char* cur, unsigned char* nxt) {
+    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's DMA into `cur` has landed
+    __syncthreads();                     // ... and every other wave's
+    const int lo = lo_next;
+    if (t + 1 < ntiles) lo_next = dma_fast(nxt);
+    if (!wave_active || (CAUSAL && lo > wave_lim)) return;  // tile above this wave's diagonal
+    f32x16 sc[NKB];
+    qk(cur, sc);
+    if (CAUSAL && static_cast<int64_t>(lo) + (KT - 1) > wave_lim_lo) mask_fast(lo, sc);
+    bool upd;
+    const float alpha = softmax_core(sc, true, upd);
+    if (__ballot(upd) != 0) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+    }
+    pv(cur, sc);
+  };
   if (ntiles > 0) {
-    dma_tile(0, st0, tk0);
-    for (int t = 0; t < ntiles; t += 2) {
-      step(t, st0, tk0, st1, tk1);
-      if (t + 1 < ntiles) step(t + 1, st1, tk1, st0, tk0);
+    if (FAST) {
+      lo_next = dma_fast(st0);
+      for (int t = 0; t < ntiles; t += 2) {
+        step_fast(t, st0, st1);
+        if (t + 1 < ntiles) step_fast(t + 1, st1, st0);
+      }
+    } else {
+      dma_tile(0, st0, tk0);
+      for (int t = 0; t < ntiles; t += 2) {
+        step(t, st0, tk0, st1, tk1);
+        if (t + 1 < ntiles) step(t + 1, st1, tk1, st0, tk0);
+      }
     }
   }
 
@@ -403,7 +482,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
 template <typename T, int NW, int KT>
 hipError_t launch_variant(const AttnArgs& a, bool causal, bool lens, hipStream_t st) {
   const dim3 grid(a.num_tiles), block(NW * 64);
-  const bool bt = a.C % KT == 0;
+  // block tiles also need every row offset of a tile (KT rows) to fit 31 bits
+  const int64_t max_stride = a.k_stride > a.v_stride ? a.k_stride : a.v_stride;
+  const bool bt = a.C % KT == 0 && static_cast<int64_t>(KT) * 2 * max_stride < (int64_t{1} << 31);
 #define BSA_TILE_LAUNCH(CA, LE)                                                              \
   if (bt) attn_tile_kernel<T, NW, KT, CA, LE, true><<<grid, block, 0, st>>>(a);              \
   else attn_tile_kernel<T, NW, KT, CA, LE, false><<<grid, block, 0, st>>>(a);
