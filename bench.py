@@ -30,16 +30,21 @@ METRIC = "KV GB/s (decode) & TFLOP/s (sparse prefill), % of MI355X HBM/MFMA peak
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}
 DECODE = {"paged_decode", "sparse_mla", "worked_example"}
-KERNEL_SOURCES = ["attn_tile.hip", "attn_decode.hip", "attn_mla.hip", "merge.hip", "device_common.h", "kernels.h"]
+# sources of each attention kernel (the traffic counters are valid while these are unchanged)
+KERNEL_SOURCES = {
+    "attn_tile_kernel": ["attn_tile.hip", "device_common.h", "kernels.h"],
+    "attn_decode_kernel": ["attn_decode.hip", "device_common.h", "kernels.h"],
+    "attn_mla_kernel": ["attn_mla.hip", "device_common.h", "kernels.h"],
+}
 
 
 def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "paged_attention_bsr_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -236,9 +241,9 @@ def main() -> int:
         # exact bf16 MFMA arithmetic bounds this shape too; report its MFMA fraction beside HBM
         mfma_tf = alg_flops / (attn_avg_ms * 1e-3) / 1e12
         roof["mfma_frac_bf16"] = mfma_tf / MFMA_PEAK_TFLOPS["bf16"]
-    roof["traffic"] = measured_traffic(args.workload, kernel_source_hash())
     roof["kernel"] = {L.BSA_KERNEL_MLA: "attn_mla_kernel", L.BSA_KERNEL_DECODE: "attn_decode_kernel"}.get(
         info["kernel"], "attn_tile_kernel")
+    roof["traffic"] = measured_traffic(args.workload, kernel_source_hash(roof["kernel"]))
     roof["alg_bytes_per_launch"] = alg_bytes
     roof["alg_flops_per_launch"] = alg_flops
     roof["avg_launch_ms"] = attn_avg_ms
