@@ -81,7 +81,8 @@ __device__ __forceinline__ int kx(int key) {
 __device__ __forceinline__ int k_off(int key, int u) { return key * MlaLds::kKRow + ((u ^ kx(key)) << 4); }
 
 
-template <int NW, bool CAUSAL, bool LENS>
+// C1: blocks of one key (index-selected rows), so positions are block ids
+template <int NW, bool CAUSAL, bool LENS, bool C1>
 __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
   constexpr int NBUF = 2;  // LDS tile buffers: tile kt + 1 is stored while tile kt is computed
   using L = MlaLds;
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
   const int cb = trec[4];
   const int ce = trec[5];
   const int part = trec[6];
-  const int C = a.C;
+  const int C = C1 ? 1 : a.C;
   const int npos = (ce - cb) * C;
   const int ntiles = (npos + kKT - 1) / kKT;
 
@@ -149,14 +150,14 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
   };
   auto fetch_blk = [&](int t) -> BlkRef {
     const int tc = t < npos ? t : npos - 1;
-    const int blk = tc / C;
+    const int blk = C1 ? tc : tc / C;
     BlkRef r;
     r.J = cols[cb + blk];
     r.len = LENS ? lens[cb + blk] : C;
     return r;
   };
   auto finish_tok = [&](int t, const BlkRef& r) -> int {
-    const int off = t - (t / C) * C;
+    const int off = C1 ? 0 : t - (t / C) * C;
     bool ok = t < npos;
     if (LENS) ok = ok && off < r.len;
     return ok ? r.J * C + off : -1;
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
     // tile-level decisions are the same for every wave (one query token)
     const int t0 = kt * kKT;
     const int t1 = (t0 + kKT < npos ? t0 + kKT : npos) - 1;
-    const int blk0 = t0 / C, blk1 = t1 / C;
+    const int blk0 = C1 ? t0 : t0 / C, blk1 = C1 ? t1 : t1 / C;
     const int64_t tok_lo = static_cast<int64_t>(cols[cb + blk0]) * C + (t0 - blk0 * C);
     const int64_t tok_hi = static_cast<int64_t>(cols[cb + blk1]) * C + (t1 - blk1 * C);
     const bool skip = CAUSAL && tok_lo > static_cast<int64_t>(qtok) + a.causal_off;
@@ -248,7 +249,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
     // dims, 18 k-steps; K fragments through a small register ring
     if (group_active && !skip) {
       constexpr int kSteps = kDqk / 32;
-      constexpr int kRing = 4;
+      constexpr int kRing = 8;
       // unit quad + 4 ks of key 16 hf + col: the XOR touches the low three
       // unit bits only, so even and odd ks each have one base and
       // immediate offsets
@@ -259,15 +260,20 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
         return *reinterpret_cast<const bf16x8*>((ks & 1 ? kod : kev) + (ks >> 1) * 128);
       };
       f32x4 sacc = f32x4{};
-      bf16x8 kr[kRing];
+      bf16x8 kr[kSteps];
 #pragma unroll
-      for (int j = 0; j < kRing; ++j) kr[j] = kfrag(j);
+      for (int ks = 0; ks < kSteps; ++ks) kr[ks] = kfrag(ks);
 #pragma unroll
-      for (int ks = 0; ks < kSteps; ++ks) {
-        const bf16x8 kf = kr[ks % kRing];
-        if (ks + kRing < kSteps) kr[ks % kRing] = kfrag(ks + kRing);
-        sacc = MfmaType<__bf16>::mfma16(kf, qf[ks], sacc);
+      for (int ks = 0; ks < kSteps; ++ks) sacc = MfmaType<__bf16>::mfma16(kr[ks], qf[ks], sacc);
+      // reads run kRing fragments ahead of the products (the scheduler would
+      // otherwise issue each read one or two products before its use)
+      __builtin_amdgcn_sched_group_barrier(0x100, kRing, 0);
+#pragma unroll
+      for (int ks = 0; ks < kSteps - kRing; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
+      __builtin_amdgcn_sched_group_barrier(0x008, kRing, 0);
       // lane holds head col, keys 16 * hf + 4 * quad + v
       *reinterpret_cast<f32x4*>(xs + col * L::kXsRow + hf * 16 + 4 * quad) = sacc;
     }
@@ -343,6 +349,15 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
             bf16x8, __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7));
         oacc[db] = MfmaType<__bf16>::mfma16(vf, pf, oacc[db]);
       }
+      // the transposed reads run kVRing products ahead
+      constexpr int kVRing = 6;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kVRing, 0);
+#pragma unroll
+      for (int db = 0; db < NDB - kVRing; ++db) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kVRing, 0);
     }
   };
   if (ntiles > 0) {
@@ -394,11 +409,13 @@ hipError_t launch_attn_mla(const AttnArgs& a, bool causal, bool has_lens, hipStr
   constexpr int NW = 8;
   const dim3 grid(a.num_tiles), block(NW * 64);
   if (causal) {
-    if (has_lens) attn_mla_kernel<NW, true, true><<<grid, block, 0, st>>>(a);
-    else attn_mla_kernel<NW, true, false><<<grid, block, 0, st>>>(a);
+    if (has_lens) attn_mla_kernel<NW, true, true, false><<<grid, block, 0, st>>>(a);
+    else if (a.C == 1) attn_mla_kernel<NW, true, false, true><<<grid, block, 0, st>>>(a);
+    else attn_mla_kernel<NW, true, false, false><<<grid, block, 0, st>>>(a);
   } else {
-    if (has_lens) attn_mla_kernel<NW, false, true><<<grid, block, 0, st>>>(a);
-    else attn_mla_kernel<NW, false, false><<<grid, block, 0, st>>>(a);
+    if (has_lens) attn_mla_kernel<NW, false, true, false><<<grid, block, 0, st>>>(a);
+    else if (a.C == 1) attn_mla_kernel<NW, false, false, true><<<grid, block, 0, st>>>(a);
+    else attn_mla_kernel<NW, false, false, false><<<grid, block, 0, st>>>(a);
   }
   return hipGetLastError();
 }

@@ -257,3 +257,22 @@ def test_mla_kernel_variants(causal, lens):
         assert any(int(j) > t + off for t in range(w.M) for j in w.indices[w.indptr[t]:w.indptr[t + 1]])
     _check(w, 1, what=f"mla variant causal={causal} lens={lens}")
     _check(w, 3, what=f"mla variant causal={causal} lens={lens} splits=3")
+
+
+@pytest.mark.parametrize("causal,lens", [(False, False), (True, True)])
+def test_mla_kernel_multi_row_blocks(causal, lens):
+    """The sparse-MLA kernel with blocks of 4 latent rows (C = 4) instead of single rows: key
+    positions map to blocks by division, and with lengths the last rows of some blocks are
+    masked (their cache slots hold garbage that must not reach the output)."""
+    w = W.sparse_mla(seed=38, num_tokens=48, num_heads=64, cache_rows=1024, topk=8, min_ctx=1024,
+                     max_ctx=1024)
+    rng = np.random.default_rng(38)
+    C, nb = 4, 1024 // 4
+    w.C = C
+    w.indptr = (np.arange(w.M + 1) * 24).astype(np.int32)
+    w.indices = np.concatenate([rng.choice(nb, 24, replace=False) for _ in range(w.M)]).astype(np.int32)
+    w.causal = causal
+    if lens:
+        w.kv_block_lens = rng.integers(1, C + 1, nb).astype(np.int32)
+    _check(w, 1, what=f"mla C=4 causal={causal} lens={lens}")
+    _check(w, 2, what=f"mla C=4 causal={causal} lens={lens} splits=2")
