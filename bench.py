@@ -50,21 +50,38 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def unmasked_pairs(w, rows=None):
-    """Unmasked (query row, key) pairs (the same for every head), counted block by block."""
+def head_structures(w):
+    """The (indptr, indices) rows of each structure head: one shared BSR, or one per kv
+    head for a per-head block mask (``w.meta["block_mask"]``)."""
     import numpy as np
+    bm = w.meta.get("block_mask")
+    if bm is None:
+        return [(w.indptr, w.indices)]
+    out = []
+    for h in range(bm.shape[0]):
+        rows = [np.nonzero(bm[h, I])[0] for I in range(bm.shape[1])]
+        out.append((np.cumsum([0] + [len(r) for r in rows]), np.concatenate(rows).astype(np.int32)))
+    return out
+
+
+def unmasked_pairs(w, rows=None, indptr=None, indices=None):
+    """Unmasked (query row, key) pairs of one structure (the shared BSR unless given),
+    counted block by block."""
+    import numpy as np
+    indptr = w.indptr if indptr is None else indptr
+    indices = w.indices if indices is None else indices
     lens = w.kv_block_lens
     off = w.N - w.M
     row_set = None if rows is None else np.asarray(sorted(rows))
     total = 0
-    for I in range(len(w.indptr) - 1):
+    for I in range(len(indptr) - 1):
         r0, r1 = I * w.R, min(w.M, (I + 1) * w.R)
         rr = np.arange(r0, r1)
         if row_set is not None:
             rr = rr[np.isin(rr, row_set)]
             if rr.size == 0:
                 continue
-        for J in w.indices[w.indptr[I]:w.indptr[I + 1]]:
+        for J in indices[indptr[I]:indptr[I + 1]]:
             n = w.C if lens is None else int(lens[J])
             if not w.causal:
                 total += n * rr.size
@@ -84,19 +101,27 @@ def algorithmic_work(w, rows=None):
     flops: 2 * (head_dim + head_dim_vo) per unmasked pair and qo head
     (QK^T and PV).
     """
-    pairs = unmasked_pairs(w, rows)
+    structs = head_structures(w)
+    # pairs summed over kv heads (a shared structure counts once per kv head)
+    if len(structs) == 1:
+        kv_pairs = unmasked_pairs(w, rows) * w.num_kv_heads
+    else:
+        kv_pairs = sum(unmasked_pairs(w, rows, ip, ix) for ip, ix in structs)
+    g = w.num_qo_heads // w.num_kv_heads
     m = w.M if rows is None else len(rows)
     e_kv = w.kv_dtype.itemsize
     if w.v_aliases_k:
-        kv_bytes = pairs * w.num_kv_heads * w.head_dim * e_kv
+        kv_bytes = kv_pairs * w.head_dim * e_kv
     else:
-        kv_bytes = pairs * w.num_kv_heads * (w.head_dim + w.head_dim_vo) * e_kv
+        kv_bytes = kv_pairs * (w.head_dim + w.head_dim_vo) * e_kv
     qo = m * w.num_qo_heads * (w.head_dim * w.q_dtype.itemsize + w.head_dim_vo * w.o_dtype.itemsize + 4)
-    nnz_rows = w.nnz if rows is None else sum(int(w.indptr[r // w.R + 1] - w.indptr[r // w.R]) for r in rows)
-    idx = 4 * (m + 1 + nnz_rows)
-    if w.kv_block_lens is not None:
-        idx += 4 * nnz_rows
-    flops = 2 * pairs * w.num_qo_heads * (w.head_dim + w.head_dim_vo)
+    idx = 0
+    for ip, ix in structs:
+        nnz_rows = len(ix) if rows is None else sum(int(ip[r // w.R + 1] - ip[r // w.R]) for r in rows)
+        idx += 4 * (m + 1 + nnz_rows)
+        if w.kv_block_lens is not None:
+            idx += 4 * nnz_rows
+    flops = 2 * kv_pairs * g * (w.head_dim + w.head_dim_vo)
     return kv_bytes + qo + idx, flops
 
 
@@ -122,8 +147,13 @@ def cpu_baseline(w, budget_s: float):
     while done < w.M and t_used < budget_s:
         rows = order[done:done + batch].tolist()
         t0 = time.perf_counter()
-        oracle.bsr_attention(w.indptr, w.indices, w.M, w.N, w.R, w.C, q, k, v, sm_scale=w.sm_scale,
-                             causal=w.causal, kv_block_lens=w.kv_block_lens, rows=rows)
+        if "block_mask" in w.meta:
+            oracle.block_mask_attention(w.meta["block_mask"], w.M, w.N, w.R, w.C, q, k, v,
+                                        sm_scale=w.sm_scale, causal=w.causal,
+                                        kv_block_lens=w.kv_block_lens, rows=rows)
+        else:
+            oracle.bsr_attention(w.indptr, w.indices, w.M, w.N, w.R, w.C, q, k, v, sm_scale=w.sm_scale,
+                                 causal=w.causal, kv_block_lens=w.kv_block_lens, rows=rows)
         t_used += time.perf_counter() - t0
         done += len(rows)
         batch = min(batch * 2, 64)
@@ -137,7 +167,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="paged_decode",
-                    choices=["worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla"])
+                    choices=["worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla",
+                             "head_sparse_prefill"])
     ap.add_argument("--kv-splits", type=int, default=None, help="override the workload's split-KV setting")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
@@ -172,7 +203,7 @@ def main() -> int:
                 head_dim_vo=w.head_dim_vo, causal=w.causal, sm_scale=w.sm_scale, kv_splits=kv_splits,
                 kv_block_lens=w.kv_block_lens, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, o_dtype=w.o_dtype,
                 k_descale=w.k_descale, v_descale=w.v_descale, k_token_stride=w.k_token_stride,
-                v_token_stride=w.v_token_stride)
+                v_token_stride=w.v_token_stride, block_mask=w.meta.get("block_mask"))
     plan_ms = (time.perf_counter() - t0) * 1e3
     info = plan.info()
     q = w.q.to(dev)
@@ -262,7 +293,8 @@ def main() -> int:
 
     cfg = {"workload": args.workload, "M": w.M, "N": w.N, "R": w.R, "C": w.C,
            "num_qo_heads": w.num_qo_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
-           "head_dim_vo": w.head_dim_vo, "causal": w.causal, "nnz_blocks": w.nnz, "kv_splits": kv_splits,
+           "head_dim_vo": w.head_dim_vo, "causal": w.causal, "nnz_blocks": sum(len(ix) for _, ix in head_structures(w)),
+           "per_head_structure": "block_mask" in w.meta, "kv_splits": kv_splits,
            "tiles": info["num_tiles"], "merges": info["num_merges"], "plan_ms": plan_ms,
            "alg_bytes": alg_bytes, "alg_flops": alg_flops}
     line = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,

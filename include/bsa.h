@@ -43,7 +43,7 @@ extern "C" {
 #endif
 
 #define BSA_VERSION_MAJOR 0
-#define BSA_VERSION_MINOR 1
+#define BSA_VERSION_MINOR 2
 
 typedef struct bsa_plan_s* bsa_plan_t;
 
@@ -98,6 +98,25 @@ typedef enum {
  *                  v_token_stride == k_token_stride).
  *   num_cus        0 = query the current device; > 0 = plan for that many CUs
  *                  without touching the GPU (host-only planning)
+ *
+ * Per-head structure (BlockSparseAttentionWrapper.plan: block_mask,
+ * q2k_indices / q2k_num; VariableBlockSparseAttentionWrapper: each kv head
+ * its own pattern).  Set at most one of block_mask and q2k_indices; then
+ * indptr / indices are ignored and kv head h attends by its own structure:
+ *   struct_heads   heads of the structure arrays: num_kv_heads, or
+ *                  num_qo_heads -- then the qo heads of one kv head (h*g ..
+ *                  h*g+g-1) must describe the same blocks (the kv head shares
+ *                  every K/V load between them); a mismatch is
+ *                  BSA_ERR_INVALID_ARGUMENT
+ *   block_mask     NULL, or uint8[struct_heads][MB][NB]: nonzero = query
+ *                  block I attends to key block J for that head
+ *   q2k_indices    NULL, or int32[struct_heads][MB][q2k_topk]: the selected key
+ *                  blocks of each (head, query block), each in [0, NB), no
+ *                  duplicate among a row's first q2k_num entries, any order
+ *   q2k_num        NULL (every row uses all q2k_topk entries), or
+ *                  int32[struct_heads][MB] with entries in [0, q2k_topk]
+ *   q2k_topk       entries per selection row (>= 0)
+ * kv_block_lens, causal, kv_splits and everything else apply as for BSR.
  */
 typedef struct {
   const int32_t* indptr;
@@ -114,6 +133,11 @@ typedef struct {
   float q_descale, k_descale, v_descale;
   int64_t q_token_stride, k_token_stride, v_token_stride, o_token_stride;
   int32_t num_cus;
+  int32_t struct_heads;
+  const uint8_t* block_mask;
+  const int32_t* q2k_indices;
+  const int32_t* q2k_num;
+  int32_t q2k_topk;
 } bsa_plan_desc_t;
 
 /* Defaults: fp16 everywhere, head_dim_vo = head_dim_qk, non-causal, default
@@ -236,7 +260,8 @@ bsa_status_t bsa_plan_info(bsa_plan_t plan, bsa_plan_info_t* info);
  *   merges  int32[num_merges][8] = {row_block, kv_head, row0, nrows,
  *                                   first_partial, num_splits, partial_stride, 0}
  *   cols    int32[num_cols]: per row block, its column blocks in ascending
- *           order, without blocks that the causal mask removes entirely.
+ *           order, without blocks that the causal mask removes entirely
+ *           (with a per-head structure: per kv head, then per row block).
  */
 bsa_status_t bsa_plan_export(bsa_plan_t plan, int32_t* tiles, int32_t* merges, int32_t* cols);
 

@@ -11,4 +11,7 @@ from .bsr_attention import (  # noqa: F401
     masked_attention,
     bsr_attention,
     merge_states,
+    q2k_block_mask,
+    head_block_masks,
+    block_mask_attention,
 )

@@ -23,13 +23,19 @@ the same boolean mask).  Every step is written out plainly in float64:
   O6  softmax over unmasked keys, o = P v / l, lse = m + ln l
                                           (run(): o and the log-sum-exp of the logits)
   O7  merge of (o, lse) attention states  (flashinfer.cascade merge_state(s))
+  O8  per-head structure                  (plan(): block_mask (heads, MB, NB) and
+                                           q2k_indices / q2k_num; VariableBlockSparse-
+                                           AttentionWrapper: each kv head its own pattern)
 
 Readings taken where the pages are silent:
   * lse is the natural log of sum(exp(sm_scale * q.k)) over unmasked keys;
   * a row with no unmasked key has o = 0 and lse = -inf;
   * causal masking keeps key j for query i iff j <= i + (N - M);
   * duplicate column indices within a row are rejected;
-  * rows i >= M of a partial last row block do not exist.
+  * rows i >= M of a partial last row block do not exist;
+  * a per-head structure given per qo head applies to that qo head (the
+    library requires the qo heads of one kv head to agree, which makes this
+    the same as using the first qo head of each group).
 """
 from __future__ import annotations
 
@@ -46,6 +52,9 @@ __all__ = [
     "masked_attention",
     "bsr_attention",
     "merge_states",
+    "q2k_block_mask",
+    "head_block_masks",
+    "block_mask_attention",
 ]
 
 
@@ -209,4 +218,90 @@ def merge_states(o_states, lse_states):
     o = contrib.sum(axis=0) / total_safe[..., None]
     o = np.where(any_keys[..., None], o, 0.0)
     lse = np.where(any_keys, top_safe + np.log(total_safe), -np.inf)
+    return o, lse
+
+
+def q2k_block_mask(q2k_indices, q2k_num, NB: int) -> np.ndarray:
+    """O8: direct selections -> block mask.
+
+    flashinfer.sparse plan(): q2k_indices (heads, MB, topk) lists the selected
+    KV blocks of each (head, query block); q2k_num (heads, MB) says how many
+    leading entries of each row are valid (all topk when absent).  Entry
+    (h, I, J) of the result is True iff J is among the first q2k_num[h, I]
+    entries of row (h, I).  Entries must lie in [0, NB) and not repeat.
+    """
+    sel = np.asarray(q2k_indices)
+    H, MB, topk = sel.shape
+    num = np.full((H, MB), topk) if q2k_num is None else np.asarray(q2k_num)
+    out = np.zeros((H, MB, NB), dtype=bool)
+    for h in range(H):
+        for I in range(MB):
+            n = int(num[h, I])
+            if not 0 <= n <= topk:
+                raise ValueError("q2k_num entries must lie in [0, topk]")
+            row = [int(x) for x in sel[h, I, :n]]
+            if any(not 0 <= J < NB for J in row) or len(set(row)) != len(row):
+                raise ValueError("selections must lie in [0, NB) without repeats")
+            out[h, I, row] = True
+    return out
+
+
+def head_block_masks(block_mask, M: int, N: int, R: int, C: int, kv_block_lens=None,
+                     causal: bool = False, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """O8 with O2 + O3: per-head block mask -> dense boolean masks (heads, rows, N).
+
+    Entry (h, i, j) is True iff block_mask[h, i // R, j // C] is set,
+    j % C < len_J for J = j // C (kv_block_lens, or C when absent), and, when
+    causal, j <= i + (N - M).
+    """
+    bm = np.asarray(block_mask).astype(bool)
+    if C < 1 or R < 1 or N % C != 0:
+        raise ValueError("R, C must be >= 1 and N divisible by C")
+    MB, NB = -(-M // R), N // C
+    if bm.ndim != 3 or bm.shape[1:] != (MB, NB):
+        raise ValueError(f"block_mask must have shape (heads, {MB}, {NB})")
+    row_list = list(range(M)) if rows is None else [int(r) for r in rows]
+    lens = np.full(NB, C) if kv_block_lens is None else np.asarray(kv_block_lens)
+    key_ok = (np.arange(N) % C) < lens[np.arange(N) // C]       # position inside its block's length
+    out = np.zeros((bm.shape[0], len(row_list), N), dtype=bool)
+    for h in range(bm.shape[0]):
+        for out_row, i in enumerate(row_list):
+            if not 0 <= i < M:
+                raise ValueError("row out of range")
+            blocks = bm[h, i // R]                               # (NB,) selected key blocks
+            out[h, out_row] = np.repeat(blocks, C) & key_ok
+            if causal:
+                out[h, out_row, max(0, i + (N - M) + 1):] = False
+    return out
+
+
+def block_mask_attention(block_mask, M: int, N: int, R: int, C: int, q, k, v,
+                         sm_scale: Optional[float] = None, causal: bool = False,
+                         kv_block_lens=None, rows: Optional[Iterable[int]] = None):
+    """Attention under a per-head block mask (O8, then O5 + O6 head by head).
+
+    block_mask has num_kv_heads or num_qo_heads heads; qo head h uses mask
+    h // (Hq / Hkv) in the first case (the heads of a kv group share its
+    pattern) and mask h in the second.  Returns o (rows, Hq, Dv), lse (rows, Hq).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    Hq, Hkv = q.shape[1], k.shape[1]
+    group = Hq // Hkv
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[-1])
+    row_list = None if rows is None else [int(r) for r in rows]
+    masks = head_block_masks(block_mask, M, N, R, C, kv_block_lens, causal, row_list)
+    if masks.shape[0] not in (Hkv, Hq):
+        raise ValueError("block_mask must have num_kv_heads or num_qo_heads heads")
+    if row_list is not None:
+        q = q[row_list]
+    o = np.zeros((q.shape[0], Hq, v.shape[2]))
+    lse = np.zeros((q.shape[0], Hq))
+    for h in range(Hq):
+        kvh = h // group
+        mh = masks[kvh] if masks.shape[0] == Hkv else masks[h]
+        oh, lh = masked_attention(q[:, h:h + 1], k[:, kvh:kvh + 1], v[:, kvh:kvh + 1], mh, sm_scale)
+        o[:, h], lse[:, h] = oh[:, 0], lh[:, 0]
     return o, lse

@@ -48,6 +48,11 @@ class PlanDesc(ctypes.Structure):
         ("v_token_stride", ctypes.c_int64),
         ("o_token_stride", ctypes.c_int64),
         ("num_cus", ctypes.c_int32),
+        ("struct_heads", ctypes.c_int32),
+        ("block_mask", ctypes.POINTER(ctypes.c_uint8)),
+        ("q2k_indices", _i32p),
+        ("q2k_num", _i32p),
+        ("q2k_topk", ctypes.c_int32),
     ]
 
 

@@ -24,6 +24,12 @@ def _i32(a) -> np.ndarray:
     return np.ascontiguousarray(np.asarray(a), dtype=np.int32)
 
 
+def _np(a) -> np.ndarray:
+    if isinstance(a, torch.Tensor):
+        a = a.detach().cpu().numpy()
+    return np.asarray(a)
+
+
 def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
@@ -34,6 +40,11 @@ class Plan:
     indptr / indices / kv_block_lens are host arrays (numpy or CPU tensors).
     ``kv_splits``: 1 = none, k = at most k partitions per row tile, 0 or
     "auto" = automatic.  ``num_cus`` = 0 asks the current device.
+
+    Per-head structure (plan(): block_mask, q2k_indices / q2k_num): pass
+    ``block_mask`` (heads, MB, NB) bool, or ``q2k_indices`` (heads, MB, topk)
+    int with optional ``q2k_num`` (heads, MB); heads = num_kv_heads or
+    num_qo_heads.  indptr / indices are then ignored (may be None).
     """
 
     def __init__(self, indptr, indices, M: int, N: int, R: int, C: int, num_qo_heads: int,
@@ -43,11 +54,15 @@ class Plan:
                  kv_dtype: Optional[torch.dtype] = None, o_dtype: Optional[torch.dtype] = None,
                  q_descale: float = 1.0, k_descale: float = 1.0, v_descale: float = 1.0,
                  q_token_stride: int = 0, k_token_stride: int = 0, v_token_stride: int = 0,
-                 o_token_stride: int = 0, num_cus: int = 0):
+                 o_token_stride: int = 0, num_cus: int = 0, block_mask=None, q2k_indices=None,
+                 q2k_num=None):
         lib = L.lib()
         self._handle = ctypes.c_void_p()
-        self._indptr = _i32(indptr)
-        self._indices = _i32(indices)
+        self._indptr = _i32(np.zeros(1) if indptr is None else indptr)
+        self._indices = _i32(np.zeros(0) if indices is None else indices)
+        self._mask = None if block_mask is None else np.ascontiguousarray(_np(block_mask), dtype=np.uint8)
+        self._q2k = None if q2k_indices is None else _i32(q2k_indices)
+        self._q2k_num = None if q2k_num is None else _i32(q2k_num)
         self._lens = None if kv_block_lens is None else _i32(kv_block_lens)
         kv_dtype = q_dtype if kv_dtype is None else kv_dtype
         o_dtype = q_dtype if o_dtype is None else o_dtype
@@ -71,6 +86,23 @@ class Plan:
         d.q_token_stride, d.k_token_stride = int(q_token_stride), int(k_token_stride)
         d.v_token_stride, d.o_token_stride = int(v_token_stride), int(o_token_stride)
         d.num_cus = int(num_cus)
+        if self._mask is not None:
+            if self._mask.ndim != 3:
+                raise ValueError("block_mask must have shape (heads, MB, NB)")
+            d.struct_heads = int(self._mask.shape[0])
+            d.block_mask = self._mask.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+        if self._q2k is not None:
+            if self._q2k.ndim != 3:
+                raise ValueError("q2k_indices must have shape (heads, MB, topk)")
+            d.struct_heads = int(self._q2k.shape[0])
+            d.q2k_topk = int(self._q2k.shape[2])
+            if self._q2k.size == 0:  # topk = 0: a valid pointer that is never read
+                self._q2k = np.zeros(1, np.int32)
+            d.q2k_indices = _ptr(self._q2k)
+            if self._q2k_num is not None:
+                if self._q2k_num.shape != self._q2k.shape[:2]:
+                    raise ValueError("q2k_num must have shape (heads, MB)")
+                d.q2k_num = _ptr(self._q2k_num)
         L.check(lib.bsa_plan_ex(ctypes.byref(d), ctypes.byref(self._handle)))
         self.M, self.N, self.R, self.C = int(M), int(N), int(R), int(C)
         self.num_qo_heads, self.num_kv_heads = int(num_qo_heads), int(num_kv_heads)

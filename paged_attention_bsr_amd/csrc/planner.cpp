@@ -26,6 +26,10 @@
 //  6. Tiles are emitted in (I, row tile, h, split) order, then stably sorted
 //     by descending work (longest processing time first); workgroup t runs
 //     tile t.
+//  Per-head structure (block_mask or q2k selections): every kv head has its
+//     own column lists (step 1 per kv head, then per row block), row tiles
+//     are made per (kv head, row block) in that order and each is emitted
+//     for its own head only (G = 1 below); the rest is unchanged.
 //  Decode kernel: a workgroup takes G = decode_heads_per_wg(Hkv) kv heads at
 //     once, so the unit of steps 4-6 is (I, head group gi) and every piece
 //     emits G tiles (heads gi*G .. gi*G+G-1, same blocks) as one group; head
@@ -93,22 +97,78 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
 
   const int64_t MB = ceil_div(d.M, d.R);
   const int64_t NB = d.N / d.C;
-  if (!d.indptr) return fail(err, BSA_ERR_INVALID_ARGUMENT, "indptr is NULL");
-  if (d.indptr[0] != 0) return fail(err, BSA_ERR_INVALID_ARGUMENT, "indptr[0] must be 0");
-  for (int64_t I = 0; I < MB; ++I)
-    if (d.indptr[I + 1] < d.indptr[I])
-      return fail(err, BSA_ERR_INVALID_ARGUMENT, "indptr must be non-decreasing");
-  const int64_t nnz = d.indptr[MB];
-  if (nnz > 0 && !d.indices) return fail(err, BSA_ERR_INVALID_ARGUMENT, "indices is NULL");
+  // The structure as one CSR per structure head: HS = 1 (the BSR indptr /
+  // indices, shared by every kv head) or HS = num_kv_heads (block_mask or
+  // q2k selections, one list per kv head).  List (hs, I) is
+  // sidx[sptr[hs * MB + I] .. sptr[hs * MB + I + 1]).
+  const bool per_head = d.block_mask || d.q2k_indices;
+  const int32_t g0 = d.num_qo_heads / d.num_kv_heads;
+  const int64_t HS = per_head ? d.num_kv_heads : 1;
+  std::vector<int64_t> sptr(static_cast<size_t>(HS * MB + 1), 0);
+  std::vector<int32_t> sidx;
+  if (!per_head) {
+    if (!d.indptr) return fail(err, BSA_ERR_INVALID_ARGUMENT, "indptr is NULL");
+    if (d.indptr[0] != 0) return fail(err, BSA_ERR_INVALID_ARGUMENT, "indptr[0] must be 0");
+    for (int64_t I = 0; I < MB; ++I)
+      if (d.indptr[I + 1] < d.indptr[I])
+        return fail(err, BSA_ERR_INVALID_ARGUMENT, "indptr must be non-decreasing");
+    const int64_t nnz0 = d.indptr[MB];
+    if (nnz0 > 0 && !d.indices) return fail(err, BSA_ERR_INVALID_ARGUMENT, "indices is NULL");
+    for (int64_t I = 0; I <= MB; ++I) sptr[I] = d.indptr[I];
+    sidx.assign(d.indices, d.indices + nnz0);
+  } else {
+    if (d.block_mask && d.q2k_indices)
+      return fail(err, BSA_ERR_INVALID_ARGUMENT, "block_mask and q2k_indices are mutually exclusive");
+    if (d.struct_heads != d.num_kv_heads && d.struct_heads != d.num_qo_heads)
+      return fail(err, BSA_ERR_INVALID_ARGUMENT, "struct_heads must be num_kv_heads or num_qo_heads");
+    if (d.q2k_indices && d.q2k_topk < 0) return fail(err, BSA_ERR_INVALID_ARGUMENT, "q2k_topk must be >= 0");
+    // the selected blocks of structure head sh, row block I, in given order
+    std::vector<int32_t> row, other;
+    auto get_row = [&](int64_t sh, int64_t I, std::vector<int32_t>& out) -> bool {
+      out.clear();
+      if (d.block_mask) {
+        const uint8_t* m = d.block_mask + (sh * MB + I) * NB;
+        for (int64_t J = 0; J < NB; ++J)
+          if (m[J]) out.push_back(static_cast<int32_t>(J));
+        return true;
+      }
+      const int64_t n = d.q2k_num ? d.q2k_num[sh * MB + I] : d.q2k_topk;
+      if (n < 0 || n > d.q2k_topk) return false;
+      const int32_t* q = d.q2k_indices + (sh * MB + I) * d.q2k_topk;
+      out.assign(q, q + n);
+      return true;
+    };
+    const int32_t per_kv = d.struct_heads == d.num_kv_heads ? 1 : g0;
+    for (int64_t h = 0; h < HS; ++h) {
+      for (int64_t I = 0; I < MB; ++I) {
+        if (!get_row(h * per_kv, I, row))
+          return fail(err, BSA_ERR_INVALID_ARGUMENT, "q2k_num entries must lie in [0, q2k_topk]");
+        // the qo heads of one kv head must select the same blocks
+        for (int32_t j = 1; j < per_kv; ++j) {
+          if (!get_row(h * per_kv + j, I, other))
+            return fail(err, BSA_ERR_INVALID_ARGUMENT, "q2k_num entries must lie in [0, q2k_topk]");
+          std::vector<int32_t> a = row, b = other;
+          std::sort(a.begin(), a.end());
+          std::sort(b.begin(), b.end());
+          if (a != b)
+            return fail(err, BSA_ERR_INVALID_ARGUMENT,
+                        "the qo heads of one kv head must select the same key blocks");
+        }
+        sidx.insert(sidx.end(), row.begin(), row.end());
+        sptr[h * MB + I + 1] = static_cast<int64_t>(sidx.size());
+      }
+    }
+  }
+  const int64_t nnz = static_cast<int64_t>(sidx.size());
   std::vector<uint8_t> seen(static_cast<size_t>(NB), 0);
-  for (int64_t I = 0; I < MB; ++I) {
-    for (int64_t p = d.indptr[I]; p < d.indptr[I + 1]; ++p) {
-      const int32_t J = d.indices[p];
+  for (int64_t u = 0; u < HS * MB; ++u) {
+    for (int64_t p = sptr[u]; p < sptr[u + 1]; ++p) {
+      const int32_t J = sidx[p];
       if (J < 0 || J >= NB) return fail(err, BSA_ERR_INVALID_ARGUMENT, "indices must lie in [0, NB)");
       if (seen[J]) return fail(err, BSA_ERR_INVALID_ARGUMENT, "duplicate column index within a row block");
       seen[J] = 1;
     }
-    for (int64_t p = d.indptr[I]; p < d.indptr[I + 1]; ++p) seen[d.indices[p]] = 0;
+    for (int64_t p = sptr[u]; p < sptr[u + 1]; ++p) seen[sidx[p]] = 0;
   }
   if (d.kv_block_lens) {
     for (int64_t J = 0; J < NB; ++J)
@@ -159,6 +219,9 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
   }
 
   P.d = d;
+  // the host arrays are read during planning only
+  P.d.indptr = P.d.indices = P.d.kv_block_lens = P.d.q2k_indices = P.d.q2k_num = nullptr;
+  P.d.block_mask = nullptr;
   P.MB = MB;
   P.NB = NB;
   P.group = g;
@@ -173,18 +236,20 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
   const int64_t off = d.N - d.M;  // causal offset: key j allowed for query i iff j <= i + off
 
   // ---- 1. sorted, causally trimmed column lists
-  std::vector<int64_t> bptr(MB + 1, 0);
+  // (per structure head, then per row block: list hs * MB + I)
+  std::vector<int64_t> bptr(static_cast<size_t>(HS * MB + 1), 0);
   P.cols.clear();
   P.cols.reserve(static_cast<size_t>(nnz));
-  for (int64_t I = 0; I < MB; ++I) {
-    std::vector<int32_t> row(d.indices + d.indptr[I], d.indices + d.indptr[I + 1]);
+  for (int64_t u = 0; u < HS * MB; ++u) {
+    const int64_t I = u % MB;
+    std::vector<int32_t> row(sidx.begin() + sptr[u], sidx.begin() + sptr[u + 1]);
     std::sort(row.begin(), row.end());
     const int64_t last_tok = std::min<int64_t>(d.M, (I + 1) * d.R) - 1;
     for (int32_t J : row) {
       if (d.causal && static_cast<int64_t>(J) * d.C > last_tok + off) break;
       P.cols.push_back(J);
     }
-    bptr[I + 1] = static_cast<int64_t>(P.cols.size());
+    bptr[u + 1] = static_cast<int64_t>(P.cols.size());
   }
   // valid length of each column-list entry (parallel to cols), so kernels
   // read a block's length with the same index as the block itself
@@ -195,34 +260,42 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
   }
 
   // ---- 2./3. row tiles with their (prefix) column ranges and work
+  // (hs = the structure head of the row tile's columns: 0 when shared)
   struct RowTile {
-    int64_t I, row0, nrows, cb, n, keys, work;
+    int64_t I, row0, nrows, cb, n, keys, work, hs;
   };
   std::vector<RowTile> rts;
   std::vector<int64_t> pref;  // prefix key counts, reused
-  for (int64_t I = 0; I < MB; ++I) {
+  for (int64_t u = 0; u < HS * MB; ++u) {
+    const int64_t I = u % MB;
     const int64_t rows_I = std::min<int64_t>(d.R, d.M - I * d.R);
     const int64_t U = rows_I * g;
     for (int64_t r0 = 0; r0 < U; r0 += tile_rows) {
       const int64_t nr = std::min<int64_t>(tile_rows, U - r0);
-      int64_t n = bptr[I + 1] - bptr[I];
+      int64_t n = bptr[u + 1] - bptr[u];
       if (d.causal) {
         const int64_t lim = I * d.R + (r0 + nr - 1) / g + off;
         int64_t k = 0;
-        while (k < n && static_cast<int64_t>(P.cols[bptr[I] + k]) * d.C <= lim) ++k;
+        while (k < n && static_cast<int64_t>(P.cols[bptr[u] + k]) * d.C <= lim) ++k;
         n = k;
       }
       int64_t keys = 0;
-      for (int64_t k = 0; k < n; ++k) keys += blen(P.cols[bptr[I] + k]);
-      rts.push_back({I, r0, nr, bptr[I], n, keys, keys * ceil_div(nr, 32)});
+      for (int64_t k = 0; k < n; ++k) keys += blen(P.cols[bptr[u] + k]);
+      rts.push_back({I, r0, nr, bptr[u], n, keys, keys * ceil_div(nr, 32), u / MB});
     }
   }
 
   // Tiles come in groups: one group per (row tile, head group, key range)
   // holds the tiles of G consecutive kv heads (G = 1 except for the decode
   // kernel, whose workgroup gives each of its waves one kv head of the group).
-  const int32_t G = kernel == BSA_KERNEL_DECODE ? decode_heads_per_wg(d.num_kv_heads) : 1;
+  // With a per-head structure every kv head has its own columns, so groups
+  // hold one head and a row tile serves only its own head.
+  const int32_t G = kernel == BSA_KERNEL_DECODE && !per_head ? decode_heads_per_wg(d.num_kv_heads) : 1;
   const int32_t NG = d.num_kv_heads / G;
+  const int32_t units_per_rt = per_head ? 1 : NG;  // head groups each row tile is emitted for
+  auto group_of = [&](const RowTile& rt, int32_t k) -> int32_t {
+    return per_head ? static_cast<int32_t>(rt.hs) : k;
+  };
   struct TileRec {
     int32_t f[kTileInts];
   };
@@ -283,7 +356,7 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
   if (kernel == BSA_KERNEL_DECODE && d.kv_splits == 0) {
     // ---- 4.-6. balanced partition over resident workgroups
     int64_t K = 0;
-    for (const auto& rt : rts) K += rt.keys * NG;
+    for (const auto& rt : rts) K += rt.keys * units_per_rt;
     W = std::max<int64_t>(1, std::min<int64_t>((int64_t)kDecodeWgPerCu * num_cus, K / kBalancedMinKeys));
     auto wg_of = [&](int64_t X) -> int64_t {
       if (K == 0) return 0;
@@ -293,7 +366,8 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
     int64_t X = 0;
     for (const auto& rt : rts) {
       row_prefix(rt);
-      for (int32_t gi = 0; gi < NG; ++gi) {
+      for (int32_t k = 0; k < units_per_rt; ++k) {
+        const int32_t gi = group_of(rt, k);
         // maximal runs of blocks with one workgroup
         cut.assign(1, 0);
         cut_wg.assign(1, wg_of(X));
@@ -313,7 +387,7 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
   } else {
     // ---- 4. split counts
     int64_t total_work = 0;
-    for (const auto& rt : rts) total_work += rt.work * d.num_kv_heads;
+    for (const auto& rt : rts) total_work += rt.work * (per_head ? 1 : d.num_kv_heads);
     const int64_t chunk = std::max<int64_t>(1, ceil_div(total_work, (int64_t)kAutoTilesPerCu * num_cus));
     for (const auto& rt : rts) {
       int64_t s = 1;
@@ -336,8 +410,8 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
         p = std::min<int64_t>(p, rt.n - (s - j));
         cut[j] = p;
       }
-      for (int32_t gi = 0; gi < NG; ++gi)
-        if (!emit_unit(rt, gi, cut.data(), nullptr, s))
+      for (int32_t k = 0; k < units_per_rt; ++k)
+        if (!emit_unit(rt, group_of(rt, k), cut.data(), nullptr, s))
           return fail(err, BSA_ERR_UNSUPPORTED, "split partials exceed 2^31 floats");
     }
     // ---- 6. longest first, one group per workgroup

@@ -42,6 +42,7 @@ __all__ = [
     "bsr_prefill",
     "window_prefill",
     "sparse_mla",
+    "head_sparse_prefill",
     "random_bsr",
     "by_name",
     "WORKLOAD_NAMES",
@@ -179,6 +180,35 @@ def bsr_prefill(seed: int = 3, M: int = 8192, block: int = 64, density: float = 
     return w
 
 
+def head_sparse_prefill(seed: int = 6, M: int = 8192, block: int = 64, density: float = 0.10,
+                        num_qo_heads: int = 32, num_kv_heads: int = 8, head_dim: int = 128,
+                        dtype: torch.dtype = torch.float16, values: bool = True) -> Workload:
+    """bsr_prefill with a pattern of its own for every kv head: all diagonal blocks plus
+    i.i.d. Bernoulli(density) strictly-lower blocks drawn per (kv head, block); causal.
+
+    The per-head block mask (num_kv_heads, MB, MB) is in ``meta["block_mask"]``; the
+    workload's indptr / indices hold the union over heads (a BSR view for sizing only).
+    """
+    rng = np.random.default_rng(seed)
+    MB = M // block
+    bm = np.zeros((num_kv_heads, MB, MB), dtype=bool)
+    for h in range(num_kv_heads):
+        for i in range(MB):
+            bm[h, i, np.nonzero(rng.random(i) < density)[0]] = True
+            bm[h, i, i] = True
+    union = bm.any(axis=0)
+    indptr, indices = _csr_from_rows([np.nonzero(union[i])[0] for i in range(MB)])
+    w = Workload("head_sparse_prefill", indptr, indices, M, M, block, block, num_qo_heads,
+                 num_kv_heads, head_dim, head_dim, True, 1.0 / np.sqrt(head_dim),
+                 q_dtype=dtype, kv_dtype=dtype, o_dtype=dtype, meta={"block_mask": bm})
+    if values:
+        g = torch.Generator().manual_seed(seed)
+        w.q = _randn(g, (M, num_qo_heads, head_dim), dtype)
+        w.k = _randn(g, (M, num_kv_heads, head_dim), dtype)
+        w.v = _randn(g, (M, num_kv_heads, head_dim), dtype)
+    return w
+
+
 def window_prefill(seed: int = 4, M: int = 32768, block: int = 128, window: int = 8,
                    stride: int = 16, num_qo_heads: int = 64, num_kv_heads: int = 8,
                    head_dim: int = 128, dtype: torch.dtype = torch.float16,
@@ -281,12 +311,13 @@ def random_bsr(seed: int, M: int, N: int, R: int, C: int, num_qo_heads: int,
 # Split-KV setting each workload is timed (and parity-checked at full size) with:
 # 0 = automatic, 1 = no split.
 BENCH_KV_SPLITS = {"worked_example": 1, "paged_decode": 0, "bsr_prefill": 1, "window_prefill": 1,
-                   "sparse_mla": 1}
+                   "sparse_mla": 1, "head_sparse_prefill": 1}
 
-WORKLOAD_NAMES = ["worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla"]
+WORKLOAD_NAMES = ["worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla",
+                  "head_sparse_prefill"]
 
 
 def by_name(name: str, **kw) -> Workload:
     return {"worked_example": worked_example, "paged_decode": paged_decode,
             "bsr_prefill": bsr_prefill, "window_prefill": window_prefill,
-            "sparse_mla": sparse_mla}[name](**kw)
+            "sparse_mla": sparse_mla, "head_sparse_prefill": head_sparse_prefill}[name](**kw)

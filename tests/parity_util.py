@@ -29,12 +29,19 @@ def say(msg: str) -> None:
 
 
 def plan_for(w, kv_splits=1, num_cus=0) -> Plan:
+    """The library plan of a workload; a per-head structure (w.meta["block_mask"], or
+    w.meta["q2k"] = (q2k_indices, q2k_num)) replaces the shared BSR rows."""
+    extra = {}
+    if "block_mask" in w.meta:
+        extra["block_mask"] = w.meta["block_mask"]
+    if "q2k" in w.meta:
+        extra["q2k_indices"], extra["q2k_num"] = w.meta["q2k"]
     return Plan(w.indptr, w.indices, w.M, w.N, w.R, w.C, w.num_qo_heads, w.num_kv_heads, w.head_dim,
                 head_dim_vo=w.head_dim_vo, causal=w.causal, sm_scale=w.sm_scale,
                 kv_splits=kv_splits, kv_block_lens=w.kv_block_lens, q_dtype=w.q_dtype,
                 kv_dtype=w.kv_dtype, o_dtype=w.o_dtype, k_descale=w.k_descale,
                 v_descale=w.v_descale, k_token_stride=w.k_token_stride,
-                v_token_stride=w.v_token_stride, num_cus=num_cus)
+                v_token_stride=w.v_token_stride, num_cus=num_cus, **extra)
 
 
 def to_device(w, device="cuda"):
@@ -68,6 +75,11 @@ def oracle_inputs(w):
 
 def oracle_result(w, rows=None, inputs=None):
     q, k, v = oracle_inputs(w) if inputs is None else inputs
+    if "block_mask" in w.meta or "q2k" in w.meta:
+        bm = (w.meta["block_mask"] if "block_mask" in w.meta
+              else oracle.q2k_block_mask(w.meta["q2k"][0], w.meta["q2k"][1], w.NB))
+        return oracle.block_mask_attention(bm, w.M, w.N, w.R, w.C, q, k, v, sm_scale=w.sm_scale,
+                                           causal=w.causal, kv_block_lens=w.kv_block_lens, rows=rows)
     return oracle.bsr_attention(w.indptr, w.indices, w.M, w.N, w.R, w.C, q, k, v, sm_scale=w.sm_scale,
                                 causal=w.causal, kv_block_lens=w.kv_block_lens, rows=rows)
 

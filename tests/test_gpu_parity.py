@@ -168,6 +168,7 @@ FULL_ROWS = {
     "bsr_prefill": [0, 1, 63, 64, 127, 4095, 4096, 6000, 8190, 8191],
     "window_prefill": [0, 1, 127, 128, 1100, 1151, 2048, 16383, 30000, 32767],
     "sparse_mla": [0, 1, 17, 64, 100, 127],
+    "head_sparse_prefill": [0, 1, 63, 64, 127, 4095, 4096, 6000, 8190, 8191],
 }
 
 
@@ -276,3 +277,71 @@ def test_mla_kernel_multi_row_blocks(causal, lens):
         w.kv_block_lens = rng.integers(1, C + 1, nb).astype(np.int32)
     _check(w, 1, what=f"mla C=4 causal={causal} lens={lens}")
     _check(w, 2, what=f"mla C=4 causal={causal} lens={lens} splits=2")
+
+
+
+# ---------------------------------------------------------------- per-head structure
+# Each kv head attends by its own block pattern (block_mask per kv or qo head, or
+# q2k_indices / q2k_num selections); tile kernel and decode kernel shapes.
+PER_HEAD = [
+    # (seed, M, NB, R, C, Hq, Hkv, causal, lens, density, form)
+    (41, 130, 6, 64, 64, 16, 4, True, False, 0.5, "kv"),     # M % R != 0, whole 64-key block tiles
+    (42, 256, 4, 128, 128, 16, 2, True, False, 0.7, "qo"),   # 128-key tiles; mask given per qo head
+    (43, 37, 9, 5, 7, 8, 2, False, True, 0.5, "q2k"),        # generic key lookup, garbage past lengths
+    (44, 20, 40, 1, 16, 32, 8, False, True, 0.3, "kv"),      # decode kernel, one kv head per workgroup
+    (45, 12, 30, 1, 32, 16, 4, True, True, 0.5, "q2k"),      # decode kernel, causal, lengths
+    (46, 96, 12, 32, 32, 8, 8, True, False, 0.4, "qo"),      # g = 1: qo and kv heads coincide
+]
+
+
+def _per_head_workload(case):
+    seed, M, NB, R, C, Hq, Hkv, causal, lens, dens, form = case
+    w = W.random_bsr(seed, M, NB * C, R, C, Hq, Hkv, causal=causal, partial_lens=lens, density=dens,
+                     garbage=6e4 if lens else 0.0)
+    rng = np.random.default_rng(seed)
+    bm = rng.random((Hkv, w.MB, NB)) < dens
+    bm[:, -1, :] = False                      # an empty row block for every head
+    if Hkv > 1:
+        bm[1] = rng.random((w.MB, NB)) < 0.9  # a head far denser than the others
+    g = Hq // Hkv
+    if form == "kv":
+        w.meta["block_mask"] = bm
+    elif form == "qo":
+        w.meta["block_mask"] = np.repeat(bm, g, axis=0)
+    else:
+        topk = int(bm.sum(axis=2).max()) + 1
+        sel = np.full((Hkv, w.MB, topk), NB + 7, np.int32)   # entries past q2k_num are never read
+        num = bm.sum(axis=2).astype(np.int32)
+        for h in range(Hkv):
+            for I in range(w.MB):
+                js = rng.permutation(np.nonzero(bm[h, I])[0])
+                sel[h, I, :js.size] = js
+        w.meta["q2k"] = (np.repeat(sel, g, axis=0), np.repeat(num, g, axis=0))
+    return w
+
+
+@pytest.mark.parametrize("case", PER_HEAD, ids=[f"h{c[0]}" for c in PER_HEAD])
+@pytest.mark.parametrize("kv_splits", [1, 3, 0])
+def test_per_head_structure(case, kv_splits):
+    w = _per_head_workload(case)
+    kern = plan_for(w, kv_splits).info()["kernel"]
+    _check(w, kv_splits, what=f"per-head {case[-1]} s{case[0]} kernel={kern} splits={kv_splits}")
+
+
+def test_per_head_identical_heads_match_shared_plan_bitwise():
+    """A per-head mask that repeats the shared rows for every head runs the same tiles through the
+    tile kernel as the shared plan: the outputs agree bit for bit."""
+    w = W.random_bsr(47, 200, 10 * 64, 64, 64, 32, 4, causal=True, density=0.6)
+    bm = np.zeros((w.num_kv_heads, w.MB, w.NB), bool)
+    for I in range(w.MB):
+        bm[:, I, w.indices[w.indptr[I]:w.indptr[I + 1]]] = True
+    o1, l1 = run_gpu(w, 1)
+    w.meta["block_mask"] = bm
+    o2, l2 = run_gpu(w, 1)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_reduced_head_sparse_prefill():
+    w = W.head_sparse_prefill(seed=48, M=1024)
+    _check(w, 1)
+    _check(w, 0)

@@ -18,7 +18,8 @@ from tests.test_oracle import _brute_force
 SRC = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle", "bsr_attention.py")
 
 MUTATIONS = {
-    "gqa_modulo": ("kvh = h // group", "kvh = h % Hkv"),
+    "gqa_modulo": ("kvh = h // group\n        s = sm_scale", "kvh = h % Hkv\n        s = sm_scale"),
+    "per_head_gqa_modulo": ("kvh = h // group\n        mh = ", "kvh = h % Hkv\n        mh = "),
     "ignore_block_lens": ("mask[out_row, J * C:J * C + length] = True",
                           "mask[out_row, J * C:J * C + C] = True"),
     "causal_top_left": ("mask[out_row, max(0, i + (N - M) + 1):] = False",
@@ -36,6 +37,15 @@ MUTATIONS = {
                            "p = np.where(mask, np.exp(s), 0.0)"),
     "off_by_one_block_end": ("mask[out_row, J * C:J * C + length] = True",
                              "mask[out_row, J * C:J * C + length - 1] = True"),
+    # per-head structure (block_mask / q2k selections)
+    "per_head_modulo": ("mh = masks[kvh] if masks.shape[0] == Hkv else masks[h]",
+                        "mh = masks[h % masks.shape[0]]"),
+    "q2k_ignore_num": ("row = [int(x) for x in sel[h, I, :n]]", "row = [int(x) for x in sel[h, I, :topk]]"),
+    "per_head_ignore_lens": ("key_ok = (np.arange(N) % C) < lens[np.arange(N) // C]",
+                             "key_ok = np.ones(N, dtype=bool)"),
+    "per_head_causal_top_left": ("out[h, out_row, max(0, i + (N - M) + 1):] = False",
+                                 "out[h, out_row, max(0, i + 1):] = False"),
+    "per_head_rows_by_C": ("blocks = bm[h, i // R]", "blocks = bm[h, min(i // C, bm.shape[1] - 1)]"),
 }
 
 
@@ -120,7 +130,42 @@ def _pin_merge(mod):
     return np.allclose(om, o_full, rtol=1e-12) and np.allclose(lm, l_full, rtol=1e-12)
 
 
-PINS = [_pin_brute_force, _pin_equal_scores, _pin_sdpa, _pin_fp8, _pin_merge]
+def _pin_per_head_sdpa(mod):
+    """Per-kv-head block masks (R != C, M < N, lengths, causal) against torch SDPA on a dense
+    per-head mask built with torch ops."""
+    from tests.test_oracle_per_head import _dense_masks_torch
+    rng = np.random.default_rng(4)
+    Hkv, g, R, C, M, NB = 3, 2, 3, 2, 8, 6
+    N, MB = NB * C, -(-M // R)
+    bm = rng.random((Hkv, MB, NB)) < 0.5
+    bm[:, :, 0] = True
+    ln = rng.integers(1, C + 1, NB).astype(np.int32)
+    q, k, v = rng.standard_normal((M, Hkv * g, 4)), rng.standard_normal((N, Hkv, 4)), rng.standard_normal((N, Hkv, 3))
+    try:
+        o, _ = mod.block_mask_attention(bm, M, N, R, C, q, k, v, sm_scale=0.5, causal=True, kv_block_lens=ln)
+    except (ValueError, IndexError):
+        return False
+    dense = _dense_masks_torch(bm, M, N, R, C, ln, True).repeat_interleave(g, dim=0)
+    tq = torch.from_numpy(q).permute(1, 0, 2)
+    tk = torch.from_numpy(k).repeat_interleave(g, 1).permute(1, 0, 2)
+    tv = torch.from_numpy(v).repeat_interleave(g, 1).permute(1, 0, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=dense, scale=0.5)
+    return np.allclose(o, ref.permute(1, 0, 2).numpy(), rtol=1e-11, atol=1e-12)
+
+
+def _pin_q2k(mod):
+    sel = np.array([[[2, 0, 0], [1, 3, 3]]], np.int32)
+    try:
+        bm = mod.q2k_block_mask(sel, np.array([[2, 1]], np.int32), 4)
+    except ValueError:
+        return False
+    want = np.zeros((1, 2, 4), bool)
+    want[0, 0, [0, 2]] = True
+    want[0, 1, 1] = True
+    return np.array_equal(bm, want)
+
+
+PINS = [_pin_brute_force, _pin_equal_scores, _pin_sdpa, _pin_fp8, _pin_merge, _pin_per_head_sdpa, _pin_q2k]
 
 
 def test_unmutated_copy_passes_every_pin():

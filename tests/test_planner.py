@@ -22,46 +22,55 @@ def _cdiv(a, b):
     return -(-a // b)
 
 
-def model_plan(w, kv_splits, num_cus, tile_rows):
+def model_plan(w, kv_splits, num_cus, tile_rows, head_lists=None):
     """Python model of the planner's partition rule (steps 1-6 of planner.cpp,
     and the balanced partition of the decode kernel with kv_splits = 0).
+    ``head_lists``: None (the BSR rows of ``w``, shared by every kv head) or,
+    for a per-head structure, head_lists[h][I] = the blocks of kv head h.
     Returns (tiles, merges, cols, wg_ptr)."""
     M, N, R, C = w.M, w.N, w.R, w.C
     g = w.num_qo_heads // w.num_kv_heads
     MB = _cdiv(M, R)
     off = N - M
     blen = (lambda J: int(w.kv_block_lens[J])) if w.kv_block_lens is not None else (lambda J: C)
+    per_head = head_lists is not None
+    if not per_head:
+        head_lists = [[w.indices[w.indptr[I]:w.indptr[I + 1]] for I in range(MB)]]
+    HS = len(head_lists)
     cols, bptr = [], [0]
-    for I in range(MB):
-        row = sorted(int(x) for x in w.indices[w.indptr[I]:w.indptr[I + 1]])
-        last = min(M, (I + 1) * R) - 1
-        for J in row:
-            if w.causal and J * C > last + off:
-                break
-            cols.append(J)
-        bptr.append(len(cols))
+    for hs in range(HS):
+        for I in range(MB):
+            row = sorted(int(x) for x in head_lists[hs][I])
+            last = min(M, (I + 1) * R) - 1
+            for J in row:
+                if w.causal and J * C > last + off:
+                    break
+                cols.append(J)
+            bptr.append(len(cols))
     rts = []
-    for I in range(MB):
+    for u in range(HS * MB):
+        I, hs = u % MB, u // MB
         U = min(R, M - I * R) * g
         for r0 in range(0, U, tile_rows):
             nr = min(tile_rows, U - r0)
-            n = bptr[I + 1] - bptr[I]
+            n = bptr[u + 1] - bptr[u]
             if w.causal:
                 lim = I * R + (r0 + nr - 1) // g + off
                 k = 0
-                while k < n and cols[bptr[I] + k] * C <= lim:
+                while k < n and cols[bptr[u] + k] * C <= lim:
                     k += 1
                 n = k
-            keys = sum(blen(cols[bptr[I] + k]) for k in range(n))
-            rts.append((I, r0, nr, bptr[I], n, keys, keys * _cdiv(nr, 32)))
+            keys = sum(blen(cols[bptr[u] + k]) for k in range(n))
+            rts.append((I, r0, nr, bptr[u], n, keys, keys * _cdiv(nr, 32), hs))
     decode = model_kernel(w, num_cus)[0] == 2
-    G = min(8, w.num_kv_heads & -w.num_kv_heads) if decode else 1
+    G = min(8, w.num_kv_heads & -w.num_kv_heads) if decode and not per_head else 1
     NG = w.num_kv_heads // G
+    heads_of = (lambda rt: [rt[7]]) if per_head else (lambda rt: range(NG))
     st = {"part": 0, "tiles": [], "merges": [], "groups": []}
 
     def emit_unit(rt, gi, pref, b, wgs):
         """Pieces b[j]..b[j+1] of head group gi; head i's partial of piece j at base + (i*s + j)*psize."""
-        (I, r0, nr, cb, n, keys, work) = rt
+        (I, r0, nr, cb, n, keys, work, _) = rt
         s = len(b) - 1
         psize = _cdiv(nr * (w.head_dim_vo + 1), 64) * 64
         base = st["part"]
@@ -82,14 +91,14 @@ def model_plan(w, kv_splits, num_cus, tile_rows):
         return pref
 
     if kv_splits == 0 and decode:
-        K = sum(rt[5] for rt in rts) * NG
+        K = sum(rt[5] * len(heads_of(rt)) for rt in rts)
         Wn = max(1, min(DECODE_WG_PER_CU * num_cus, K // BALANCED_MIN_KEYS))
         wg_of = (lambda X: min(Wn - 1, X * Wn // K)) if K > 0 else (lambda X: 0)
         X = 0
         for rt in rts:
             pref = prefix(rt)
             n = rt[4]
-            for gi in range(NG):
+            for gi in heads_of(rt):
                 b, wgs = [0], [wg_of(X)]
                 for k in range(1, n):
                     if wg_of(X + pref[k]) != wgs[-1]:
@@ -104,10 +113,10 @@ def model_plan(w, kv_splits, num_cus, tile_rows):
             count[wg] += G
         wg_ptr = np.concatenate([[0], np.cumsum(count)]).astype(np.int32)
     else:
-        total = sum(rt[6] for rt in rts) * w.num_kv_heads
+        total = sum(rt[6] for rt in rts) * (1 if per_head else w.num_kv_heads)
         chunk = max(1, _cdiv(total, AUTO_TILES_PER_CU * num_cus))
         for rt in rts:
-            (I, r0, nr, cb, n, keys, work) = rt
+            (I, r0, nr, cb, n, keys, work, _) = rt
             if kv_splits == 1:
                 s = 1
             elif kv_splits > 1:
@@ -126,7 +135,7 @@ def model_plan(w, kv_splits, num_cus, tile_rows):
                 p = max(p, b[j - 1] + 1)
                 p = min(p, n - (s - j))
                 b[j] = p
-            for gi in range(NG):
+            for gi in heads_of(rt):
                 emit_unit(rt, gi, pref, b, None)
         order = sorted(st["groups"], key=lambda gr: -gr[1])  # stable
         wg_ptr = (np.arange(len(order) + 1) * G).astype(np.int32)
@@ -355,3 +364,113 @@ def test_small_grids_use_128_row_tiles():
     assert _plan(w, 1, num_cus=64).info()["tile_rows"] == 256
     w = W.by_name("window_prefill", values=False)  # 8192 tiles of 256 rows
     assert _plan(w, 1, num_cus=256).info()["tile_rows"] == 256
+
+
+# ---------------------------------------------------------------- per-head structure
+def _per_head_case(seed, decode):
+    """A random problem with one block mask per kv head (tile or decode kernel shapes)."""
+    rng = np.random.default_rng(900 + seed)
+    if decode:
+        R, C = 1, int(rng.choice([16, 32]))
+        g = int(rng.choice([1, 4, 8]))
+    else:
+        R, C = int(rng.choice([2, 16, 64])), int(rng.choice([1, 16, 64]))
+        g = int(rng.choice([1, 4]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    M = int(rng.integers(1, 200 if not decode else 30))
+    NB = int(rng.integers(1, 30))
+    w = W.random_bsr(seed, M, NB * C, R, C, Hkv * g, Hkv, causal=bool(seed % 2), partial_lens=seed % 3 == 0,
+                     density=0.3, values=False)
+    bm = rng.random((Hkv, w.MB, w.NB)) < float(rng.choice([0.1, 0.4, 0.8]))
+    return w, bm
+
+
+def _plan_heads(w, kv_splits, num_cus, **kw):
+    return Plan(None, None, w.M, w.N, w.R, w.C, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                head_dim_vo=w.head_dim_vo, causal=w.causal, kv_block_lens=w.kv_block_lens,
+                q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, o_dtype=w.o_dtype, kv_splits=kv_splits,
+                num_cus=num_cus, **kw)
+
+
+def _lists(bm):
+    return [[np.nonzero(bm[h, I])[0] for I in range(bm.shape[1])] for h in range(bm.shape[0])]
+
+
+@pytest.mark.parametrize("kv_splits", [1, 2, 0])
+@pytest.mark.parametrize("case", range(8))
+def test_per_head_planner_matches_model(case, kv_splits):
+    w, bm = _per_head_case(case, decode=case % 2 == 1)
+    p = _plan_heads(w, kv_splits, 8, block_mask=bm)
+    t = p.tables()
+    tiles, merges, cols, wg_ptr = model_plan(w, kv_splits, 8, p.info()["tile_rows"], _lists(bm))
+    np.testing.assert_array_equal(t["cols"], cols)
+    np.testing.assert_array_equal(t["tiles"], tiles)
+    np.testing.assert_array_equal(t["merges"], merges)
+    np.testing.assert_array_equal(t["wg_ptr"], wg_ptr)
+    assert p.info()["heads_per_wg"] == 1
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_per_head_forms_agree(case):
+    """block_mask per kv head, the same mask per qo head, and q2k selections of the same
+    blocks (shuffled, padded past q2k_num) give identical tables."""
+    w, bm = _per_head_case(case, decode=case % 2 == 1)
+    g = w.num_qo_heads // w.num_kv_heads
+    ref = _plan_heads(w, 0, 16, block_mask=bm).tables()
+    by_qo = _plan_heads(w, 0, 16, block_mask=np.repeat(bm, g, axis=0)).tables()
+    rng = np.random.default_rng(case)
+    topk = max(1, int(bm.sum(axis=2).max()) + 2)
+    sel = np.full(bm.shape[:2] + (topk,), -5, np.int32)      # padding past q2k_num is never read
+    num = bm.sum(axis=2).astype(np.int32)
+    for h in range(bm.shape[0]):
+        for I in range(bm.shape[1]):
+            js = rng.permutation(np.nonzero(bm[h, I])[0])
+            sel[h, I, :js.size] = js
+    by_q2k = _plan_heads(w, 0, 16, q2k_indices=np.repeat(sel, g, axis=0), q2k_num=np.repeat(num, g, axis=0)).tables()
+    for k in ref:
+        np.testing.assert_array_equal(ref[k], by_qo[k])
+        np.testing.assert_array_equal(ref[k], by_q2k[k])
+
+
+@pytest.mark.parametrize("case", range(6))
+@pytest.mark.parametrize("kv_splits", [1, 3, 0])
+def test_per_head_coverage_exactly_once(case, kv_splits):
+    w, bm = _per_head_case(case, decode=case % 3 == 0)
+    p = _plan_heads(w, kv_splits, 4, block_mask=bm)
+    t = p.tables()
+    g = w.num_qo_heads // w.num_kv_heads
+    seen = _coverage(w, t, g)
+    assert all(v == 1 for v in seen.values())
+    want = set()
+    for i in range(w.M):
+        for h in range(w.num_kv_heads):
+            for J in np.nonzero(bm[h, i // w.R])[0]:
+                if w.causal and J * w.C > i + (w.N - w.M):
+                    continue
+                want.update((i, h * g + j, int(J)) for j in range(g))
+    assert want <= set(seen)
+    # a tile visits only blocks of its own head's structure (rows past their causal limit are masked
+    # inside the kernel)
+    assert all(bm[hq // g, int(i) // w.R, J] for (i, hq, J) in seen)
+
+
+def test_per_head_structure_errors():
+    w, bm = _per_head_case(0, decode=False)
+    g = w.num_qo_heads // w.num_kv_heads
+    with pytest.raises(RuntimeError, match="mutually exclusive"):
+        _plan_heads(w, 1, 8, block_mask=bm, q2k_indices=np.zeros((w.num_kv_heads, w.MB, 1), np.int32))
+    with pytest.raises(RuntimeError, match="struct_heads"):
+        _plan_heads(w, 1, 8, block_mask=np.concatenate([bm, bm[:1]]))
+    sel = np.zeros((w.num_kv_heads, w.MB, 2), np.int32)
+    with pytest.raises(RuntimeError, match="duplicate"):
+        _plan_heads(w, 1, 8, q2k_indices=sel)
+    with pytest.raises(RuntimeError, match="q2k_num"):
+        _plan_heads(w, 1, 8, q2k_indices=sel, q2k_num=np.full((w.num_kv_heads, w.MB), 3, np.int32))
+    sel[..., 1] = w.NB
+    with pytest.raises(RuntimeError, match=r"\[0, NB\)"):
+        _plan_heads(w, 1, 8, q2k_indices=sel)
+    if g > 1:
+        bq = np.repeat(bm, g, axis=0)
+        bq[1, 0] = ~bq[1, 0]
+        with pytest.raises(RuntimeError, match="same key blocks"):
+            _plan_heads(w, 1, 8, block_mask=bq)
