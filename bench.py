@@ -29,7 +29,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 METRIC = "KV GB/s (decode) & TFLOP/s (sparse prefill), % of MI355X HBM/MFMA peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6}
-DECODE = {"paged_decode", "sparse_mla", "worked_example"}
+DECODE = {"paged_decode", "sparse_mla", "worked_example", "paged_decode_fp8"}
 # sources of each attention kernel (the traffic counters are valid while these are unchanged)
 KERNEL_SOURCES = {
     "attn_tile_kernel": ["attn_tile.hip", "device_common.h", "kernels.h"],
@@ -122,7 +122,8 @@ def algorithmic_work(w, rows=None):
         if w.kv_block_lens is not None:
             idx += 4 * nnz_rows
     flops = 2 * kv_pairs * g * (w.head_dim + w.head_dim_vo)
-    return kv_bytes + qo + idx, flops
+    scale_bytes = sum(4 * len(w.meta[f"scale_{n}"]) for n in ("q", "k", "v") if f"scale_{n}" in w.meta)
+    return kv_bytes + qo + idx + scale_bytes, flops
 
 
 def cpu_baseline(w, budget_s: float):
@@ -135,13 +136,18 @@ def cpu_baseline(w, budget_s: float):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    if w.kv_dtype == torch.float8_e4m3fn:
+    if w.kv_dtype == torch.float8_e4m3fn and not w.v_aliases_k:
+        k = oracle.fp8_dequant(w.k.view(torch.uint8).numpy(), w.meta.get("scale_k"), w.k_descale)
+        v = oracle.fp8_dequant(w.v.view(torch.uint8).numpy(), w.meta.get("scale_v"), w.v_descale)
+    elif w.kv_dtype == torch.float8_e4m3fn:
         kf = oracle.e4m3fn_decode(w.k.view(torch.uint8).numpy())
         k = (kf * w.k_descale)[:, None, :]
         v = (kf[:, :w.head_dim_vo] * w.v_descale)[:, None, :]
     else:
         k, v = w.k.double().numpy(), w.v.double().numpy()
     q = w.q.double().numpy()
+    if "scale_q" in w.meta:
+        q = q * w.meta["scale_q"].astype(np.float64)[None, :, None]
     order = np.random.default_rng(0).permutation(w.M)
     done, t_used, batch = 0, 0.0, 1
     while done < w.M and t_used < budget_s:
@@ -168,7 +174,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="paged_decode",
                     choices=["worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla",
-                             "head_sparse_prefill"])
+                             "head_sparse_prefill", "paged_decode_fp8"])
     ap.add_argument("--kv-splits", type=int, default=None, help="override the workload's split-KV setting")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
@@ -216,14 +222,18 @@ def main() -> int:
     torch.cuda.synchronize()
     log(f"[bench] plan {plan_ms:.1f} ms: {info}")
 
+    # per-head run() scales (fp8 KV workloads), device float32
+    scales = {f"scale_{n}": torch.from_numpy(w.meta[f"scale_{n}"]).to(dev)
+              for n in ("q", "k", "v") if f"scale_{n}" in w.meta}
+
     def step(evs=None):
         if evs is None:
-            plan.run(q, k, v, out=out, lse=lse, workspace=ws)
+            plan.run(q, k, v, out=out, lse=lse, workspace=ws, **scales)
             return
         evs[0].record()
-        plan.run(q, k, v, out=out, lse=lse, workspace=ws, phase=L.BSA_PHASE_ATTENTION)
+        plan.run(q, k, v, out=out, lse=lse, workspace=ws, phase=L.BSA_PHASE_ATTENTION, **scales)
         evs[1].record()
-        plan.run(q, k, v, out=out, lse=lse, workspace=ws, phase=L.BSA_PHASE_MERGE)
+        plan.run(q, k, v, out=out, lse=lse, workspace=ws, phase=L.BSA_PHASE_MERGE, **scales)
 
     for _ in range(args.warmup):
         step()
@@ -254,7 +264,7 @@ def main() -> int:
     alg_bytes, alg_flops = algorithmic_work(w)
     dtype = {torch.float16: "f16", torch.bfloat16: "bf16"}[w.q_dtype]
     if w.kv_dtype == torch.float8_e4m3fn:
-        dtype = "bf16 (fp8 e4m3 KV storage)"
+        dtype = f"{dtype} (fp8 e4m3 KV storage)"
     decode = args.workload in DECODE
     if decode:
         value = alg_bytes / (ms_per_step * 1e-3) / 1e9

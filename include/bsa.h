@@ -62,7 +62,7 @@ typedef enum { BSA_F16 = 0, BSA_BF16 = 1, BSA_FP8_E4M3 = 2 } bsa_dtype_t;
 typedef enum {
   BSA_KERNEL_TILE = 0,    /* MFMA tile kernel: head_dim 128, fp16/bf16, any R, C */
   BSA_KERNEL_MLA = 1,     /* MFMA sparse-MLA kernel: Dqk 576 / Dv 512, bf16 q/o, fp8 e4m3 kv, R = 1 */
-  BSA_KERNEL_DECODE = 2   /* paged-decode kernel: R = 1, C >= 16, head_dim 128, fp16/bf16, <= 16 qo heads per kv head */
+  BSA_KERNEL_DECODE = 2   /* paged-decode kernel: R = 1, C >= 16, head_dim 128, fp16/bf16 (kv also fp8 e4m3), <= 16 qo heads per kv head */
 } bsa_kernel_t;
 
 /*
@@ -86,7 +86,9 @@ typedef enum {
  *                  a second kernel.
  *   kv_block_lens  NULL, or int32[NB] valid tokens per key block, each in [1, C]
  *   q/kv/o_dtype   storage types.  Supported: all BSA_F16, or all BSA_BF16
- *                  (head_dim 128); or q/o BSA_BF16 with kv BSA_FP8_E4M3 and
+ *                  (head_dim 128); q/o BSA_F16 or BSA_BF16 with kv BSA_FP8_E4M3
+ *                  for head_dim 128 decode shapes (R = 1, C >= 16, at most 16
+ *                  qo heads per kv head); or q/o BSA_BF16 with kv BSA_FP8_E4M3 and
  *                  head_dim_qk 576 / head_dim_vo 512 / one kv head / R = 1.
  *   q_descale etc. per-tensor dequant scales: real value = stored * descale
  *                  (MATE scale folding: the logit scale becomes
@@ -206,6 +208,20 @@ bsa_status_t bsa_run(bsa_plan_t plan, const void* q, const void* k, const void* 
 #define BSA_PHASE_ALL 3
 bsa_status_t bsa_run_phase(bsa_plan_t plan, int32_t phase, const void* q, const void* k, const void* v,
                            void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bsa_run_phase with per-head dequant scales (BlockSparseAttentionWrapper.run:
+ * scale_q (num_qo_heads), scale_k and scale_v (num_kv_heads), per-head
+ * quantization used with FP8): device float32 arrays, each NULL for 1.0.  The
+ * value a kernel uses is stored value * descale of the plan * scale of the
+ * head, i.e. logits are scaled by sm_scale * q_descale * k_descale *
+ * scale_q[h] * scale_k[h / g] and outputs by v_descale * scale_v[h / g].
+ * Supported by the paged-decode kernel (R = 1, C >= 16; K/V fp16, bf16 or
+ * fp8 e4m3); BSA_ERR_UNSUPPORTED for other plans when any scale is given.
+ */
+bsa_status_t bsa_run_ex(bsa_plan_t plan, int32_t phase, const void* q, const void* k, const void* v,
+                        void* o, float* lse, const float* scale_q, const float* scale_k, const float* scale_v,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * LSE merge of attention states (flashinfer.cascade merge_states): for each

@@ -7,6 +7,7 @@ from .bsr_attention import (  # noqa: F401
     validate_bsr,
     bsr_mask,
     e4m3fn_decode,
+    fp8_dequant,
     bf16_bits_decode,
     masked_attention,
     bsr_attention,

@@ -48,6 +48,7 @@ __all__ = [
     "validate_bsr",
     "bsr_mask",
     "e4m3fn_decode",
+    "fp8_dequant",
     "bf16_bits_decode",
     "masked_attention",
     "bsr_attention",
@@ -134,6 +135,22 @@ def e4m3fn_decode(codes) -> np.ndarray:
     val = np.where(e == 0, sub, normal)
     val = np.where((e == 15) & (m == 7), np.nan, val)
     return sign * val
+
+
+def fp8_dequant(codes, head_scales=None, descale: float = 1.0) -> np.ndarray:
+    """O4 with per-head scales: e4m3 codes (tokens, heads, dim) -> float64 values.
+
+    value = decode(code) * descale * head_scales[head] (BlockSparseAttentionWrapper.run:
+    scale_k / scale_v per kv head, scale_q per qo head, "per-head quantization"; the
+    plan's per-tensor descale as in the MATE scale folding).  head_scales None = 1.
+    """
+    vals = e4m3fn_decode(codes) * float(descale)
+    if head_scales is not None:
+        sc = np.asarray(head_scales, dtype=np.float64)
+        if sc.shape != (vals.shape[1],):
+            raise ValueError("one scale per head")
+        vals = vals * sc[None, :, None]
+    return vals
 
 
 def bf16_bits_decode(bits) -> np.ndarray:

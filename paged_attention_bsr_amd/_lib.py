@@ -103,6 +103,8 @@ def lib() -> ctypes.CDLL:
     L.bsa_run.restype = st
     L.bsa_run_phase.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     L.bsa_run_phase.restype = st
+    L.bsa_run_ex.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.bsa_run_ex.restype = st
     L.bsa_merge_states.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, vp]
     L.bsa_merge_states.restype = st
     L.bsa_plan_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]

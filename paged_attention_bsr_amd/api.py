@@ -150,10 +150,13 @@ class Plan:
     def run(self, q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor] = None,
             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
             return_lse: bool = True, workspace: Optional[torch.Tensor] = None, stream=None,
-            phase: int = L.BSA_PHASE_ALL):
+            phase: int = L.BSA_PHASE_ALL, scale_q: Optional[torch.Tensor] = None,
+            scale_k: Optional[torch.Tensor] = None, scale_v: Optional[torch.Tensor] = None):
         """o (M, Hq, Dv) and, if requested, lse (M, Hq) float32.  v=None aliases k (MLA).
 
-        ``phase`` selects bsa_run_phase's attention-only / merge-only halves."""
+        ``phase`` selects bsa_run_phase's attention-only / merge-only halves.
+        ``scale_q`` (num_qo_heads,), ``scale_k`` / ``scale_v`` (num_kv_heads,): per-head
+        float32 dequant scales on the device (run(): scale_q/k/v), None = 1."""
         if v is None:
             v = k
         for name, t, dt in (("q", q, self.q_dtype), ("k", k, self.kv_dtype), ("v", v, self.kv_dtype)):
@@ -177,9 +180,18 @@ class Plan:
             lse = torch.empty((self.M, self.num_qo_heads), dtype=torch.float32, device=q.device)
         ws = self.workspace(q.device) if workspace is None else workspace
         st = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
-        L.check(L.lib().bsa_run_phase(self._handle, int(phase), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                      out.data_ptr(), lse.data_ptr() if lse is not None else None,
-                                      ws.data_ptr(), ws.numel() * ws.element_size(), st))
+        scales = []
+        for name, t, n in (("scale_q", scale_q, self.num_qo_heads), ("scale_k", scale_k, self.num_kv_heads),
+                           ("scale_v", scale_v, self.num_kv_heads)):
+            if t is None:
+                scales.append(None)
+                continue
+            if not t.is_cuda or t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous float32 device tensor of {n} entries")
+            scales.append(t.data_ptr())
+        L.check(L.lib().bsa_run_ex(self._handle, int(phase), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                   out.data_ptr(), lse.data_ptr() if lse is not None else None, *scales,
+                                   ws.data_ptr(), ws.numel() * ws.element_size(), st))
         return (out, lse) if return_lse else out
 
     def __del__(self):

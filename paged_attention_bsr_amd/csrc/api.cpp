@@ -167,12 +167,23 @@ bsa_status_t bsa_run(bsa_plan_t plan, const void* q, const void* k, const void* 
 
 bsa_status_t bsa_run_phase(bsa_plan_t plan, int32_t phase, const void* q, const void* k, const void* v, void* o,
                            float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return bsa_run_ex(plan, phase, q, k, v, o, lse, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream);
+}
+
+bsa_status_t bsa_run_ex(bsa_plan_t plan, int32_t phase, const void* q, const void* k, const void* v, void* o,
+                        float* lse, const float* scale_q, const float* scale_k, const float* scale_v,
+                        void* workspace, size_t workspace_bytes, void* stream) {
   g_err.clear();
   if (!plan) return set_err(BSA_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (phase < BSA_PHASE_ATTENTION || phase > BSA_PHASE_ALL)
     return set_err(BSA_ERR_INVALID_ARGUMENT, "phase must be BSA_PHASE_ATTENTION, BSA_PHASE_MERGE or BSA_PHASE_ALL");
   const bsa::Plan& P = plan->p;
   const bsa_plan_desc_t& d = P.d;
+  if ((scale_q || scale_k || scale_v) && P.kernel != BSA_KERNEL_DECODE)
+    return set_err(BSA_ERR_UNSUPPORTED, "per-head scales are supported by the paged-decode kernel (R = 1, C >= 16)");
+  if ((reinterpret_cast<uintptr_t>(scale_q) | reinterpret_cast<uintptr_t>(scale_k) |
+       reinterpret_cast<uintptr_t>(scale_v)) & 3u)
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "scale arrays must be 4-byte aligned");
   if (!q || !k || !v || !o || !workspace)
     return set_err(BSA_ERR_INVALID_ARGUMENT, "q, k, v, o and workspace must be non-NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
@@ -222,12 +233,16 @@ bsa_status_t bsa_run_phase(bsa_plan_t plan, int32_t phase, const void* q, const 
   a.num_tiles = static_cast<int32_t>(P.tiles.size() / bsa::kTileInts);
   a.num_wgs = static_cast<int32_t>(P.wg_ptr.size()) - 1;
   a.heads_per_wg = P.heads_per_wg;
+  a.q_scale = scale_q;
+  a.k_scale = scale_k;
+  a.v_scale = scale_v;
 
   hipError_t e;
   if (phase & BSA_PHASE_ATTENTION) {
     if (P.kernel == BSA_KERNEL_MLA) e = bsa::launch_attn_mla(a, d.causal != 0, a.lens != nullptr, st);
     else if (P.kernel == BSA_KERNEL_DECODE)
-      e = bsa::launch_attn_decode(a, d.q_dtype == BSA_BF16, d.causal != 0, a.lens != nullptr, st);
+      e = bsa::launch_attn_decode(a, d.q_dtype == BSA_BF16, d.kv_dtype == BSA_FP8_E4M3, d.causal != 0,
+                                  a.lens != nullptr, st);
     else e = bsa::launch_attn_tile(a, d.q_dtype == BSA_BF16, P.tile_rows, d.causal != 0, a.lens != nullptr, st);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   }

@@ -30,6 +30,8 @@
 //   * keys outside a page's valid length (or past the range) load from a
 //     zero row in the workspace, so unused cache slots never reach the
 //     arithmetic, and are masked to -inf in the scores.
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -50,17 +52,15 @@ constexpr int kVBytes = kKT * kD * 2;   // wave-private V tile
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-template <typename T>
-__device__ __forceinline__ u32x4 load_kv(const T* p) {
-  return *reinterpret_cast<const u32x4*>(p);
-}
-
 // LDS byte offset of 16-byte chunk `c` of key row `k` in a V tile.
 __device__ __forceinline__ int v_chunk_off(int k, int c) {
   return k * (kD * 2) + ((c ^ (((k & 3) << 1) | (((k >> 3) & 1) << 3))) << 4);
 }
 
-template <typename T, int NW, bool CAUSAL, bool LENS, bool POW2C>
+// KV8: K and V are stored as OCP fp8 e4m3 (one byte per value) and widened
+// exactly to T where they are used (K before its products, V before its LDS
+// store); per-head dequant scales fold into the logit and output scales.
+template <typename T, bool KV8, int NW, bool CAUSAL, bool LENS, bool POW2C>
 __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_kernel(AttnArgs a) {
   using Ops = MfmaType<T>;
   using v8 = typename Ops::v8;
@@ -85,7 +85,6 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
   const int C = a.C;
   const int cshift = POW2C ? __builtin_ctz(C) : 0;  // C = 1 << cshift when POW2C
   const int g = a.group;
-  const T* zrow = static_cast<const T*>(a.zero_row);
   const cint32_t* cols = (const cint32_t*)(a.cols);
   const cint32_t* lens = (const cint32_t*)(a.lens);
   const cint32_t* zints = (const cint32_t*)(a.zero_row);
@@ -178,28 +177,36 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
 
   // per-key-tile registers: K fragments and V chunks, both indexed (kb, ks):
   // lane (col, quad) holds dims ks*32 + quad*8 .. +8 of key (kb, col)
+  // (raw bytes: 16 of T, or 8 of e4m3)
+  using Raw = typename std::conditional<KV8, u32x2, u32x4>::type;
   struct Stage {
-    v8 k[2][4];
-    u32x4 v[2][4];
+    Raw k[2][4];
+    Raw v[2][4];
     uint32_t valid[2];  // bit m: key (kb, m) valid
   };
   // key of S^T row m in block kb: 8*(m/4) + 4*kb + m%4
+  constexpr int kElt = KV8 ? 1 : 2;  // bytes per K/V value
   auto load_stage = [&](Stage& s, const Src& b) {
-    const T* kbase = static_cast<const T*>(a.k) + static_cast<int64_t>(b.kvh) * kD;
-    const T* vbase = static_cast<const T*>(a.v) + static_cast<int64_t>(b.kvh) * kD;
+    const unsigned char* kbase = static_cast<const unsigned char*>(a.k) + static_cast<int64_t>(b.kvh) * kD * kElt;
+    const unsigned char* vbase = static_cast<const unsigned char*>(a.v) + static_cast<int64_t>(b.kvh) * kD * kElt;
+    const unsigned char* zb = static_cast<const unsigned char*>(a.zero_row);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key = 8 * (col >> 2) + 4 * kb + (col & 3);
       const int tok = key_token(b, b.t0 + key);
-      const T* pk = tok >= 0 ? kbase + static_cast<int64_t>(tok) * a.k_stride : zrow;
-      const T* pv = tok >= 0 ? vbase + static_cast<int64_t>(tok) * a.v_stride : zrow;
+      const unsigned char* pk = tok >= 0 ? kbase + static_cast<int64_t>(tok) * a.k_stride * kElt : zb;
+      const unsigned char* pv = tok >= 0 ? vbase + static_cast<int64_t>(tok) * a.v_stride * kElt : zb;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) s.k[kb][ks] = bitcast<v8>(load_kv(pk + ks * 32 + quad * 8));
+      for (int ks = 0; ks < 4; ++ks) s.k[kb][ks] = *reinterpret_cast<const Raw*>(pk + (ks * 32 + quad * 8) * kElt);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) s.v[kb][ks] = load_kv(pv + ks * 32 + quad * 8);
+      for (int ks = 0; ks < 4; ++ks) s.v[kb][ks] = *reinterpret_cast<const Raw*>(pv + (ks * 32 + quad * 8) * kElt);
       const uint64_t bal = __ballot(tok >= 0);
       s.valid[kb] = static_cast<uint32_t>(bal & 0xffffu);
     }
+  };
+  auto widen = [&](const Raw& r) -> u32x4 {
+    if constexpr (KV8) return fp8x8_widen<T>(r);
+    else return r;
   };
 
   // Q^T as the B operand: column `col` is qo head kvh*g + row0 + col.  Columns
@@ -217,7 +224,17 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
   unsigned char* vl = lds + wave * kVBytes;
   f32x4 oacc[8];
   float m_run, l_run;
-  const float sl2 = a.scale_log2;
+  // logit scale of this lane's column (qo head) in the current group:
+  // sm_scale * q/k dequant scales * log2(e); sln is the next group's
+  float sl2 = a.scale_log2, sln = a.scale_log2;
+  auto lane_scale = [&](const Ctx& c) -> float {
+    const int cc = col < c.nrows ? col : (c.nrows > 0 ? c.nrows - 1 : 0);
+    float s = a.scale_log2;
+    if (a.q_scale) s *= a.q_scale[c.kvh * g + c.row0 + cc];
+    if (a.k_scale) s *= a.k_scale[c.kvh];
+    return s;
+  };
+  auto out_scale = [&](int kvh) -> float { return a.v_scale ? a.out_scale * a.v_scale[kvh] : a.out_scale; };
 
   // First half of a key tile's math: stage V into this wave's LDS tile
   // (row-major, swizzled chunks) and form the masked scores S^T = K Q^T.
@@ -227,13 +244,13 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
     for (int kb = 0; kb < 2; ++kb) {
       const int key = 8 * (col >> 2) + 4 * kb + (col & 3);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<u32x4*>(vl + v_chunk_off(key, ks * 4 + quad)) = s.v[kb][ks];
+      for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<u32x4*>(vl + v_chunk_off(key, ks * 4 + quad)) = widen(s.v[kb][ks]);
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sc[kb] = f32x4{};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) sc[kb] = Ops::mfma16(s.k[kb][ks], qf[ks], sc[kb]);
+      for (int ks = 0; ks < 4; ++ks) sc[kb] = Ops::mfma16(bitcast<v8>(widen(s.k[kb][ks])), qf[ks], sc[kb]);
 #pragma unroll
       for (int v = 0; v < 4; ++v)
         if (!((s.valid[kb] >> (4 * quad + v)) & 1u)) sc[kb][v] = -INFINITY;
@@ -293,7 +310,7 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
       // the same bytes: no predicated stores.
       const int cc = col < c.nrows ? col : c.nrows - 1;
       const int head = c.kvh * g + c.row0 + cc;
-      const float inv = l_tot > 0.f ? a.out_scale / l_tot : 0.f;
+      const float inv = l_tot > 0.f ? out_scale(c.kvh) / l_tot : 0.f;
       const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
       if (c.part < 0) {
         T* op = static_cast<T*>(a.o) + static_cast<int64_t>(c.I) * a.o_stride + static_cast<int64_t>(head) * kD + 4 * quad;
@@ -345,7 +362,7 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
         L += red_l[w2][cq] * sc;
         acc += sc * *reinterpret_cast<const f32x4*>(ob + (w2 * 16 + cq) * kD + d4);
       }
-      const float inv = L > 0.f ? a.out_scale / L : 0.f;
+      const float inv = L > 0.f ? out_scale(head_kvh[hs]) / L : 0.f;
       const float lse_v = L > 0.f ? (Mu + __log2f(L)) * kLn2 : -INFINITY;
       const int head = head_kvh[hs] * g + c.row0 + cq;
       const int part = head_part[hs];
@@ -376,6 +393,7 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
   // wait covers exactly the older stage.
   Ctx cur = read_ctx(t_begin);
   load_q(cur, qf);
+  sl2 = lane_scale(cur);
   Stage s0, s1;
   Src sA = make_src(cur, sub), sB = make_src(cur, sub + WPH);
   load_stage(s0, sA);
@@ -383,6 +401,7 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
   for (int gn = t_begin + HG;; gn += HG) {
     const Ctx nxt = read_ctx(gn);
     load_q(nxt, qn);
+    sln = lane_scale(nxt);
     const int nT = cur.ntiles > sub ? (cur.ntiles - sub + WPH - 1) >> lg_wph : 0;
     const int nTe = nT < 2 ? 2 : (nT + 1) & ~1;
     // key tile loaded for item q: item q of this group for q < nTe, else item
@@ -414,35 +433,41 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
     finish_tile(cur);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[ks] = qn[ks];
+    sl2 = sln;
     if (gn >= t_end) break;
     cur = nxt;
   }
 }
 
-template <typename T, int NW, bool CAUSAL, bool LENS, bool POW2C>
+template <typename T, bool KV8, int NW, bool CAUSAL, bool LENS, bool POW2C>
 hipError_t launch_variant(const AttnArgs& a, hipStream_t st) {
-  attn_decode_kernel<T, NW, CAUSAL, LENS, POW2C><<<dim3(a.num_wgs), dim3(NW * 64), 0, st>>>(a);
+  attn_decode_kernel<T, KV8, NW, CAUSAL, LENS, POW2C><<<dim3(a.num_wgs), dim3(NW * 64), 0, st>>>(a);
   return hipGetLastError();
 }
 
-template <typename T, int NW, bool POW2C>
+template <typename T, bool KV8, int NW, bool POW2C>
 hipError_t launch_nw(const AttnArgs& a, bool causal, bool lens, hipStream_t st) {
-  if (causal) return lens ? launch_variant<T, NW, true, true, POW2C>(a, st) : launch_variant<T, NW, true, false, POW2C>(a, st);
-  return lens ? launch_variant<T, NW, false, true, POW2C>(a, st) : launch_variant<T, NW, false, false, POW2C>(a, st);
+  if (causal)
+    return lens ? launch_variant<T, KV8, NW, true, true, POW2C>(a, st) : launch_variant<T, KV8, NW, true, false, POW2C>(a, st);
+  return lens ? launch_variant<T, KV8, NW, false, true, POW2C>(a, st) : launch_variant<T, KV8, NW, false, false, POW2C>(a, st);
 }
 
-template <typename T>
+template <typename T, bool KV8>
 hipError_t launch_typed(const AttnArgs& a, bool causal, bool lens, hipStream_t st) {
-  if ((a.C & (a.C - 1)) == 0) return launch_nw<T, BSA_DECODE_NW, true>(a, causal, lens, st);
-  return launch_nw<T, BSA_DECODE_NW, false>(a, causal, lens, st);
+  if ((a.C & (a.C - 1)) == 0) return launch_nw<T, KV8, BSA_DECODE_NW, true>(a, causal, lens, st);
+  return launch_nw<T, KV8, BSA_DECODE_NW, false>(a, causal, lens, st);
 }
 
 }  // namespace
 
-hipError_t launch_attn_decode(const AttnArgs& a, bool bf16, bool causal, bool has_lens, hipStream_t stream) {
+hipError_t launch_attn_decode(const AttnArgs& a, bool bf16, bool kv8, bool causal, bool has_lens,
+                              hipStream_t stream) {
   if (a.num_tiles == 0 || a.num_wgs <= 0) return hipSuccess;
-  return bf16 ? launch_typed<__bf16>(a, causal, has_lens, stream)
-              : launch_typed<_Float16>(a, causal, has_lens, stream);
+  if (kv8)
+    return bf16 ? launch_typed<__bf16, true>(a, causal, has_lens, stream)
+                : launch_typed<_Float16, true>(a, causal, has_lens, stream);
+  return bf16 ? launch_typed<__bf16, false>(a, causal, has_lens, stream)
+              : launch_typed<_Float16, false>(a, causal, has_lens, stream);
 }
 
 }  // namespace bsa

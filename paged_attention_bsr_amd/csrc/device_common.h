@@ -56,6 +56,24 @@ __device__ __forceinline__ To bitcast(const From& x) {
   return __builtin_bit_cast(To, x);
 }
 
+// Two OCP e4m3 bytes (the low or high 16-bit half of `w`) -> two values of T
+// packed in one dword (gfx950's scaled conversion at scale 1: exact, every
+// e4m3 value is an fp16 and a bf16 value).
+template <typename T, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_widen(uint32_t w) {
+  if constexpr (sizeof(T) == 2 && static_cast<T>(1.0009765625f) != static_cast<T>(1.f))
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// Eight e4m3 bytes -> eight values of T (16 bytes).
+template <typename T>
+__device__ __forceinline__ u32x4 fp8x8_widen(u32x2 w) {
+  return u32x4{fp8x2_widen<T, false>(w[0]), fp8x2_widen<T, true>(w[0]), fp8x2_widen<T, false>(w[1]),
+               fp8x2_widen<T, true>(w[1])};
+}
+
 // v_exp_f32: 2^x, with 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -28,6 +28,11 @@ struct AttnArgs {
   int32_t num_tiles;
   int32_t num_wgs;         // workgroups of the launch (decode kernel)
   int32_t heads_per_wg;    // decode kernel: kv heads of one workgroup (a power of two <= 8)
+  // per-head dequant scales (device float arrays, or null = 1): q per qo head,
+  // k and v per kv head (decode kernel)
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
 };
 
 struct MergeArgs {
@@ -45,9 +50,11 @@ struct MergeArgs {
 hipError_t launch_attn_tile(const AttnArgs& a, bool bf16, int tile_rows, bool causal, bool has_lens,
                             hipStream_t stream);
 
-// Paged-decode kernel: R = 1, C >= 16, head_dim 128, fp16 or bf16, g <= 16;
-// workgroup w runs the tile groups wg_ptr[w] .. wg_ptr[w+1]-1 (heads_per_wg tiles each).
-hipError_t launch_attn_decode(const AttnArgs& a, bool bf16, bool causal, bool has_lens, hipStream_t stream);
+// Paged-decode kernel: R = 1, C >= 16, head_dim 128, q/o fp16 or bf16, K/V in
+// the same type or fp8 e4m3 (kv8), g <= 16; workgroup w runs the tile groups
+// wg_ptr[w] .. wg_ptr[w+1]-1 (heads_per_wg tiles each).
+hipError_t launch_attn_decode(const AttnArgs& a, bool bf16, bool kv8, bool causal, bool has_lens,
+                              hipStream_t stream);
 
 // Sparse-MLA kernel: bf16 q/o, fp8 e4m3 kv, Dqk 576, Dv 512, one kv head.
 hipError_t launch_attn_mla(const AttnArgs& a, bool causal, bool has_lens, hipStream_t stream);

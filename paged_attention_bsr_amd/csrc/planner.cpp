@@ -64,7 +64,7 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
 bool is_mla_shape(const bsa_plan_desc_t& d) {
-  return d.kv_dtype == BSA_FP8_E4M3;
+  return d.kv_dtype == BSA_FP8_E4M3 && d.head_dim_qk != 128;
 }
 
 bsa_status_t fail(std::string& err, bsa_status_t st, const std::string& msg) {
@@ -189,14 +189,20 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
     tile_rows = 64;
     key_tile = 32;
   } else {
-    const bool f16 = d.q_dtype == BSA_F16 && d.kv_dtype == BSA_F16 && d.o_dtype == BSA_F16;
-    const bool bf16 = d.q_dtype == BSA_BF16 && d.kv_dtype == BSA_BF16 && d.o_dtype == BSA_BF16;
+    const bool kv8 = d.kv_dtype == BSA_FP8_E4M3;
+    const bool f16 = d.q_dtype == BSA_F16 && (d.kv_dtype == BSA_F16 || kv8) && d.o_dtype == BSA_F16;
+    const bool bf16 = d.q_dtype == BSA_BF16 && (d.kv_dtype == BSA_BF16 || kv8) && d.o_dtype == BSA_BF16;
     if (!(f16 || bf16))
-      return fail(err, BSA_ERR_UNSUPPORTED, "q/k/v/o must all be fp16 or all bf16 for this head_dim");
+      return fail(err, BSA_ERR_UNSUPPORTED,
+                  "q/o must both be fp16 or both bf16, with k/v in the same type or fp8 e4m3, for this head_dim");
     if (d.head_dim_qk != 128 || d.head_dim_vo != 128)
       return fail(err, BSA_ERR_UNSUPPORTED, "head_dim 128 (q/k and v/o) is the supported size");
-    if (d.q_descale != 1.f || d.k_descale != 1.f || d.v_descale != 1.f)
+    if (!kv8 && (d.q_descale != 1.f || d.k_descale != 1.f || d.v_descale != 1.f))
       return fail(err, BSA_ERR_UNSUPPORTED, "dequant scales apply to fp8 KV only");
+    if (kv8 && !(d.R == 1 && g <= 16 && d.C >= 16))
+      return fail(err, BSA_ERR_UNSUPPORTED,
+                  "fp8 e4m3 KV with head_dim 128 is supported for decode shapes (R = 1, C >= 16, at most 16 qo "
+                  "heads per kv head)");
     if (d.R == 1 && g <= 16 && d.C >= 16) {
       kernel = BSA_KERNEL_DECODE;
       tile_rows = 16;

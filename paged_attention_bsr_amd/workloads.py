@@ -43,6 +43,8 @@ __all__ = [
     "window_prefill",
     "sparse_mla",
     "head_sparse_prefill",
+    "paged_decode_fp8",
+    "fp8_kv",
     "random_bsr",
     "by_name",
     "WORKLOAD_NAMES",
@@ -155,6 +157,39 @@ def paged_decode(seed: int = 2, batch: int = 64, min_len: int = 512, max_len: in
         w.q = _randn(g, (batch, num_qo_heads, head_dim), dtype)
         w.k = _randn(g, (N, num_kv_heads, head_dim), dtype)
         w.v = _randn(g, (N, num_kv_heads, head_dim), dtype)
+    return w
+
+
+def fp8_kv(w: Workload, seed: int, q_scales: bool = False) -> Workload:
+    """Give ``w`` fp8 e4m3 K and V with one dequant scale per kv head
+    (BlockSparseAttentionWrapper.run: scale_k / scale_v, per-head quantization).
+
+    K and V are float32 normals; head h's scale is s_h = max |x[:, h, :]| / 448 and
+    its stored values are x / s_h rounded to e4m3 (torch.float8_e4m3fn); the
+    scales go to ``meta["scale_k"]`` / ``meta["scale_v"]`` (float32).  q keeps its
+    16-bit type; with ``q_scales`` a per-qo-head multiplier in [0.5, 2) is drawn
+    into ``meta["scale_q"]`` too.  Returns ``w``.
+    """
+    g = torch.Generator().manual_seed(seed)
+    for name in ("k", "v"):
+        x = torch.randn(w.N, w.num_kv_heads, w.head_dim, generator=g, dtype=torch.float32)
+        s = x.abs().amax(dim=(0, 2)) / 448.0
+        setattr(w, name, (x / s[None, :, None]).to(torch.float8_e4m3fn))
+        w.meta[f"scale_{name}"] = s.numpy().astype(np.float32)
+    if q_scales:
+        w.meta["scale_q"] = (0.5 + 1.5 * torch.rand(w.num_qo_heads, generator=g)).numpy().astype(np.float32)
+    w.kv_dtype = torch.float8_e4m3fn
+    return w
+
+
+def paged_decode_fp8(seed: int = 7, values: bool = True) -> Workload:
+    """paged_decode's structure (same requests, lengths and pages) with fp8 e4m3 K/V
+    and per-kv-head dequant scales (see fp8_kv); q and o fp16."""
+    w = paged_decode(values=values)
+    w.name = "paged_decode_fp8"
+    w.kv_dtype = torch.float8_e4m3fn
+    if values:
+        fp8_kv(w, seed)
     return w
 
 
@@ -311,13 +346,14 @@ def random_bsr(seed: int, M: int, N: int, R: int, C: int, num_qo_heads: int,
 # Split-KV setting each workload is timed (and parity-checked at full size) with:
 # 0 = automatic, 1 = no split.
 BENCH_KV_SPLITS = {"worked_example": 1, "paged_decode": 0, "bsr_prefill": 1, "window_prefill": 1,
-                   "sparse_mla": 1, "head_sparse_prefill": 1}
+                   "sparse_mla": 1, "head_sparse_prefill": 1, "paged_decode_fp8": 0}
 
 WORKLOAD_NAMES = ["worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla",
-                  "head_sparse_prefill"]
+                  "head_sparse_prefill", "paged_decode_fp8"]
 
 
 def by_name(name: str, **kw) -> Workload:
     return {"worked_example": worked_example, "paged_decode": paged_decode,
             "bsr_prefill": bsr_prefill, "window_prefill": window_prefill,
-            "sparse_mla": sparse_mla, "head_sparse_prefill": head_sparse_prefill}[name](**kw)
+            "sparse_mla": sparse_mla, "head_sparse_prefill": head_sparse_prefill,
+            "paged_decode_fp8": paged_decode_fp8}[name](**kw)

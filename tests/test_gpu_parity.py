@@ -169,6 +169,7 @@ FULL_ROWS = {
     "window_prefill": [0, 1, 127, 128, 1100, 1151, 2048, 16383, 30000, 32767],
     "sparse_mla": [0, 1, 17, 64, 100, 127],
     "head_sparse_prefill": [0, 1, 63, 64, 127, 4095, 4096, 6000, 8190, 8191],
+    "paged_decode_fp8": None,                                   # all 64 requests
 }
 
 
@@ -345,3 +346,33 @@ def test_reduced_head_sparse_prefill():
     w = W.head_sparse_prefill(seed=48, M=1024)
     _check(w, 1)
     _check(w, 0)
+
+
+
+# ---------------------------------------------------------------- fp8 e4m3 KV, head_dim 128 (decode kernel)
+FP8_DECODE = [
+    # (seed, M, NB, C, Hq, Hkv, causal, lens, dtype, q_scales)
+    (51, 9, 40, 16, 32, 8, False, True, torch.float16, False),
+    (52, 20, 30, 32, 16, 4, True, True, torch.float16, True),
+    (53, 7, 50, 16, 16, 1, False, False, torch.bfloat16, True),   # one kv head, 16 qo heads
+    (54, 33, 20, 48, 24, 3, False, True, torch.bfloat16, False),  # odd kv heads, C not a power of two
+]
+
+
+@pytest.mark.parametrize("case", FP8_DECODE, ids=[f"f{c[0]}" for c in FP8_DECODE])
+@pytest.mark.parametrize("kv_splits", [1, 3, 0])
+def test_fp8_kv_decode(case, kv_splits):
+    """fp8 e4m3 K/V with per-kv-head scales (and per-qo-head q scales) through the decode
+    kernel; unused slots of partial pages hold the largest finite codes (+-448)."""
+    seed, M, NB, C, Hq, Hkv, causal, lens, dtype, qs = case
+    w = W.random_bsr(seed, M, NB * C, 1, C, Hq, Hkv, causal=causal, partial_lens=lens, density=0.5, dtype=dtype)
+    W.fp8_kv(w, seed, q_scales=qs)
+    if lens:
+        kb, vb = w.k.view(torch.uint8), w.v.view(torch.uint8)
+        for J in range(NB):
+            n = int(w.kv_block_lens[J])
+            if n < C:
+                kb[J * C + n:(J + 1) * C] = 0x7E      # +448
+                vb[J * C + n:(J + 1) * C] = 0xFE      # -448
+    assert plan_for(w, kv_splits).info()["kernel"] == 2
+    _check(w, kv_splits, what=f"fp8 decode s{seed} {dtype} splits={kv_splits}")

@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from oracle import (bf16_bits_decode, bsr_attention, bsr_mask, e4m3fn_decode,
                     masked_attention, merge_states, validate_bsr)
 
@@ -352,3 +353,20 @@ def test_validation_rejects_bad_lens():
         validate_bsr(np.array([0, 1]), np.array([0]), 1, 4, 1, 2, kv_block_lens=np.array([0, 2]))
     with pytest.raises(ValueError):
         validate_bsr(np.array([0, 1]), np.array([0]), 1, 4, 1, 2, kv_block_lens=np.array([3, 2]))
+
+
+# ---------------------------------------------------------------- fp8 KV with per-head scales
+def test_fp8_dequant_matches_torch_with_head_scales():
+    """O4 with per-head scales: torch's e4m3fn decode times the head's scale and the descale."""
+    rng = np.random.default_rng(21)
+    codes = rng.integers(0, 256, size=(7, 3, 16)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0          # no NaN codes in KV data
+    scales = np.array([0.5, 2.0, 3.25], np.float32)
+    got = oracle.fp8_dequant(codes, scales, descale=0.75)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ref = ref * 0.75 * scales.astype(np.float64)[None, :, None]
+    assert np.array_equal(got, ref)
+    assert np.array_equal(oracle.fp8_dequant(codes), torch.from_numpy(codes).view(torch.float8_e4m3fn)
+                          .to(torch.float64).numpy())
+    with pytest.raises(ValueError):
+        oracle.fp8_dequant(codes, scales[:2])

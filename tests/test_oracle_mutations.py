@@ -46,6 +46,7 @@ MUTATIONS = {
     "per_head_causal_top_left": ("out[h, out_row, max(0, i + (N - M) + 1):] = False",
                                  "out[h, out_row, max(0, i + 1):] = False"),
     "per_head_rows_by_C": ("blocks = bm[h, i // R]", "blocks = bm[h, min(i // C, bm.shape[1] - 1)]"),
+    "fp8_scale_axis": ("vals = vals * sc[None, :, None]", "vals = vals * sc[None, None, :1]"),
 }
 
 
@@ -165,7 +166,19 @@ def _pin_q2k(mod):
     return np.array_equal(bm, want)
 
 
-PINS = [_pin_brute_force, _pin_equal_scores, _pin_sdpa, _pin_fp8, _pin_merge, _pin_per_head_sdpa, _pin_q2k]
+def _pin_fp8_heads(mod):
+    codes = np.arange(96, dtype=np.uint8).reshape(4, 3, 8)
+    scales = np.array([0.5, 2.0, 3.0])
+    try:
+        got = mod.fp8_dequant(codes, scales, descale=0.25)
+    except (ValueError, IndexError):
+        return False
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy() * 0.25 * scales[None, :, None]
+    return np.array_equal(got, ref)
+
+
+PINS = [_pin_brute_force, _pin_equal_scores, _pin_sdpa, _pin_fp8, _pin_merge, _pin_per_head_sdpa, _pin_q2k,
+        _pin_fp8_heads]
 
 
 def test_unmutated_copy_passes_every_pin():

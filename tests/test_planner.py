@@ -330,7 +330,7 @@ TILE_SMALL_GRID_PER_CU = 8
 def model_kernel(w, num_cus):
     """Python model of the planner's kernel / row-tile choice."""
     g = w.num_qo_heads // w.num_kv_heads
-    if w.kv_dtype == torch.float8_e4m3fn:
+    if w.kv_dtype == torch.float8_e4m3fn and w.head_dim != 128:
         return 1, 64
     if w.R == 1 and g <= 16 and w.C >= 16:
         return 2, 16
@@ -474,3 +474,28 @@ def test_per_head_structure_errors():
         bq[1, 0] = ~bq[1, 0]
         with pytest.raises(RuntimeError, match="same key blocks"):
             _plan_heads(w, 1, 8, block_mask=bq)
+
+
+
+def test_fp8_kv_head_dim_128_selects_decode_kernel_only():
+    w = W.by_name("paged_decode_fp8", values=False)
+    inf = _plan(w, 0).info()
+    assert inf["kernel"] == 2
+    # fp8 KV at head_dim 128 outside the decode shapes has no kernel
+    w2 = W.random_bsr(5, 64, 64 * 4, 16, 16, 8, 2, values=False)
+    w2.kv_dtype = torch.float8_e4m3fn
+    with pytest.raises(RuntimeError, match="decode shapes"):
+        _plan(w2, 1)
+
+
+def test_run_scales_rejected_outside_decode_kernel():
+    """Per-head run scales are a decode-kernel feature; other plans refuse them before
+    touching any pointer."""
+    import ctypes
+    from paged_attention_bsr_amd import _lib as L
+    w = W.random_bsr(6, 64, 64 * 4, 16, 16, 8, 2, values=False)
+    p = _plan(w, 1)
+    lib = L.lib()
+    st = lib.bsa_run_ex(p._handle, L.BSA_PHASE_ALL, None, None, None, None, None, 16, None, None, None, 0, None)
+    assert st == L.BSA_ERR_UNSUPPORTED
+    assert b"per-head scales" in lib.bsa_last_error()
