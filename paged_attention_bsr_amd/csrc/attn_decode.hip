@@ -177,11 +177,16 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
 
   // per-key-tile registers: K fragments and V chunks, both indexed (kb, ks):
   // lane (col, quad) holds dims ks*32 + quad*8 .. +8 of key (kb, col)
-  // (raw bytes: 16 of T, or 8 of e4m3)
-  using Raw = typename std::conditional<KV8, u32x2, u32x4>::type;
+  // Raw K/V bytes of a key, as 16-byte loads.  16-bit storage: four loads,
+  // load j = dims j*32 + quad*8 .. +8 (k-step j).  fp8: two loads, load j =
+  // dims j*64 + quad*16 .. +16, so every load covers whole 64-byte sectors;
+  // k-step ks then takes half ks % 2 of load ks / 2.  Q is loaded in the same
+  // dim order (the dot product is indifferent to it), and V goes back to its
+  // own chunks in LDS.
+  constexpr int NLD = KV8 ? 2 : 4;
   struct Stage {
-    Raw k[2][4];
-    Raw v[2][4];
+    u32x4 k[2][NLD];
+    u32x4 v[2][NLD];
     uint32_t valid[2];  // bit m: key (kb, m) valid
   };
   // key of S^T row m in block kb: 8*(m/4) + 4*kb + m%4
@@ -197,16 +202,23 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
       const unsigned char* pk = tok >= 0 ? kbase + static_cast<int64_t>(tok) * a.k_stride * kElt : zb;
       const unsigned char* pv = tok >= 0 ? vbase + static_cast<int64_t>(tok) * a.v_stride * kElt : zb;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) s.k[kb][ks] = *reinterpret_cast<const Raw*>(pk + (ks * 32 + quad * 8) * kElt);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) s.v[kb][ks] = *reinterpret_cast<const Raw*>(pv + (ks * 32 + quad * 8) * kElt);
+      for (int j = 0; j < NLD; ++j) {
+        const int off = KV8 ? j * 64 + quad * 16 : (j * 32 + quad * 8) * 2;
+        s.k[kb][j] = *reinterpret_cast<const u32x4*>(pk + off);
+        s.v[kb][j] = *reinterpret_cast<const u32x4*>(pv + off);
+      }
       const uint64_t bal = __ballot(tok >= 0);
       s.valid[kb] = static_cast<uint32_t>(bal & 0xffffu);
     }
   };
-  auto widen = [&](const Raw& r) -> u32x4 {
-    if constexpr (KV8) return fp8x8_widen<T>(r);
-    else return r;
+  // the eight K values of k-step ks, in T
+  auto kfrag = [&](const Stage& s, int kb, int ks) -> v8 {
+    if constexpr (KV8) {
+      const u32x4 r = s.k[kb][ks >> 1];
+      return bitcast<v8>(fp8x8_widen<T>((ks & 1) ? u32x2{r[2], r[3]} : u32x2{r[0], r[1]}));
+    } else {
+      return bitcast<v8>(s.k[kb][ks]);
+    }
   };
 
   // Q^T as the B operand: column `col` is qo head kvh*g + row0 + col.  Columns
@@ -216,9 +228,10 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
   auto load_q = [&](const Ctx& c, v8 (&q)[4]) {
     const int cc = col < c.nrows ? col : (c.nrows > 0 ? c.nrows - 1 : 0);
     const T* qp = static_cast<const T*>(a.q) + static_cast<int64_t>(c.I) * a.q_stride +
-                  static_cast<int64_t>(c.kvh * g + c.row0 + cc) * kD + quad * 8;
+                  static_cast<int64_t>(c.kvh * g + c.row0 + cc) * kD;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) q[ks] = *reinterpret_cast<const v8*>(qp + ks * 32);
+    for (int ks = 0; ks < 4; ++ks)
+      q[ks] = *reinterpret_cast<const v8*>(qp + (KV8 ? (ks >> 1) * 64 + quad * 16 + (ks & 1) * 8 : ks * 32 + quad * 8));
   };
 
   unsigned char* vl = lds + wave * kVBytes;
@@ -243,14 +256,23 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key = 8 * (col >> 2) + 4 * kb + (col & 3);
+      if constexpr (KV8) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<u32x4*>(vl + v_chunk_off(key, ks * 4 + quad)) = widen(s.v[kb][ks]);
+        for (int j = 0; j < 2; ++j) {
+          const u32x4 r = s.v[kb][j];
+          *reinterpret_cast<u32x4*>(vl + v_chunk_off(key, j * 8 + quad * 2)) = fp8x8_widen<T>(u32x2{r[0], r[1]});
+          *reinterpret_cast<u32x4*>(vl + v_chunk_off(key, j * 8 + quad * 2 + 1)) = fp8x8_widen<T>(u32x2{r[2], r[3]});
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) *reinterpret_cast<u32x4*>(vl + v_chunk_off(key, ks * 4 + quad)) = s.v[kb][ks];
+      }
     }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       sc[kb] = f32x4{};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) sc[kb] = Ops::mfma16(bitcast<v8>(widen(s.k[kb][ks])), qf[ks], sc[kb]);
+      for (int ks = 0; ks < 4; ++ks) sc[kb] = Ops::mfma16(kfrag(s, kb, ks), qf[ks], sc[kb]);
 #pragma unroll
       for (int v = 0; v < 4; ++v)
         if (!((s.valid[kb] >> (4 * quad + v)) & 1u)) sc[kb][v] = -INFINITY;
@@ -385,7 +407,7 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
 
   // The workgroup runs its groups in order.  Within a group the WPH waves of
   // a head take its 32-key tiles sub, sub+WPH, ...; each wave's sequence is
-  // padded to an even length (at least 2) with key tiles past the end, which
+  // padded to a multiple of NS (at least NS) with key tiles past the end, which
   // load the zero row and are fully masked (so computing them leaves the
   // softmax state unchanged), and the loads run two items ahead across tile
   // boundaries, so the next group's first keys are in flight during the
@@ -394,16 +416,17 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
   Ctx cur = read_ctx(t_begin);
   load_q(cur, qf);
   sl2 = lane_scale(cur);
-  Stage s0, s1;
-  Src sA = make_src(cur, sub), sB = make_src(cur, sub + WPH);
-  load_stage(s0, sA);
-  load_stage(s1, sB);
+  // NS register stages of key tiles in flight (three or four fp8 stages measured slower)
+  constexpr int NS = 2;
+  Stage stg[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) load_stage(stg[i], make_src(cur, sub + i * WPH));
   for (int gn = t_begin + HG;; gn += HG) {
     const Ctx nxt = read_ctx(gn);
     load_q(nxt, qn);
     sln = lane_scale(nxt);
     const int nT = cur.ntiles > sub ? (cur.ntiles - sub + WPH - 1) >> lg_wph : 0;
-    const int nTe = nT < 2 ? 2 : (nT + 1) & ~1;
+    const int nTe = nT < NS ? NS : (nT + NS - 1) / NS * NS;
     // key tile loaded for item q: item q of this group for q < nTe, else item
     // q - nTe of the next one
     auto src_of = [&](int q) {
@@ -415,20 +438,19 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
     for (int db = 0; db < 8; ++db) oacc[db] = f32x4{};
     m_run = -INFINITY;
     l_run = 0.f;
-    // s0 and s1 hold items p and p + 1 at the top of each pass; a stage is
-    // reloaded (item p + 2, p + 3) as soon as its scores are formed
+    // stage i holds item p + i at the top of each pass; it is reloaded (item
+    // p + NS + i) as soon as its scores are formed
     int p = 0;
-    do {  // nTe >= 2: at least one pair, so the waits never see a skipped body
-      f32x4 sc[2];
-      sA = src_of(p + 2);
-      scores(s0, sc);
-      load_stage(s0, sA);
-      accumulate(sc);
-      sB = src_of(p + 3);
-      scores(s1, sc);
-      load_stage(s1, sB);
-      accumulate(sc);
-      p += 2;
+    do {  // nTe >= NS: at least one pass, so the waits never see a skipped body
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        f32x4 sc[2];
+        const Src sn = src_of(p + NS + i);
+        scores(stg[i], sc);
+        load_stage(stg[i], sn);
+        accumulate(sc);
+      }
+      p += NS;
     } while (p < nTe);
     finish_tile(cur);
 #pragma unroll
