@@ -91,6 +91,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
   constexpr int CH_PER_T = (NCHUNK + NTHR - 1) / NTHR;
   constexpr int NGROUP = NW / 2;             // 16-head groups per tile
   static_assert(NTHR % kKT == 0 && NW % 2 == 0, "loader maps one key per thread; waves pair up");
+  static_assert(NW == 8, "the gather mapping below covers 32 keys x 16 chunks per round with 512 threads");
 
   __shared__ __attribute__((aligned(16))) unsigned char lds[NBUF * L::kBuf + NGROUP * L::kXsBytes];
 
@@ -164,7 +165,12 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
   };
   auto key_tok = [&](int t) -> int { return finish_tok(t, fetch_blk(t)); };
   const uint8_t* kv = static_cast<const uint8_t*>(a.k);
-  const int my_key = tid % kKT;
+  // gather mapping: lane l of a wave takes key l % 16 (+ 16 for odd waves) and
+  // 16-byte chunk l / 16 (+ 4 per pair of waves, + 16 per round), so one load
+  // instruction covers 16 keys x 64 contiguous bytes and one 16-lane store pass
+  // 16 keys at one unit; each thread keeps one key
+  const int my_key = (tid & 15) + 16 * ((tid >> 6) & 1);
+  auto chunk_of = [&](int i) { return ((tid & 63) >> 4) + 4 * (tid >> 7) + 16 * i; };
   // two register sets: the rows of tile kt + 2 are in flight while tile kt is
   // stored and computed
   u32x4 creg_a[CH_PER_T], creg_b[CH_PER_T];
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < CH_PER_T; ++i) {
       const int ci = tid + i * NTHR;
-      const int c = ci / kKT;  // 16-byte chunk of the fp8 row (< 48, inside the 1 KB zero row)
+      const int c = chunk_of(i);  // 16-byte chunk of the fp8 row (< 48, inside the 1 KB zero row)
       const uint8_t* src = (ci < NCHUNK && tok >= 0) ? kv + static_cast<int64_t>(tok) * a.k_stride : zrow;
       creg[i] = *reinterpret_cast<const u32x4*>(src + c * 16);
     }
@@ -188,7 +194,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
     for (int i = 0; i < CH_PER_T; ++i) {
       const int ci = tid + i * NTHR;
       if (ci >= NCHUNK) continue;
-      const int c = ci / kKT;
+      const int c = chunk_of(i);
       uint32_t b[8];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -199,7 +205,7 @@ __global__ __launch_bounds__(NW * 64) void attn_mla_kernel(AttnArgs a) {
       *reinterpret_cast<u32x4*>(base + k_off(my_key, 2 * c)) = u32x4{b[0], b[1], b[2], b[3]};
       *reinterpret_cast<u32x4*>(base + k_off(my_key, 2 * c + 1)) = u32x4{b[4], b[5], b[6], b[7]};
     }
-    if (tid < kKT) reinterpret_cast<int*>(base + L::kKBytes)[tid] = tok;
+    if (tid < 128 && ((tid >> 4) & 3) == 0) reinterpret_cast<int*>(base + L::kKBytes)[my_key] = tok;
   };
 
   // this wave's output: O^T for dv in [256 * hf, 256 * hf + 256), its 16 heads
