@@ -15,4 +15,9 @@ from .bsr_attention import (  # noqa: F401
     q2k_block_mask,
     head_block_masks,
     block_mask_attention,
+    unpack_block_masks,
+    element_mask,
+    element_mask_attention,
+    variable_block_masks,
+    variable_block_attention,
 )

@@ -26,6 +26,10 @@ the same boolean mask).  Every step is written out plainly in float64:
   O8  per-head structure                  (plan(): block_mask (heads, MB, NB) and
                                            q2k_indices / q2k_num; VariableBlockSparse-
                                            AttentionWrapper: each kv head its own pattern)
+  O9  element masks inside blocks         (plan(): mask (nnz, R, C), packed_mask from
+                                           flashinfer.quantization.packbits)
+  O10 variable block sizes                (VariableBlockSparseAttentionWrapper.plan:
+                                           block_mask_map, block_row_sz, block_col_sz)
 
 Readings taken where the pages are silent:
   * lse is the natural log of sum(exp(sm_scale * q.k)) over unmasked keys;
@@ -35,7 +39,17 @@ Readings taken where the pages are silent:
   * rows i >= M of a partial last row block do not exist;
   * a per-head structure given per qo head applies to that qo head (the
     library requires the qo heads of one kv head to agree, which makes this
-    the same as using the first qo head of each group).
+    the same as using the first qo head of each group);
+  * element mask p belongs to the block indices[p] of the BSR arrays as
+    given (before any sorting), its entry [r, c] to query row I*R + r and key
+    J*C + c; with an element mask the causal flag has no effect (plan():
+    causal is only effective when neither mask nor packed_mask is given);
+  * packed_mask holds the flattened (nnz, R, C) mask eight entries a byte,
+    entry i in bit i % 8 (least significant first) of byte i // 8;
+  * variable blocks: row block a of kv head h covers the block_row_sz[h, a]
+    query rows after those of blocks 0..a-1 (columns likewise), the sizes of
+    each head sum to the query / key counts, and causal masking (j <= i + N - M)
+    applies on top of the block map.
 """
 from __future__ import annotations
 
@@ -56,6 +70,11 @@ __all__ = [
     "q2k_block_mask",
     "head_block_masks",
     "block_mask_attention",
+    "unpack_block_masks",
+    "element_mask",
+    "element_mask_attention",
+    "variable_block_masks",
+    "variable_block_attention",
 ]
 
 
@@ -320,5 +339,122 @@ def block_mask_attention(block_mask, M: int, N: int, R: int, C: int, q, k, v,
         kvh = h // group
         mh = masks[kvh] if masks.shape[0] == Hkv else masks[h]
         oh, lh = masked_attention(q[:, h:h + 1], k[:, kvh:kvh + 1], v[:, kvh:kvh + 1], mh, sm_scale)
+        o[:, h], lse[:, h] = oh[:, 0], lh[:, 0]
+    return o, lse
+
+
+def unpack_block_masks(packed, nnz: int, R: int, C: int) -> np.ndarray:
+    """O9: packed_mask -> the (nnz, R, C) boolean element masks.
+
+    Entry i of the flattened mask is bit i % 8, least significant first, of
+    byte i // 8 (the reading of packbits' bit order stated above); trailing
+    bits of the last byte are ignored.
+    """
+    packed = np.asarray(packed, dtype=np.uint8).ravel()
+    n = nnz * R * C
+    if packed.size < -(-n // 8):
+        raise ValueError("packed_mask is shorter than nnz * R * C bits")
+    i = np.arange(n)
+    return ((packed[i // 8] >> (i % 8)) & 1).astype(bool).reshape(nnz, R, C)
+
+
+def element_mask(indptr, indices, M: int, N: int, R: int, C: int, mask,
+                 rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """O9 + O2: dense boolean mask of a BSR structure with element masks.
+
+    Entry (i, j) is True iff, for I = i // R, some p in indptr[I] ..
+    indptr[I + 1] - 1 has indices[p] == j // C and mask[p, i % R, j % C].
+    """
+    validate_bsr(indptr, indices, M, N, R, C)
+    mask = np.asarray(mask).astype(bool)
+    nnz = int(indptr[-1])
+    if mask.shape != (nnz, R, C):
+        raise ValueError(f"mask must have shape ({nnz}, {R}, {C})")
+    row_list = list(range(M)) if rows is None else [int(r) for r in rows]
+    out = np.zeros((len(row_list), N), dtype=bool)
+    for out_row, i in enumerate(row_list):
+        if not 0 <= i < M:
+            raise ValueError("row out of range")
+        I = i // R
+        for p in range(int(indptr[I]), int(indptr[I + 1])):
+            J = int(indices[p])
+            out[out_row, J * C:(J + 1) * C] = mask[p, i % R]
+    return out
+
+
+def element_mask_attention(indptr, indices, M: int, N: int, R: int, C: int, mask, q, k, v,
+                           sm_scale: Optional[float] = None, rows: Optional[Iterable[int]] = None):
+    """Attention under BSR blocks with element masks (O9, then O5 + O6).
+
+    ``mask`` is the (nnz, R, C) boolean array (unpack a packed_mask with
+    unpack_block_masks first).  No causal flag: the mask replaces it.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[-1])
+    row_list = None if rows is None else [int(r) for r in rows]
+    dense = element_mask(indptr, indices, M, N, R, C, mask, row_list)
+    if row_list is not None:
+        q = q[row_list]
+    return masked_attention(q, k, v, dense, sm_scale)
+
+
+def variable_block_masks(block_mask_map, block_row_sz, block_col_sz, causal: bool = False,
+                         rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """O10: variable-size block map -> dense boolean masks (kv heads, rows, N).
+
+    Token row i of head h lies in the row block a whose row range (the sizes
+    of blocks before it summed, plus its own) holds i, key j in column block b
+    likewise; (h, i, j) is True iff block_mask_map[h, a, b], and, when causal,
+    j <= i + (N - M).
+    """
+    bm = np.asarray(block_mask_map).astype(bool)
+    rs = np.asarray(block_row_sz, dtype=np.int64)
+    cs = np.asarray(block_col_sz, dtype=np.int64)
+    if bm.ndim != 3 or rs.shape != bm.shape[:2] or cs.shape != (bm.shape[0], bm.shape[2]):
+        raise ValueError("block_row_sz must be (heads, MB) and block_col_sz (heads, NB) for a (heads, MB, NB) map")
+    if (rs < 0).any() or (cs < 0).any():
+        raise ValueError("block sizes must be >= 0")
+    M, N = int(rs[0].sum()), int(cs[0].sum())
+    if (rs.sum(axis=1) != M).any() or (cs.sum(axis=1) != N).any():
+        raise ValueError("every head's block sizes must sum to the same query / key counts")
+    row_list = list(range(M)) if rows is None else [int(r) for r in rows]
+    out = np.zeros((bm.shape[0], len(row_list), N), dtype=bool)
+    for h in range(bm.shape[0]):
+        row_block = np.repeat(np.arange(bm.shape[1]), rs[h])    # token row -> its row block
+        col_block = np.repeat(np.arange(bm.shape[2]), cs[h])    # key -> its column block
+        for out_row, i in enumerate(row_list):
+            if not 0 <= i < M:
+                raise ValueError("row out of range")
+            out[h, out_row] = bm[h, row_block[i], col_block]
+            if causal:
+                out[h, out_row, max(0, i + (N - M) + 1):] = False
+    return out
+
+
+def variable_block_attention(block_mask_map, block_row_sz, block_col_sz, q, k, v,
+                             sm_scale: Optional[float] = None, causal: bool = False,
+                             rows: Optional[Iterable[int]] = None):
+    """Attention under variable-size blocks, each kv head its own map (O10, then
+    O5 + O6 head by head; the qo heads of a kv group share its map).
+    q (M, Hq, D), k (N, Hkv, D), v (N, Hkv, Dv) float64; returns o, lse."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    Hq, Hkv = q.shape[1], k.shape[1]
+    group = Hq // Hkv
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(q.shape[-1])
+    row_list = None if rows is None else [int(r) for r in rows]
+    masks = variable_block_masks(block_mask_map, block_row_sz, block_col_sz, causal, row_list)
+    if masks.shape[0] != Hkv:
+        raise ValueError("block_mask_map must have num_kv_heads heads")
+    if row_list is not None:
+        q = q[row_list]
+    o = np.zeros((q.shape[0], Hq, v.shape[2]))
+    lse = np.zeros((q.shape[0], Hq))
+    for h in range(Hq):
+        kvh = h // group
+        oh, lh = masked_attention(q[:, h:h + 1], k[:, kvh:kvh + 1], v[:, kvh:kvh + 1], masks[kvh], sm_scale)
         o[:, h], lse[:, h] = oh[:, 0], lh[:, 0]
     return o, lse

@@ -26,7 +26,8 @@ MUTATIONS = {
                         "mask[out_row, max(0, i + 1):] = False"),
     "lse_base2": ("m + np.log(safe_l)", "m + np.log2(safe_l)"),
     "no_sm_scale": ("s = sm_scale * (q[:, h, :] @ k[:, kvh, :].T)", "s = (q[:, h, :] @ k[:, kvh, :].T)"),
-    "row_block_index": ("        I = i // R\n", "        I = min(i, len(indptr) - 2)\n"),
+    "row_block_index": ("        I = i // R\n        for p in range(int(indptr[I]), int(indptr[I + 1])):\n            J = int(indices[p])\n            length",
+                        "        I = min(i, len(indptr) - 2)\n        for p in range(int(indptr[I]), int(indptr[I + 1])):\n            J = int(indices[p])\n            length"),
     "fp8_bias8": ("np.exp2(e.astype(np.float64) - 7.0)", "np.exp2(e.astype(np.float64) - 8.0)"),
     "fp8_subnormal": ("sub = (m / 8.0) * 2.0 ** -6", "sub = (1.0 + m / 8.0) * 2.0 ** -7"),
     "merge_unweighted": ("w = np.where(np.isfinite(lse_states), np.exp(lse_states - top_safe), 0.0)",
@@ -43,10 +44,22 @@ MUTATIONS = {
     "q2k_ignore_num": ("row = [int(x) for x in sel[h, I, :n]]", "row = [int(x) for x in sel[h, I, :topk]]"),
     "per_head_ignore_lens": ("key_ok = (np.arange(N) % C) < lens[np.arange(N) // C]",
                              "key_ok = np.ones(N, dtype=bool)"),
-    "per_head_causal_top_left": ("out[h, out_row, max(0, i + (N - M) + 1):] = False",
-                                 "out[h, out_row, max(0, i + 1):] = False"),
+    "per_head_causal_top_left": ("out[h, out_row, max(0, i + (N - M) + 1):] = False\n    return out\n\n\ndef block_mask_attention",
+                                 "out[h, out_row, max(0, i + 1):] = False\n    return out\n\n\ndef block_mask_attention"),
     "per_head_rows_by_C": ("blocks = bm[h, i // R]", "blocks = bm[h, min(i // C, bm.shape[1] - 1)]"),
     "fp8_scale_axis": ("vals = vals * sc[None, :, None]", "vals = vals * sc[None, None, :1]"),
+    # element masks and variable block sizes
+    "packed_big_endian": ("((packed[i // 8] >> (i % 8)) & 1)", "((packed[i // 8] >> (7 - i % 8)) & 1)"),
+    "elem_mask_row_shift": ("out[out_row, J * C:(J + 1) * C] = mask[p, i % R]",
+                            "out[out_row, J * C:(J + 1) * C] = mask[p, (i + 1) % R]"),
+    "elem_mask_sorted_order": ("out[out_row, J * C:(J + 1) * C] = mask[p, i % R]",
+                               "out[out_row, J * C:(J + 1) * C] = mask[int(indptr[I]) + sorted(indices[int(indptr[I]):int(indptr[I + 1])]).index(J), i % R]"),
+    "variable_sizes_swapped": ("row_block = np.repeat(np.arange(bm.shape[1]), rs[h])",
+                               "row_block = np.repeat(np.arange(bm.shape[1]), rs[h][::-1])"),
+    "variable_head_zero_sizes": ("col_block = np.repeat(np.arange(bm.shape[2]), cs[h])",
+                                 "col_block = np.repeat(np.arange(bm.shape[2]), cs[0])"),
+    "variable_causal_top_left": ("                out[h, out_row, max(0, i + (N - M) + 1):] = False\n    return out\n\n\ndef variable_block_attention",
+                                 "                out[h, out_row, max(0, i + 1):] = False\n    return out\n\n\ndef variable_block_attention"),
 }
 
 
@@ -177,8 +190,59 @@ def _pin_fp8_heads(mod):
     return np.array_equal(got, ref)
 
 
+def _pin_packed_bits(mod):
+    try:
+        got = mod.unpack_block_masks(np.array([0b101, 0b1], np.uint8), 1, 3, 3)
+    except (ValueError, IndexError):
+        return False
+    want = np.zeros((1, 3, 3), bool)
+    want[0, 0, 0] = want[0, 0, 2] = want[0, 2, 2] = True
+    return np.array_equal(got, want)
+
+
+def _pin_element_masks(mod):
+    """Element masks (unsorted indices, R != C, partial last row block) against a dense
+    mask written block by block with torch ops."""
+    rng = np.random.default_rng(61)
+    M, R, C, NB = 11, 3, 2, 5
+    N = NB * C
+    rows = [rng.permutation(np.nonzero(rng.random(NB) < 0.7)[0]) for _ in range(-(-M // R))]
+    indptr = np.cumsum([0] + [len(r) for r in rows]).astype(np.int32)
+    indices = np.concatenate(rows).astype(np.int32)
+    mask = rng.random((int(indptr[-1]), R, C)) < 0.6
+    dense = torch.zeros(-(-M // R) * R, N, dtype=torch.bool)
+    for I in range(len(indptr) - 1):
+        for p in range(indptr[I], indptr[I + 1]):
+            dense[I * R:(I + 1) * R, indices[p] * C:(indices[p] + 1) * C] = torch.from_numpy(mask[p])
+    try:
+        got = mod.element_mask(indptr, indices, M, N, R, C, mask)
+    except (ValueError, IndexError):
+        return False
+    return np.array_equal(got, dense[:M].numpy())
+
+
+def _pin_variable_blocks(mod):
+    """The variable-block worked example's hand-written token mask, and a two-head causal
+    case against a pure-Python walk over the block boundaries."""
+    from tests.test_oracle_masks import _loop_token_mask
+    import json
+    with open(os.path.join(os.path.dirname(__file__), "golden", "variable_block_example_6x6.json")) as f:
+        gd = json.load(f)
+    rs = np.array([[2, 5, 0, 3], [4, 4, 1, 1]])
+    cs = np.array([[6, 1, 5], [3, 3, 6]])
+    bm = np.random.default_rng(8).random((2, 4, 3)) < 0.6
+    try:
+        ex = mod.variable_block_masks(gd["block_mask_map"], gd["block_row_sz"], gd["block_col_sz"])
+        got = [mod.variable_block_masks(bm, rs, cs, causal=c) for c in (False, True)]
+    except (ValueError, IndexError):
+        return False
+    return (np.array_equal(ex[0], np.array(gd["token_mask"], bool)) and
+            all(np.array_equal(got[c], _loop_token_mask(bm.tolist(), rs.tolist(), cs.tolist(), bool(c)))
+                for c in (0, 1)))
+
+
 PINS = [_pin_brute_force, _pin_equal_scores, _pin_sdpa, _pin_fp8, _pin_merge, _pin_per_head_sdpa, _pin_q2k,
-        _pin_fp8_heads]
+        _pin_fp8_heads, _pin_packed_bits, _pin_element_masks, _pin_variable_blocks]
 
 
 def test_unmutated_copy_passes_every_pin():
