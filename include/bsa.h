@@ -43,7 +43,7 @@ extern "C" {
 #endif
 
 #define BSA_VERSION_MAJOR 0
-#define BSA_VERSION_MINOR 2
+#define BSA_VERSION_MINOR 3
 
 typedef struct bsa_plan_s* bsa_plan_t;
 
@@ -73,7 +73,7 @@ typedef enum {
  *   indices        int32[nnz]; column block of each non-zero block, 0 <= J < NB,
  *                  no duplicate within a row block; any order within a row
  *   M, N           query rows / key rows; N % C == 0
- *   R, C           block rows / block columns, >= 1
+ *   R, C           block rows / block columns, >= 1 (variable blocks: see below)
  *   num_qo_heads   multiple of num_kv_heads (grouped-query attention)
  *   head_dim_qk    q/k head dim; head_dim_vo: v/o head dim (0 = head_dim_qk)
  *   causal         0/1: also mask key j > i + (N - M)
@@ -119,6 +119,38 @@ typedef enum {
  *                  int32[struct_heads][MB] with entries in [0, q2k_topk]
  *   q2k_topk       entries per selection row (>= 0)
  * kv_block_lens, causal, kv_splits and everything else apply as for BSR.
+ *
+ * Element masks inside blocks (BlockSparseAttentionWrapper.plan: mask of
+ * shape (nnz, R, C), packed_mask from flashinfer.quantization.packbits).
+ * BSR form only (not with block_mask / q2k):
+ *   mask           NULL (every block full), or the visibility of each element of
+ *                  each BSR block: row r, column c of the block indices[p] (the
+ *                  p-th entry as given, before any sorting) is entry
+ *                  i = (p*R + r)*C + c; query I*R + r sees key J*C + c iff it is set
+ *   mask_packed    0: uint8[nnz*R*C], nonzero = visible; 1: uint8[ceil(nnz*R*C / 8)],
+ *                  entry i in bit i % 8 (least significant first) of byte i / 8
+ * With a mask the causal flag has no effect (the pages: causal applies only
+ * when no mask is given); kv_block_lens must be NULL (lengths belong in the
+ * mask).  Element masks run on the tile kernel (head_dim 128, fp16/bf16), also
+ * for R = 1 shapes.
+ *
+ * Variable block sizes (VariableBlockSparseAttentionWrapper.plan:
+ * block_mask_map, block_row_sz, block_col_sz; each kv head its own pattern):
+ *   block_row_sz   NULL (fixed R x C blocks), or int32[num_kv_heads][var_row_blocks]:
+ *                  row block a of kv head h covers the block_row_sz[h][a] query
+ *                  rows after those of blocks 0..a-1; entries >= 0, each head's
+ *                  sum equal to M
+ *   block_col_sz   int32[num_kv_heads][var_col_blocks], the same for keys; each
+ *                  head's sum equal to N
+ *   var_row_blocks, var_col_blocks  >= 1
+ *   block_mask     then uint8[num_kv_heads][var_row_blocks][var_col_blocks]
+ *                  (struct_heads must be num_kv_heads; q2k, indptr / indices,
+ *                  mask and kv_block_lens unused and must be NULL where listed)
+ *   R, C           the fixed grid the planner maps the variable blocks onto (each
+ *                  fixed block touched by a set variable block becomes a block
+ *                  with an element mask): 0 = chosen by the planner (C the
+ *                  largest of 64, 32, ..., 1 dividing N; R = max(1, 256 / g))
+ * causal applies on top of the block map (key j <= i + N - M).
  */
 typedef struct {
   const int32_t* indptr;
@@ -140,6 +172,11 @@ typedef struct {
   const int32_t* q2k_indices;
   const int32_t* q2k_num;
   int32_t q2k_topk;
+  const uint8_t* mask;
+  int32_t mask_packed;
+  const int32_t* block_row_sz;
+  const int32_t* block_col_sz;
+  int32_t var_row_blocks, var_col_blocks;
 } bsa_plan_desc_t;
 
 /* Defaults: fp16 everywhere, head_dim_vo = head_dim_qk, non-causal, default
@@ -258,6 +295,8 @@ typedef struct {
   int64_t partial_bytes;   /* split partials after the tables */
   int64_t workspace_bytes;
   int64_t valid_pairs;     /* block-level key positions x query rows, summed over tiles */
+  int32_t R, C;            /* block grid the plan runs on (for variable blocks: the one chosen) */
+  int64_t mask_plane_words; /* words per element-mask bit plane; 0 = no element masks */
 } bsa_plan_info_t;
 
 bsa_status_t bsa_plan_info(bsa_plan_t plan, bsa_plan_info_t* info);
@@ -295,6 +334,14 @@ bsa_status_t bsa_plan_export(bsa_plan_t plan, int32_t* tiles, int32_t* merges, i
  * array.
  */
 bsa_status_t bsa_plan_export_workgroups(bsa_plan_t plan, int32_t* wg_ptr);
+
+/* Copy the element-mask bit planes (R * mask_plane_words uint32 words, see
+ * bsa_plan_info) into host `bits`.  Plane r holds, for entry e of the column
+ * table (bsa_plan_export) and key c < C of that block, whether query row
+ * I*R + r of the entry's row block sees key cols[e]*C + c: bit (e*C + c) % 32
+ * of word (e*C + c) / 32.  BSA_ERR_INVALID_ARGUMENT for a NULL plan or array;
+ * nothing is copied for a plan without element masks. */
+bsa_status_t bsa_plan_export_mask_bits(bsa_plan_t plan, uint32_t* bits);
 
 void bsa_plan_destroy(bsa_plan_t plan);
 

@@ -53,6 +53,12 @@ class PlanDesc(ctypes.Structure):
         ("q2k_indices", _i32p),
         ("q2k_num", _i32p),
         ("q2k_topk", ctypes.c_int32),
+        ("mask", ctypes.POINTER(ctypes.c_uint8)),
+        ("mask_packed", ctypes.c_int32),
+        ("block_row_sz", _i32p),
+        ("block_col_sz", _i32p),
+        ("var_row_blocks", ctypes.c_int32),
+        ("var_col_blocks", ctypes.c_int32),
     ]
 
 
@@ -72,6 +78,9 @@ class PlanInfo(ctypes.Structure):
         ("partial_bytes", ctypes.c_int64),
         ("workspace_bytes", ctypes.c_int64),
         ("valid_pairs", ctypes.c_int64),
+        ("R", ctypes.c_int32),
+        ("C", ctypes.c_int32),
+        ("mask_plane_words", ctypes.c_int64),
     ]
 
 
@@ -113,6 +122,8 @@ def lib() -> ctypes.CDLL:
     L.bsa_plan_export.restype = st
     L.bsa_plan_export_workgroups.argtypes = [vp, _i32p]
     L.bsa_plan_export_workgroups.restype = st
+    L.bsa_plan_export_mask_bits.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32)]
+    L.bsa_plan_export_mask_bits.restype = st
     L.bsa_plan_destroy.argtypes = [vp]
     L.bsa_plan_destroy.restype = None
     L.bsa_last_error.argtypes = []

@@ -45,6 +45,13 @@ class Plan:
     ``block_mask`` (heads, MB, NB) bool, or ``q2k_indices`` (heads, MB, topk)
     int with optional ``q2k_num`` (heads, MB); heads = num_kv_heads or
     num_qo_heads.  indptr / indices are then ignored (may be None).
+
+    Element masks inside blocks (plan(): mask, packed_mask): ``mask`` (nnz, R, C)
+    bool, mask[p] belonging to block indices[p]; or ``packed_mask``, its
+    flattening eight entries a byte, least significant bit first (then
+    ``mask`` is ignored).  With either, ``causal`` has no effect.
+
+    Variable block sizes: use ``Plan.variable``.
     """
 
     def __init__(self, indptr, indices, M: int, N: int, R: int, C: int, num_qo_heads: int,
@@ -55,7 +62,7 @@ class Plan:
                  q_descale: float = 1.0, k_descale: float = 1.0, v_descale: float = 1.0,
                  q_token_stride: int = 0, k_token_stride: int = 0, v_token_stride: int = 0,
                  o_token_stride: int = 0, num_cus: int = 0, block_mask=None, q2k_indices=None,
-                 q2k_num=None):
+                 q2k_num=None, mask=None, packed_mask=None, block_row_sz=None, block_col_sz=None):
         lib = L.lib()
         self._handle = ctypes.c_void_p()
         self._indptr = _i32(np.zeros(1) if indptr is None else indptr)
@@ -64,6 +71,20 @@ class Plan:
         self._q2k = None if q2k_indices is None else _i32(q2k_indices)
         self._q2k_num = None if q2k_num is None else _i32(q2k_num)
         self._lens = None if kv_block_lens is None else _i32(kv_block_lens)
+        if packed_mask is not None:
+            self._emask = np.ascontiguousarray(_np(packed_mask).ravel(), dtype=np.uint8)
+        elif mask is not None:
+            self._emask = np.ascontiguousarray(_np(mask).astype(bool), dtype=np.uint8)
+            if self._emask.shape != (int(self._indptr[-1]), int(R), int(C)):
+                raise ValueError(f"mask must have shape (nnz, R, C) = ({int(self._indptr[-1])}, {int(R)}, {int(C)})")
+        else:
+            self._emask = None
+        if self._emask is not None and packed_mask is not None:
+            nbits = int(self._indptr[-1]) * int(R) * int(C)
+            if self._emask.size < -(-nbits // 8):
+                raise ValueError(f"packed_mask needs {-(-nbits // 8)} bytes for nnz * R * C = {nbits} entries")
+        self._row_sz = None if block_row_sz is None else _i32(block_row_sz)
+        self._col_sz = None if block_col_sz is None else _i32(block_col_sz)
         kv_dtype = q_dtype if kv_dtype is None else kv_dtype
         o_dtype = q_dtype if o_dtype is None else o_dtype
         for t in (q_dtype, kv_dtype, o_dtype):
@@ -103,14 +124,40 @@ class Plan:
                 if self._q2k_num.shape != self._q2k.shape[:2]:
                     raise ValueError("q2k_num must have shape (heads, MB)")
                 d.q2k_num = _ptr(self._q2k_num)
+        if self._emask is not None:
+            if self._emask.size == 0:  # nnz = 0: a valid pointer that is never read
+                self._emask = np.zeros(1, np.uint8)
+            d.mask = self._emask.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+            d.mask_packed = int(packed_mask is not None)
+        if self._row_sz is not None or self._col_sz is not None:
+            if self._row_sz is None or self._col_sz is None or self._row_sz.ndim != 2 or self._col_sz.ndim != 2:
+                raise ValueError("block_row_sz (heads, MB) and block_col_sz (heads, NB) go together")
+            d.block_row_sz, d.block_col_sz = _ptr(self._row_sz), _ptr(self._col_sz)
+            d.var_row_blocks, d.var_col_blocks = int(self._row_sz.shape[1]), int(self._col_sz.shape[1])
         L.check(lib.bsa_plan_ex(ctypes.byref(d), ctypes.byref(self._handle)))
-        self.M, self.N, self.R, self.C = int(M), int(N), int(R), int(C)
+        inf = self.info()
+        self.M, self.N, self.R, self.C = int(M), int(N), int(inf["R"]), int(inf["C"])
         self.num_qo_heads, self.num_kv_heads = int(num_qo_heads), int(num_kv_heads)
         self.head_dim, self.head_dim_vo = int(head_dim), int(d.head_dim_vo)
         self.q_dtype, self.kv_dtype, self.o_dtype = q_dtype, kv_dtype, o_dtype
         self.k_token_stride = int(k_token_stride) or self.num_kv_heads * self.head_dim
         self.v_token_stride = int(v_token_stride) or self.num_kv_heads * self.head_dim_vo
         self._workspace: Optional[torch.Tensor] = None
+
+    @classmethod
+    def variable(cls, block_mask_map, block_row_sz, block_col_sz, num_qo_heads: int, num_kv_heads: int,
+                 head_dim: int, *, R: int = 0, C: int = 0, **kw) -> "Plan":
+        """Variable block sizes (VariableBlockSparseAttentionWrapper.plan): block_mask_map
+        (num_kv_heads, MB, NB) bool, block_row_sz (num_kv_heads, MB) and block_col_sz
+        (num_kv_heads, NB) int, each head's sizes summing to the query / key counts.
+        q, k, v, o keep the token-major (tokens, heads, dim) layout of run().  R, C:
+        the fixed grid the library maps the blocks onto (0 = its choice); other keyword
+        arguments as for Plan."""
+        rs, cs = _i32(block_row_sz), _i32(block_col_sz)
+        if rs.ndim != 2 or cs.ndim != 2 or rs.shape[0] < 1:
+            raise ValueError("block_row_sz must be (heads, MB) and block_col_sz (heads, NB)")
+        return cls(None, None, int(rs[0].sum()), int(cs[0].sum()), R, C, num_qo_heads, num_kv_heads, head_dim,
+                   block_mask=block_mask_map, block_row_sz=rs, block_col_sz=cs, **kw)
 
     # ------------------------------------------------------------------ info
     def info(self) -> dict:
@@ -131,7 +178,13 @@ class Plan:
         wg_ptr = np.zeros(inf["num_workgroups"] + 1, np.int32)
         L.check(L.lib().bsa_plan_export(self._handle, _ptr(tiles), _ptr(merges), _ptr(cols)))
         L.check(L.lib().bsa_plan_export_workgroups(self._handle, _ptr(wg_ptr)))
-        return {"tiles": tiles, "merges": merges, "cols": cols, "wg_ptr": wg_ptr}
+        out = {"tiles": tiles, "merges": merges, "cols": cols, "wg_ptr": wg_ptr}
+        if inf["mask_plane_words"] > 0:
+            bits = np.zeros((inf["R"], inf["mask_plane_words"]), np.uint32)
+            L.check(L.lib().bsa_plan_export_mask_bits(self._handle,
+                                                      bits.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32))))
+            out["mask_bits"] = bits
+        return out
 
     # ------------------------------------------------------------------ run
     def workspace(self, device=None) -> torch.Tensor:

@@ -233,6 +233,8 @@ bsa_status_t bsa_run_ex(bsa_plan_t plan, int32_t phase, const void* q, const voi
   a.num_tiles = static_cast<int32_t>(P.tiles.size() / bsa::kTileInts);
   a.num_wgs = static_cast<int32_t>(P.wg_ptr.size()) - 1;
   a.heads_per_wg = P.heads_per_wg;
+  a.mbits = P.mbits.empty() ? nullptr : reinterpret_cast<const uint32_t*>(ws + P.off_mbits);
+  a.mask_plane_words = P.mask_plane_words;
   a.q_scale = scale_q;
   a.k_scale = scale_k;
   a.v_scale = scale_v;
@@ -243,7 +245,8 @@ bsa_status_t bsa_run_ex(bsa_plan_t plan, int32_t phase, const void* q, const voi
     else if (P.kernel == BSA_KERNEL_DECODE)
       e = bsa::launch_attn_decode(a, d.q_dtype == BSA_BF16, d.kv_dtype == BSA_FP8_E4M3, d.causal != 0,
                                   a.lens != nullptr, st);
-    else e = bsa::launch_attn_tile(a, d.q_dtype == BSA_BF16, P.tile_rows, d.causal != 0, a.lens != nullptr, st);
+    else e = bsa::launch_attn_tile(a, d.q_dtype == BSA_BF16, P.tile_rows, d.causal != 0, a.lens != nullptr,
+                                   a.mbits != nullptr, st);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   }
   if (!(phase & BSA_PHASE_MERGE)) return BSA_OK;
@@ -300,6 +303,17 @@ bsa_status_t bsa_plan_info(bsa_plan_t plan, bsa_plan_info_t* info) {
   info->partial_bytes = P.partial_bytes;
   info->workspace_bytes = P.workspace_bytes;
   info->valid_pairs = P.valid_pairs;
+  info->R = P.d.R;
+  info->C = P.d.C;
+  info->mask_plane_words = P.mask_plane_words;
+  return BSA_OK;
+}
+
+bsa_status_t bsa_plan_export_mask_bits(bsa_plan_t plan, uint32_t* bits) {
+  g_err.clear();
+  if (!plan || !bits) return set_err(BSA_ERR_INVALID_ARGUMENT, "plan and bits must be non-NULL");
+  const bsa::Plan& P = plan->p;
+  if (!P.mbits.empty()) std::memcpy(bits, P.mbits.data(), P.mbits.size() * 4);
   return BSA_OK;
 }
 

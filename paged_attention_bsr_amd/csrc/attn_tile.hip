@@ -24,6 +24,10 @@
 //     up with the transposed V fragments below;
 //   * causal / valid-length masking runs only on tiles that need it, and a
 //     wave skips tiles that lie wholly above its causal diagonal;
+//   * element masks inside blocks (MASK): the planner's bit planes hold, per
+//     row offset in the row block, one bit per key position of the column
+//     list; each lane loads the KT + 32 bits around its tile from its row's
+//     plane (a funnel shift aligns them) and ANDs them into the score mask;
 //   * online softmax in the log2 domain (scale folded into one FMA); the
 //     running max only moves when a tile exceeds it by more than 2^8, so
 //     the rescale of O is rare (probabilities stay below 256);
@@ -69,7 +73,7 @@ __device__ __forceinline__ int v_off(int key, int c) { return key * 256 + ((c ^ 
 // S^T row m of a 32-key block holds key swap23(m) (bits 2 and 3 exchanged).
 __device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-template <typename T, int NW, int KT, bool CAUSAL, bool LENS, bool BLOCKTILE>
+template <typename T, int NW, int KT, bool CAUSAL, bool LENS, bool BLOCKTILE, bool MASK>
 __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   using Ops = MfmaType<T>;
   using v8 = typename Ops::v8;
@@ -204,12 +208,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     }
   };
 
+  // this lane's element-mask plane (row offset inside the row block; rows past
+  // the tile read plane 0 and are never stored)
+  const uint32_t* mplane = nullptr;
+  if (MASK) mplane = a.mbits + static_cast<int64_t>(row_ok ? qtok - I * a.R : 0) * a.mask_plane_words;
+  constexpr int NMW = KT / 32 + 1;  // words covering a tile at any bit offset
+
   // Full blocks that each hold whole key tiles (BLOCKTILE without lengths):
   // every key of a tile is valid and its tokens are consecutive, so the DMA
   // needs one scalar base per tile plus per-lane byte offsets fixed for the
   // whole loop, blocks advance without a division, and masks follow from the
   // tile's first token (no token array).
-  constexpr bool FAST = BLOCKTILE && !LENS;
+  constexpr bool FAST = BLOCKTILE && !LENS && !MASK;
   uint32_t koff[BPW], voff[BPW];
   if (FAST) {
     const int u = lane & 15;
@@ -281,8 +291,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   float l_run = 0.f;
   const float sl2 = a.scale_log2;
 
-  // causal / length mask of S (only on tiles that need it)
-  auto mask_scores = [&](bool need_mask, const int* ktok, f32x16 (&sacc)[NKB]) {
+  // causal / length mask of S (only on tiles that need it), and the element
+  // mask: bits mw[0..NMW) of this row's plane start at bit `sh` of mw[0]
+  auto mask_scores = [&](bool need_mask, const int* ktok, const uint32_t (&mw)[NMW], int sh,
+                         f32x16 (&sacc)[NKB]) {
     if (!need_mask) return;
     // value 4*g4 + e of this lane is S^T row 8*g4 + 4*half + e, i.e. key
     // 16*(g4/2) + 8*half + 4*(g4%2) + e of the block
@@ -295,6 +307,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
                                 static_cast<uint32_t>(tk.z), static_cast<uint32_t>(tk.w)};
 #pragma unroll
         for (int e = 0; e < 4; ++e) sacc[kb][g4 * 4 + e] = tt[e] < qbound ? sacc[kb][g4 * 4 + e] : -INFINITY;
+      }
+      if (MASK) {
+        // the 32 keys of block kb; this lane's keys sit 8*half further up
+        const uint64_t pair = (static_cast<uint64_t>(mw[kb + 1]) << 32) | mw[kb];
+        const uint32_t w = static_cast<uint32_t>(pair >> sh) >> (8 * half);
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int b = 16 * (g4 >> 1) + 4 * (g4 & 1) + e;
+            sacc[kb][g4 * 4 + e] = (w >> b) & 1u ? sacc[kb][g4 * 4 + e] : -INFINITY;
+          }
       }
     }
   };
@@ -398,12 +422,26 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     // drain (both share one counter)
     int64_t lo = 0, hi = 0;
     if (CAUSAL) tile_tok_range(t, lo, hi);
+    // this tile's mask words, loaded ahead of the next tile's DMA so that
+    // waiting for them does not wait for that DMA
+    uint32_t mw[NMW];
+    int sh = 0;
+    if (MASK) {
+      const int64_t p0 = static_cast<int64_t>(cb) * C + static_cast<int64_t>(t) * KT;
+      const uint32_t* src = mplane + (p0 >> 5);
+      sh = static_cast<int>(p0 & 31);
+#pragma unroll
+      for (int i = 0; i < NMW; ++i) mw[i] = src[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NMW; ++i) mw[i] = 0u;
+    }
     if (t + 1 < ntiles) dma_tile(t + 1, nxt, nxttok);
     if (!wave_active || (CAUSAL && lo > wave_lim)) return;  // tile above this wave's diagonal
-    const bool need_mask = LENS || (t * KT + KT > npos) || (CAUSAL && hi > wave_lim_lo);
+    const bool need_mask = MASK || LENS || (t * KT + KT > npos) || (CAUSAL && hi > wave_lim_lo);
     f32x16 sc[NKB];
     qk(cur, sc);
-    mask_scores(need_mask, curtok, sc);
+    mask_scores(need_mask, curtok, mw, sh, sc);
     bool upd;
     const float alpha = softmax_core(sc, true, upd);
     if (__ballot(upd) != 0) {
@@ -480,31 +518,41 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
 }
 
 template <typename T, int NW, int KT>
-hipError_t launch_variant(const AttnArgs& a, bool causal, bool lens, hipStream_t st) {
+hipError_t launch_variant(const AttnArgs& a, bool causal, bool lens, bool mask, hipStream_t st) {
   const dim3 grid(a.num_tiles), block(NW * 64);
   // block tiles also need every row offset of a tile (KT rows) to fit 31 bits
   const int64_t max_stride = a.k_stride > a.v_stride ? a.k_stride : a.v_stride;
   const bool bt = a.C % KT == 0 && static_cast<int64_t>(KT) * 2 * max_stride < (int64_t{1} << 31);
+  // element masks come without block lengths (the planner folds neither in)
+  if (mask && (lens || !a.mbits || a.mask_plane_words < 1)) return hipErrorInvalidValue;
 #define BSA_TILE_LAUNCH(CA, LE)                                                              \
-  if (bt) attn_tile_kernel<T, NW, KT, CA, LE, true><<<grid, block, 0, st>>>(a);              \
-  else attn_tile_kernel<T, NW, KT, CA, LE, false><<<grid, block, 0, st>>>(a);
-  if (causal) {
+  if (bt) attn_tile_kernel<T, NW, KT, CA, LE, true, false><<<grid, block, 0, st>>>(a);       \
+  else attn_tile_kernel<T, NW, KT, CA, LE, false, false><<<grid, block, 0, st>>>(a);
+#define BSA_TILE_LAUNCH_MASK(CA)                                                             \
+  if (bt) attn_tile_kernel<T, NW, KT, CA, false, true, true><<<grid, block, 0, st>>>(a);     \
+  else attn_tile_kernel<T, NW, KT, CA, false, false, true><<<grid, block, 0, st>>>(a);
+  if (mask) {
+    // masked plans run 64-key tiles (the mask words of 128-key ones spill)
+    if constexpr (KT == 128) return hipErrorInvalidValue;
+    else if (causal) { BSA_TILE_LAUNCH_MASK(true) } else { BSA_TILE_LAUNCH_MASK(false) }
+  } else if (causal) {
     if (lens) { BSA_TILE_LAUNCH(true, true) } else { BSA_TILE_LAUNCH(true, false) }
   } else {
     if (lens) { BSA_TILE_LAUNCH(false, true) } else { BSA_TILE_LAUNCH(false, false) }
   }
 #undef BSA_TILE_LAUNCH
+#undef BSA_TILE_LAUNCH_MASK
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_typed(const AttnArgs& a, int tile_rows, bool causal, bool lens, hipStream_t st) {
+hipError_t launch_typed(const AttnArgs& a, int tile_rows, bool causal, bool lens, bool mask, hipStream_t st) {
   switch (tile_rows) {
-    case 32: return launch_variant<T, 1, 32>(a, causal, lens, st);
-    case 128: return launch_variant<T, 4, 64>(a, causal, lens, st);
+    case 32: return launch_variant<T, 1, 32>(a, causal, lens, mask, st);
+    case 128: return launch_variant<T, 4, 64>(a, causal, lens, mask, st);
     // 128-key tiles (two 64 KB LDS stages) when every tile lies in one block
-    case 256: return a.C % 128 == 0 ? launch_variant<T, 8, 128>(a, causal, lens, st)
-                                     : launch_variant<T, 8, 64>(a, causal, lens, st);
+    case 256: return a.C % 128 == 0 && !mask ? launch_variant<T, 8, 128>(a, causal, lens, mask, st)
+                                     : launch_variant<T, 8, 64>(a, causal, lens, mask, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -512,10 +560,10 @@ hipError_t launch_typed(const AttnArgs& a, int tile_rows, bool causal, bool lens
 }  // namespace
 
 hipError_t launch_attn_tile(const AttnArgs& a, bool bf16, int tile_rows, bool causal, bool has_lens,
-                            hipStream_t stream) {
+                            bool has_mask, hipStream_t stream) {
   if (a.num_tiles == 0) return hipSuccess;
-  return bf16 ? launch_typed<__bf16>(a, tile_rows, causal, has_lens, stream)
-              : launch_typed<_Float16>(a, tile_rows, causal, has_lens, stream);
+  return bf16 ? launch_typed<__bf16>(a, tile_rows, causal, has_lens, has_mask, stream)
+              : launch_typed<_Float16>(a, tile_rows, causal, has_lens, has_mask, stream);
 }
 
 }  // namespace bsa

@@ -33,6 +33,10 @@ struct AttnArgs {
   const float* q_scale;
   const float* k_scale;
   const float* v_scale;
+  // element-mask bit planes (tile kernel): plane r, bit e*C + c = row r of
+  // column-list entry e's row block sees key c of that block; null = none
+  const uint32_t* mbits;
+  int64_t mask_plane_words;
 };
 
 struct MergeArgs {
@@ -48,7 +52,7 @@ struct MergeArgs {
 // Generic MFMA tile kernel, head_dim 128, fp16 or bf16 storage.
 // tile_rows in {32, 128, 256}.
 hipError_t launch_attn_tile(const AttnArgs& a, bool bf16, int tile_rows, bool causal, bool has_lens,
-                            hipStream_t stream);
+                            bool has_mask, hipStream_t stream);
 
 // Paged-decode kernel: R = 1, C >= 16, head_dim 128, q/o fp16 or bf16, K/V in
 // the same type or fp8 e4m3 (kv8), g <= 16; workgroup w runs the tile groups

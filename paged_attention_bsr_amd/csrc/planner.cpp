@@ -42,6 +42,14 @@
 //     to the workgroup of its position (at most W - 1); a unit's maximal runs
 //     of blocks with one workgroup are its pieces, emitted in order, which is
 //     workgroup order.
+//  Element masks (mask of the BSR blocks, or variable block sizes mapped onto
+//     a fixed R x C grid): the structure and the partition are those of the
+//     blocks; the masks become bit planes over the column lists (Plan::mbits)
+//     that the tile kernel ANDs into each key tile.  A mask of the BSR form
+//     follows its block through the sort of step 1 and turns the causal flag
+//     off; a variable-block map first marks every fixed block that a set
+//     variable block touches (a per-kv-head block mask), and each bit of such
+//     a block is then looked up through the token -> variable block maps.
 // Kernel choice: sparse-MLA shape -> MLA kernel (64-row tiles); R = 1 with
 // g <= 16 and C >= 16 -> decode kernel (16-row tiles, i.e. one per unit);
 // otherwise the generic tile kernel with 32, 128 or 256-row tiles for units
@@ -72,9 +80,18 @@ bsa_status_t fail(std::string& err, bsa_status_t st, const std::string& msg) {
   return st;
 }
 
-}  // namespace
+// Where element visibility inside blocks comes from.
+struct MaskSrc {
+  int kind = 0;                    // 0: whole blocks; 1: masks of the BSR blocks; 2: variable blocks
+  const uint8_t* mask = nullptr;   // kind 1: entry (p*R + r)*C + c of BSR block p
+  bool packed = false;             // kind 1: eight entries a byte, least significant bit first
+  const uint8_t* vmap = nullptr;   // kind 2: [kv head][var row block][var col block]
+  int64_t vmb = 0, vnb = 0;
+  std::vector<std::vector<int32_t>> row_block, col_block;  // kind 2: per kv head, token -> variable block
+};
 
-bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, std::string& err) {
+bsa_status_t build_plan_impl(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, std::string& err,
+                             const MaskSrc& ms) {
   const bsa_plan_desc_t& d = desc;
   // ---- validation of sizes and structure (plan() parameter contract)
   if (d.R < 1 || d.C < 1) return fail(err, BSA_ERR_INVALID_ARGUMENT, "R and C must be >= 1");
@@ -176,6 +193,9 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
         return fail(err, BSA_ERR_INVALID_ARGUMENT, "kv_block_lens entries must lie in [1, C]");
   }
 
+  // a mask given per element replaces the causal flag
+  const bool causal = d.causal && ms.kind != 1;
+
   // ---- kernel selection (supported dtype / head_dim sets)
   const int32_t g = d.num_qo_heads / d.num_kv_heads;
   int32_t kernel, tile_rows, key_tile;
@@ -203,7 +223,7 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
       return fail(err, BSA_ERR_UNSUPPORTED,
                   "fp8 e4m3 KV with head_dim 128 is supported for decode shapes (R = 1, C >= 16, at most 16 qo "
                   "heads per kv head)");
-    if (d.R == 1 && g <= 16 && d.C >= 16) {
+    if (d.R == 1 && g <= 16 && d.C >= 16 && ms.kind == 0) {
       kernel = BSA_KERNEL_DECODE;
       tile_rows = 16;
       key_tile = 32;
@@ -227,7 +247,9 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
   P.d = d;
   // the host arrays are read during planning only
   P.d.indptr = P.d.indices = P.d.kv_block_lens = P.d.q2k_indices = P.d.q2k_num = nullptr;
-  P.d.block_mask = nullptr;
+  P.d.block_mask = P.d.mask = nullptr;
+  P.d.block_row_sz = P.d.block_col_sz = nullptr;
+  P.d.causal = causal;
   P.MB = MB;
   P.NB = NB;
   P.group = g;
@@ -243,17 +265,22 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
 
   // ---- 1. sorted, causally trimmed column lists
   // (per structure head, then per row block: list hs * MB + I)
+  // (csrc: the sidx position each entry came from, for masks of the BSR blocks)
   std::vector<int64_t> bptr(static_cast<size_t>(HS * MB + 1), 0);
+  std::vector<int64_t> csrc, ord;
   P.cols.clear();
   P.cols.reserve(static_cast<size_t>(nnz));
   for (int64_t u = 0; u < HS * MB; ++u) {
     const int64_t I = u % MB;
-    std::vector<int32_t> row(sidx.begin() + sptr[u], sidx.begin() + sptr[u + 1]);
-    std::sort(row.begin(), row.end());
+    ord.resize(static_cast<size_t>(sptr[u + 1] - sptr[u]));
+    std::iota(ord.begin(), ord.end(), sptr[u]);
+    std::sort(ord.begin(), ord.end(), [&](int64_t x, int64_t y) { return sidx[x] < sidx[y]; });
     const int64_t last_tok = std::min<int64_t>(d.M, (I + 1) * d.R) - 1;
-    for (int32_t J : row) {
-      if (d.causal && static_cast<int64_t>(J) * d.C > last_tok + off) break;
+    for (int64_t x : ord) {
+      const int32_t J = sidx[x];
+      if (causal && static_cast<int64_t>(J) * d.C > last_tok + off) break;
       P.cols.push_back(J);
+      if (ms.kind == 1) csrc.push_back(x);
     }
     bptr[u + 1] = static_cast<int64_t>(P.cols.size());
   }
@@ -263,6 +290,39 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
   if (d.kv_block_lens) {
     P.lens.resize(P.cols.size());
     for (size_t p = 0; p < P.cols.size(); ++p) P.lens[p] = d.kv_block_lens[P.cols[p]];
+  }
+  // element-mask bit planes (layout in planner.h)
+  P.mbits.clear();
+  P.mask_plane_words = 0;
+  if (ms.kind != 0) {
+    const int64_t W = ceil_div(static_cast<int64_t>(P.cols.size()) * d.C, 32) + 8;
+    if (static_cast<int64_t>(d.R) * W > (int64_t{1} << 29))
+      return fail(err, BSA_ERR_UNSUPPORTED, "element-mask bit planes would exceed 2 GiB");
+    P.mask_plane_words = W;
+    P.mbits.assign(static_cast<size_t>(d.R * W), 0u);
+    for (int64_t u = 0; u < HS * MB; ++u) {
+      const int64_t I = u % MB, hs = u / MB;
+      const int64_t rows_I = std::min<int64_t>(d.R, d.M - I * d.R);
+      for (int64_t e = bptr[u]; e < bptr[u + 1]; ++e) {
+        const int64_t J = P.cols[e];
+        for (int64_t r = 0; r < rows_I; ++r) {
+          uint32_t* plane = P.mbits.data() + r * W;
+          const uint8_t* vrow =
+              ms.kind == 2 ? ms.vmap + (hs * ms.vmb + ms.row_block[hs][I * d.R + r]) * ms.vnb : nullptr;
+          for (int64_t c = 0; c < d.C; ++c) {
+            bool bit;
+            if (ms.kind == 1) {
+              const int64_t i = (csrc[e] * d.R + r) * d.C + c;
+              bit = ms.packed ? ((ms.mask[i >> 3] >> (i & 7)) & 1) != 0 : ms.mask[i] != 0;
+            } else {
+              bit = vrow[ms.col_block[hs][J * d.C + c]] != 0;
+            }
+            const int64_t pos = e * d.C + c;
+            if (bit) plane[pos >> 5] |= 1u << (pos & 31);
+          }
+        }
+      }
+    }
   }
 
   // ---- 2./3. row tiles with their (prefix) column ranges and work
@@ -279,7 +339,7 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
     for (int64_t r0 = 0; r0 < U; r0 += tile_rows) {
       const int64_t nr = std::min<int64_t>(tile_rows, U - r0);
       int64_t n = bptr[u + 1] - bptr[u];
-      if (d.causal) {
+      if (causal) {
         const int64_t lim = I * d.R + (r0 + nr - 1) / g + off;
         int64_t k = 0;
         while (k < n && static_cast<int64_t>(P.cols[bptr[u] + k]) * d.C <= lim) ++k;
@@ -440,7 +500,7 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
   P.max_splits = max_s;
   P.partial_floats = part;
 
-  // ---- workspace layout: [tiles | merges | cols | lens | wg_ptr | zero row] then partials
+  // ---- workspace layout: [tiles | merges | cols | lens | wg_ptr | zero row | mask bits] then partials
   int64_t o = 0;
   P.off_tiles = o;
   o = round_up(o + (int64_t)P.tiles.size() * 4, 256);
@@ -454,6 +514,8 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
   o = round_up(o + (int64_t)P.wg_ptr.size() * 4, 256);
   P.off_zero = o;  // zero row: masked keys load from here
   o = round_up(o + 1024, 256);
+  P.off_mbits = o;
+  o = round_up(o + (int64_t)P.mbits.size() * 4, 256);
   P.table_bytes = std::max<int64_t>(o, 256);
   P.partial_bytes = round_up(P.partial_floats * 4, 256);
   P.workspace_bytes = P.table_bytes + P.partial_bytes;
@@ -468,7 +530,114 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
   put(P.off_cols, P.cols);
   put(P.off_lens, P.lens);
   put(P.off_wg, P.wg_ptr);
+  if (!P.mbits.empty())
+    std::copy(reinterpret_cast<const uint8_t*>(P.mbits.data()),
+              reinterpret_cast<const uint8_t*>(P.mbits.data()) + P.mbits.size() * 4, P.table_blob.begin() + P.off_mbits);
   return BSA_OK;
+}
+
+}  // namespace
+
+bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, std::string& err) {
+  const bool var = desc.block_row_sz || desc.block_col_sz;
+  MaskSrc ms;
+  if (!desc.mask && !var) return build_plan_impl(desc, num_cus, P, err, ms);
+  if (desc.kv_dtype == BSA_FP8_E4M3 || desc.head_dim_qk != 128 || desc.head_dim_vo != 128)
+    return fail(err, BSA_ERR_UNSUPPORTED,
+                "element masks and variable block sizes are supported for head_dim 128 with fp16 or bf16 storage");
+  if (desc.kv_block_lens)
+    return fail(err, BSA_ERR_INVALID_ARGUMENT,
+                "kv_block_lens must be NULL with element masks or variable block sizes (lengths belong in the mask)");
+  if (desc.mask && var)
+    return fail(err, BSA_ERR_INVALID_ARGUMENT, "mask applies to fixed-size BSR blocks, not to variable block sizes");
+  if (desc.mask) {
+    if (desc.block_mask || desc.q2k_indices)
+      return fail(err, BSA_ERR_INVALID_ARGUMENT,
+                  "element masks apply to the BSR form (indptr / indices), not to block_mask or q2k selections");
+    if (desc.mask_packed != 0 && desc.mask_packed != 1)
+      return fail(err, BSA_ERR_INVALID_ARGUMENT, "mask_packed must be 0 or 1");
+    ms.kind = 1;
+    ms.mask = desc.mask;
+    ms.packed = desc.mask_packed != 0;
+    return build_plan_impl(desc, num_cus, P, err, ms);
+  }
+  // ---- variable block sizes -> per-kv-head fixed blocks with element masks
+  if (!desc.block_row_sz || !desc.block_col_sz || !desc.block_mask)
+    return fail(err, BSA_ERR_INVALID_ARGUMENT, "variable block sizes need block_row_sz, block_col_sz and block_mask");
+  if (desc.q2k_indices)
+    return fail(err, BSA_ERR_INVALID_ARGUMENT, "q2k selections do not combine with variable block sizes");
+  if (desc.num_kv_heads < 1 || desc.num_qo_heads < 1 || desc.num_qo_heads % desc.num_kv_heads != 0)
+    return fail(err, BSA_ERR_INVALID_ARGUMENT, "num_qo_heads must be a positive multiple of num_kv_heads");
+  if (desc.struct_heads != desc.num_kv_heads)
+    return fail(err, BSA_ERR_INVALID_ARGUMENT,
+                "variable block sizes take one pattern per kv head (struct_heads = num_kv_heads)");
+  if (desc.var_row_blocks < 1 || desc.var_col_blocks < 1)
+    return fail(err, BSA_ERR_INVALID_ARGUMENT, "var_row_blocks and var_col_blocks must be >= 1");
+  if (desc.M < 0 || desc.N < 0 || desc.M > INT32_MAX || desc.N > INT32_MAX)
+    return fail(err, BSA_ERR_INVALID_ARGUMENT, "M and N must lie in [0, 2^31)");
+  if (desc.R < 0 || desc.C < 0) return fail(err, BSA_ERR_INVALID_ARGUMENT, "R and C must be >= 0");
+  const int64_t H = desc.num_kv_heads, VMB = desc.var_row_blocks, VNB = desc.var_col_blocks;
+  for (int64_t h = 0; h < H; ++h) {
+    int64_t sr = 0, sc = 0;
+    for (int64_t a = 0; a < VMB; ++a) {
+      if (desc.block_row_sz[h * VMB + a] < 0) return fail(err, BSA_ERR_INVALID_ARGUMENT, "block sizes must be >= 0");
+      sr += desc.block_row_sz[h * VMB + a];
+    }
+    for (int64_t b = 0; b < VNB; ++b) {
+      if (desc.block_col_sz[h * VNB + b] < 0) return fail(err, BSA_ERR_INVALID_ARGUMENT, "block sizes must be >= 0");
+      sc += desc.block_col_sz[h * VNB + b];
+    }
+    if (sr != desc.M || sc != desc.N)
+      return fail(err, BSA_ERR_INVALID_ARGUMENT,
+                  "every kv head's block_row_sz must sum to M and its block_col_sz to N");
+  }
+  const int64_t g = desc.num_qo_heads / desc.num_kv_heads;
+  int32_t C = desc.C;
+  if (C == 0) {
+    C = 64;
+    while (C > 1 && desc.N % C != 0) C /= 2;
+  }
+  const int32_t R = desc.R > 0 ? desc.R : static_cast<int32_t>(std::max<int64_t>(1, 256 / g));
+  if (desc.N % C != 0) return fail(err, BSA_ERR_INVALID_ARGUMENT, "N must be divisible by C");
+  const int64_t MB = ceil_div(desc.M, R), NB = desc.N / C;
+  ms.kind = 2;
+  ms.vmap = desc.block_mask;
+  ms.vmb = VMB;
+  ms.vnb = VNB;
+  ms.row_block.assign(static_cast<size_t>(H), {});
+  ms.col_block.assign(static_cast<size_t>(H), {});
+  std::vector<uint8_t> fixed(static_cast<size_t>(H * MB * NB), 0);
+  std::vector<int64_t> c0(static_cast<size_t>(VNB + 1));
+  for (int64_t h = 0; h < H; ++h) {
+    auto& rb = ms.row_block[h];
+    auto& cbk = ms.col_block[h];
+    rb.reserve(static_cast<size_t>(desc.M));
+    cbk.reserve(static_cast<size_t>(desc.N));
+    for (int64_t a = 0; a < VMB; ++a) rb.insert(rb.end(), desc.block_row_sz[h * VMB + a], static_cast<int32_t>(a));
+    c0[0] = 0;
+    for (int64_t b = 0; b < VNB; ++b) {
+      cbk.insert(cbk.end(), desc.block_col_sz[h * VNB + b], static_cast<int32_t>(b));
+      c0[b + 1] = c0[b] + desc.block_col_sz[h * VNB + b];
+    }
+    int64_t r0 = 0;
+    for (int64_t a = 0; a < VMB; ++a) {
+      const int64_t r1 = r0 + desc.block_row_sz[h * VMB + a];
+      for (int64_t b = 0; r1 > r0 && b < VNB; ++b) {
+        if (!desc.block_mask[(h * VMB + a) * VNB + b] || c0[b + 1] == c0[b]) continue;
+        for (int64_t I = r0 / R; I <= (r1 - 1) / R; ++I)
+          for (int64_t J = c0[b] / C; J <= (c0[b + 1] - 1) / C; ++J) fixed[(h * MB + I) * NB + J] = 1;
+      }
+      r0 = r1;
+    }
+  }
+  bsa_plan_desc_t dl = desc;
+  dl.R = R;
+  dl.C = C;
+  dl.indptr = dl.indices = nullptr;
+  dl.block_mask = fixed.data();
+  dl.struct_heads = desc.num_kv_heads;
+  dl.block_row_sz = dl.block_col_sz = nullptr;
+  return build_plan_impl(dl, num_cus, P, err, ms);
 }
 
 }  // namespace bsa

@@ -67,12 +67,19 @@ struct Plan {
   std::vector<int32_t> cols;     // column blocks per row block, ascending, causally trimmed
   std::vector<int32_t> lens;     // valid length of each cols entry, empty when every block is full
   std::vector<int32_t> wg_ptr;   // workgroup w runs tiles wg_ptr[w] .. wg_ptr[w+1]-1, in order
+  // Element-mask bit planes (element masks or variable blocks; empty otherwise):
+  // plane r (r < R) holds, for column-list entry e and key c < C of its block,
+  // the visibility of query row I*R + r (I = the entry's row block) at bit
+  // e*C + c: word (e*C + c) / 32, bit (e*C + c) % 32.  mask_plane_words words
+  // per plane, padded so that a key tile read past a list's end stays inside.
+  std::vector<uint32_t> mbits;
+  int64_t mask_plane_words = 0;
   int32_t max_splits = 1;
   int32_t heads_per_wg = 1;      // kv heads per tile group (decode kernel: one workgroup)
   int64_t partial_floats = 0;
   int64_t valid_pairs = 0;
   // workspace layout (bytes)
-  int64_t off_tiles = 0, off_merges = 0, off_cols = 0, off_lens = 0, off_wg = 0, off_zero = 0;
+  int64_t off_tiles = 0, off_merges = 0, off_cols = 0, off_lens = 0, off_wg = 0, off_zero = 0, off_mbits = 0;
   int64_t table_bytes = 0, partial_bytes = 0, workspace_bytes = 0;
   std::vector<uint8_t> table_blob;  // exact image of the table region
   uint64_t id = 0;                  // process-unique plan id

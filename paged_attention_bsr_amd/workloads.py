@@ -244,6 +244,107 @@ def head_sparse_prefill(seed: int = 6, M: int = 8192, block: int = 64, density: 
     return w
 
 
+def element_mask_prefill(seed: int = 8, M: int = 8192, block: int = 64, density: float = 0.10,
+                         keep: float = 0.75, num_qo_heads: int = 32, num_kv_heads: int = 8,
+                         head_dim: int = 128, dtype: torch.dtype = torch.float16,
+                         values: bool = True) -> Workload:
+    """bsr_prefill's block pattern (all diagonal blocks plus i.i.d. Bernoulli(density)
+    strictly-lower blocks, each row's blocks in random order) with an element mask in
+    every block: each (query, key) entry kept i.i.d. with probability ``keep``; the
+    diagonal blocks keep only entries with key <= query and always the key equal to
+    the query, so every row sees a key.  Not causal (the masks take its place).
+
+    ``meta["mask"]``: (nnz, R, C) bool, mask[p] for block indices[p];
+    ``meta["packed_mask"]``: its flattening packed eight entries a byte, least
+    significant bit first.
+    """
+    rng = np.random.default_rng(seed)
+    MB = M // block
+    rows = []
+    for i in range(MB):
+        lower = np.nonzero(rng.random(i) < density)[0]
+        rows.append(rng.permutation(np.concatenate([lower, [i]]).astype(np.int64)))
+    indptr, indices = _csr_from_rows(rows)
+    mask = rng.random((int(indptr[-1]), block, block)) < keep
+    tri = np.tril(np.ones((block, block), bool))
+    for I in range(MB):
+        for p in range(indptr[I], indptr[I + 1]):
+            if indices[p] == I:
+                mask[p] &= tri
+                mask[p][np.arange(block), np.arange(block)] = True
+    w = Workload("element_mask_prefill", indptr, indices, M, M, block, block, num_qo_heads,
+                 num_kv_heads, head_dim, head_dim, False, 1.0 / np.sqrt(head_dim),
+                 q_dtype=dtype, kv_dtype=dtype, o_dtype=dtype,
+                 meta={"mask": mask, "packed_mask": np.packbits(mask.ravel(), bitorder="little")})
+    if values:
+        g = torch.Generator().manual_seed(seed)
+        w.q = _randn(g, (M, num_qo_heads, head_dim), dtype)
+        w.k = _randn(g, (M, num_kv_heads, head_dim), dtype)
+        w.v = _randn(g, (M, num_kv_heads, head_dim), dtype)
+    return w
+
+
+def _variable_sizes(rng, total: int, lo: int, hi: int) -> list:
+    """Block sizes drawn uniformly from [lo, hi] until they cover ``total``; the
+    last one is cut to fit."""
+    sizes, acc = [], 0
+    while acc < total:
+        s = int(min(rng.integers(lo, hi + 1), total - acc))
+        sizes.append(s)
+        acc += s
+    return sizes
+
+
+def variable_block_prefill(seed: int = 9, M: int = 8192, min_block: int = 32, max_block: int = 160,
+                           density: float = 0.15, causal: bool = False, num_qo_heads: int = 32,
+                           num_kv_heads: int = 8, head_dim: int = 128, dtype: torch.dtype = torch.float16,
+                           values: bool = True) -> Workload:
+    """Variable block sizes with a pattern per kv head (VariableBlockSparseAttentionWrapper):
+    each kv head cuts the M query rows and the M keys into blocks of sizes drawn
+    uniformly from [min_block, max_block] (its own cuts for rows and for keys), padded
+    with empty blocks to the longest head's count; each (row block, column block)
+    pair is set i.i.d. with probability ``density``, and so is the column block
+    holding a row block's first row (every row sees a key).
+
+    ``meta["variable"]`` = (block_mask_map, block_row_sz, block_col_sz); the workload's
+    R = C = 64 BSR arrays are the union of the fixed 64 x 64 blocks the map touches
+    (a view for sizing only).
+    """
+    rng = np.random.default_rng(seed)
+    rs = [_variable_sizes(rng, M, min_block, max_block) for _ in range(num_kv_heads)]
+    cs = [_variable_sizes(rng, M, min_block, max_block) for _ in range(num_kv_heads)]
+    MBv, NBv = max(map(len, rs)), max(map(len, cs))
+    rsz = np.zeros((num_kv_heads, MBv), np.int32)
+    csz = np.zeros((num_kv_heads, NBv), np.int32)
+    bm = np.zeros((num_kv_heads, MBv, NBv), bool)
+    for h in range(num_kv_heads):
+        rsz[h, :len(rs[h])] = rs[h]
+        csz[h, :len(cs[h])] = cs[h]
+        bm[h, :len(rs[h]), :len(cs[h])] = rng.random((len(rs[h]), len(cs[h]))) < density
+        col_start = np.cumsum([0] + cs[h])
+        for a, r0 in enumerate(np.cumsum([0] + rs[h])[:-1]):
+            bm[h, a, int(np.searchsorted(col_start, r0, side="right")) - 1] = True
+    # union of touched 64 x 64 blocks
+    blk = 64
+    MB = -(-M // blk)
+    touched = np.zeros((MB, MB), bool)
+    for h in range(num_kv_heads):
+        r0s, c0s = np.cumsum(np.r_[0, rsz[h]]), np.cumsum(np.r_[0, csz[h]])
+        for a, b in zip(*np.nonzero(bm[h])):
+            if rsz[h, a] and csz[h, b]:
+                touched[r0s[a] // blk:(r0s[a + 1] - 1) // blk + 1, c0s[b] // blk:(c0s[b + 1] - 1) // blk + 1] = True
+    indptr, indices = _csr_from_rows([np.nonzero(touched[i])[0] for i in range(MB)])
+    w = Workload("variable_block_prefill", indptr, indices, M, M, blk, blk, num_qo_heads, num_kv_heads,
+                 head_dim, head_dim, causal, 1.0 / np.sqrt(head_dim), q_dtype=dtype, kv_dtype=dtype,
+                 o_dtype=dtype, meta={"variable": (bm, rsz, csz)})
+    if values:
+        g = torch.Generator().manual_seed(seed)
+        w.q = _randn(g, (M, num_qo_heads, head_dim), dtype)
+        w.k = _randn(g, (M, num_kv_heads, head_dim), dtype)
+        w.v = _randn(g, (M, num_kv_heads, head_dim), dtype)
+    return w
+
+
 def window_prefill(seed: int = 4, M: int = 32768, block: int = 128, window: int = 8,
                    stride: int = 16, num_qo_heads: int = 64, num_kv_heads: int = 8,
                    head_dim: int = 128, dtype: torch.dtype = torch.float16,
@@ -346,14 +447,16 @@ def random_bsr(seed: int, M: int, N: int, R: int, C: int, num_qo_heads: int,
 # Split-KV setting each workload is timed (and parity-checked at full size) with:
 # 0 = automatic, 1 = no split.
 BENCH_KV_SPLITS = {"worked_example": 1, "paged_decode": 0, "bsr_prefill": 1, "window_prefill": 1,
-                   "sparse_mla": 1, "head_sparse_prefill": 1, "paged_decode_fp8": 0}
+                   "sparse_mla": 1, "head_sparse_prefill": 1, "paged_decode_fp8": 0,
+                   "element_mask_prefill": 1, "variable_block_prefill": 1}
 
 WORKLOAD_NAMES = ["worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla",
-                  "head_sparse_prefill", "paged_decode_fp8"]
+                  "head_sparse_prefill", "paged_decode_fp8", "element_mask_prefill", "variable_block_prefill"]
 
 
 def by_name(name: str, **kw) -> Workload:
     return {"worked_example": worked_example, "paged_decode": paged_decode,
             "bsr_prefill": bsr_prefill, "window_prefill": window_prefill,
             "sparse_mla": sparse_mla, "head_sparse_prefill": head_sparse_prefill,
-            "paged_decode_fp8": paged_decode_fp8}[name](**kw)
+            "paged_decode_fp8": paged_decode_fp8, "element_mask_prefill": element_mask_prefill,
+            "variable_block_prefill": variable_block_prefill}[name](**kw)

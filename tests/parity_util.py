@@ -30,8 +30,19 @@ def say(msg: str) -> None:
 
 def plan_for(w, kv_splits=1, num_cus=0) -> Plan:
     """The library plan of a workload; a per-head structure (w.meta["block_mask"], or
-    w.meta["q2k"] = (q2k_indices, q2k_num)) replaces the shared BSR rows."""
+    w.meta["q2k"] = (q2k_indices, q2k_num)) replaces the shared BSR rows; element masks
+    come from w.meta["packed_mask"] (else w.meta["mask"]); w.meta["variable"] =
+    (block_mask_map, block_row_sz, block_col_sz) plans variable block sizes."""
+    if "variable" in w.meta:
+        bm, rs, cs = w.meta["variable"]
+        return Plan.variable(bm, rs, cs, w.num_qo_heads, w.num_kv_heads, w.head_dim, causal=w.causal,
+                             sm_scale=w.sm_scale, kv_splits=kv_splits, q_dtype=w.q_dtype, num_cus=num_cus,
+                             **w.meta.get("grid", {}))
     extra = {}
+    if "packed_mask" in w.meta:
+        extra["packed_mask"] = w.meta["packed_mask"]
+    elif "mask" in w.meta:
+        extra["mask"] = w.meta["mask"]
     if "block_mask" in w.meta:
         extra["block_mask"] = w.meta["block_mask"]
     if "q2k" in w.meta:
@@ -86,6 +97,14 @@ def oracle_inputs(w):
 
 def oracle_result(w, rows=None, inputs=None):
     q, k, v = oracle_inputs(w) if inputs is None else inputs
+    if "variable" in w.meta:
+        bm, rs, cs = w.meta["variable"]
+        return oracle.variable_block_attention(bm, rs, cs, q, k, v, sm_scale=w.sm_scale, causal=w.causal, rows=rows)
+    if "mask" in w.meta or "packed_mask" in w.meta:
+        mask = (w.meta["mask"] if "mask" in w.meta
+                else oracle.unpack_block_masks(w.meta["packed_mask"], w.nnz, w.R, w.C))
+        return oracle.element_mask_attention(w.indptr, w.indices, w.M, w.N, w.R, w.C, mask, q, k, v,
+                                             sm_scale=w.sm_scale, rows=rows)
     if "block_mask" in w.meta or "q2k" in w.meta:
         bm = (w.meta["block_mask"] if "block_mask" in w.meta
               else oracle.q2k_block_mask(w.meta["q2k"][0], w.meta["q2k"][1], w.NB))

@@ -170,6 +170,8 @@ FULL_ROWS = {
     "sparse_mla": [0, 1, 17, 64, 100, 127],
     "head_sparse_prefill": [0, 1, 63, 64, 127, 4095, 4096, 6000, 8190, 8191],
     "paged_decode_fp8": None,                                   # all 64 requests
+    "element_mask_prefill": [0, 1, 63, 64, 127, 4095, 4096, 6000, 8190, 8191],
+    "variable_block_prefill": [0, 1, 31, 95, 160, 4095, 4096, 6000, 8190, 8191],
 }
 
 
@@ -376,3 +378,75 @@ def test_fp8_kv_decode(case, kv_splits):
                 vb[J * C + n:(J + 1) * C] = 0xFE      # -448
     assert plan_for(w, kv_splits).info()["kernel"] == 2
     _check(w, kv_splits, what=f"fp8 decode s{seed} {dtype} splits={kv_splits}")
+
+
+# ---------------------------------------------------------------- element masks and variable blocks
+# Element masks inside BSR blocks (mask / packed_mask; the causal flag has no effect
+# with them) and variable block sizes mapped onto a fixed grid with masks.
+MASKED = [
+    # (seed, M, NB, R, C, Hq, Hkv, keep, packed, bf16)
+    (51, 130, 6, 64, 64, 16, 4, 0.6, True, False),     # M % R != 0, whole 64-key block tiles
+    (52, 256, 4, 128, 128, 16, 2, 0.5, False, False),  # 256-row tiles: 64-key tiles when masked
+    (53, 37, 9, 5, 7, 8, 2, 0.5, True, True),          # generic key lookup, bf16
+    (54, 20, 40, 1, 16, 32, 8, 0.7, False, False),     # decode shape, run by the tile kernel
+    (55, 96, 12, 32, 32, 8, 8, 0.3, True, False),      # g = 1
+]
+
+
+def _masked_workload(case):
+    seed, M, NB, R, C, Hq, Hkv, keep, packed, bf16 = case
+    w = W.random_bsr(seed, M, NB * C, R, C, Hq, Hkv, causal=True, density=0.6,
+                     dtype=torch.bfloat16 if bf16 else torch.float16)
+    rng = np.random.default_rng(seed)
+    mask = rng.random((w.nnz, R, C)) < keep
+    if w.nnz:
+        mask[0] = False                                              # a block with nothing visible
+        mask[w.indptr[-2]:] = False                                  # last row block: rows without keys
+    if packed:
+        w.meta["packed_mask"] = np.packbits(mask.ravel(), bitorder="little")
+    else:
+        w.meta["mask"] = mask
+    return w
+
+
+@pytest.mark.parametrize("case", MASKED, ids=[f"m{c[0]}" for c in MASKED])
+@pytest.mark.parametrize("kv_splits", [1, 3, 0])
+def test_element_masks(case, kv_splits):
+    w = _masked_workload(case)
+    _check(w, kv_splits, what=f"element masks s{case[0]} packed={case[8]} splits={kv_splits}")
+
+
+VARIABLE = [
+    # (seed, M, min_block, max_block, density, causal, Hq, Hkv, grid)
+    (61, 300, 8, 40, 0.3, False, 8, 2, {}),
+    (62, 257, 20, 90, 0.25, True, 16, 4, {}),            # N odd: a grid of 1-key blocks
+    (63, 512, 1, 200, 0.2, True, 4, 4, {"R": 32, "C": 16}),
+    (64, 200, 50, 50, 0.5, False, 32, 8, {"C": 8}),
+]
+
+
+@pytest.mark.parametrize("case", VARIABLE, ids=[f"v{c[0]}" for c in VARIABLE])
+@pytest.mark.parametrize("kv_splits", [1, 0])
+def test_variable_blocks(case, kv_splits):
+    seed, M, lo, hi, dens, causal, Hq, Hkv, grid = case
+    w = W.variable_block_prefill(seed=seed, M=M, min_block=lo, max_block=hi, density=dens, causal=causal,
+                                 num_qo_heads=Hq, num_kv_heads=Hkv)
+    w.meta["grid"] = grid
+    _check(w, kv_splits, what=f"variable blocks s{seed} grid={grid} splits={kv_splits}")
+
+
+def test_variable_worked_example():
+    bm = np.array([[[0, 0, 1], [1, 0, 1], [0, 1, 1]]], bool)
+    w = W.Workload("variable_example", np.zeros(1, np.int32), np.zeros(0, np.int32), 6, 6, 1, 1, 1, 1, 128, 128,
+                   False, 128 ** -0.5, meta={"variable": (bm, np.array([[1, 2, 3]]), np.array([[3, 1, 2]]))})
+    g = torch.Generator().manual_seed(12)
+    w.q, w.k, w.v = (torch.randn(6, 1, 128, generator=g).half() for _ in range(3))
+    _check(w, 1, what="variable-block worked example")
+
+
+def test_reduced_element_mask_prefill():
+    _check(W.element_mask_prefill(seed=58, M=1024), 1, what="element_mask_prefill M=1024")
+
+
+def test_reduced_variable_block_prefill():
+    _check(W.variable_block_prefill(seed=59, M=1024), 1, what="variable_block_prefill M=1024")
