@@ -91,6 +91,39 @@ def unmasked_pairs(w, rows=None, indptr=None, indices=None):
     return total
 
 
+def masked_kv_pairs(w, rows=None):
+    """Visible (query row, key) pairs summed over kv heads for element masks
+    (``w.meta["mask"]``, shared by every kv head) or variable blocks
+    (``w.meta["variable"]``, one map per kv head); None for other workloads."""
+    import numpy as np
+    row_list = np.arange(w.M) if rows is None else np.asarray(sorted(rows))
+    if "mask" in w.meta:
+        mask = w.meta["mask"]
+        total = 0
+        for I in range(len(w.indptr) - 1):
+            sel = row_list[(row_list >= I * w.R) & (row_list < (I + 1) * w.R)] - I * w.R
+            if sel.size:
+                total += int(mask[w.indptr[I]:w.indptr[I + 1]][:, sel, :].sum())
+        return total * w.num_kv_heads
+    if "variable" in w.meta:
+        bm, rs, cs = w.meta["variable"]
+        total = 0
+        for h in range(bm.shape[0]):
+            row_block = np.repeat(np.arange(bm.shape[1]), rs[h])
+            c_end = np.cumsum(cs[h])
+            c_start = c_end - cs[h]
+            if not w.causal:
+                keys = (bm[h] * cs[h][None, :]).sum(axis=1)
+                total += int(keys[row_block[row_list]].sum())
+            else:
+                for i in row_list:
+                    lim = i + w.N - w.M + 1
+                    vis = np.clip(np.minimum(c_end, lim) - c_start, 0, None)
+                    total += int((bm[h, row_block[i]] * vis).sum())
+        return total
+    return None
+
+
 def algorithmic_work(w, rows=None):
     """(bytes, flops) the method itself must move / compute for one run (or for `rows` only).
 
@@ -103,7 +136,10 @@ def algorithmic_work(w, rows=None):
     """
     structs = head_structures(w)
     # pairs summed over kv heads (a shared structure counts once per kv head)
-    if len(structs) == 1:
+    masked = masked_kv_pairs(w, rows)
+    if masked is not None:
+        kv_pairs = masked
+    elif len(structs) == 1:
         kv_pairs = unmasked_pairs(w, rows) * w.num_kv_heads
     else:
         kv_pairs = sum(unmasked_pairs(w, rows, ip, ix) for ip, ix in structs)
@@ -123,6 +159,11 @@ def algorithmic_work(w, rows=None):
             idx += 4 * nnz_rows
     flops = 2 * kv_pairs * g * (w.head_dim + w.head_dim_vo)
     scale_bytes = sum(4 * len(w.meta[f"scale_{n}"]) for n in ("q", "k", "v") if f"scale_{n}" in w.meta)
+    if "mask" in w.meta:   # the element masks, one bit each, for the rows taken
+        idx += w.meta["mask"].size // 8 * m // w.M
+    if "variable" in w.meta:   # the block map (one bit per block) and the int32 sizes
+        bm, rs, cs = w.meta["variable"]
+        idx += bm.size // 8 + 4 * (rs.size + cs.size)
     return kv_bytes + qo + idx + scale_bytes, flops
 
 
@@ -153,7 +194,13 @@ def cpu_baseline(w, budget_s: float):
     while done < w.M and t_used < budget_s:
         rows = order[done:done + batch].tolist()
         t0 = time.perf_counter()
-        if "block_mask" in w.meta:
+        if "variable" in w.meta:
+            bm, rs, cs = w.meta["variable"]
+            oracle.variable_block_attention(bm, rs, cs, q, k, v, sm_scale=w.sm_scale, causal=w.causal, rows=rows)
+        elif "mask" in w.meta:
+            oracle.element_mask_attention(w.indptr, w.indices, w.M, w.N, w.R, w.C, w.meta["mask"], q, k, v,
+                                          sm_scale=w.sm_scale, rows=rows)
+        elif "block_mask" in w.meta:
             oracle.block_mask_attention(w.meta["block_mask"], w.M, w.N, w.R, w.C, q, k, v,
                                         sm_scale=w.sm_scale, causal=w.causal,
                                         kv_block_lens=w.kv_block_lens, rows=rows)
@@ -174,8 +221,11 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="paged_decode",
                     choices=["worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla",
-                             "head_sparse_prefill", "paged_decode_fp8"])
+                             "head_sparse_prefill", "paged_decode_fp8", "element_mask_prefill",
+                             "variable_block_prefill"])
     ap.add_argument("--kv-splits", type=int, default=None, help="override the workload's split-KV setting")
+    ap.add_argument("--var-grid", type=int, nargs=2, default=(0, 0), metavar=("R", "C"),
+                    help="variable-block workloads: the fixed grid the blocks are mapped onto (0 = library's choice)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
     ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
                     help="after the timed region, copy MIB MiB device-to-device once (a known-size "
@@ -205,11 +255,18 @@ def main() -> int:
     w = W.by_name(args.workload)
     kv_splits = W.BENCH_KV_SPLITS[args.workload] if args.kv_splits is None else args.kv_splits
     t0 = time.perf_counter()
-    plan = Plan(w.indptr, w.indices, w.M, w.N, w.R, w.C, w.num_qo_heads, w.num_kv_heads, w.head_dim,
-                head_dim_vo=w.head_dim_vo, causal=w.causal, sm_scale=w.sm_scale, kv_splits=kv_splits,
-                kv_block_lens=w.kv_block_lens, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, o_dtype=w.o_dtype,
-                k_descale=w.k_descale, v_descale=w.v_descale, k_token_stride=w.k_token_stride,
-                v_token_stride=w.v_token_stride, block_mask=w.meta.get("block_mask"))
+    if "variable" in w.meta:
+        bm, rs, cs = w.meta["variable"]
+        plan = Plan.variable(bm, rs, cs, w.num_qo_heads, w.num_kv_heads, w.head_dim, causal=w.causal,
+                             sm_scale=w.sm_scale, kv_splits=kv_splits, q_dtype=w.q_dtype,
+                             R=args.var_grid[0], C=args.var_grid[1])
+    else:
+        plan = Plan(w.indptr, w.indices, w.M, w.N, w.R, w.C, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                    head_dim_vo=w.head_dim_vo, causal=w.causal, sm_scale=w.sm_scale, kv_splits=kv_splits,
+                    kv_block_lens=w.kv_block_lens, q_dtype=w.q_dtype, kv_dtype=w.kv_dtype, o_dtype=w.o_dtype,
+                    k_descale=w.k_descale, v_descale=w.v_descale, k_token_stride=w.k_token_stride,
+                    v_token_stride=w.v_token_stride, block_mask=w.meta.get("block_mask"),
+                    packed_mask=w.meta.get("packed_mask"))
     plan_ms = (time.perf_counter() - t0) * 1e3
     info = plan.info()
     q = w.q.to(dev)
@@ -301,10 +358,11 @@ def main() -> int:
                "sample": f"{cb['rows']} of {w.M} query rows (all heads), float64 dense-mask oracle, "
                          f"{cb['seconds']:.1f} s"}
 
-    cfg = {"workload": args.workload, "M": w.M, "N": w.N, "R": w.R, "C": w.C,
+    cfg = {"workload": args.workload, "M": w.M, "N": w.N, "R": info["R"], "C": info["C"],
            "num_qo_heads": w.num_qo_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
            "head_dim_vo": w.head_dim_vo, "causal": w.causal, "nnz_blocks": sum(len(ix) for _, ix in head_structures(w)),
-           "per_head_structure": "block_mask" in w.meta, "kv_splits": kv_splits,
+           "per_head_structure": "block_mask" in w.meta or "variable" in w.meta,
+           "element_masks": "mask" in w.meta or "variable" in w.meta, "kv_splits": kv_splits,
            "tiles": info["num_tiles"], "merges": info["num_merges"], "plan_ms": plan_ms,
            "alg_bytes": alg_bytes, "alg_flops": alg_flops}
     line = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,

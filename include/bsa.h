@@ -148,8 +148,9 @@ typedef enum {
  *                  mask and kv_block_lens unused and must be NULL where listed)
  *   R, C           the fixed grid the planner maps the variable blocks onto (each
  *                  fixed block touched by a set variable block becomes a block
- *                  with an element mask): 0 = chosen by the planner (C the
- *                  largest of 64, 32, ..., 1 dividing N; R = max(1, 256 / g))
+ *                  with an element mask): 0 = chosen by the planner (R =
+ *                  max(1, 128 / g); C the largest power of two up to min(64, a
+ *                  quarter of the mean non-empty column block size) dividing N)
  * causal applies on top of the block map (key j <= i + N - M).
  */
 typedef struct {

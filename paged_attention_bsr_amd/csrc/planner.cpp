@@ -591,13 +591,20 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
       return fail(err, BSA_ERR_INVALID_ARGUMENT,
                   "every kv head's block_row_sz must sum to M and its block_col_sz to N");
   }
+  // Default grid: R*g = 128 query rows per row block (one 4-wave tile); C the
+  // largest power of two up to min(64, a quarter of the mean non-empty column
+  // block) that divides N -- finer blocks waste fewer masked keys, coarser ones
+  // keep whole key tiles inside a block.
   const int64_t g = desc.num_qo_heads / desc.num_kv_heads;
   int32_t C = desc.C;
   if (C == 0) {
+    int64_t nonempty = 0;
+    for (int64_t i = 0; i < H * VNB; ++i) nonempty += desc.block_col_sz[i] > 0;
+    const int64_t quarter = nonempty > 0 ? desc.N * H / nonempty / 4 : 64;
     C = 64;
-    while (C > 1 && desc.N % C != 0) C /= 2;
+    while (C > 1 && (C > quarter || desc.N % C != 0)) C /= 2;
   }
-  const int32_t R = desc.R > 0 ? desc.R : static_cast<int32_t>(std::max<int64_t>(1, 256 / g));
+  const int32_t R = desc.R > 0 ? desc.R : static_cast<int32_t>(std::max<int64_t>(1, 128 / g));
   if (desc.N % C != 0) return fail(err, BSA_ERR_INVALID_ARGUMENT, "N must be divisible by C");
   const int64_t MB = ceil_div(desc.M, R), NB = desc.N / C;
   ms.kind = 2;

@@ -95,10 +95,15 @@ def test_variable_worked_example_plan():
 
 
 def test_variable_default_grid():
-    # g = 4: R = 256 / 4; N = 96 -> C = 32 (largest power of two up to 64 dividing N)
+    # g = 4: R = 128 / 4; mean column block 96 * 2 / 4 = 48, a quarter 12 -> C = 8 (divides N = 96)
     p = Plan.variable(np.ones((2, 1, 2), bool), [[100], [100]], [[40, 56], [90, 6]], 8, 2, 128, num_cus=CUS)
-    assert (p.info()["R"], p.info()["C"]) == (64, 32)
-    assert (p.R, p.C, p.M, p.N) == (64, 32, 100, 96)
+    assert (p.info()["R"], p.info()["C"]) == (32, 8)
+    assert (p.R, p.C, p.M, p.N) == (32, 8, 100, 96)
+    # large blocks keep 64-key blocks; N = 4100 is not a multiple of 8 -> C = 4
+    p = Plan.variable(np.ones((1, 1, 2), bool), [[10]], [[2048, 2048]], 1, 1, 128, num_cus=CUS)
+    assert (p.info()["R"], p.info()["C"]) == (128, 64)
+    p = Plan.variable(np.ones((1, 1, 2), bool), [[10]], [[2050, 2050]], 1, 1, 128, num_cus=CUS)
+    assert p.info()["C"] == 4
 
 
 def _expect_error(**kw):
