@@ -42,8 +42,8 @@ Readings taken where the pages are silent:
     the same as using the first qo head of each group);
   * element mask p belongs to the block indices[p] of the BSR arrays as
     given (before any sorting), its entry [r, c] to query row I*R + r and key
-    J*C + c; with an element mask the causal flag has no effect (plan():
-    causal is only effective when neither mask nor packed_mask is given);
+    J*C + c; with an element mask the causal flag has no effect (plan()
+    documents causal as ignored whenever a mask or packed mask is passed);
   * packed_mask holds the flattened (nnz, R, C) mask eight entries a byte,
     entry i in bit i % 8 (least significant first) of byte i // 8;
   * variable blocks: row block a of kv head h covers the block_row_sz[h, a]
