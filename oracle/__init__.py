@@ -21,3 +21,8 @@ from .bsr_attention import (  # noqa: F401
     variable_block_masks,
     variable_block_attention,
 )
+from .rope_quantize import (  # noqa: F401
+    e4m3fn_encode,
+    rope_fp32,
+    mla_rope_quantize_fp8,
+)
