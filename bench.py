@@ -35,6 +35,7 @@ KERNEL_SOURCES = {
     "attn_tile_kernel": ["attn_tile.hip", "device_common.h", "kernels.h"],
     "attn_decode_kernel": ["attn_decode.hip", "device_common.h", "kernels.h"],
     "attn_mla_kernel": ["attn_mla.hip", "device_common.h", "kernels.h"],
+    "rope_quant_kernel": ["rope_quant.hip", "rope_quant.h", "device_common.h"],
 }
 
 
@@ -222,7 +223,7 @@ def main() -> int:
     ap.add_argument("--workload", default="paged_decode",
                     choices=["worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla",
                              "head_sparse_prefill", "paged_decode_fp8", "element_mask_prefill",
-                             "variable_block_prefill"])
+                             "variable_block_prefill", "rope_quantize"])
     ap.add_argument("--kv-splits", type=int, default=None, help="override the workload's split-KV setting")
     ap.add_argument("--var-grid", type=int, nargs=2, default=(0, 0), metavar=("R", "C"),
                     help="variable-block workloads: the fixed grid the blocks are mapped onto (0 = library's choice)")
@@ -251,6 +252,9 @@ def main() -> int:
     torch.cuda.set_device(dev)
     props = torch.cuda.get_device_properties(dev)
     log(f"[bench] device {props.name} CUs={props.multi_processor_count} workload={args.workload}")
+
+    if args.workload == "rope_quantize":
+        return run_rope_quantize(args, dev)
 
     w = W.by_name(args.workload)
     kv_splits = W.BENCH_KV_SPLITS[args.workload] if args.kv_splits is None else args.kv_splits
@@ -369,6 +373,94 @@ def main() -> int:
             "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": dtype, "data": "synthetic", "config": cfg,
             "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def rope_bytes(nnz: int, heads: int) -> int:
+    """Algorithmic bytes of the RoPE + FP8 quantize producer for nnz tokens: the bf16 q
+    (heads x 576) and k (576) rows read, their fp8 codes written, the int32 position and
+    the token's 64-value fp32 cache row read."""
+    return nnz * (heads * 576 * 3 + 576 * 3 + 4 + 256)
+
+
+def run_rope_quantize(args, dev) -> int:
+    """One step = one bsa_mla_rope_quantize_fp8 over the workload's token chunk."""
+    import numpy as np
+    import torch
+    from paged_attention_bsr_amd import mla_rope_quantize_fp8
+    from paged_attention_bsr_amd import workloads as W
+    w = W.rope_quantize()
+    nnz, H = w["nnz"], w["num_heads"]
+    d = {k: w[k].to(dev) for k in ("q_rope", "k_rope", "q_nope", "k_nope", "cos_sin_cache", "pos_ids")}
+    f8 = torch.float8_e4m3fn
+    outs = {"q_rope_out": torch.empty(nnz, H, 64, dtype=f8, device=dev),
+            "k_rope_out": torch.empty(nnz, 64, dtype=f8, device=dev),
+            "q_nope_out": torch.empty(nnz, H, 512, dtype=f8, device=dev),
+            "k_nope_out": torch.empty(nnz, 512, dtype=f8, device=dev)}
+
+    def step():
+        mla_rope_quantize_fp8(d["q_rope"], d["k_rope"], d["q_nope"], d["k_nope"], d["cos_sin_cache"], d["pos_ids"],
+                              w["is_neox"], w["quant_scale_q"], w["quant_scale_kv"], **outs)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        events[i][0].record()
+        step()
+        events[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    k_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
+    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step; kernel avg {k_ms:.4f} ms")
+    if args.calibration_copy > 0:
+        n = args.calibration_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    alg = rope_bytes(nnz, H)
+    achieved = alg / (k_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "kernel": "rope_quant_kernel", "traffic": measured_traffic("rope_quantize", kernel_source_hash("rope_quant_kernel")),
+            "alg_bytes_per_launch": alg, "alg_flops_per_launch": 0, "avg_launch_ms": k_ms}
+    cpu = None
+    if args.cpu_budget > 0:
+        import oracle
+        log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s budget)")
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            threads = os.cpu_count() or 1
+        cache = w["cos_sin_cache"].float().numpy()
+        done, used, batch = 0, 0.0, 8
+        while done < nnz and used < args.cpu_budget:
+            sl = slice(done, min(nnz, done + batch))
+            f = lambda t: t[sl].float().numpy()
+            t1 = time.perf_counter()
+            oracle.mla_rope_quantize_fp8(f(w["q_rope"]), f(w["k_rope"]), f(w["q_nope"]), f(w["k_nope"]), cache,
+                                         w["pos_ids"][sl].numpy(), w["is_neox"], w["quant_scale_q"],
+                                         w["quant_scale_kv"])
+            used += time.perf_counter() - t1
+            done = sl.stop
+            batch = min(batch * 2, 256)
+        cpu = {"value": rope_bytes(done, H) / used / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"{done} of {nnz} tokens (all heads), numpy float32 rotary + nearest-value fp8 encode, "
+                         f"{used:.1f} s"}
+    cfg = {"workload": "rope_quantize", "nnz": nnz, "num_heads": H, "q_row": "512 latent + 64 rope",
+           "max_seq_len": w["max_seq_len"], "is_neox": w["is_neox"], "cache": "fp32",
+           "quant_scale_q": w["quant_scale_q"], "quant_scale_kv": w["quant_scale_kv"], "alg_bytes": alg}
+    line = {"metric": METRIC, "value": alg / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in, fp8 e4m3 out (f32 arithmetic)",
+            "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
     return 0
 

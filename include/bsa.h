@@ -280,6 +280,63 @@ bsa_status_t bsa_merge_states(const float* v, const float* s, void* v_out, float
                               int64_t seq_len, int32_t num_states, int32_t num_heads,
                               int32_t head_dim, int32_t out_dtype, void* stream);
 
+/*
+ * MLA RoPE + FP8 quantize: the producer of the sparse-MLA decode inputs (MATE
+ * sparse-MLA API page and its FlashInfer-wrapper page, "RoPE and FP8
+ * quantization", mla_rope_quantize_fp8).  For every token t (position
+ * pos_ids[t]) it turns the 64-value RoPE tails of q (each of num_heads heads)
+ * and k by the position's angles, multiplies every q value (latent 512 and
+ * tail 64) by quant_scale_q and every k value by quant_scale_kv, and casts to
+ * FP8 E4M3.  Rotation: cache row pos holds cosines in columns 0..31 and sines in
+ * 32..63; pair i uses column i and is values (i, i + 32) when is_neox, else
+ * (2i, 2i + 1); a' = a cos - b sin, b' = b cos + a sin, each product and sum a
+ * float32 operation of its own.  The cast rounds to nearest even and saturates
+ * at +-448 (inputs are finite).
+ *
+ *   q_rope, q_nope   bf16 device arrays [nnz][num_heads][64] / [nnz][num_heads][512]
+ *   k_rope, k_nope   bf16 device arrays [nnz][64] / [nnz][512]
+ *   cos_sin_cache    device [max_seq_len][64], float32 (cache_bf16 = 0) or bf16 (1), contiguous
+ *   pos_ids          device [nnz] int32 (pos_int64 = 0) or int64 (1); each in [0, max_seq_len):
+ *                    a token whose position lies outside gets NaN codes (0x7F) in both its
+ *                    rotated tails and never reads the cache
+ *   *_out            fp8 e4m3 device arrays of the same shapes; may be slices of merged
+ *                    [..., 576] rows (q_nope_out = row[:512], q_rope_out = row[512:])
+ *   *_stride         leading-dimension strides, in elements of the array's own type (bf16
+ *                    inputs, 1-byte outputs): [0] between tokens, [1] between heads; 0 =
+ *                    dense.  Every stride must be a multiple of 8, inputs and the cache
+ *                    16-byte aligned, outputs 8-byte aligned; the last dimension is always
+ *                    contiguous.  Output rows must not overlap one another (not checked).
+ * Runs one kernel on `stream`; nnz = 0 launches nothing.  BSA_ERR_INVALID_ARGUMENT for a
+ * NULL argument struct or array, a bad size, stride or alignment, or a non-finite scale.
+ */
+typedef struct {
+  const void* q_rope;
+  const void* k_rope;
+  const void* q_nope;
+  const void* k_nope;
+  const void* cos_sin_cache;
+  int32_t cache_bf16;
+  const void* pos_ids;
+  int32_t pos_int64;
+  int64_t nnz;
+  int32_t num_heads;
+  int64_t max_seq_len;
+  int32_t is_neox;
+  float quant_scale_q, quant_scale_kv;
+  void* q_rope_out;
+  void* k_rope_out;
+  void* q_nope_out;
+  void* k_nope_out;
+  int64_t q_rope_stride[2], q_nope_stride[2], k_rope_stride, k_nope_stride;
+  int64_t q_rope_out_stride[2], q_nope_out_stride[2], k_rope_out_stride, k_nope_out_stride;
+} bsa_rope_quant_t;
+
+/* Defaults: everything zero / NULL (dense strides), is_neox = 1, scales 1. */
+void bsa_rope_quant_init(bsa_rope_quant_t* args);
+/* sizeof(bsa_rope_quant_t) as compiled into the library. */
+size_t bsa_rope_quant_sizeof(void);
+bsa_status_t bsa_mla_rope_quantize_fp8(const bsa_rope_quant_t* args, void* stream);
+
 /* Plan statistics, and the tables themselves, for inspection and tests. */
 typedef struct {
   int32_t kernel;          /* bsa_kernel_t */

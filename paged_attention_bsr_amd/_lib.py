@@ -84,6 +84,37 @@ class PlanInfo(ctypes.Structure):
     ]
 
 
+class RopeQuant(ctypes.Structure):
+    _fields_ = [
+        ("q_rope", ctypes.c_void_p),
+        ("k_rope", ctypes.c_void_p),
+        ("q_nope", ctypes.c_void_p),
+        ("k_nope", ctypes.c_void_p),
+        ("cos_sin_cache", ctypes.c_void_p),
+        ("cache_bf16", ctypes.c_int32),
+        ("pos_ids", ctypes.c_void_p),
+        ("pos_int64", ctypes.c_int32),
+        ("nnz", ctypes.c_int64),
+        ("num_heads", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int64),
+        ("is_neox", ctypes.c_int32),
+        ("quant_scale_q", ctypes.c_float),
+        ("quant_scale_kv", ctypes.c_float),
+        ("q_rope_out", ctypes.c_void_p),
+        ("k_rope_out", ctypes.c_void_p),
+        ("q_nope_out", ctypes.c_void_p),
+        ("k_nope_out", ctypes.c_void_p),
+        ("q_rope_stride", ctypes.c_int64 * 2),
+        ("q_nope_stride", ctypes.c_int64 * 2),
+        ("k_rope_stride", ctypes.c_int64),
+        ("k_nope_stride", ctypes.c_int64),
+        ("q_rope_out_stride", ctypes.c_int64 * 2),
+        ("q_nope_out_stride", ctypes.c_int64 * 2),
+        ("k_rope_out_stride", ctypes.c_int64),
+        ("k_nope_out_stride", ctypes.c_int64),
+    ]
+
+
 _lib = None
 
 
@@ -124,6 +155,12 @@ def lib() -> ctypes.CDLL:
     L.bsa_plan_export_workgroups.restype = st
     L.bsa_plan_export_mask_bits.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32)]
     L.bsa_plan_export_mask_bits.restype = st
+    L.bsa_rope_quant_init.argtypes = [ctypes.POINTER(RopeQuant)]
+    L.bsa_rope_quant_init.restype = None
+    L.bsa_rope_quant_sizeof.argtypes = []
+    L.bsa_rope_quant_sizeof.restype = sz
+    L.bsa_mla_rope_quantize_fp8.argtypes = [ctypes.POINTER(RopeQuant), vp]
+    L.bsa_mla_rope_quantize_fp8.restype = st
     L.bsa_plan_destroy.argtypes = [vp]
     L.bsa_plan_destroy.restype = None
     L.bsa_last_error.argtypes = []

@@ -275,3 +275,57 @@ def merge_states(v: torch.Tensor, s: torch.Tensor, out_dtype: torch.dtype = torc
     L.check(L.lib().bsa_merge_states(v.data_ptr(), s.data_ptr(), v_out.data_ptr(), s_out.data_ptr(),
                                      seq, ns, heads, dim, code, st))
     return v_out, s_out
+
+
+def mla_rope_quantize_fp8(q_rope: torch.Tensor, k_rope: torch.Tensor, q_nope: torch.Tensor, k_nope: torch.Tensor,
+                          cos_sin_cache: torch.Tensor, pos_ids: torch.Tensor, is_neox: bool = True,
+                          quant_scale_q: float = 1.0, quant_scale_kv: float = 1.0,
+                          q_rope_out: Optional[torch.Tensor] = None, k_rope_out: Optional[torch.Tensor] = None,
+                          q_nope_out: Optional[torch.Tensor] = None, k_nope_out: Optional[torch.Tensor] = None,
+                          stream=None):
+    """RoPE on the 64-value tails and per-tensor FP8 E4M3 quantization of MLA q / k
+    (bsa_mla_rope_quantize_fp8; MATE mla_rope_quantize_fp8).  q_rope (nnz, H, 64),
+    k_rope (nnz, 64), q_nope (nnz, H, 512), k_nope (nnz, 512): bf16 device tensors with a
+    contiguous last dimension; cos_sin_cache (max_seq_len, 64) fp32 or bf16; pos_ids (nnz,)
+    int32 or int64.  Outputs may be given (fp8 views, e.g. slices of [..., 576] rows) or are
+    allocated.  Returns (q_rope_out, k_rope_out, q_nope_out, k_nope_out)."""
+    nnz, H = q_rope.shape[0], q_rope.shape[1]
+    shapes = {"q_rope": (q_rope, (nnz, H, 64)), "k_rope": (k_rope, (nnz, 64)),
+              "q_nope": (q_nope, (nnz, H, 512)), "k_nope": (k_nope, (nnz, 512))}
+    for name, (t, shp) in shapes.items():
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != shp or not t.is_cuda or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be a bf16 device tensor of shape {shp} with a contiguous last dimension")
+    if cos_sin_cache.dtype not in (torch.float32, torch.bfloat16) or cos_sin_cache.dim() != 2 or \
+            cos_sin_cache.shape[1] != 64 or not cos_sin_cache.is_contiguous():
+        raise ValueError("cos_sin_cache must be a contiguous (max_seq_len, 64) float32 or bf16 tensor")
+    if pos_ids.dtype not in (torch.int32, torch.int64) or tuple(pos_ids.shape) != (nnz,) or not pos_ids.is_contiguous():
+        raise ValueError("pos_ids must be a contiguous int32 or int64 tensor of nnz entries")
+    f8 = torch.float8_e4m3fn
+    outs = []
+    for name, t in (("q_rope", q_rope_out), ("k_rope", k_rope_out), ("q_nope", q_nope_out), ("k_nope", k_nope_out)):
+        shp = shapes[name][1]
+        if t is None:
+            t = torch.empty(shp, dtype=f8, device=q_rope.device)
+        elif t.dtype != f8 or tuple(t.shape) != shp or t.stride(-1) != 1:
+            raise ValueError(f"{name}_out must be a float8_e4m3fn tensor of shape {shp} with a contiguous last dimension")
+        outs.append(t)
+    a = L.RopeQuant()
+    lib = L.lib()
+    lib.bsa_rope_quant_init(ctypes.byref(a))
+    a.q_rope, a.k_rope, a.q_nope, a.k_nope = (t.data_ptr() for t in (q_rope, k_rope, q_nope, k_nope))
+    a.cos_sin_cache, a.cache_bf16 = cos_sin_cache.data_ptr(), int(cos_sin_cache.dtype == torch.bfloat16)
+    a.pos_ids, a.pos_int64 = pos_ids.data_ptr(), int(pos_ids.dtype == torch.int64)
+    a.nnz, a.num_heads, a.max_seq_len = nnz, H, cos_sin_cache.shape[0]
+    a.is_neox = int(bool(is_neox))
+    a.quant_scale_q, a.quant_scale_kv = float(quant_scale_q), float(quant_scale_kv)
+    a.q_rope_out, a.k_rope_out, a.q_nope_out, a.k_nope_out = (t.data_ptr() for t in outs)
+    a.q_rope_stride[0], a.q_rope_stride[1] = q_rope.stride(0), q_rope.stride(1)
+    a.q_nope_stride[0], a.q_nope_stride[1] = q_nope.stride(0), q_nope.stride(1)
+    a.k_rope_stride, a.k_nope_stride = k_rope.stride(0), k_nope.stride(0)
+    a.q_rope_out_stride[0], a.q_rope_out_stride[1] = outs[0].stride(0), outs[0].stride(1)
+    a.q_nope_out_stride[0], a.q_nope_out_stride[1] = outs[2].stride(0), outs[2].stride(1)
+    a.k_rope_out_stride, a.k_nope_out_stride = outs[1].stride(0), outs[3].stride(0)
+    st = torch.cuda.current_stream(q_rope.device).cuda_stream if stream is None else stream
+    L.check(lib.bsa_mla_rope_quantize_fp8(ctypes.byref(a), st))
+    return tuple(outs)
+

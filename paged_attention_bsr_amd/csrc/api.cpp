@@ -11,6 +11,7 @@
 
 #include "bsa.h"
 #include "kernels.h"
+#include "rope_quant.h"
 #include "planner.h"
 
 struct bsa_plan_s {
@@ -348,5 +349,75 @@ void bsa_plan_destroy(bsa_plan_t plan) {
 }
 
 const char* bsa_last_error(void) { return g_err.c_str(); }
+
+void bsa_rope_quant_init(bsa_rope_quant_t* args) {
+  if (!args) return;
+  std::memset(args, 0, sizeof(*args));
+  args->is_neox = 1;
+  args->quant_scale_q = args->quant_scale_kv = 1.f;
+}
+
+size_t bsa_rope_quant_sizeof(void) { return sizeof(bsa_rope_quant_t); }
+
+bsa_status_t bsa_mla_rope_quantize_fp8(const bsa_rope_quant_t* p, void* stream) {
+  g_err.clear();
+  if (!p) return set_err(BSA_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (p->nnz < 0 || p->nnz > 0x7fffffff) return set_err(BSA_ERR_INVALID_ARGUMENT, "nnz must lie in [0, 2^31)");
+  if (p->num_heads < 1 || p->num_heads > 65535 * 16)
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "num_heads must lie in [1, 1048560]");
+  if (p->max_seq_len < 1) return set_err(BSA_ERR_INVALID_ARGUMENT, "max_seq_len must be >= 1");
+  if (!std::isfinite(p->quant_scale_q) || !std::isfinite(p->quant_scale_kv))
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "quantization scales must be finite");
+  if (p->nnz == 0) return BSA_OK;
+  const void* in[] = {p->q_rope, p->k_rope, p->q_nope, p->k_nope, p->cos_sin_cache, p->pos_ids};
+  const void* out[] = {p->q_rope_out, p->k_rope_out, p->q_nope_out, p->k_nope_out};
+  for (const void* q : in)
+    if (!q || reinterpret_cast<uintptr_t>(q) % 16 != 0)
+      return set_err(BSA_ERR_INVALID_ARGUMENT, "inputs and the cache must be non-NULL and 16-byte aligned");
+  for (const void* q : out)
+    if (!q || reinterpret_cast<uintptr_t>(q) % 8 != 0)
+      return set_err(BSA_ERR_INVALID_ARGUMENT, "outputs must be non-NULL and 8-byte aligned");
+  const int64_t H = p->num_heads;
+  bsa::RopeArgs a{};
+  a.q_rope = p->q_rope;
+  a.k_rope = p->k_rope;
+  a.q_nope = p->q_nope;
+  a.k_nope = p->k_nope;
+  a.cos_sin = p->cos_sin_cache;
+  a.pos = p->pos_ids;
+  a.q_rope_out = p->q_rope_out;
+  a.k_rope_out = p->k_rope_out;
+  a.q_nope_out = p->q_nope_out;
+  a.k_nope_out = p->k_nope_out;
+  // a zero stride selects the dense one
+  auto pick = [](int64_t s, int64_t dense) { return s != 0 ? s : dense; };
+  a.qr_s[0] = pick(p->q_rope_stride[0], H * 64);
+  a.qr_s[1] = pick(p->q_rope_stride[1], 64);
+  a.qn_s[0] = pick(p->q_nope_stride[0], H * 512);
+  a.qn_s[1] = pick(p->q_nope_stride[1], 512);
+  a.kr_s = pick(p->k_rope_stride, 64);
+  a.kn_s = pick(p->k_nope_stride, 512);
+  a.qro_s[0] = pick(p->q_rope_out_stride[0], H * 64);
+  a.qro_s[1] = pick(p->q_rope_out_stride[1], 64);
+  a.qno_s[0] = pick(p->q_nope_out_stride[0], H * 512);
+  a.qno_s[1] = pick(p->q_nope_out_stride[1], 512);
+  a.kro_s = pick(p->k_rope_out_stride, 64);
+  a.kno_s = pick(p->k_nope_out_stride, 512);
+  const int64_t strides[] = {a.qr_s[0], a.qr_s[1], a.qn_s[0], a.qn_s[1], a.kr_s, a.kn_s,
+                             a.qro_s[0], a.qro_s[1], a.qno_s[0], a.qno_s[1], a.kro_s, a.kno_s};
+  for (int64_t st : strides)
+    if (st < 0 || st % 8 != 0) return set_err(BSA_ERR_INVALID_ARGUMENT, "strides must be non-negative multiples of 8");
+  a.nnz = p->nnz;
+  a.max_seq_len = p->max_seq_len;
+  a.num_heads = p->num_heads;
+  a.is_neox = p->is_neox != 0;
+  a.cache_bf16 = p->cache_bf16 != 0;
+  a.pos_int64 = p->pos_int64 != 0;
+  a.scale_q = p->quant_scale_q;
+  a.scale_kv = p->quant_scale_kv;
+  const hipError_t e = bsa::launch_rope_quant(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "rope quantize kernel launch");
+  return BSA_OK;
+}
 
 }  // extern "C"

@@ -444,6 +444,31 @@ def random_bsr(seed: int, M: int, N: int, R: int, C: int, num_qo_heads: int,
     return w
 
 
+def rope_cache(max_seq_len: int, theta: float = 10000.0, dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """(max_seq_len, 64) rotary cache: column i < 32 = cos(p * theta^(-i/32)), column 32 + i = its sine."""
+    inv = theta ** (-np.arange(32, dtype=np.float64) / 32.0)
+    ang = np.arange(max_seq_len, dtype=np.float64)[:, None] * inv[None, :]
+    return torch.from_numpy(np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)).to(dtype)
+
+
+def rope_quantize(seed: int = 10, nnz: int = 4096, num_heads: int = 128, max_seq_len: int = 32768,
+                  is_neox: bool = True, scale: float = 64.0, cache_dtype: torch.dtype = torch.float32,
+                  values: bool = True) -> dict:
+    """The producer of the sparse-MLA inputs for a chunk of ``nnz`` tokens: bf16 q (nnz, H, 512 latent
+    + 64 RoPE) and k (nnz, 512 + 64) standard normals, int32 positions uniform in
+    [0, max_seq_len), an fp32 rotary cache (theta 10000), NeoX layout, quant scales ``scale``
+    for q and kv (a unit normal's tail beyond 7 saturates)."""
+    w = {"name": "rope_quantize", "nnz": nnz, "num_heads": num_heads, "max_seq_len": max_seq_len,
+         "is_neox": is_neox, "quant_scale_q": scale, "quant_scale_kv": scale}
+    if values:
+        g = torch.Generator().manual_seed(seed)
+        bf = lambda *shape: torch.randn(*shape, generator=g).to(torch.bfloat16)
+        w.update(q_rope=bf(nnz, num_heads, 64), k_rope=bf(nnz, 64), q_nope=bf(nnz, num_heads, 512),
+                 k_nope=bf(nnz, 512), cos_sin_cache=rope_cache(max_seq_len, dtype=cache_dtype),
+                 pos_ids=torch.randint(0, max_seq_len, (nnz,), generator=g, dtype=torch.int32))
+    return w
+
+
 # Split-KV setting each workload is timed (and parity-checked at full size) with:
 # 0 = automatic, 1 = no split.
 BENCH_KV_SPLITS = {"worked_example": 1, "paged_decode": 0, "bsr_prefill": 1, "window_prefill": 1,

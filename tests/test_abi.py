@@ -128,3 +128,29 @@ def test_merge_states_validates():
     assert lib.bsa_merge_states(None, None, None, None, 4, 2, 2, 6, 0, None) == L.BSA_ERR_INVALID_ARGUMENT
     assert lib.bsa_merge_states(None, None, None, None, 4, 2, 2, 8, 9, None) == L.BSA_ERR_UNSUPPORTED
     assert lib.bsa_merge_states(None, None, None, None, 0, 2, 2, 8, 0, None) == L.BSA_OK
+
+
+def test_rope_quant_layout_matches_binding():
+    import ctypes
+    from paged_attention_bsr_amd import _lib as L
+    assert L.lib().bsa_rope_quant_sizeof() == ctypes.sizeof(L.RopeQuant)
+    a = L.RopeQuant()
+    L.lib().bsa_rope_quant_init(ctypes.byref(a))
+    assert (a.is_neox, a.quant_scale_q, a.quant_scale_kv, a.nnz) == (1, 1.0, 1.0, 0)
+
+
+def test_rope_quant_validates_before_touching_the_gpu():
+    import ctypes
+    from paged_attention_bsr_amd import _lib as L
+    lib = L.lib()
+    a = L.RopeQuant()
+    lib.bsa_rope_quant_init(ctypes.byref(a))
+    a.num_heads, a.max_seq_len, a.nnz = 4, 16, 0
+    assert lib.bsa_mla_rope_quantize_fp8(ctypes.byref(a), None) == L.BSA_OK      # nothing to do
+    a.nnz = 3
+    assert lib.bsa_mla_rope_quantize_fp8(ctypes.byref(a), None) == L.BSA_ERR_INVALID_ARGUMENT  # NULL arrays
+    a.nnz, a.num_heads = 0, 0
+    assert lib.bsa_mla_rope_quantize_fp8(ctypes.byref(a), None) == L.BSA_ERR_INVALID_ARGUMENT
+    a.num_heads, a.quant_scale_q = 4, float("inf")
+    assert lib.bsa_mla_rope_quantize_fp8(ctypes.byref(a), None) == L.BSA_ERR_INVALID_ARGUMENT
+    assert lib.bsa_mla_rope_quantize_fp8(None, None) == L.BSA_ERR_INVALID_ARGUMENT

@@ -1,0 +1,118 @@
+"""GPU parity of the MLA RoPE + FP8 quantize kernel (bsa_mla_rope_quantize_fp8)
+against the CPU oracle: every output code must be identical."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from paged_attention_bsr_amd import mla_rope_quantize_fp8
+from paged_attention_bsr_amd import workloads as W
+from tests.parity_util import say
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(w, tokens=None):
+    sel = slice(None) if tokens is None else tokens
+    f = lambda t: t[sel].float().numpy()
+    return oracle.mla_rope_quantize_fp8(f(w["q_rope"]), f(w["k_rope"]), f(w["q_nope"]), f(w["k_nope"]),
+                                        w["cos_sin_cache"].float().numpy(), w["pos_ids"][sel].numpy(),
+                                        w["is_neox"], w["quant_scale_q"], w["quant_scale_kv"])
+
+
+def _gpu(w, **outs):
+    d = lambda t: t.cuda()
+    res = mla_rope_quantize_fp8(d(w["q_rope"]), d(w["k_rope"]), d(w["q_nope"]), d(w["k_nope"]),
+                                d(w["cos_sin_cache"]), d(w["pos_ids"]), w["is_neox"], w["quant_scale_q"],
+                                w["quant_scale_kv"], **outs)
+    torch.cuda.synchronize()
+    return res
+
+
+def _same(got, want, what):
+    for name, g, r in zip(("q_rope", "k_rope", "q_nope", "k_nope"), got, want):
+        g = g.view(torch.uint8).cpu().numpy()
+        bad = g != r
+        assert not bad.any(), f"{what} {name}: {int(bad.sum())} of {bad.size} codes differ; first at " \
+                              f"{np.argwhere(bad)[0].tolist()}: gpu {g[bad][0]:#x} oracle {r[bad][0]:#x}"
+
+
+CASES = [
+    # (seed, nnz, H, neox, cache dtype, pos dtype, scale_q, scale_kv)
+    (1, 37, 16, True, torch.float32, torch.int32, 64.0, 0.5),
+    (2, 20, 128, False, torch.float32, torch.int64, 1.0, 300.0),     # interleaved pairs; heavy saturation
+    (3, 9, 7, True, torch.bfloat16, torch.int32, 3.0, 3.0),          # bf16 cache; heads not a multiple of 16
+    (4, 64, 33, False, torch.bfloat16, torch.int64, 0.01, 2000.0),   # subnormal codes and saturation
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"r{c[0]}" for c in CASES])
+def test_rope_quantize_matches_oracle(case):
+    seed, nnz, H, neox, cdt, pdt, sq, skv = case
+    w = W.rope_quantize(seed=seed, nnz=nnz, num_heads=H, max_seq_len=500, is_neox=neox, cache_dtype=cdt)
+    w["pos_ids"] = w["pos_ids"].to(pdt)
+    w["quant_scale_q"], w["quant_scale_kv"] = sq, skv
+    say(f"[rope] case {case}")
+    _same(_gpu(w), _oracle(w), f"case {seed}")
+
+
+def test_rope_quantize_ties_zero_and_saturation():
+    """Latent values at every tie between neighbouring E4M3 values (exact in bf16), both
+    zeros and magnitudes past 448, with unit scales: the rounding and saturation decisions."""
+    vals = oracle.e4m3fn_decode(np.arange(0x7F, dtype=np.uint8))
+    special = np.concatenate([(vals[:-1] + vals[1:]) / 2, [0.0, -0.0, 448.0, 464.0, 500.0, -1024.0, 2.0 ** -10]])
+    special = np.concatenate([special, -special])
+    w = W.rope_quantize(seed=5, nnz=4, num_heads=2, max_seq_len=16, scale=1.0)
+    flat = np.resize(special, w["q_nope"].numel()).astype(np.float32)
+    w["q_nope"] = torch.from_numpy(flat).bfloat16().view(w["q_nope"].shape)
+    assert np.array_equal(w["q_nope"].float().numpy().ravel(), flat)   # exact in bf16
+    _same(_gpu(w), _oracle(w), "ties")
+
+
+def test_rope_quantize_into_merged_rows_from_strided_inputs():
+    """Outputs written into [..., 576] rows (latent then tail), inputs sliced from wider rows."""
+    nnz, H = 24, 8
+    w = W.rope_quantize(seed=6, nnz=nnz, num_heads=H, max_seq_len=100)
+    wide = torch.zeros(nnz, H, 640, dtype=torch.bfloat16)
+    wide[..., 8:72] = w["q_rope"]
+    d = lambda t: t.cuda()
+    q8 = torch.zeros(nnz, H, 576, dtype=torch.float8_e4m3fn, device="cuda")
+    kv8 = torch.zeros(nnz, 576, dtype=torch.float8_e4m3fn, device="cuda")
+    q_rope_in = d(wide)[..., 8:72]
+    assert q_rope_in.stride() == (H * 640, 640, 1)
+    mla_rope_quantize_fp8(q_rope_in, d(w["k_rope"]), d(w["q_nope"]), d(w["k_nope"]), d(w["cos_sin_cache"]),
+                          d(w["pos_ids"]), True, 64.0, 64.0, q_rope_out=q8[..., 512:], k_rope_out=kv8[:, 512:],
+                          q_nope_out=q8[..., :512], k_nope_out=kv8[:, :512])
+    torch.cuda.synchronize()
+    _same((q8[..., 512:], kv8[:, 512:], q8[..., :512], kv8[:, :512]), _oracle(w), "merged rows")
+
+
+def test_rope_quantize_position_out_of_range_gives_nan_tails():
+    w = W.rope_quantize(seed=7, nnz=6, num_heads=3, max_seq_len=50)
+    w["pos_ids"][2] = 50
+    w["pos_ids"][4] = -1
+    qr, kr, qn, kn = (t.view(torch.uint8).cpu().numpy() for t in _gpu(w))
+    ok = [0, 1, 3, 5]
+    want = _oracle(w, ok)
+    assert np.array_equal(qr[ok], want[0]) and np.array_equal(kr[ok], want[1])
+    assert np.all(qr[[2, 4]] == 0x7F) and np.all(kr[[2, 4]] == 0x7F)
+    # the latent parts do not depend on the position
+    full = oracle.mla_rope_quantize_fp8(np.zeros((6, 3, 64), np.float32), np.zeros((6, 64), np.float32),
+                                        w["q_nope"].float().numpy(), w["k_nope"].float().numpy(),
+                                        w["cos_sin_cache"].numpy(), np.zeros(6, np.int64), True, 64.0, 64.0)
+    assert np.array_equal(qn, full[2]) and np.array_equal(kn, full[3])
+
+
+def test_rope_quantize_empty():
+    w = W.rope_quantize(seed=8, nnz=0, num_heads=4, max_seq_len=10)
+    outs = _gpu(w)
+    assert all(o.numel() == 0 for o in outs)
+
+
+def test_full_size_rope_quantize_sampled_tokens():
+    """The benchmark's workload (4096 tokens x 128 heads) in its launch, checked on sampled tokens."""
+    w = W.rope_quantize()
+    got = _gpu(w)
+    tokens = [0, 1, 77, 1024, 2048, 3000, 4094, 4095]
+    want = _oracle(w, tokens)
+    _same(tuple(g[tokens] for g in got), want, "full size")
