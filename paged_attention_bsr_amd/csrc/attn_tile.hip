@@ -219,7 +219,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   // needs one scalar base per tile plus per-lane byte offsets fixed for the
   // whole loop, blocks advance without a division, and masks follow from the
   // tile's first token (no token array).
-  constexpr bool FAST = BLOCKTILE && !LENS && !MASK;
+  constexpr bool FAST = BLOCKTILE && !LENS;
   uint32_t koff[BPW], voff[BPW];
   if (FAST) {
     const int u = lane & 15;
@@ -291,8 +291,23 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   float l_run = 0.f;
   const float sl2 = a.scale_log2;
 
-  // causal / length mask of S (only on tiles that need it), and the element
-  // mask: bits mw[0..NMW) of this row's plane start at bit `sh` of mw[0]
+  // element mask: bits mw[0..NMW) of this row's plane start at bit `sh` of mw[0]
+  auto mask_bits = [&](const uint32_t (&mw)[NMW], int sh, f32x16 (&sacc)[NKB]) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      // the 32 keys of block kb; this lane's keys sit 8*half further up
+      const uint64_t pair = (static_cast<uint64_t>(mw[kb + 1]) << 32) | mw[kb];
+      const uint32_t w = static_cast<uint32_t>(pair >> sh) >> (8 * half);
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int b = 16 * (g4 >> 1) + 4 * (g4 & 1) + e;
+          sacc[kb][g4 * 4 + e] = (w >> b) & 1u ? sacc[kb][g4 * 4 + e] : -INFINITY;
+        }
+    }
+  };
+  // causal / length mask of S (only on tiles that need it), and the element mask
   auto mask_scores = [&](bool need_mask, const int* ktok, const uint32_t (&mw)[NMW], int sh,
                          f32x16 (&sacc)[NKB]) {
     if (!need_mask) return;
@@ -308,19 +323,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) sacc[kb][g4 * 4 + e] = tt[e] < qbound ? sacc[kb][g4 * 4 + e] : -INFINITY;
       }
-      if (MASK) {
-        // the 32 keys of block kb; this lane's keys sit 8*half further up
-        const uint64_t pair = (static_cast<uint64_t>(mw[kb + 1]) << 32) | mw[kb];
-        const uint32_t w = static_cast<uint32_t>(pair >> sh) >> (8 * half);
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int b = 16 * (g4 >> 1) + 4 * (g4 & 1) + e;
-            sacc[kb][g4 * 4 + e] = (w >> b) & 1u ? sacc[kb][g4 * 4 + e] : -INFINITY;
-          }
-      }
     }
+    if (MASK) mask_bits(mw, sh, sacc);
   };
   // FAST causal mask: key idx of the tile is visible iff idx <= qtok + N - M - lo
   auto mask_fast = [&](int lo, f32x16 (&sacc)[NKB]) {
@@ -412,6 +416,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     }
   };
 
+  // element-mask words of key tile t (positions cb*C + t*KT ..); returns the bit offset
+  auto load_mask_words = [&](int t, uint32_t (&mw)[NMW]) -> int {
+    if (!MASK) {
+#pragma unroll
+      for (int i = 0; i < NMW; ++i) mw[i] = 0u;
+      return 0;
+    }
+    const int64_t p0 = static_cast<int64_t>(cb) * C + static_cast<int64_t>(t) * KT;
+    const uint32_t* src = mplane + (p0 >> 5);
+#pragma unroll
+    for (int i = 0; i < NMW; ++i) mw[i] = src[i];
+    return static_cast<int>(p0 & 31);
+  };
+
   // ---- key loop: two LDS stages, one barrier per tile; the DMA of tile t+1
   // is in flight while tile t is computed
   auto step = [&](int t, unsigned char* cur, const int* curtok, unsigned char* nxt, int* nxttok) {
@@ -425,17 +443,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     // this tile's mask words, loaded ahead of the next tile's DMA so that
     // waiting for them does not wait for that DMA
     uint32_t mw[NMW];
-    int sh = 0;
-    if (MASK) {
-      const int64_t p0 = static_cast<int64_t>(cb) * C + static_cast<int64_t>(t) * KT;
-      const uint32_t* src = mplane + (p0 >> 5);
-      sh = static_cast<int>(p0 & 31);
-#pragma unroll
-      for (int i = 0; i < NMW; ++i) mw[i] = src[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < NMW; ++i) mw[i] = 0u;
-    }
+    const int sh = load_mask_words(t, mw);
     if (t + 1 < ntiles) dma_tile(t + 1, nxt, nxttok);
     if (!wave_active || (CAUSAL && lo > wave_lim)) return;  // tile above this wave's diagonal
     const bool need_mask = MASK || LENS || (t * KT + KT > npos) || (CAUSAL && hi > wave_lim_lo);
@@ -455,11 +463,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's DMA into `cur` has landed
     __syncthreads();                     // ... and every other wave's
     const int lo = lo_next;
+    uint32_t mw[NMW];
+    const int sh = load_mask_words(t, mw);
     if (t + 1 < ntiles) lo_next = dma_fast(nxt);
     if (!wave_active || (CAUSAL && lo > wave_lim)) return;  // tile above this wave's diagonal
     f32x16 sc[NKB];
     qk(cur, sc);
     if (CAUSAL && static_cast<int64_t>(lo) + (KT - 1) > wave_lim_lo) mask_fast(lo, sc);
+    if (MASK) mask_bits(mw, sh, sc);
     bool upd;
     const float alpha = softmax_core(sc, true, upd);
     if (__ballot(upd) != 0) {
