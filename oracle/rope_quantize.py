@@ -25,9 +25,13 @@ Readings taken where the pages are silent:
     the scale multiplication rounded to float32 on its own (no fused
     multiply-add), so the float32 value each code is cast from is fixed;
   * the cast rounds to the nearest finite E4M3 value, ties to the even code,
-    and saturates: magnitudes beyond 448 become +-448; zero keeps its sign;
-  * inputs are finite; a position outside [0, max_seq_len) is the caller's
-    error (the library writes NaN codes for that token's rotated tails).
+    and saturates: magnitudes beyond 448, infinities included, become +-448;
+    zero keeps its sign;
+  * a NaN value is cast to a NaN code (OCP E4M3: 0x7F or 0xFF; this oracle
+    writes 0x7F, and which of the two a NaN becomes is not part of the
+    result), so a bad activation is not turned into a large finite key;
+  * a position outside [0, max_seq_len) is the caller's error (the library
+    writes NaN codes for that token's rotated tails).
 """
 from __future__ import annotations
 
@@ -43,18 +47,19 @@ _POS_VALUES = e4m3fn_decode(np.arange(0x7F, dtype=np.uint8))
 
 def e4m3fn_encode(values) -> np.ndarray:
     """R2: float values -> E4M3 codes (uint8): nearest finite value, ties to the even
-    code, magnitudes above 448 saturated to 448, the sign bit from the value's sign."""
+    code, magnitudes above 448 (and infinities) saturated to 448, the sign bit from the
+    value's sign; NaN -> the NaN code 0x7F."""
     v = np.asarray(values, dtype=np.float64)
-    if not np.isfinite(v).all():
-        raise ValueError("inputs must be finite")
-    mag = np.minimum(np.abs(v), _POS_VALUES[-1])
+    nan = np.isnan(v)
+    mag = np.minimum(np.abs(np.where(nan, 0.0, v)), _POS_VALUES[-1])
     hi = np.clip(np.searchsorted(_POS_VALUES, mag, side="left"), 0, len(_POS_VALUES) - 1)
     lo = np.maximum(hi - 1, 0)
     d_lo = mag - _POS_VALUES[lo]
     d_hi = _POS_VALUES[hi] - mag
     pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
     code = np.where(pick_hi, hi, lo).astype(np.uint8)
-    return code | np.where(np.signbit(v), 0x80, 0).astype(np.uint8)
+    code = code | np.where(np.signbit(v), 0x80, 0).astype(np.uint8)
+    return np.where(nan, np.uint8(0x7F), code).astype(np.uint8)
 
 
 def rope_fp32(x, cos, sin, is_neox: bool) -> np.ndarray:

@@ -43,7 +43,13 @@ __device__ __forceinline__ float rounded(float x) {
   return x;
 }
 
-__device__ __forceinline__ float sat448(float x) { return fminf(fmaxf(x, -kFp8Max), kFp8Max); }
+// Saturate to the largest finite E4M3 magnitude; NaN passes through (min/max
+// return their non-NaN operand, so it is selected around them) and becomes a
+// NaN code in the cast, infinities become +-448 like any other magnitude.
+__device__ __forceinline__ float sat448(float x) {
+  const float c = fminf(fmaxf(x, -kFp8Max), kFp8Max);
+  return x != x ? x : c;
+}
 
 // eight float32 values -> eight E4M3 codes (little-endian byte order = value order)
 __device__ __forceinline__ u32x2_t fp8x8(const float (&v)[8]) {

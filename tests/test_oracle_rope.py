@@ -35,6 +35,16 @@ def test_encode_decode_round_trip_and_saturation():
     assert e4m3fn_encode(np.array([-0.0, 0.0])).tolist() == [0x80, 0x00]
 
 
+def test_encode_nan_and_infinities():
+    """A NaN value is cast to a NaN code (as torch's float8_e4m3fn cast does, and as the OCP
+    format defines 0x7F / 0xFF); infinities saturate to +-448 like any larger magnitude."""
+    x = np.array([np.nan, -np.nan, np.inf, -np.inf], np.float32)
+    codes = e4m3fn_encode(x)
+    assert np.isnan(e4m3fn_decode(codes[:2])).all()
+    assert np.isnan(e4m3fn_decode(_torch_cast(x[:2]))).all()
+    assert codes[2:].tolist() == [0x7E, 0xFE]
+
+
 def test_rope_closed_forms():
     rng = np.random.default_rng(1)
     x = rng.standard_normal((3, 64)).astype(np.float32)
@@ -127,7 +137,8 @@ MUTATIONS = {
     "layouts_swapped": ("    if is_neox:\n        a, b = x[..., :32], x[..., 32:]", "    if not is_neox:\n        a, b = x[..., :32], x[..., 32:]"),
     "ties_to_odd": ("(hi % 2 == 0)", "(hi % 2 == 1)"),
     "ties_away": ("(d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))", "(d_hi <= d_lo)"),
-    "sign_dropped": ("return code | np.where(np.signbit(v), 0x80, 0).astype(np.uint8)", "return code"),
+    "sign_dropped": ("code = code | np.where(np.signbit(v), 0x80, 0).astype(np.uint8)", "code = code"),
+    "nan_saturated": ("return np.where(nan, np.uint8(0x7F), code).astype(np.uint8)", "return code"),
     "scale_dropped": ("e4m3fn_encode(np.asarray(q_nope, dtype=np.float32) * sq)", "e4m3fn_encode(np.asarray(q_nope, dtype=np.float32))"),
     "cos_sin_swapped": ("cos, sin = cache[pos, :32], cache[pos, 32:]", "cos, sin = cache[pos, 32:], cache[pos, :32]"),
     "kv_scale_for_q": ("q_rot = rope_fp32(q_rope, cos[:, None, :], sin[:, None, :], is_neox)\n    k_rot", "q_rot = rope_fp32(q_rope, cos[:, None, :], sin[:, None, :], is_neox) * (skv / sq)\n    k_rot"),
@@ -145,6 +156,7 @@ def _mutant(name):
 
 
 PINS = [test_encode_matches_torch_cast_in_range, test_encode_decode_round_trip_and_saturation, test_rope_closed_forms,
+        test_encode_nan_and_infinities,
         lambda: test_rope_is_complex_rotation(True), lambda: test_rope_is_complex_rotation(False),
         test_neox_and_interleaved_layouts_are_a_permutation_apart, lambda: test_quantized_outputs_within_half_a_step(True),
         lambda: test_quantized_outputs_within_half_a_step(False), test_scale_applies_before_the_cast]
