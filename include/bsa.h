@@ -201,19 +201,33 @@ bsa_status_t bsa_plan(const int32_t* indptr, const int32_t* indices, int64_t M, 
 bsa_status_t bsa_plan_ex(const bsa_plan_desc_t* desc, bsa_plan_t* out_plan);
 
 /* Bytes of device workspace bsa_run needs for this plan (multiple of 256).
- * The workspace holds the plan's tables (uploaded once) and the split-KV
- * partials.  Returns 0 for a NULL plan. */
+ * The caller owns and allocates the workspace, as the wrappers of
+ * flashinfer.sparse take a user-reserved float_workspace_buffer in their
+ * constructor (BlockSparseAttentionWrapper.__init__: it stores the
+ * intermediate results of the split-k algorithm).  Here it holds the plan's
+ * tables followed by the split-KV partials; the library never allocates
+ * device memory.  Returns 0 for a NULL plan. */
 size_t bsa_workspace_size(bsa_plan_t plan);
 
-/* Copy the plan's tables into `workspace` (device memory of at least
- * bsa_workspace_size bytes, 256-byte aligned) on `stream`.  bsa_run does this
- * by itself the first time it sees a workspace that does not hold this
- * plan's tables, so calling it is only needed to keep the copy out of a
- * later run (for example before capturing runs in a HIP graph).  The
- * library remembers, per device and workspace address, which plan's tables
- * it last wrote there; if anything else writes that memory afterwards, call
- * bsa_upload again. */
+/* Bind `workspace` (device memory of at least bsa_workspace_size bytes,
+ * 256-byte aligned) to the plan: copy the plan's tables into it on `stream`
+ * and pin them there, so that later bsa_run calls on this workspace skip the
+ * copy (BlockSparseAttentionWrapper.plan copies its auxiliary structures to
+ * the device once and every run reuses them; reset_workspace_buffer hands a
+ * wrapper new buffers).  The pin is remembered per device and workspace
+ * address, and it is the caller's promise that the memory keeps the tables:
+ * while pinned, nothing else may write it, and it must not be freed and
+ * reused.  A pin ends with bsa_unpin, bsa_plan_destroy, a bsa_upload of
+ * another plan to the same address, or any bsa_run of another plan on it.
+ * bsa_run on a workspace that is not pinned to its plan copies the tables
+ * itself, every time: that is always correct, only slower.  Pin before
+ * capturing runs in a HIP graph (the copy is then not part of the run). */
 bsa_status_t bsa_upload(bsa_plan_t plan, void* workspace, size_t workspace_bytes, void* stream);
+
+/* End the plan's pin on `workspace` (see bsa_upload), e.g. before freeing
+ * the memory; nothing happens if the plan is not pinned there.  Host-only:
+ * launches nothing.  BSA_ERR_INVALID_ARGUMENT for NULL arguments. */
+bsa_status_t bsa_unpin(bsa_plan_t plan, void* workspace);
 
 /*
  * Run the planned attention on `stream` (hipStream_t; NULL = default stream).
@@ -226,8 +240,11 @@ bsa_status_t bsa_upload(bsa_plan_t plan, void* workspace, size_t workspace_bytes
  * q, k, v, o must be 16-byte aligned and must not overlap the workspace.
  * Every one of the M * num_qo_heads output rows is written; rows with no
  * unmasked key get o = 0 and lse = -inf.  The call only enqueues work on
- * `stream` (after the one-time table upload described at bsa_upload): it
- * neither synchronises nor allocates device memory.
+ * `stream`: it neither synchronises nor allocates device memory.  Unless the
+ * workspace is pinned to this plan (bsa_upload), the plan's tables are first
+ * copied into it on `stream` (BlockSparseAttentionWrapper.run reuses what
+ * plan() prepared; run() takes q, k, v and returns o and, with return_lse,
+ * the lse).
  */
 bsa_status_t bsa_run(bsa_plan_t plan, const void* q, const void* k, const void* v, void* o,
                      float* lse, void* workspace, size_t workspace_bytes, void* stream);
@@ -401,10 +418,19 @@ bsa_status_t bsa_plan_export_workgroups(bsa_plan_t plan, int32_t* wg_ptr);
  * nothing is copied for a plan without element masks. */
 bsa_status_t bsa_plan_export_mask_bits(bsa_plan_t plan, uint32_t* bits);
 
+/* Free the plan's host memory and end its workspace pins.  A plan is made
+ * once and reused across runs until the structure changes (MATE sparse-MLA
+ * decode, "Metadata reuse": a new metadata object for new sequence lengths,
+ * query shape or top-k); destroying it is the end of that reuse.  The caller
+ * must not destroy a plan whose runs are still being enqueued on another
+ * thread.  NULL is a no-op. */
 void bsa_plan_destroy(bsa_plan_t plan);
 
 /* Text of the calling thread's last error ("" if none).  Valid until the
- * thread's next bsa_* call. */
+ * thread's next bsa_* call.  Unsupported shapes, dtypes or layouts are
+ * reported, never silently run another way (MATE FlashInfer wrapper, FP8
+ * sparse MLA decode: unsupported inputs "fail explicitly"; flashinfer.sparse
+ * plan(): a GQA ratio the kernel lacks raises an error). */
 const char* bsa_last_error(void);
 
 #ifdef __cplusplus

@@ -139,6 +139,8 @@ def lib() -> ctypes.CDLL:
     L.bsa_workspace_size.restype = sz
     L.bsa_upload.argtypes = [vp, vp, sz, vp]
     L.bsa_upload.restype = st
+    L.bsa_unpin.argtypes = [vp, vp]
+    L.bsa_unpin.restype = st
     L.bsa_run.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.bsa_run.restype = st
     L.bsa_run_phase.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]

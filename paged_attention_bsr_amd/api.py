@@ -8,6 +8,7 @@ flashinfer.sparse BlockSparseAttentionWrapper plan()/run() parameters.
 from __future__ import annotations
 
 import ctypes
+import weakref
 from typing import Optional
 
 import numpy as np
@@ -143,6 +144,9 @@ class Plan:
         self.k_token_stride = int(k_token_stride) or self.num_kv_heads * self.head_dim
         self.v_token_stride = int(v_token_stride) or self.num_kv_heads * self.head_dim_vo
         self._workspace: Optional[torch.Tensor] = None
+        # the workspace tensor this plan's tables are pinned in (bsa_upload), held weakly:
+        # a freed tensor whose memory comes back at the same address is a new workspace
+        self._pinned: Optional[tuple] = None
 
     @classmethod
     def variable(cls, block_mask_map, block_row_sz, block_col_sz, num_qo_heads: int, num_kv_heads: int,
@@ -196,9 +200,20 @@ class Plan:
         return self._workspace
 
     def upload(self, workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+        """Copy the tables into ``workspace`` and pin them there (bsa_upload); later runs on
+        the same tensor skip the copy."""
         ws = self.workspace() if workspace is None else workspace
         st = torch.cuda.current_stream(ws.device).cuda_stream if stream is None else stream
         L.check(L.lib().bsa_upload(self._handle, ws.data_ptr(), ws.numel() * ws.element_size(), st))
+        self._pinned = (weakref.ref(ws), ws.data_ptr(), ws.numel() * ws.element_size())
+
+    def _ensure_pinned(self, ws: torch.Tensor, stream) -> None:
+        """Pin the tables in ``ws`` unless this very tensor (alive, same memory) holds them."""
+        pin = self._pinned
+        if pin is not None and pin[0]() is ws and pin[1] == ws.data_ptr() and \
+                pin[2] == ws.numel() * ws.element_size():
+            return
+        self.upload(ws, stream)
 
     def run(self, q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor] = None,
             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
@@ -233,6 +248,7 @@ class Plan:
             lse = torch.empty((self.M, self.num_qo_heads), dtype=torch.float32, device=q.device)
         ws = self.workspace(q.device) if workspace is None else workspace
         st = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+        self._ensure_pinned(ws, st)
         scales = []
         for name, t, n in (("scale_q", scale_q, self.num_qo_heads), ("scale_k", scale_k, self.num_kv_heads),
                            ("scale_v", scale_v, self.num_kv_heads)):

@@ -27,9 +27,16 @@ bsa_status_t set_err(bsa_status_t st, const std::string& msg) {
   return st;
 }
 
-// Which plan's tables each (device, workspace address) currently holds.
+// Which plan's tables each (device, workspace address) currently holds, and
+// whether the caller pinned them there with bsa_upload.  Only a pinned entry
+// lets bsa_run skip the upload: an address alone says nothing about the
+// memory's contents once the caller may have freed and reused it.
+struct Binding {
+  uint64_t plan_id;
+  bool pinned;
+};
 std::mutex g_reg_mu;
-std::map<std::pair<int, uintptr_t>, uint64_t> g_registry;
+std::map<std::pair<int, uintptr_t>, Binding> g_registry;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -44,23 +51,26 @@ bsa_status_t hip_fail(hipError_t e, const char* what) {
   return set_err(BSA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-bsa_status_t do_upload(const bsa::Plan& P, void* ws, hipStream_t st) {
+// Copies the plan's tables into `ws` and records them there, pinned or not
+// (an unpinned upload also drops any other plan's pin at that address: its
+// tables are gone).
+bsa_status_t do_upload(const bsa::Plan& P, void* ws, hipStream_t st, bool pin) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   e = hipMemcpyAsync(ws, P.table_blob.data(), static_cast<size_t>(P.table_bytes), hipMemcpyHostToDevice, st);
   if (e != hipSuccess) return hip_fail(e, "table upload");
   std::lock_guard<std::mutex> lk(g_reg_mu);
-  g_registry[{dev, reinterpret_cast<uintptr_t>(ws)}] = P.id;
+  g_registry[{dev, reinterpret_cast<uintptr_t>(ws)}] = Binding{P.id, pin};
   return BSA_OK;
 }
 
-bool holds_tables(const bsa::Plan& P, void* ws) {
+bool pinned_here(const bsa::Plan& P, void* ws) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
   std::lock_guard<std::mutex> lk(g_reg_mu);
   auto it = g_registry.find({dev, reinterpret_cast<uintptr_t>(ws)});
-  return it != g_registry.end() && it->second == P.id;
+  return it != g_registry.end() && it->second.plan_id == P.id && it->second.pinned;
 }
 
 }  // namespace
@@ -158,7 +168,19 @@ bsa_status_t bsa_upload(bsa_plan_t plan, void* workspace, size_t workspace_bytes
     return set_err(BSA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   if (workspace_bytes < static_cast<size_t>(plan->p.workspace_bytes))
     return set_err(BSA_ERR_WORKSPACE_TOO_SMALL, "workspace smaller than bsa_workspace_size(plan)");
-  return do_upload(plan->p, workspace, static_cast<hipStream_t>(stream));
+  return do_upload(plan->p, workspace, static_cast<hipStream_t>(stream), true);
+}
+
+bsa_status_t bsa_unpin(bsa_plan_t plan, void* workspace) {
+  g_err.clear();
+  if (!plan || !workspace) return set_err(BSA_ERR_INVALID_ARGUMENT, "plan and workspace must be non-NULL");
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_reg_mu);
+  auto it = g_registry.find({dev, reinterpret_cast<uintptr_t>(workspace)});
+  if (it != g_registry.end() && it->second.plan_id == plan->p.id) g_registry.erase(it);
+  return BSA_OK;
 }
 
 bsa_status_t bsa_run(bsa_plan_t plan, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -203,8 +225,8 @@ bsa_status_t bsa_run_ex(bsa_plan_t plan, int32_t phase, const void* q, const voi
     return set_err(BSA_ERR_INVALID_ARGUMENT, "o must not overlap q");
 
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (!holds_tables(P, workspace)) {
-    const bsa_status_t s = do_upload(P, workspace, st);
+  if (!pinned_here(P, workspace)) {
+    const bsa_status_t s = do_upload(P, workspace, st, false);
     if (s != BSA_OK) return s;
   }
   unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -341,7 +363,7 @@ void bsa_plan_destroy(bsa_plan_t plan) {
   {
     std::lock_guard<std::mutex> lk(g_reg_mu);
     for (auto it = g_registry.begin(); it != g_registry.end();) {
-      if (it->second == plan->p.id) it = g_registry.erase(it);
+      if (it->second.plan_id == plan->p.id) it = g_registry.erase(it);
       else ++it;
     }
   }
