@@ -417,22 +417,31 @@ def test_element_masks(case, kv_splits):
 
 
 VARIABLE = [
-    # (seed, M, min_block, max_block, density, causal, Hq, Hkv, grid)
-    (61, 300, 8, 40, 0.3, False, 8, 2, {}),
-    (62, 257, 20, 90, 0.25, True, 16, 4, {}),            # N odd: a grid of 1-key blocks
-    (63, 512, 1, 200, 0.2, True, 4, 4, {"R": 32, "C": 16}),
-    (64, 200, 50, 50, 0.5, False, 32, 8, {"C": 8}),
+    # (seed, M, min_block, max_block, density, causal, Hq, Hkv, grid, dtype)
+    (61, 300, 8, 40, 0.3, False, 8, 2, {}, torch.float16),
+    (62, 257, 20, 90, 0.25, True, 16, 4, {}, torch.float16),            # N odd: a grid of 1-key blocks
+    (63, 512, 1, 200, 0.2, True, 4, 4, {"R": 32, "C": 16}, torch.float16),
+    (64, 200, 50, 50, 0.5, False, 32, 8, {"C": 8}, torch.float16),
+    # causal on grids whose key blocks hold whole key tiles: the masked whole-tile path
+    # with the causal mask on top (128-row tiles over 64-key blocks; 32-row tiles over
+    # 32-key blocks), fp16 and bf16
+    (65, 512, 20, 120, 0.3, True, 16, 4, {"R": 32, "C": 64}, torch.bfloat16),
+    (66, 384, 20, 120, 0.3, True, 8, 2, {"R": 32, "C": 64}, torch.float16),
+    (67, 256, 10, 60, 0.3, True, 8, 8, {"R": 32, "C": 32}, torch.float16),
 ]
 
 
 @pytest.mark.parametrize("case", VARIABLE, ids=[f"v{c[0]}" for c in VARIABLE])
 @pytest.mark.parametrize("kv_splits", [1, 0])
 def test_variable_blocks(case, kv_splits):
-    seed, M, lo, hi, dens, causal, Hq, Hkv, grid = case
+    seed, M, lo, hi, dens, causal, Hq, Hkv, grid, dtype = case
     w = W.variable_block_prefill(seed=seed, M=M, min_block=lo, max_block=hi, density=dens, causal=causal,
-                                 num_qo_heads=Hq, num_kv_heads=Hkv)
+                                 num_qo_heads=Hq, num_kv_heads=Hkv, dtype=dtype)
     w.meta["grid"] = grid
-    _check(w, kv_splits, what=f"variable blocks s{seed} grid={grid} splits={kv_splits}")
+    if grid.get("C") in (32, 64):
+        inf = plan_for(w, kv_splits).info()
+        assert inf["kernel"] == 0 and inf["key_tile"] == grid["C"], inf
+    _check(w, kv_splits, what=f"variable blocks s{seed} grid={grid} {dtype} splits={kv_splits}")
 
 
 def test_variable_worked_example():
