@@ -265,6 +265,24 @@ bsa_status_t bsa_run_phase(bsa_plan_t plan, int32_t phase, const void* q, const 
                            void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * bsa_run for callers that cannot allocate device memory or pass a workspace:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments and results as bsa_run without the workspace:
+ * the library runs the plan in its own workspace, a static device array of
+ * BSA_NOALLOC_MAX_WORKSPACE bytes per GPU, held from the library's load
+ * until the process ends.  No call allocates or frees device memory.  The
+ * plan's tables are copied into that array on `stream` when another plan
+ * used it last, else reused.  Every call on one GPU shares the array: calls
+ * that overlap on one GPU (other threads, other streams) race, and the
+ * caller must order them.  A plan with bsa_workspace_size(plan) >
+ * BSA_NOALLOC_MAX_WORKSPACE is refused with BSA_ERR_WORKSPACE_TOO_SMALL,
+ * before anything touches the GPU; other errors as for bsa_run.
+ */
+#define BSA_NOALLOC_MAX_WORKSPACE (32u << 20)
+bsa_status_t bsa_run_noalloc(bsa_plan_t plan, const void* q, const void* k, const void* v, void* o,
+                             float* lse, void* stream);
+
+/*
  * bsa_run_phase with per-head dequant scales (BlockSparseAttentionWrapper.run:
  * scale_q (num_qo_heads), scale_k and scale_v (num_kv_heads), per-head
  * quantization used with FP8): device float32 arrays, each NULL for 1.0.  The

@@ -17,6 +17,7 @@ BSA_ERR_HOST_ALLOC = 5
 BSA_F16, BSA_BF16, BSA_FP8_E4M3, BSA_FP32_OUT = 0, 1, 2, 3
 BSA_KERNEL_TILE, BSA_KERNEL_MLA, BSA_KERNEL_DECODE = 0, 1, 2
 BSA_PHASE_ATTENTION, BSA_PHASE_MERGE, BSA_PHASE_ALL = 1, 2, 3
+BSA_NOALLOC_MAX_WORKSPACE = 32 << 20   # bytes of bsa_run_noalloc's own workspace (bsa.h)
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
@@ -147,6 +148,8 @@ def lib() -> ctypes.CDLL:
     L.bsa_run_phase.restype = st
     L.bsa_run_ex.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.bsa_run_ex.restype = st
+    L.bsa_run_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    L.bsa_run_noalloc.restype = st
     L.bsa_merge_states.argtypes = [vp, vp, vp, vp, i64, i32, i32, i32, i32, vp]
     L.bsa_merge_states.restype = st
     L.bsa_plan_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]

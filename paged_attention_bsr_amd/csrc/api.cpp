@@ -65,6 +65,36 @@ bsa_status_t do_upload(const bsa::Plan& P, void* ws, hipStream_t st, bool pin) {
   return BSA_OK;
 }
 
+// Library-owned workspace for bsa_run_noalloc: a file-scope device array
+// (each device holds its own copy for the life of the process).  In host code
+// `scratch` names a host-side stand-in, never the device memory: host code
+// only uses the address hipGetSymbolAddress returns for the current device.
+constexpr size_t kScratchBytes = BSA_NOALLOC_MAX_WORKSPACE;
+static_assert(kScratchBytes % 256 == 0, "scratch holds 256-byte aligned workspaces");
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;  // device -> address of its copy of `scratch`
+
+// The current device's copy of `scratch` (looked up once per device, with that
+// device current).
+bsa_status_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return set_err(BSA_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    it = g_scratch_ptr.emplace(dev, ptr).first;
+  }
+  *out = it->second;
+  return BSA_OK;
+}
+
 bool pinned_here(const bsa::Plan& P, void* ws) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return false;
@@ -288,6 +318,26 @@ bsa_status_t bsa_run_ex(bsa_plan_t plan, int32_t phase, const void* q, const voi
   e = bsa::launch_merge(m, d.o_dtype == BSA_BF16 ? 1 : 0, st);
   if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
   return BSA_OK;
+}
+
+bsa_status_t bsa_run_noalloc(bsa_plan_t plan, const void* q, const void* k, const void* v, void* o, float* lse,
+                             void* stream) {
+  g_err.clear();
+  if (!plan) return set_err(BSA_ERR_INVALID_ARGUMENT, "plan is NULL");
+  if (static_cast<size_t>(plan->p.workspace_bytes) > kScratchBytes)
+    return set_err(BSA_ERR_WORKSPACE_TOO_SMALL,
+                   "plan needs " + std::to_string(plan->p.workspace_bytes) + " bytes of workspace; bsa_run_noalloc "
+                   "has " + std::to_string(kScratchBytes) + " (use bsa_run with a caller workspace)");
+  void* ws = nullptr;
+  const bsa_status_t st = scratch_address(&ws);
+  if (st != BSA_OK) return st;
+  // the library alone writes `scratch`, so a pin there is exact: copy the tables only
+  // when another plan ran here last
+  if (!pinned_here(plan->p, ws)) {
+    const bsa_status_t su = do_upload(plan->p, ws, static_cast<hipStream_t>(stream), true);
+    if (su != BSA_OK) return su;
+  }
+  return bsa_run_ex(plan, BSA_PHASE_ALL, q, k, v, o, lse, nullptr, nullptr, nullptr, ws, kScratchBytes, stream);
 }
 
 bsa_status_t bsa_merge_states(const float* v, const float* s, void* v_out, float* s_out, int64_t seq_len,

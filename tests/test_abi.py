@@ -154,3 +154,24 @@ def test_rope_quant_validates_before_touching_the_gpu():
     a.num_heads, a.quant_scale_q = 4, float("inf")
     assert lib.bsa_mla_rope_quantize_fp8(ctypes.byref(a), None) == L.BSA_ERR_INVALID_ARGUMENT
     assert lib.bsa_mla_rope_quantize_fp8(None, None) == L.BSA_ERR_INVALID_ARGUMENT
+
+
+def test_noalloc_limit_matches_header_and_refuses_large_plans_on_the_host():
+    """bsa_run_noalloc's workspace limit is the header's BSA_NOALLOC_MAX_WORKSPACE; a plan
+    needing more is refused before anything touches the GPU (fake pointers: never used)."""
+    text = open(HEADER).read()
+    m = re.search(r"#define BSA_NOALLOC_MAX_WORKSPACE \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == L.BSA_NOALLOC_MAX_WORKSPACE
+    from paged_attention_bsr_amd import workloads as W
+    w = W.bsr_prefill(M=8192, values=False)
+    d = _desc(indptr=w.indptr, indices=w.indices, M=w.M, N=w.N, R=w.R, C=w.C, num_qo_heads=32, num_kv_heads=8,
+              head_dim_qk=128, causal=1, kv_splits=8, num_cus=256)
+    lib = L.lib()
+    h = ctypes.c_void_p()
+    assert lib.bsa_plan_ex(ctypes.byref(d), ctypes.byref(h)) == L.BSA_OK
+    assert lib.bsa_workspace_size(h) > L.BSA_NOALLOC_MAX_WORKSPACE
+    fake = 1 << 40
+    st = lib.bsa_run_noalloc(h, fake, fake, fake, fake + (1 << 32), None, None)
+    assert st == L.BSA_ERR_WORKSPACE_TOO_SMALL and "bsa_run_noalloc" in lib.bsa_last_error().decode()
+    lib.bsa_plan_destroy(h)
+    assert lib.bsa_run_noalloc(None, fake, fake, fake, fake, None, None) == L.BSA_ERR_INVALID_ARGUMENT
