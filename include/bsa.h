@@ -60,7 +60,7 @@ typedef enum { BSA_F16 = 0, BSA_BF16 = 1, BSA_FP8_E4M3 = 2 } bsa_dtype_t;
 
 /* Kernel family a plan selected (informational). */
 typedef enum {
-  BSA_KERNEL_TILE = 0,    /* MFMA tile kernel: head_dim 128, fp16/bf16, any R, C */
+  BSA_KERNEL_TILE = 0,    /* MFMA tile kernel: head_dim 128, fp16/bf16 (kv also fp8 e4m3), any R, C */
   BSA_KERNEL_MLA = 1,     /* MFMA sparse-MLA kernel: Dqk 576 / Dv 512, bf16 q/o, fp8 e4m3 kv, R = 1 */
   BSA_KERNEL_DECODE = 2   /* paged-decode kernel: R = 1, C >= 16, head_dim 128, fp16/bf16 (kv also fp8 e4m3), <= 16 qo heads per kv head */
 } bsa_kernel_t;
@@ -87,8 +87,9 @@ typedef enum {
  *   kv_block_lens  NULL, or int32[NB] valid tokens per key block, each in [1, C]
  *   q/kv/o_dtype   storage types.  Supported: all BSA_F16, or all BSA_BF16
  *                  (head_dim 128); q/o BSA_F16 or BSA_BF16 with kv BSA_FP8_E4M3
- *                  for head_dim 128 decode shapes (R = 1, C >= 16, at most 16
- *                  qo heads per kv head); or q/o BSA_BF16 with kv BSA_FP8_E4M3 and
+ *                  for head_dim 128, any R and C (decode and prefill shapes;
+ *                  BlockSparseAttentionWrapper.run: scale_k / scale_v "used with
+ *                  FP8 Quantization"); or q/o BSA_BF16 with kv BSA_FP8_E4M3 and
  *                  head_dim_qk 576 / head_dim_vo 512 / one kv head / R = 1.
  *   q_descale etc. per-tensor dequant scales: real value = stored * descale
  *                  (MATE scale folding: the logit scale becomes
@@ -131,8 +132,8 @@ typedef enum {
  *                  entry i in bit i % 8 (least significant first) of byte i / 8
  * With a mask the causal flag has no effect (the pages: causal applies only
  * when no mask is given); kv_block_lens must be NULL (lengths belong in the
- * mask).  Element masks run on the tile kernel (head_dim 128, fp16/bf16), also
- * for R = 1 shapes.
+ * mask).  Element masks run on the tile kernel (head_dim 128, fp16/bf16, K/V
+ * also fp8 e4m3), also for R = 1 shapes.
  *
  * Variable block sizes (VariableBlockSparseAttentionWrapper.plan:
  * block_mask_map, block_row_sz, block_col_sz; each kv head its own pattern):
@@ -289,8 +290,9 @@ bsa_status_t bsa_run_noalloc(bsa_plan_t plan, const void* q, const void* k, cons
  * value a kernel uses is stored value * descale of the plan * scale of the
  * head, i.e. logits are scaled by sm_scale * q_descale * k_descale *
  * scale_q[h] * scale_k[h / g] and outputs by v_descale * scale_v[h / g].
- * Supported by the paged-decode kernel (R = 1, C >= 16; K/V fp16, bf16 or
- * fp8 e4m3); BSA_ERR_UNSUPPORTED for other plans when any scale is given.
+ * Supported by every head_dim 128 plan (tile and paged-decode kernels; K/V
+ * fp16, bf16 or fp8 e4m3); BSA_ERR_UNSUPPORTED for the sparse-MLA shape (one
+ * kv head: its per-tensor descales are the plan's) when any scale is given.
  */
 bsa_status_t bsa_run_ex(bsa_plan_t plan, int32_t phase, const void* q, const void* k, const void* v,
                         void* o, float* lse, const float* scale_q, const float* scale_k, const float* scale_v,

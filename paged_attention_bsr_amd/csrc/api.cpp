@@ -232,8 +232,9 @@ bsa_status_t bsa_run_ex(bsa_plan_t plan, int32_t phase, const void* q, const voi
     return set_err(BSA_ERR_INVALID_ARGUMENT, "phase must be BSA_PHASE_ATTENTION, BSA_PHASE_MERGE or BSA_PHASE_ALL");
   const bsa::Plan& P = plan->p;
   const bsa_plan_desc_t& d = P.d;
-  if ((scale_q || scale_k || scale_v) && P.kernel != BSA_KERNEL_DECODE)
-    return set_err(BSA_ERR_UNSUPPORTED, "per-head scales are supported by the paged-decode kernel (R = 1, C >= 16)");
+  if ((scale_q || scale_k || scale_v) && P.kernel == BSA_KERNEL_MLA)
+    return set_err(BSA_ERR_UNSUPPORTED, "per-head scales apply to head_dim 128 plans (the sparse-MLA shape has "
+                                        "one kv head: use the plan's per-tensor descales)");
   if ((reinterpret_cast<uintptr_t>(scale_q) | reinterpret_cast<uintptr_t>(scale_k) |
        reinterpret_cast<uintptr_t>(scale_v)) & 3u)
     return set_err(BSA_ERR_INVALID_ARGUMENT, "scale arrays must be 4-byte aligned");
@@ -298,8 +299,8 @@ bsa_status_t bsa_run_ex(bsa_plan_t plan, int32_t phase, const void* q, const voi
     else if (P.kernel == BSA_KERNEL_DECODE)
       e = bsa::launch_attn_decode(a, d.q_dtype == BSA_BF16, d.kv_dtype == BSA_FP8_E4M3, d.causal != 0,
                                   a.lens != nullptr, st);
-    else e = bsa::launch_attn_tile(a, d.q_dtype == BSA_BF16, P.tile_rows, d.causal != 0, a.lens != nullptr,
-                                   a.mbits != nullptr, st);
+    else e = bsa::launch_attn_tile(a, d.q_dtype == BSA_BF16, d.kv_dtype == BSA_FP8_E4M3, P.tile_rows,
+                                   d.causal != 0, a.lens != nullptr, a.mbits != nullptr, st);
     if (e != hipSuccess) return hip_fail(e, "attention kernel launch");
   }
   if (!(phase & BSA_PHASE_MERGE)) return BSA_OK;

@@ -16,6 +16,12 @@
 //     swizzled by key, each lane fetching the chunk that belongs in its slot.
 //     The DMA of tile t+1 lands in the other of two LDS stages while tile t
 //     is computed; one wait + barrier per tile;
+//   * fp8 e4m3 K/V (KV8; run()'s per-head scale_k / scale_v with FP8 KV):
+//     the tile is staged through registers instead -- loaded one tile ahead
+//     as 16-byte pieces (16 values), widened exactly to the 16-bit type
+//     (every e4m3 value is an fp16 and a bf16 value) and stored into the
+//     same swizzled LDS layout at the end of the step, so every later read
+//     is unchanged; the dequant scales fold into the logit and output scales;
 //   * each wave computes S^T = K Q^T for its 32 rows with
 //     v_mfma_f32_32x32x16 (K from LDS as the A operand, Q^T held in
 //     registers as B), so every lane owns one query row and its row max
@@ -73,7 +79,7 @@ __device__ __forceinline__ int v_off(int key, int c) { return key * 256 + ((c ^ 
 // S^T row m of a 32-key block holds key swap23(m) (bits 2 and 3 exchanged).
 __device__ __forceinline__ int swap23(int m) { return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1); }
 
-template <typename T, int NW, int KT, bool CAUSAL, bool LENS, bool BLOCKTILE, bool MASK>
+template <typename T, int NW, int KT, bool CAUSAL, bool LENS, bool BLOCKTILE, bool MASK, bool KV8>
 __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   using Ops = MfmaType<T>;
   using v8 = typename Ops::v8;
@@ -179,9 +185,13 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     }
   };
 
+  constexpr int kElt = KV8 ? 1 : 2;  // bytes per stored K/V value
   const T* kbase = static_cast<const T*>(a.k) + static_cast<int64_t>(kvh) * kD;
   const T* vbase = static_cast<const T*>(a.v) + static_cast<int64_t>(kvh) * kD;
   const T* zrow = static_cast<const T*>(a.zero_row);
+  const unsigned char* kbase8 = static_cast<const unsigned char*>(a.k) + static_cast<int64_t>(kvh) * kD * kElt;
+  const unsigned char* vbase8 = static_cast<const unsigned char*>(a.v) + static_cast<int64_t>(kvh) * kD * kElt;
+  const unsigned char* zrow8 = static_cast<const unsigned char*>(a.zero_row);
   // ---- global -> LDS by DMA (global_load_lds, 16 B per lane): a K or V tile
   // is KT/4 blocks of 1 KB = 4 rows; wave w fills blocks w*BPW .. (w+1)*BPW-1
   // of both.  Lane l of a block serves row 4b + l/16 and slot l%16, i.e. it
@@ -205,6 +215,46 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
                                        (__attribute__((address_space(3))) void*)(st + L::kKBytes + b * 1024), 16, 0,
                                        0);
       if (u == 0) ktok[row] = tok;
+    }
+  };
+
+  // ---- KV8 staging: a tile's fp8 K (and V) rows are KT x 8 pieces of 16 bytes;
+  // thread tid takes pieces tid, tid + NTHR, ... (8 consecutive threads read one
+  // 128-byte row), keeps them in registers while the current tile is computed,
+  // then widens each piece to two 16-byte chunks of the 16-bit row and stores
+  // them where the DMA would have put those chunks.  Masked keys read the zero row.
+  constexpr int PPT = KV8 ? KT * 8 / NTHR : 1;  // pieces per thread
+  static_assert(!KV8 || (KT * 8) % NTHR == 0, "fp8 pieces per thread");
+  u32x4 k8[PPT], v8r[PPT];
+  int tok8[PPT];
+  auto load8 = [&](int kt) {
+    const TileInfo ti = tile_info(kt);
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int piece = tid + i * NTHR;
+      const int row = piece >> 3;
+      const int pc = (piece & 7) * 16;
+      const int tok = key_tok(kt, ti, row);
+      const unsigned char* pk = tok >= 0 ? kbase8 + static_cast<int64_t>(tok) * a.k_stride : zrow8;
+      const unsigned char* pv = tok >= 0 ? vbase8 + static_cast<int64_t>(tok) * a.v_stride : zrow8;
+      k8[i] = *reinterpret_cast<const u32x4*>(pk + pc);
+      v8r[i] = *reinterpret_cast<const u32x4*>(pv + pc);
+      tok8[i] = tok;
+    }
+  };
+  auto store8 = [&](unsigned char* st, int* ktok) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int piece = tid + i * NTHR;
+      const int row = piece >> 3;
+      const int c = (piece & 7) * 2;  // its two 16-bit chunks
+      *reinterpret_cast<u32x4*>(st + k_off(row, c)) = fp8x8_widen<T>(u32x2{k8[i][0], k8[i][1]});
+      *reinterpret_cast<u32x4*>(st + k_off(row, c + 1)) = fp8x8_widen<T>(u32x2{k8[i][2], k8[i][3]});
+      *reinterpret_cast<u32x4*>(st + L::kKBytes + v_off(row, c)) = fp8x8_widen<T>(u32x2{v8r[i][0], v8r[i][1]});
+      *reinterpret_cast<u32x4*>(st + L::kKBytes + v_off(row, c + 1)) = fp8x8_widen<T>(u32x2{v8r[i][2], v8r[i][3]});
+      // the whole-tile path (full blocks, whole key tiles) keeps no token array
+      if (!(BLOCKTILE && !LENS))
+        if ((piece & 7) == 0) ktok[row] = tok8[i];
     }
   };
 
@@ -289,7 +339,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY;
   float l_run = 0.f;
-  const float sl2 = a.scale_log2;
+  // logit scale of this lane's row (run()'s per-head scales multiply the plan's)
+  float sl2 = a.scale_log2;
+  if (a.q_scale) sl2 *= a.q_scale[qhead];
+  if (a.k_scale) sl2 *= a.k_scale[kvh];
+  const float out_scale = a.v_scale ? a.out_scale * a.v_scale[kvh] : a.out_scale;
 
   // element mask: bits mw[0..NMW) of this row's plane start at bit `sh` of mw[0]
   auto mask_bits = [&](const uint32_t (&mw)[NMW], int sh, f32x16 (&sacc)[NKB]) {
@@ -433,8 +487,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   // ---- key loop: two LDS stages, one barrier per tile; the DMA of tile t+1
   // is in flight while tile t is computed
   auto step = [&](int t, unsigned char* cur, const int* curtok, unsigned char* nxt, int* nxttok) {
-    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's DMA into `cur` has landed
-    __syncthreads();                     // ... and every other wave's
+    if (!KV8) __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's DMA into `cur` has landed
+    __syncthreads();                     // ... and every other wave's (KV8: their stores)
     // every scalar table read of the iteration happens here, before the LDS
     // math: an outstanding scalar load would turn each LDS wait into a full
     // drain (both share one counter)
@@ -444,50 +498,95 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     // waiting for them does not wait for that DMA
     uint32_t mw[NMW];
     const int sh = load_mask_words(t, mw);
-    if (t + 1 < ntiles) dma_tile(t + 1, nxt, nxttok);
-    if (!wave_active || (CAUSAL && lo > wave_lim)) return;  // tile above this wave's diagonal
-    const bool need_mask = MASK || LENS || (t * KT + KT > npos) || (CAUSAL && hi > wave_lim_lo);
-    f32x16 sc[NKB];
-    qk(cur, sc);
-    mask_scores(need_mask, curtok, mw, sh, sc);
-    bool upd;
-    const float alpha = softmax_core(sc, true, upd);
-    if (__ballot(upd) != 0) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+    if (t + 1 < ntiles) {
+      if (KV8) load8(t + 1);
+      else dma_tile(t + 1, nxt, nxttok);
     }
-    pv(cur, sc);
+    // tiles above this wave's diagonal are skipped
+    if (wave_active && !(CAUSAL && lo > wave_lim)) {
+      const bool need_mask = MASK || LENS || (t * KT + KT > npos) || (CAUSAL && hi > wave_lim_lo);
+      f32x16 sc[NKB];
+      qk(cur, sc);
+      mask_scores(need_mask, curtok, mw, sh, sc);
+      bool upd;
+      const float alpha = softmax_core(sc, true, upd);
+      if (__ballot(upd) != 0) {
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      }
+      pv(cur, sc);
+    }
+    if (KV8 && t + 1 < ntiles) store8(nxt, nxttok);
   };
   int lo_next = 0;  // first token of the tile in flight (FAST)
+  // FAST + KV8: the tile's first token, then fixed per-thread byte offsets
+  uint32_t koff8[PPT], voff8[PPT];
+  if (FAST && KV8) {
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int piece = tid + i * NTHR;
+      koff8[i] = static_cast<uint32_t>(piece >> 3) * static_cast<uint32_t>(a.k_stride) + (piece & 7) * 16;
+      voff8[i] = static_cast<uint32_t>(piece >> 3) * static_cast<uint32_t>(a.v_stride) + (piece & 7) * 16;
+    }
+  }
+  auto load8_fast = [&]() -> int {
+    const int lo = cols[cb + dblk] * C + doff;
+    doff += KT;
+    if (doff == C) {
+      doff = 0;
+      ++dblk;
+    }
+    const unsigned char* kt = kbase8 + static_cast<int64_t>(lo) * a.k_stride;
+    const unsigned char* vt = vbase8 + static_cast<int64_t>(lo) * a.v_stride;
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      k8[i] = *reinterpret_cast<const u32x4*>(kt + koff8[i]);
+      v8r[i] = *reinterpret_cast<const u32x4*>(vt + voff8[i]);
+    }
+    return lo;
+  };
   auto step_fast = [&](int t, unsigned char* cur, unsigned char* nxt) {
-    __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's DMA into `cur` has landed
-    __syncthreads();                     // ... and every other wave's
+    if (!KV8) __builtin_amdgcn_s_waitcnt(0x3f70);  // vmcnt(0): this wave's DMA into `cur` has landed
+    __syncthreads();                     // ... and every other wave's (KV8: their stores)
     const int lo = lo_next;
     uint32_t mw[NMW];
     const int sh = load_mask_words(t, mw);
-    if (t + 1 < ntiles) lo_next = dma_fast(nxt);
-    if (!wave_active || (CAUSAL && lo > wave_lim)) return;  // tile above this wave's diagonal
-    f32x16 sc[NKB];
-    qk(cur, sc);
-    if (CAUSAL && static_cast<int64_t>(lo) + (KT - 1) > wave_lim_lo) mask_fast(lo, sc);
-    if (MASK) mask_bits(mw, sh, sc);
-    bool upd;
-    const float alpha = softmax_core(sc, true, upd);
-    if (__ballot(upd) != 0) {
+    if (t + 1 < ntiles) lo_next = KV8 ? load8_fast() : dma_fast(nxt);
+    // tiles above this wave's diagonal are skipped
+    if (wave_active && !(CAUSAL && lo > wave_lim)) {
+      f32x16 sc[NKB];
+      qk(cur, sc);
+      if (CAUSAL && static_cast<int64_t>(lo) + (KT - 1) > wave_lim_lo) mask_fast(lo, sc);
+      if (MASK) mask_bits(mw, sh, sc);
+      bool upd;
+      const float alpha = softmax_core(sc, true, upd);
+      if (__ballot(upd) != 0) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      }
+      pv(cur, sc);
     }
-    pv(cur, sc);
+    if (KV8 && t + 1 < ntiles) store8(nxt, nullptr);
   };
   if (ntiles > 0) {
     if (FAST) {
-      lo_next = dma_fast(st0);
+      if (KV8) {
+        lo_next = load8_fast();
+        store8(st0, nullptr);
+      } else {
+        lo_next = dma_fast(st0);
+      }
       for (int t = 0; t < ntiles; t += 2) {
         step_fast(t, st0, st1);
         if (t + 1 < ntiles) step_fast(t + 1, st1, st0);
       }
     } else {
-      dma_tile(0, st0, tk0);
+      if (KV8) {
+        load8(0);
+        store8(st0, tk0);
+      } else {
+        dma_tile(0, st0, tk0);
+      }
       for (int t = 0; t < ntiles; t += 2) {
         step(t, st0, tk0, st1, tk1);
         if (t + 1 < ntiles) step(t + 1, st1, tk1, st0, tk0);
@@ -497,7 +596,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
 
   // ---- finalize this lane's row
   const float l_tot = l_run + xor_lane32(l_run);
-  const float inv = l_tot > 0.f ? a.out_scale / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? out_scale / l_tot : 0.f;
   const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   if (!row_ok) return;
   if (part < 0) {
@@ -528,7 +627,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   }
 }
 
-template <typename T, int NW, int KT>
+template <typename T, int NW, int KT, bool KV8>
 hipError_t launch_variant(const AttnArgs& a, bool causal, bool lens, bool mask, hipStream_t st) {
   const dim3 grid(a.num_tiles), block(NW * 64);
   // block tiles also need every row offset of a tile (KT rows) to fit 31 bits
@@ -536,12 +635,12 @@ hipError_t launch_variant(const AttnArgs& a, bool causal, bool lens, bool mask, 
   const bool bt = a.C % KT == 0 && static_cast<int64_t>(KT) * 2 * max_stride < (int64_t{1} << 31);
   // element masks come without block lengths (the planner folds neither in)
   if (mask && (lens || !a.mbits || a.mask_plane_words < 1)) return hipErrorInvalidValue;
-#define BSA_TILE_LAUNCH(CA, LE)                                                              \
-  if (bt) attn_tile_kernel<T, NW, KT, CA, LE, true, false><<<grid, block, 0, st>>>(a);       \
-  else attn_tile_kernel<T, NW, KT, CA, LE, false, false><<<grid, block, 0, st>>>(a);
-#define BSA_TILE_LAUNCH_MASK(CA)                                                             \
-  if (bt) attn_tile_kernel<T, NW, KT, CA, false, true, true><<<grid, block, 0, st>>>(a);     \
-  else attn_tile_kernel<T, NW, KT, CA, false, false, true><<<grid, block, 0, st>>>(a);
+#define BSA_TILE_LAUNCH(CA, LE)                                                                  \
+  if (bt) attn_tile_kernel<T, NW, KT, CA, LE, true, false, KV8><<<grid, block, 0, st>>>(a);      \
+  else attn_tile_kernel<T, NW, KT, CA, LE, false, false, KV8><<<grid, block, 0, st>>>(a);
+#define BSA_TILE_LAUNCH_MASK(CA)                                                                 \
+  if (bt) attn_tile_kernel<T, NW, KT, CA, false, true, true, KV8><<<grid, block, 0, st>>>(a);    \
+  else attn_tile_kernel<T, NW, KT, CA, false, false, true, KV8><<<grid, block, 0, st>>>(a);
   if (mask) {
     // masked plans run 64-key tiles (the mask words of 128-key ones spill)
     if constexpr (KT == 128) return hipErrorInvalidValue;
@@ -556,25 +655,31 @@ hipError_t launch_variant(const AttnArgs& a, bool causal, bool lens, bool mask, 
   return hipGetLastError();
 }
 
-template <typename T>
+template <typename T, bool KV8>
 hipError_t launch_typed(const AttnArgs& a, int tile_rows, bool causal, bool lens, bool mask, hipStream_t st) {
   switch (tile_rows) {
-    case 32: return launch_variant<T, 1, 32>(a, causal, lens, mask, st);
-    case 128: return launch_variant<T, 4, 64>(a, causal, lens, mask, st);
-    // 128-key tiles (two 64 KB LDS stages) when every tile lies in one block
-    case 256: return a.C % 128 == 0 && !mask ? launch_variant<T, 8, 128>(a, causal, lens, mask, st)
-                                     : launch_variant<T, 8, 64>(a, causal, lens, mask, st);
+    case 32: return launch_variant<T, 1, 32, KV8>(a, causal, lens, mask, st);
+    case 128: return launch_variant<T, 4, 64, KV8>(a, causal, lens, mask, st);
+    case 256:
+      // 128-key tiles (two 64 KB LDS stages) when every tile lies in one block; fp8
+      // staging keeps 64-key tiles (the registers of the 128-key variant are full)
+      if constexpr (!KV8)
+        if (a.C % 128 == 0 && !mask) return launch_variant<T, 8, 128, false>(a, causal, lens, mask, st);
+      return launch_variant<T, 8, 64, KV8>(a, causal, lens, mask, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 }  // namespace
 
-hipError_t launch_attn_tile(const AttnArgs& a, bool bf16, int tile_rows, bool causal, bool has_lens,
+hipError_t launch_attn_tile(const AttnArgs& a, bool bf16, bool kv8, int tile_rows, bool causal, bool has_lens,
                             bool has_mask, hipStream_t stream) {
   if (a.num_tiles == 0) return hipSuccess;
-  return bf16 ? launch_typed<__bf16>(a, tile_rows, causal, has_lens, has_mask, stream)
-              : launch_typed<_Float16>(a, tile_rows, causal, has_lens, has_mask, stream);
+  if (kv8)
+    return bf16 ? launch_typed<__bf16, true>(a, tile_rows, causal, has_lens, has_mask, stream)
+                : launch_typed<_Float16, true>(a, tile_rows, causal, has_lens, has_mask, stream);
+  return bf16 ? launch_typed<__bf16, false>(a, tile_rows, causal, has_lens, has_mask, stream)
+              : launch_typed<_Float16, false>(a, tile_rows, causal, has_lens, has_mask, stream);
 }
 
 }  // namespace bsa

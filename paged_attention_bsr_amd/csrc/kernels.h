@@ -29,7 +29,7 @@ struct AttnArgs {
   int32_t num_wgs;         // workgroups of the launch (decode kernel)
   int32_t heads_per_wg;    // decode kernel: kv heads of one workgroup (a power of two <= 8)
   // per-head dequant scales (device float arrays, or null = 1): q per qo head,
-  // k and v per kv head (decode kernel)
+  // k and v per kv head (decode and tile kernels)
   const float* q_scale;
   const float* k_scale;
   const float* v_scale;
@@ -49,9 +49,9 @@ struct MergeArgs {
   int32_t num_merges;
 };
 
-// Generic MFMA tile kernel, head_dim 128, fp16 or bf16 storage.
-// tile_rows in {32, 128, 256}.
-hipError_t launch_attn_tile(const AttnArgs& a, bool bf16, int tile_rows, bool causal, bool has_lens,
+// Generic MFMA tile kernel, head_dim 128, q/o fp16 or bf16, K/V in the same
+// type or fp8 e4m3 (kv8).  tile_rows in {32, 128, 256}.
+hipError_t launch_attn_tile(const AttnArgs& a, bool bf16, bool kv8, int tile_rows, bool causal, bool has_lens,
                             bool has_mask, hipStream_t stream);
 
 // Paged-decode kernel: R = 1, C >= 16, head_dim 128, q/o fp16 or bf16, K/V in

@@ -219,10 +219,6 @@ bsa_status_t build_plan_impl(const bsa_plan_desc_t& desc, int32_t num_cus, Plan&
       return fail(err, BSA_ERR_UNSUPPORTED, "head_dim 128 (q/k and v/o) is the supported size");
     if (!kv8 && (d.q_descale != 1.f || d.k_descale != 1.f || d.v_descale != 1.f))
       return fail(err, BSA_ERR_UNSUPPORTED, "dequant scales apply to fp8 KV only");
-    if (kv8 && !(d.R == 1 && g <= 16 && d.C >= 16))
-      return fail(err, BSA_ERR_UNSUPPORTED,
-                  "fp8 e4m3 KV with head_dim 128 is supported for decode shapes (R = 1, C >= 16, at most 16 qo "
-                  "heads per kv head)");
     if (d.R == 1 && g <= 16 && d.C >= 16 && ms.kind == 0) {
       kernel = BSA_KERNEL_DECODE;
       tile_rows = 16;
@@ -542,9 +538,8 @@ bsa_status_t build_plan(const bsa_plan_desc_t& desc, int32_t num_cus, Plan& P, s
   const bool var = desc.block_row_sz || desc.block_col_sz;
   MaskSrc ms;
   if (!desc.mask && !var) return build_plan_impl(desc, num_cus, P, err, ms);
-  if (desc.kv_dtype == BSA_FP8_E4M3 || desc.head_dim_qk != 128 || desc.head_dim_vo != 128)
-    return fail(err, BSA_ERR_UNSUPPORTED,
-                "element masks and variable block sizes are supported for head_dim 128 with fp16 or bf16 storage");
+  if (desc.head_dim_qk != 128 || desc.head_dim_vo != 128)
+    return fail(err, BSA_ERR_UNSUPPORTED, "element masks and variable block sizes are supported for head_dim 128");
   if (desc.kv_block_lens)
     return fail(err, BSA_ERR_INVALID_ARGUMENT,
                 "kv_block_lens must be NULL with element masks or variable block sizes (lengths belong in the mask)");

@@ -44,6 +44,7 @@ __all__ = [
     "sparse_mla",
     "head_sparse_prefill",
     "paged_decode_fp8",
+    "bsr_prefill_fp8",
     "fp8_kv",
     "random_bsr",
     "by_name",
@@ -187,6 +188,17 @@ def paged_decode_fp8(seed: int = 7, values: bool = True) -> Workload:
     and per-kv-head dequant scales (see fp8_kv); q and o fp16."""
     w = paged_decode(values=values)
     w.name = "paged_decode_fp8"
+    w.kv_dtype = torch.float8_e4m3fn
+    if values:
+        fp8_kv(w, seed)
+    return w
+
+
+def bsr_prefill_fp8(seed: int = 11, values: bool = True) -> Workload:
+    """bsr_prefill's structure (same blocks, causal) with fp8 e4m3 K/V and per-kv-head
+    dequant scales (see fp8_kv); q and o fp16."""
+    w = bsr_prefill(values=values)
+    w.name = "bsr_prefill_fp8"
     w.kv_dtype = torch.float8_e4m3fn
     if values:
         fp8_kv(w, seed)
@@ -473,10 +485,11 @@ def rope_quantize(seed: int = 10, nnz: int = 4096, num_heads: int = 128, max_seq
 # 0 = automatic, 1 = no split.
 BENCH_KV_SPLITS = {"worked_example": 1, "paged_decode": 0, "bsr_prefill": 1, "window_prefill": 1,
                    "sparse_mla": 1, "head_sparse_prefill": 1, "paged_decode_fp8": 0,
-                   "element_mask_prefill": 1, "variable_block_prefill": 1}
+                   "element_mask_prefill": 1, "variable_block_prefill": 1, "bsr_prefill_fp8": 1}
 
 WORKLOAD_NAMES = ["worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla",
-                  "head_sparse_prefill", "paged_decode_fp8", "element_mask_prefill", "variable_block_prefill"]
+                  "head_sparse_prefill", "paged_decode_fp8", "element_mask_prefill", "variable_block_prefill",
+                  "bsr_prefill_fp8"]
 
 
 def by_name(name: str, **kw) -> Workload:
@@ -484,4 +497,4 @@ def by_name(name: str, **kw) -> Workload:
             "bsr_prefill": bsr_prefill, "window_prefill": window_prefill,
             "sparse_mla": sparse_mla, "head_sparse_prefill": head_sparse_prefill,
             "paged_decode_fp8": paged_decode_fp8, "element_mask_prefill": element_mask_prefill,
-            "variable_block_prefill": variable_block_prefill}[name](**kw)
+            "variable_block_prefill": variable_block_prefill, "bsr_prefill_fp8": bsr_prefill_fp8}[name](**kw)

@@ -80,7 +80,7 @@ def test_plan_without_gpu_succeeds():
     (dict(num_qo_heads=30), L.BSA_ERR_INVALID_ARGUMENT),            # not a multiple
     (dict(head_dim_qk=64), L.BSA_ERR_UNSUPPORTED),
     (dict(q_dtype=L.BSA_BF16), L.BSA_ERR_UNSUPPORTED),              # mixed dtypes
-    (dict(kv_dtype=L.BSA_FP8_E4M3), L.BSA_ERR_UNSUPPORTED),         # fp8 needs the MLA shape
+    (dict(q_dtype=L.BSA_FP8_E4M3, kv_dtype=L.BSA_FP8_E4M3), L.BSA_ERR_UNSUPPORTED),  # fp8 queries
     (dict(kv_splits=-1), L.BSA_ERR_INVALID_ARGUMENT),
     (dict(k_descale=0.0), L.BSA_ERR_INVALID_ARGUMENT),
     (dict(kv_block_lens=np.array([1, 2, 1]), N=3), L.BSA_ERR_INVALID_ARGUMENT),  # len > C

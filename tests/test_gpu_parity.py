@@ -172,6 +172,7 @@ FULL_ROWS = {
     "paged_decode_fp8": None,                                   # all 64 requests
     "element_mask_prefill": [0, 1, 63, 64, 127, 4095, 4096, 6000, 8190, 8191],
     "variable_block_prefill": [0, 1, 31, 95, 160, 4095, 4096, 6000, 8190, 8191],
+    "bsr_prefill_fp8": [0, 1, 63, 64, 127, 4095, 4096, 6000, 8190, 8191],
 }
 
 
@@ -378,6 +379,68 @@ def test_fp8_kv_decode(case, kv_splits):
                 vb[J * C + n:(J + 1) * C] = 0xFE      # -448
     assert plan_for(w, kv_splits).info()["kernel"] == 2
     _check(w, kv_splits, what=f"fp8 decode s{seed} {dtype} splits={kv_splits}")
+
+
+# ---------------------------------------------------------------- fp8 e4m3 KV, head_dim 128 (tile kernel)
+# Every launch shape of the tile kernel with fp8 K/V staged through registers: 32-, 128-
+# and 256-row tiles (the 256-row ones on 64-key tiles also where C is a multiple of 128),
+# whole-tile and generic key lookup, causal, valid lengths (the unused slots hold the
+# largest codes), per-kv-head scale_k / scale_v and per-qo-head scale_q.
+FP8_TILE = [
+    # (seed, M, NB, R, C, Hq, Hkv, causal, lens, dtype, q_scales, expected tile_rows)
+    (91, 128, 6, 64, 64, 16, 4, True, False, torch.float16, False, 256),    # whole 64-key block tiles
+    (92, 96, 20, 32, 48, 32, 4, False, True, torch.float16, True, 256),     # generic lookup over 48-key blocks
+    (93, 192, 4, 64, 256, 32, 4, True, True, torch.float16, False, 256),    # C = 256: 64-key tiles, lens
+    (94, 256, 3, 128, 128, 16, 4, False, False, torch.bfloat16, True, 256), # bf16 q/o
+    (95, 96, 12, 32, 32, 16, 4, True, False, torch.float16, True, 128),     # 128-row tiles over 32-key blocks
+    (96, 40, 30, 8, 16, 16, 4, True, True, torch.float16, False, 32),       # 32-row tiles
+    (97, 37, 9, 5, 7, 8, 2, False, True, torch.bfloat16, False, 32),        # odd everything
+    (98, 9, 40, 1, 4, 32, 8, False, True, torch.float16, True, 32),         # R = 1, C < 16: not the decode kernel
+]
+
+
+def _fp8_tile_workload(case):
+    seed, M, NB, R, C, Hq, Hkv, causal, lens, dtype, qs, _ = case
+    w = W.random_bsr(seed, M, NB * C, R, C, Hq, Hkv, causal=causal, partial_lens=lens, density=0.6, dtype=dtype)
+    W.fp8_kv(w, seed, q_scales=qs)
+    if lens:
+        kb, vb = w.k.view(torch.uint8), w.v.view(torch.uint8)
+        for J in range(NB):
+            n = int(w.kv_block_lens[J])
+            if n < C:
+                kb[J * C + n:(J + 1) * C] = 0x7E      # +448
+                vb[J * C + n:(J + 1) * C] = 0xFE      # -448
+    return w
+
+
+@pytest.mark.parametrize("case", FP8_TILE, ids=[f"t{c[0]}" for c in FP8_TILE])
+@pytest.mark.parametrize("kv_splits", [1, 3])
+def test_fp8_kv_tile_kernel(case, kv_splits):
+    w = _fp8_tile_workload(case)
+    p = plan_for(w, kv_splits, num_cus=1)
+    inf = p.info()
+    assert inf["kernel"] == 0 and inf["tile_rows"] == case[-1], inf
+    what = f"fp8 tile s{case[0]} rows={case[-1]} C={case[4]} {case[9]} splits={kv_splits}"
+    say(f"[parity] {what}")
+    o, lse = run_gpu(w, kv_splits, plan=p)
+    o_ref, lse_ref = oracle_result(w)
+    compare(o, lse, o_ref, lse_ref, tol_for(w), what)
+
+
+def test_fp8_kv_with_element_masks():
+    """fp8 K/V through the tile kernel's masked path (packed element masks)."""
+    case = (99, 130, 6, 64, 64, 16, 4, 0.6, True, False)
+    w = _masked_workload(case)
+    W.fp8_kv(w, 99, q_scales=True)
+    _check(w, 1, what="fp8 element masks")
+    _check(w, 3, what="fp8 element masks splits=3")
+
+
+def test_reduced_bsr_prefill_fp8():
+    w = W.bsr_prefill(seed=100, M=1024, density=0.3)
+    W.fp8_kv(w, 100)
+    _check(w, 1, what="bsr_prefill fp8 M=1024")
+    _check(w, 0, what="bsr_prefill fp8 M=1024 auto splits")
 
 
 # ---------------------------------------------------------------- element masks and variable blocks

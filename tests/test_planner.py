@@ -477,23 +477,31 @@ def test_per_head_structure_errors():
 
 
 
-def test_fp8_kv_head_dim_128_selects_decode_kernel_only():
+def test_fp8_kv_head_dim_128_kernel_choice():
+    """fp8 e4m3 K/V at head_dim 128: decode shapes (R = 1, C >= 16) run the decode kernel,
+    every other shape -- prefill blocks, C < 16, element masks -- the tile kernel."""
     w = W.by_name("paged_decode_fp8", values=False)
-    inf = _plan(w, 0).info()
-    assert inf["kernel"] == 2
-    # fp8 KV at head_dim 128 outside the decode shapes has no kernel
+    assert _plan(w, 0).info()["kernel"] == 2
     w2 = W.random_bsr(5, 64, 64 * 4, 16, 16, 8, 2, values=False)
     w2.kv_dtype = torch.float8_e4m3fn
-    with pytest.raises(RuntimeError, match="decode shapes"):
-        _plan(w2, 1)
+    assert _plan(w2, 1).info()["kernel"] == 0
+    w3 = W.random_bsr(7, 9, 8 * 4, 1, 4, 8, 2, values=False)   # R = 1 but C < 16
+    w3.kv_dtype = torch.float8_e4m3fn
+    assert _plan(w3, 1).info()["kernel"] == 0
+    # fp8 queries have no kernel
+    w4 = W.random_bsr(8, 64, 64 * 4, 16, 16, 8, 2, values=False)
+    w4.kv_dtype = w4.q_dtype = w4.o_dtype = torch.float8_e4m3fn
+    with pytest.raises(RuntimeError, match="q/o must both be fp16 or both bf16"):
+        _plan(w4, 1)
 
 
-def test_run_scales_rejected_outside_decode_kernel():
-    """Per-head run scales are a decode-kernel feature; other plans refuse them before
-    touching any pointer."""
+def test_run_scales_rejected_for_the_mla_shape():
+    """Per-head run scales apply to head_dim 128 plans; the sparse-MLA plan (one kv head,
+    per-tensor descales) refuses them before touching any pointer."""
     import ctypes
     from paged_attention_bsr_amd import _lib as L
-    w = W.random_bsr(6, 64, 64 * 4, 16, 16, 8, 2, values=False)
+    w = W.sparse_mla(seed=9, num_tokens=4, num_heads=16, cache_rows=256, topk=32, min_ctx=64, max_ctx=256,
+                     values=False)
     p = _plan(w, 1)
     lib = L.lib()
     st = lib.bsa_run_ex(p._handle, L.BSA_PHASE_ALL, None, None, None, None, None, 16, None, None, None, 0, None)

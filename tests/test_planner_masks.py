@@ -118,7 +118,8 @@ def test_mask_rejections():
     m = np.ones((1, 4, 4), bool)
     _expect_error(mask=m, kv_block_lens=np.array([4], np.int32))
     _expect_error(mask=m, block_mask=np.ones((2, 1, 1), bool))
-    _expect_error(mask=m, kv_dtype=__import__("torch").float8_e4m3fn)
+    # element masks run on the head_dim 128 tile kernel (fp16 / bf16, K/V also fp8), not the MLA shape
+    _expect_error(mask=m, kv_dtype=__import__("torch").float8_e4m3fn, head_dim=576)
     _expect_error(mask=np.ones((2, 4, 4), bool))                 # nnz is 1
     _expect_error(packed_mask=np.zeros(1, np.uint8))             # 16 bits need 2 bytes
     _expect_error(mask=m, head_dim=64)
