@@ -1,20 +1,25 @@
 #!/usr/bin/env python3
 """Benchmark of BSR block-sparse attention on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|NAME]
 
 A step is one run of the planned attention (attention kernel, plus the LSE
 merge kernel when the plan splits rows) over one batch of synthetic inputs
 already resident in HBM.  Planning (host) and the one-time table upload are
 done before the timed region and reported separately (plan_ms).
 
-Prints ONE JSON line.  For the decode workloads the metric is KV GB/s
-(algorithmic bytes: K and V of every unmasked key once per kv head, plus q,
-o, lse and the index structure); for the block-sparse prefill workloads it
-is TFLOP/s (algorithmic flops: 4 * head_dim * qo heads * unmasked query-key
-pairs).  ``roofline`` is measured live with HIP events around the attention
-kernel alone (bsa_run_phase); ``cpu_baseline`` times the CPU oracle on a
-bounded sample of the same workload on this host's cores.
+By default the five configurations of the headline metric run one after the
+other (worked example, paged decode, block-sparse prefill, windowed prefill,
+sparse MLA); ONE JSON line is printed, whose headline is the paged-decode
+figure and whose ``configs`` array holds one entry per configuration.  For
+the decode workloads the metric is KV GB/s (algorithmic bytes: K and V of
+every unmasked key once per kv head, plus q, o, lse and the index
+structure); for the block-sparse prefill workloads it is TFLOP/s
+(algorithmic flops: 4 * head_dim * qo heads * unmasked query-key pairs).
+``roofline`` divides the algorithmic work by the median GPU time of a step
+(attention + merge kernels, HIP events on the launch stream) over the timed
+steps; ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload on this host's cores.
 """
 from __future__ import annotations
 
@@ -215,49 +220,71 @@ def cpu_baseline(w, budget_s: float):
     return {"seconds": t_used, "rows": done, "bytes": b, "flops": f, "cores": threads}
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="paged_decode",
-                    choices=["worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla",
-                             "head_sparse_prefill", "paged_decode_fp8", "element_mask_prefill",
-                             "variable_block_prefill", "rope_quantize"])
-    ap.add_argument("--kv-splits", type=int, default=None, help="override the workload's split-KV setting")
-    ap.add_argument("--var-grid", type=int, nargs=2, default=(0, 0), metavar=("R", "C"),
-                    help="variable-block workloads: the fixed grid the blocks are mapped onto (0 = library's choice)")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of CPU oracle work (0 = skip)")
-    ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
-                    help="after the timed region, copy MIB MiB device-to-device once (a known-size "
-                         "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
-    args = ap.parse_args()
+# The five configurations of the headline metric, in order; the JSON line's
+# headline is the paged-decode one (the metric's decode figure), and every
+# one of them gets an entry in its "configs" array.
+CONFIGS = ["worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla"]
+HEADLINE = "paged_decode"
 
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no multi-GPU path; "
-              "the attention would shard by kv head or by request with no exchange between GPUs.", file=sys.stderr)
-        return 2
 
+def host_cores():
+    """(os.cpu_count(), CPUs this process may run on, BLAS threads in use)."""
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):  # pragma: no cover
+        affinity = os.cpu_count() or 1
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = affinity
+    return os.cpu_count() or 1, affinity, blas
+
+
+# Steps per pair of timing events: a HIP event pair costs a few microseconds of GPU
+# time on this part, so each pair brackets CHUNK consecutive steps and the step's GPU
+# time is the pair's elapsed time / CHUNK (one sample per chunk).
+CHUNK = 5
+# Seconds of warm-up work (at least --warmup steps) before a workload's timed region.
+WARM_S = 0.25
+
+
+def timed_chunks(fn, steps: int):
+    """Run fn() ceil(steps / CHUNK) * CHUNK times, bracketing every CHUNK calls with HIP events
+    on torch's current stream (the stream the library launches on).  Returns the wall
+    time of the whole region and the GPU milliseconds per call of every chunk."""
+    import torch
+    n = max(1, -(-steps // CHUNK))
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in events:
+        e0.record()
+        for _ in range(CHUNK):
+            fn()
+        e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [e0.elapsed_time(e1) / CHUNK for e0, e1 in events]
+
+
+def measure(name: str, args, dev):
+    """Plan, upload, warm up and time one workload; returns (its entry of the JSON line, the workload).
+
+    A step is bsa_run (attention kernel, then the merge kernel when rows are split).
+    Its GPU time comes from HIP events around chunks of CHUNK steps; the roofline
+    fraction uses the median over the chunks.  The attention kernel alone is timed
+    the same way in a second loop (bsa_run_phase)."""
     import numpy as np
     import torch
-    sys.path.insert(0, ROOT)
     from paged_attention_bsr_amd import Plan
     from paged_attention_bsr_amd import _lib as L
     from paged_attention_bsr_amd import workloads as W
 
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 1
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    props = torch.cuda.get_device_properties(dev)
-    log(f"[bench] device {props.name} CUs={props.multi_processor_count} workload={args.workload}")
-
-    if args.workload == "rope_quantize":
-        return run_rope_quantize(args, dev)
-
-    w = W.by_name(args.workload)
-    kv_splits = W.BENCH_KV_SPLITS[args.workload] if args.kv_splits is None else args.kv_splits
+    t0 = time.perf_counter()
+    w = W.by_name(name)
+    gen_s = time.perf_counter() - t0
+    kv_splits = W.BENCH_KV_SPLITS[name] if args.kv_splits is None else args.kv_splits
     t0 = time.perf_counter()
     if "variable" in w.meta:
         bm, rs, cs = w.meta["variable"]
@@ -281,36 +308,38 @@ def main() -> int:
     ws = plan.workspace(dev)
     plan.upload(ws)
     torch.cuda.synchronize()
-    log(f"[bench] plan {plan_ms:.1f} ms: {info}")
+    log(f"[bench] {name}: inputs {gen_s:.1f} s, plan {plan_ms:.1f} ms: {info}")
 
     # per-head run() scales (fp8 KV workloads), device float32
     scales = {f"scale_{n}": torch.from_numpy(w.meta[f"scale_{n}"]).to(dev)
               for n in ("q", "k", "v") if f"scale_{n}" in w.meta}
 
-    def step(evs=None):
-        if evs is None:
-            plan.run(q, k, v, out=out, lse=lse, workspace=ws, **scales)
-            return
-        evs[0].record()
-        plan.run(q, k, v, out=out, lse=lse, workspace=ws, phase=L.BSA_PHASE_ATTENTION, **scales)
-        evs[1].record()
-        plan.run(q, k, v, out=out, lse=lse, workspace=ws, phase=L.BSA_PHASE_MERGE, **scales)
+    def step():
+        plan.run(q, k, v, out=out, lse=lse, workspace=ws, **scales)
 
-    for _ in range(args.warmup):
+    def attention_only():
+        plan.run(q, k, v, out=out, lse=lse, workspace=ws, phase=L.BSA_PHASE_ATTENTION, **scales)
+
+    # W warm-up steps, continued until the GPU has been busy for WARM_S (its clocks come up
+    # from idle, e.g. after the previous workload's host work)
+    warm_steps, t_w = 0, time.perf_counter()
+    while warm_steps < args.warmup or time.perf_counter() - t_w < WARM_S:
         step()
+        warm_steps += 1
+        if warm_steps % 8 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    wall, step_ms = timed_chunks(step, args.steps)
+    ms_per_step = wall * 1e3 / len(step_ms) / CHUNK
+    gpu_ms = float(np.median(step_ms))
+    _, attn_ms = timed_chunks(attention_only, args.steps)
+    attn_med = float(np.median(attn_ms))
+    step()   # leave a complete result behind
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_per_step = wall * 1e3 / args.steps
-    attn_ms = [e[0].elapsed_time(e[1]) for e in events]
-    attn_avg_ms = float(np.mean(attn_ms))
-    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step; attention kernel avg {attn_avg_ms:.4f} ms "
-        f"(min {min(attn_ms):.4f}, max {max(attn_ms):.4f})")
+    log(f"[bench] {name}: {len(step_ms) * CHUNK} steps: {ms_per_step:.4f} ms/step wall; GPU step (attention + "
+        f"merge) median {gpu_ms:.4f} ms, mean {float(np.mean(step_ms)):.4f}; attention kernel median {attn_med:.4f} ms")
+    del q, k, v, out, lse, ws, scales
+    torch.cuda.empty_cache()
 
     if args.calibration_copy > 0:
         n = args.calibration_copy << 20
@@ -323,56 +352,120 @@ def main() -> int:
         del src, dst
 
     alg_bytes, alg_flops = algorithmic_work(w)
-    dtype = {torch.float16: "f16", torch.bfloat16: "bf16"}[w.q_dtype]
-    if w.kv_dtype == torch.float8_e4m3fn:
-        dtype = f"{dtype} (fp8 e4m3 KV storage)"
-    decode = args.workload in DECODE
+    decode = name in DECODE
+    kernel = {L.BSA_KERNEL_MLA: "attn_mla_kernel", L.BSA_KERNEL_DECODE: "attn_decode_kernel"}.get(
+        info["kernel"], "attn_tile_kernel")
     if decode:
         value = alg_bytes / (ms_per_step * 1e-3) / 1e9
         unit = "GB/s"
-        achieved = alg_bytes / (attn_avg_ms * 1e-3) / 1e9
+        achieved = alg_bytes / (gpu_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}
     else:
         value = alg_flops / (ms_per_step * 1e-3) / 1e12
         unit = "TFLOP/s"
-        achieved = alg_flops / (attn_avg_ms * 1e-3) / 1e12
+        achieved = alg_flops / (gpu_ms * 1e-3) / 1e12
         peak = MFMA_PEAK_TFLOPS["f16" if w.q_dtype == torch.float16 else "bf16"]
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak}
-    if args.workload == "sparse_mla":
+    if name == "worked_example":
+        roof["bound_note"] = "launch latency: 5 key blocks, 81,920 flop; a parity configuration"
+    if name == "sparse_mla":
         # exact bf16 MFMA arithmetic bounds this shape too; report its MFMA fraction beside HBM
-        mfma_tf = alg_flops / (attn_avg_ms * 1e-3) / 1e12
-        roof["mfma_frac_bf16"] = mfma_tf / MFMA_PEAK_TFLOPS["bf16"]
-    roof["kernel"] = {L.BSA_KERNEL_MLA: "attn_mla_kernel", L.BSA_KERNEL_DECODE: "attn_decode_kernel"}.get(
-        info["kernel"], "attn_tile_kernel")
-    roof["traffic"] = measured_traffic(args.workload, kernel_source_hash(roof["kernel"]))
+        roof["mfma_frac_bf16"] = alg_flops / (gpu_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS["bf16"]
+    roof["traffic"] = measured_traffic(name, kernel_source_hash(kernel))
+    roof["kernel"] = kernel
+    roof["timing"] = (f"median over {len(step_ms)} chunks of {CHUNK} steps of the HIP-event GPU time per step "
+                      "(attention + merge kernels)")
+    roof["step_gpu_ms_median"] = gpu_ms
+    roof["attention_ms_median"] = attn_med
     roof["alg_bytes_per_launch"] = alg_bytes
     roof["alg_flops_per_launch"] = alg_flops
-    roof["avg_launch_ms"] = attn_avg_ms
+    roof["frac_attention_only"] = roof["frac"] * gpu_ms / attn_med if attn_med > 0 else None
 
-    cpu = None
-    if args.cpu_budget > 0:
-        log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s budget)")
-        cb = cpu_baseline(w, args.cpu_budget)
-        if decode:
-            cval = cb["bytes"] / cb["seconds"] / 1e9
-        else:
-            cval = cb["flops"] / cb["seconds"] / 1e12
-        cpu = {"value": cval, "unit": unit, "cores": cb["cores"], "kind": "oracle",
-               "sample": f"{cb['rows']} of {w.M} query rows (all heads), float64 dense-mask oracle, "
-                         f"{cb['seconds']:.1f} s"}
-
-    cfg = {"workload": args.workload, "M": w.M, "N": w.N, "R": info["R"], "C": info["C"],
+    dtype = {torch.float16: "f16", torch.bfloat16: "bf16"}[w.q_dtype]
+    if w.kv_dtype == torch.float8_e4m3fn:
+        dtype = f"{dtype} (fp8 e4m3 KV storage)"
+    cfg = {"workload": name, "M": w.M, "N": w.N, "R": info["R"], "C": info["C"],
            "num_qo_heads": w.num_qo_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
-           "head_dim_vo": w.head_dim_vo, "causal": w.causal, "nnz_blocks": sum(len(ix) for _, ix in head_structures(w)),
+           "head_dim_vo": w.head_dim_vo, "causal": w.causal,
+           "nnz_blocks": sum(len(ix) for _, ix in head_structures(w)),
            "per_head_structure": "block_mask" in w.meta or "variable" in w.meta,
            "element_masks": "mask" in w.meta or "variable" in w.meta, "kv_splits": kv_splits,
            "tiles": info["num_tiles"], "merges": info["num_merges"], "plan_ms": plan_ms,
            "alg_bytes": alg_bytes, "alg_flops": alg_flops}
-    line = {"metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
-            "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-            "vs_baseline": None, "dtype": dtype, "data": "synthetic", "config": cfg,
-            "roofline": roof, "cpu_baseline": cpu}
+    cfg["warmup_steps_run"] = warm_steps
+    return {"workload": name, "metric": METRIC, "value": value, "unit": unit, "ms_per_step": ms_per_step,
+            "dtype": dtype, "config": cfg, "roofline": roof, "cpu_baseline": None}, w
+
+
+def cpu_entry(w, unit: str, budget_s: float) -> dict:
+    """The CPU oracle, as it stands, timed on a bounded sample of the workload, in the metric's unit."""
+    log(f"[bench] {w.name}: CPU oracle baseline (~{budget_s:.0f} s budget)")
+    cb = cpu_baseline(w, budget_s)
+    cval = (cb["bytes"] / 1e9 if unit == "GB/s" else cb["flops"] / 1e12) / cb["seconds"]
+    n_cpu, n_aff, n_blas = host_cores()
+    return {"value": cval, "unit": unit, "cores": n_blas, "os_cpu_count": n_cpu, "affinity_cores": n_aff,
+            "blas_threads": n_blas, "kind": "oracle",
+            "sample": f"{cb['rows']} of {w.M} query rows (all heads), float64 dense-mask oracle, "
+                      f"{cb['seconds']:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100, help="timed steps (rounded up to a multiple of 5)")
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla",
+                             "head_sparse_prefill", "paged_decode_fp8", "element_mask_prefill",
+                             "variable_block_prefill", "bsr_prefill_fp8", "rope_quantize"],
+                    help="all = the five configurations (headline: paged_decode); otherwise one workload")
+    ap.add_argument("--kv-splits", type=int, default=None, help="override the workload's split-KV setting")
+    ap.add_argument("--var-grid", type=int, nargs=2, default=(0, 0), metavar=("R", "C"),
+                    help="variable-block workloads: the fixed grid the blocks are mapped onto (0 = library's choice)")
+    ap.add_argument("--cpu-budget", type=float, default=8.0,
+                    help="seconds of CPU oracle work per workload (0 = skip)")
+    ap.add_argument("--calibration-copy", type=int, default=0, metavar="MIB",
+                    help="after each timed region, copy MIB MiB device-to-device once (a known-size "
+                         "reference for rocprofv3 FETCH_SIZE / WRITE_SIZE counters)")
+    args = ap.parse_args()
+    args.steps = max(CHUNK, -(-args.steps // CHUNK) * CHUNK)   # whole chunks of timed steps
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no multi-GPU path; "
+              "the attention would shard by kv head or by request with no exchange between GPUs.", file=sys.stderr)
+        return 2
+
+    import torch
+    sys.path.insert(0, ROOT)
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+    log(f"[bench] device {props.name} CUs={props.multi_processor_count} workload={args.workload}")
+
+    if args.workload == "rope_quantize":
+        return run_rope_quantize(args, dev)
+
+    names = CONFIGS if args.workload == "all" else [args.workload]
+    # every GPU measurement first (back to back, the GPU kept busy), then the host baselines
+    measured = [measure(n, args, dev) for n in names]
+    entries = []
+    for e, w in measured:
+        if args.cpu_budget > 0:
+            e["cpu_baseline"] = cpu_entry(w, e["unit"], args.cpu_budget)
+        entries.append(e)
+    del measured
+    head = next(e for e in entries if e["workload"] == (HEADLINE if args.workload == "all" else args.workload))
+    line = {"metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic",
+            "config": head["config"], "roofline": head["roofline"], "cpu_baseline": head["cpu_baseline"],
+            "configs": [{k: e[k] for k in ("workload", "value", "unit", "ms_per_step", "dtype", "roofline",
+                                           "cpu_baseline", "config")} for e in entries]}
     print(json.dumps(line), flush=True)
     return 0
 
@@ -415,8 +508,8 @@ def run_rope_quantize(args, dev) -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    k_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in events]))
-    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step; kernel avg {k_ms:.4f} ms")
+    k_ms = float(np.median([e[0].elapsed_time(e[1]) for e in events]))
+    log(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step; kernel median {k_ms:.4f} ms")
     if args.calibration_copy > 0:
         n = args.calibration_copy << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
@@ -429,16 +522,13 @@ def run_rope_quantize(args, dev) -> int:
     achieved = alg / (k_ms * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
             "kernel": "rope_quant_kernel", "traffic": measured_traffic("rope_quantize", kernel_source_hash("rope_quant_kernel")),
-            "alg_bytes_per_launch": alg, "alg_flops_per_launch": 0, "avg_launch_ms": k_ms}
+            "alg_bytes_per_launch": alg, "alg_flops_per_launch": 0, "step_gpu_ms_median": k_ms,
+            "timing": "median of HIP-event kernel time over the timed steps"}
     cpu = None
     if args.cpu_budget > 0:
         import oracle
         log(f"[bench] CPU oracle baseline (~{args.cpu_budget:.0f} s budget)")
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-        except Exception:  # pragma: no cover
-            threads = os.cpu_count() or 1
+        n_cpu, n_aff, threads = host_cores()
         cache = w["cos_sin_cache"].float().numpy()
         done, used, batch = 0, 0.0, 8
         while done < nnz and used < args.cpu_budget:
@@ -451,7 +541,8 @@ def run_rope_quantize(args, dev) -> int:
             used += time.perf_counter() - t1
             done = sl.stop
             batch = min(batch * 2, 256)
-        cpu = {"value": rope_bytes(done, H) / used / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+        cpu = {"value": rope_bytes(done, H) / used / 1e9, "unit": "GB/s", "cores": threads, "os_cpu_count": n_cpu,
+               "affinity_cores": n_aff, "blas_threads": threads, "kind": "oracle",
                "sample": f"{done} of {nnz} tokens (all heads), numpy float32 rotary + nearest-value fp8 encode, "
                          f"{used:.1f} s"}
     cfg = {"workload": "rope_quantize", "nnz": nnz, "num_heads": H, "q_row": "512 latent + 64 rope",
