@@ -245,7 +245,7 @@ def host_cores():
 # time on this part, so each pair brackets CHUNK consecutive steps and the step's GPU
 # time is the pair's elapsed time / CHUNK (one sample per chunk).
 CHUNK = 5
-# Seconds of warm-up work (at least --warmup steps) before a workload's timed region.
+# Default seconds of warm-up work (at least --warmup steps) before a workload's timed region.
 WARM_S = 0.25
 
 
@@ -323,7 +323,7 @@ def measure(name: str, args, dev):
     # W warm-up steps, continued until the GPU has been busy for WARM_S (its clocks come up
     # from idle, e.g. after the previous workload's host work)
     warm_steps, t_w = 0, time.perf_counter()
-    while warm_steps < args.warmup or time.perf_counter() - t_w < WARM_S:
+    while warm_steps < args.warmup or time.perf_counter() - t_w < args.warm_s:
         step()
         warm_steps += 1
         if warm_steps % 8 == 0:
@@ -420,6 +420,8 @@ def main() -> int:
                              "head_sparse_prefill", "paged_decode_fp8", "element_mask_prefill",
                              "variable_block_prefill", "bsr_prefill_fp8", "rope_quantize"],
                     help="all = the five configurations (headline: paged_decode); otherwise one workload")
+    ap.add_argument("--warm-s", type=float, default=WARM_S,
+                    help="keep warming up (beyond --warmup steps) until the GPU has worked this many seconds")
     ap.add_argument("--kv-splits", type=int, default=None, help="override the workload's split-KV setting")
     ap.add_argument("--var-grid", type=int, nargs=2, default=(0, 0), metavar=("R", "C"),
                     help="variable-block workloads: the fixed grid the blocks are mapped onto (0 = library's choice)")

@@ -264,6 +264,48 @@ def test_mla_kernel_variants(causal, lens):
     _check(w, 3, what=f"mla variant causal={causal} lens={lens} splits=3")
 
 
+def _mla_logit_jump(seed, q_rope_value):
+    """Sparse MLA where every token's first 32 selected rows (its first key tile) have
+    nothing in their 64 rope dims, while later rows hold +448 there and q holds
+    q_rope_value: those later keys' logits exceed the first tile's by about
+    q_rope_value * 448 s * 64 / 24 (s the dequant scale)."""
+    w = W.sparse_mla(seed=seed, num_tokens=5, num_heads=64, cache_rows=512, topk=128, min_ctx=512, max_ctx=512)
+    rng = np.random.default_rng(seed)
+    small, big = np.arange(0, 256), np.arange(256, 512)
+    rows = [np.concatenate([rng.permutation(small)[:32], rng.permutation(np.concatenate([small, big]))[:200]])
+            for _ in range(w.M)]
+    rows = [np.concatenate([r[:32], [j for j in r[32:] if j not in set(r[:32])][:96]]) for r in rows]
+    w.indices = np.concatenate(rows).astype(np.int32)
+    codes = w.k.view(torch.uint8).clone()
+    codes[small, 512:] = 0
+    codes[big, 512:] = 0x7E
+    w.k = codes.view(torch.float8_e4m3fn)
+    w.q[:, :, 512:] = q_rope_value
+    return w
+
+
+def test_mla_reference_overflow_runs_a_second_pass():
+    """Later keys beat the first tile's reference by ~580 log2 units: the first pass
+    overflows and the workgroup redoes its key loop against the true maximum."""
+    w = _mla_logit_jump(39, 30.0)
+    _check(w, 1, what="mla logit jump (second pass)")
+    _check(w, 2, what="mla logit jump (second pass) splits=2")
+
+
+def test_mla_large_logit_growth_in_one_pass():
+    """Later keys beat the first tile by ~38 log2 units: probabilities up to 2^38 in the
+    single pass."""
+    w = _mla_logit_jump(40, 2.0)
+    _check(w, 1, what="mla logit growth")
+
+
+def test_mla_paired_tiles_and_ragged_tail():
+    """18 tiles: 16 dealt in XCD pairs, 2 in the ragged tail."""
+    w = W.sparse_mla(seed=41, num_tokens=9, num_heads=128, cache_rows=2048, topk=160, min_ctx=512, max_ctx=2048)
+    assert plan_for(w, 1).info()["num_tiles"] == 18
+    _check(w, 1, what="mla 18 tiles")
+
+
 @pytest.mark.parametrize("causal,lens", [(False, False), (True, True)])
 def test_mla_kernel_multi_row_blocks(causal, lens):
     """The sparse-MLA kernel with blocks of 4 latent rows (C = 4) instead of single rows: key
