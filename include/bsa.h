@@ -438,6 +438,24 @@ bsa_status_t bsa_plan_export_workgroups(bsa_plan_t plan, int32_t* wg_ptr);
  * nothing is copied for a plan without element masks. */
 bsa_status_t bsa_plan_export_mask_bits(bsa_plan_t plan, uint32_t* bits);
 
+/*
+ * Per-tile trace records of the last attention phase run with `workspace`
+ * (a check that the kernels walk exactly the tables bsa_plan_export returns).
+ * Only a library built with BSA_TRACE keeps them: there the workspace
+ * (bsa_workspace_size) ends with int32[num_tiles][8] records, after the split
+ * partials, which each run's attention phase resets and its kernel fills in,
+ * tile t (launch order) =
+ *   {times the tile was processed, first column entry whose keys it loaded,
+ *    last such entry + 1, keys it loaded that lie inside their block's valid
+ *    length (before the causal mask), partial_offset it wrote (-1: o/lse
+ *    directly), kv_head, row0, nrows}
+ * and a tile with no valid key reads {1, INT32_MAX, 0, 0, ...}.  Waits for
+ * `stream`, then copies the records to host `records` (int32[num_tiles * 8]).
+ * The product library returns BSA_ERR_UNSUPPORTED; BSA_ERR_INVALID_ARGUMENT
+ * for NULL arguments, BSA_ERR_HIP when the copy fails.
+ */
+bsa_status_t bsa_trace_records(bsa_plan_t plan, const void* workspace, int32_t* records, void* stream);
+
 /* Free the plan's host memory and end its workspace pins.  A plan is made
  * once and reused across runs until the structure changes (MATE sparse-MLA
  * decode, "Metadata reuse": a new metadata object for new sequence lengths,

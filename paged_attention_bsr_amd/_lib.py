@@ -1,11 +1,15 @@
 """ctypes declarations of libbsa.so (include/bsa.h).  Loading fails loudly if
-the library has not been built; there is no fallback implementation."""
+the library has not been built; there is no fallback implementation.
+
+trace_lib() loads libbsa_trace.so, the same sources built with BSA_TRACE
+(per-tile trace records, bsa_trace_records), which only tests use."""
 from __future__ import annotations
 
 import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsa.so")
+TRACE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsa_trace.so")
 
 BSA_OK = 0
 BSA_ERR_INVALID_ARGUMENT = 1
@@ -117,16 +121,29 @@ class RopeQuant(ctypes.Structure):
 
 
 _lib = None
+_trace_lib = None
 
 
 def lib() -> ctypes.CDLL:
     """The loaded libbsa.so, with argument/return types declared."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m paged_attention_bsr_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    if _lib is None:
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+def trace_lib() -> ctypes.CDLL:
+    """The loaded libbsa_trace.so (test builds with per-tile trace records)."""
+    global _trace_lib
+    if _trace_lib is None:
+        _trace_lib = _load(TRACE_LIB_PATH)
+    return _trace_lib
+
+
+def _load(path: str) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_attention_bsr_amd.build`")
+    L = ctypes.CDLL(path)
     vp, st, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     L.bsa_plan_desc_init.argtypes = [ctypes.POINTER(PlanDesc)]
     L.bsa_plan_desc_init.restype = None
@@ -170,9 +187,10 @@ def lib() -> ctypes.CDLL:
     L.bsa_plan_destroy.restype = None
     L.bsa_last_error.argtypes = []
     L.bsa_last_error.restype = ctypes.c_char_p
+    L.bsa_trace_records.argtypes = [vp, vp, _i32p, vp]
+    L.bsa_trace_records.restype = st
     if L.bsa_plan_desc_sizeof() != ctypes.sizeof(PlanDesc):
         raise RuntimeError("bsa_plan_desc_t layout mismatch between bsa.h and the Python binding")
-    _lib = L
     return L
 
 
@@ -184,6 +202,7 @@ class BsaError(RuntimeError):
         self.status = status
 
 
-def check(status: int) -> None:
+def check(status: int, library: ctypes.CDLL | None = None) -> None:
+    """Raise BsaError with the last error message of ``library`` (default libbsa.so)."""
     if status != BSA_OK:
-        raise BsaError(status, lib().bsa_last_error().decode(errors="replace"))
+        raise BsaError(status, (library or lib()).bsa_last_error().decode(errors="replace"))

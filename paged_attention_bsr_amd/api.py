@@ -53,6 +53,9 @@ class Plan:
     ``mask`` is ignored).  With either, ``causal`` has no effect.
 
     Variable block sizes: use ``Plan.variable``.
+
+    ``trace=True`` plans and runs with libbsa_trace.so, whose kernels record
+    per tile what they walked (trace_records); tests only.
     """
 
     def __init__(self, indptr, indices, M: int, N: int, R: int, C: int, num_qo_heads: int,
@@ -63,8 +66,9 @@ class Plan:
                  q_descale: float = 1.0, k_descale: float = 1.0, v_descale: float = 1.0,
                  q_token_stride: int = 0, k_token_stride: int = 0, v_token_stride: int = 0,
                  o_token_stride: int = 0, num_cus: int = 0, block_mask=None, q2k_indices=None,
-                 q2k_num=None, mask=None, packed_mask=None, block_row_sz=None, block_col_sz=None):
-        lib = L.lib()
+                 q2k_num=None, mask=None, packed_mask=None, block_row_sz=None, block_col_sz=None,
+                 trace: bool = False):
+        lib = self._lib = L.trace_lib() if trace else L.lib()
         self._handle = ctypes.c_void_p()
         self._indptr = _i32(np.zeros(1) if indptr is None else indptr)
         self._indices = _i32(np.zeros(0) if indices is None else indices)
@@ -135,7 +139,7 @@ class Plan:
                 raise ValueError("block_row_sz (heads, MB) and block_col_sz (heads, NB) go together")
             d.block_row_sz, d.block_col_sz = _ptr(self._row_sz), _ptr(self._col_sz)
             d.var_row_blocks, d.var_col_blocks = int(self._row_sz.shape[1]), int(self._col_sz.shape[1])
-        L.check(lib.bsa_plan_ex(ctypes.byref(d), ctypes.byref(self._handle)))
+        self._check(lib.bsa_plan_ex(ctypes.byref(d), ctypes.byref(self._handle)))
         inf = self.info()
         self.M, self.N, self.R, self.C = int(M), int(N), int(inf["R"]), int(inf["C"])
         self.num_qo_heads, self.num_kv_heads = int(num_qo_heads), int(num_kv_heads)
@@ -163,15 +167,18 @@ class Plan:
         return cls(None, None, int(rs[0].sum()), int(cs[0].sum()), R, C, num_qo_heads, num_kv_heads, head_dim,
                    block_mask=block_mask_map, block_row_sz=rs, block_col_sz=cs, **kw)
 
+    def _check(self, status: int) -> None:
+        L.check(status, self._lib)
+
     # ------------------------------------------------------------------ info
     def info(self) -> dict:
         inf = L.PlanInfo()
-        L.check(L.lib().bsa_plan_info(self._handle, ctypes.byref(inf)))
+        self._check(self._lib.bsa_plan_info(self._handle, ctypes.byref(inf)))
         return {name: getattr(inf, name) for name, _ in inf._fields_}
 
     @property
     def workspace_size(self) -> int:
-        return int(L.lib().bsa_workspace_size(self._handle))
+        return int(self._lib.bsa_workspace_size(self._handle))
 
     def tables(self) -> dict:
         """The planner's tables (tiles (T, 8), merges (S, 8), cols, wg_ptr (W + 1)) as int32 numpy arrays."""
@@ -180,12 +187,12 @@ class Plan:
         merges = np.zeros((inf["num_merges"], 8), np.int32)
         cols = np.zeros(inf["num_cols"], np.int32)
         wg_ptr = np.zeros(inf["num_workgroups"] + 1, np.int32)
-        L.check(L.lib().bsa_plan_export(self._handle, _ptr(tiles), _ptr(merges), _ptr(cols)))
-        L.check(L.lib().bsa_plan_export_workgroups(self._handle, _ptr(wg_ptr)))
+        self._check(self._lib.bsa_plan_export(self._handle, _ptr(tiles), _ptr(merges), _ptr(cols)))
+        self._check(self._lib.bsa_plan_export_workgroups(self._handle, _ptr(wg_ptr)))
         out = {"tiles": tiles, "merges": merges, "cols": cols, "wg_ptr": wg_ptr}
         if inf["mask_plane_words"] > 0:
             bits = np.zeros((inf["R"], inf["mask_plane_words"]), np.uint32)
-            L.check(L.lib().bsa_plan_export_mask_bits(self._handle,
+            self._check(self._lib.bsa_plan_export_mask_bits(self._handle,
                                                       bits.ctypes.data_as(ctypes.POINTER(ctypes.c_uint32))))
             out["mask_bits"] = bits
         return out
@@ -204,7 +211,7 @@ class Plan:
         the same tensor skip the copy."""
         ws = self.workspace() if workspace is None else workspace
         st = torch.cuda.current_stream(ws.device).cuda_stream if stream is None else stream
-        L.check(L.lib().bsa_upload(self._handle, ws.data_ptr(), ws.numel() * ws.element_size(), st))
+        self._check(self._lib.bsa_upload(self._handle, ws.data_ptr(), ws.numel() * ws.element_size(), st))
         self._pinned = (weakref.ref(ws), ws.data_ptr(), ws.numel() * ws.element_size())
 
     def _ensure_pinned(self, ws: torch.Tensor, stream) -> None:
@@ -258,16 +265,25 @@ class Plan:
             if not t.is_cuda or t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous float32 device tensor of {n} entries")
             scales.append(t.data_ptr())
-        L.check(L.lib().bsa_run_ex(self._handle, int(phase), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+        self._check(self._lib.bsa_run_ex(self._handle, int(phase), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                    out.data_ptr(), lse.data_ptr() if lse is not None else None, *scales,
                                    ws.data_ptr(), ws.numel() * ws.element_size(), st))
         return (out, lse) if return_lse else out
 
+    def trace_records(self, workspace: torch.Tensor, stream=None) -> np.ndarray:
+        """(num_tiles, 8) int32 records of the last attention phase run in ``workspace``
+        (bsa_trace_records; trace=True plans only)."""
+        st = torch.cuda.current_stream(workspace.device).cuda_stream if stream is None else stream
+        rec = np.zeros((self.info()["num_tiles"], 8), np.int32)
+        self._check(self._lib.bsa_trace_records(self._handle, workspace.data_ptr(), _ptr(rec), st))
+        return rec
+
     def __del__(self):
         h = getattr(self, "_handle", None)
-        if h is not None and h.value:
+        lib = getattr(self, "_lib", None)
+        if h is not None and h.value and lib is not None:
             try:
-                L.lib().bsa_plan_destroy(h)
+                lib.bsa_plan_destroy(h)
             except Exception:  # interpreter shutdown
                 pass
             self._handle = None

@@ -1,11 +1,15 @@
 """Build libbsa.so in-tree with hipcc for gfx950.
 
-    python -m paged_attention_bsr_amd.build          # build (always recompiles)
+    python -m paged_attention_bsr_amd.build          # build both libraries (always recompiles)
 
 Host-only sources (the planner) are compiled with the host compiler, HIP
 sources with hipcc for --offload-arch=gfx950, then linked into
 paged_attention_bsr_amd/libbsa.so.  Packed-FP32 VALU instructions are
 disabled for all device code (-packed-fp32-ops).
+
+The same sources built with -DBSA_TRACE give libbsa_trace.so, whose
+kernels also write per-tile trace records (bsa_trace_records); only tests
+load it.
 """
 from __future__ import annotations
 
@@ -20,6 +24,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbsa.so")
+TRACE_LIB = os.path.join(PKG, "libbsa_trace.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 ARCH = os.environ.get("BSA_OFFLOAD_ARCH", "gfx950")
@@ -44,29 +49,41 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libbsa.so; returns the library path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def _variant_jobs(build_dir: str, defs: list) -> list:
     jobs = []
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD_DIR, src + ".o")
+        obj = os.path.join(build_dir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        jobs.append([HIPCC, *COMMON, *HIP_FLAGS, *EXTRA, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([HIPCC, *COMMON, *HIP_FLAGS, *EXTRA, *defs, *lang, "-c", os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
-        obj = os.path.join(BUILD_DIR, src + ".o")
-        jobs.append(["g++", *COMMON, *EXTRA, "-c", os.path.join(CSRC, src), "-o", obj])
-    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
-        outs = list(ex.map(_run, jobs))
+        obj = os.path.join(build_dir, src + ".o")
+        jobs.append(["g++", *COMMON, *EXTRA, *defs, "-c", os.path.join(CSRC, src), "-o", obj])
+    return jobs
+
+
+def build(verbose: bool = False, trace: bool = True) -> str:
+    """Compile every source and link libbsa.so (and, with ``trace``, libbsa_trace.so);
+    returns the product library's path."""
+    variants = [(LIB, BUILD_DIR, [])]
+    if trace:
+        variants.append((TRACE_LIB, os.path.join(BUILD_DIR, "trace"), ["-DBSA_TRACE"]))
+    jobs = []
+    for _, bdir, defs in variants:
+        os.makedirs(bdir, exist_ok=True)
+        jobs.append(_variant_jobs(bdir, defs))
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        outs = list(ex.map(_run, [j for vj in jobs for j in vj]))
     if verbose:
         for o in outs:
             if o.strip():
                 print(o)
-    objs = [j[-1] for j in jobs]
-    tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
+    for (lib_path, _, _), vj in zip(variants, jobs):
+        objs = [j[-1] for j in vj]
+        tmp = lib_path + ".tmp"
+        _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+        os.replace(tmp, lib_path)
     return LIB
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, trace="--no-trace" not in sys.argv))

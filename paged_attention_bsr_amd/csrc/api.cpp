@@ -289,11 +289,27 @@ bsa_status_t bsa_run_ex(bsa_plan_t plan, int32_t phase, const void* q, const voi
   a.heads_per_wg = P.heads_per_wg;
   a.mbits = P.mbits.empty() ? nullptr : reinterpret_cast<const uint32_t*>(ws + P.off_mbits);
   a.mask_plane_words = P.mask_plane_words;
+#ifdef BSA_TRACE
+  a.trace = reinterpret_cast<int32_t*>(ws + P.table_bytes + P.partial_bytes);
+#endif
   a.q_scale = scale_q;
   a.k_scale = scale_k;
   a.v_scale = scale_v;
 
   hipError_t e;
+#ifdef BSA_TRACE
+  if (phase & BSA_PHASE_ATTENTION) {
+    // every record starts as {0, INT32_MAX, 0, 0, -2, -2, -2, -2}
+    std::vector<int32_t> init(static_cast<size_t>(a.num_tiles) * bsa::kTraceInts, -2);
+    for (int32_t t = 0; t < a.num_tiles; ++t) {
+      int32_t* r = init.data() + static_cast<size_t>(t) * bsa::kTraceInts;
+      r[0] = 0, r[1] = INT32_MAX, r[2] = 0, r[3] = 0;
+    }
+    e = hipMemcpyAsync(a.trace, init.data(), init.size() * 4, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return set_err(BSA_ERR_HIP, std::string("trace reset: ") + hipGetErrorString(e));
+  }
+#endif
   if (phase & BSA_PHASE_ATTENTION) {
     if (P.kernel == BSA_KERNEL_MLA) e = bsa::launch_attn_mla(a, d.causal != 0, a.lens != nullptr, st);
     else if (P.kernel == BSA_KERNEL_DECODE)
@@ -389,6 +405,26 @@ bsa_status_t bsa_plan_export_mask_bits(bsa_plan_t plan, uint32_t* bits) {
   const bsa::Plan& P = plan->p;
   if (!P.mbits.empty()) std::memcpy(bits, P.mbits.data(), P.mbits.size() * 4);
   return BSA_OK;
+}
+
+bsa_status_t bsa_trace_records(bsa_plan_t plan, const void* workspace, int32_t* records, void* stream) {
+  g_err.clear();
+  if (!plan || !workspace || !records)
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "plan, workspace and records must be non-NULL");
+#ifdef BSA_TRACE
+  const bsa::Plan& P = plan->p;
+  const size_t n = P.tiles.size() / bsa::kTileInts * bsa::kTraceInts;
+  if (n == 0) return BSA_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const unsigned char* src = static_cast<const unsigned char*>(workspace) + P.table_bytes + P.partial_bytes;
+  hipError_t e = hipStreamSynchronize(st);
+  if (e == hipSuccess) e = hipMemcpy(records, src, n * 4, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return set_err(BSA_ERR_HIP, std::string("trace copy: ") + hipGetErrorString(e));
+  return BSA_OK;
+#else
+  (void)stream;
+  return set_err(BSA_ERR_UNSUPPORTED, "library built without per-tile trace records (BSA_TRACE)");
+#endif
 }
 
 bsa_status_t bsa_plan_export(bsa_plan_t plan, int32_t* tiles, int32_t* merges, int32_t* cols) {

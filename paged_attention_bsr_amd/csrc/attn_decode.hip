@@ -441,9 +441,19 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
     // stage i holds item p + i at the top of each pass; it is reloaded (item
     // p + NS + i) as soon as its scores are formed
     int p = 0;
+    TraceAcc tr;  // trace build: column entries and keys (before the causal mask) of this wave's items
     do {  // nTe >= NS: at least one pass, so the waits never see a skipped body
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
+        if constexpr (kTrace) {
+          // this lane's two keys of the item (quad 0 only), inside the range
+          // and their block's valid length
+          const int kt = sub + ((p + i) << lg_wph);
+          for (int kb = 0; kb < 2 && quad == 0; ++kb) {
+            const int t = kt * kKT + 8 * (col >> 2) + 4 * kb + (col & 3);
+            if (t < cur.nblk * C && t % C < (LENS ? lens[cur.cb + t / C] : C)) tr.keys(cur.cb + t / C, 1);
+          }
+        }
         f32x4 sc[2];
         const Src sn = src_of(p + NS + i);
         scores(stg[i], sc);
@@ -452,6 +462,7 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
       }
       p += NS;
     } while (p < nTe);
+    if constexpr (kTrace) trace_flush(a.trace, gn - HG + hw, tr, sub == 0 && lane == 0, cur.part, cur.kvh, cur.row0, cur.nrows);
     finish_tile(cur);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[ks] = qn[ks];

@@ -190,6 +190,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mla_kernel(AttnArgs a) {
     return ok ? r.J * C + off : -1;
   };
   auto key_tok = [&](int t) -> int { return finish_tok(t, fetch_blk(t)); };
+  // trace build: one thread per key (waves 0, 1, lanes 0-15) counts the keys
+  // and column entries of every tile it loads, in the last pass
+  TraceAcc tr;
+  auto trace_key = [&](int t, int tok) {
+    if (kTrace && tid < 128 && quad == 0 && tok >= 0) tr.keys(cb + (C1 ? t : t / C), 1);
+  };
   const uint8_t* kv = static_cast<const uint8_t*>(a.k);
   // gather mapping: lane l of wave w takes key l % 16 (+ 16 for odd waves) and
   // 16-byte unit l / 16 (+ 4 for waves 2, 3, + 8 per round), so one load
@@ -266,6 +272,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mla_kernel(AttnArgs a) {
       blk_next = fetch_blk((kt + 3) * kKT + my_key);
       load_tile(ld, t2);
       ld_tok = t2;
+      trace_key((kt + 2) * kKT + my_key, t2);
     }
     if (kt >= ntiles) return;  // the odd step after the last tile: loads only
 
@@ -407,11 +414,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mla_kernel(AttnArgs a) {
     }
   };
   for (int pass = 0;; ++pass) {
+    tr = TraceAcc{};
     if (ntiles > 0) {
       tok_a = key_tok(my_key);
       load_tile(creg_a, tok_a);
       tok_b = key_tok(kKT + my_key);
       load_tile(creg_b, tok_b);
+      trace_key(my_key, tok_a);
+      trace_key(kKT + my_key, tok_b);
       blk_next = fetch_blk(2 * kKT + my_key);
       store_tile(0, creg_a, tok_a);
     }
@@ -432,6 +442,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mla_kernel(AttnArgs a) {
     }
     over = false;
   }
+
+  trace_flush(a.trace, tile, tr, tid == 0, part, 0, row0, nrows);
 
   const int dv0 = hf * (kDv / 2);
 #pragma unroll

@@ -151,6 +151,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     for (int ks = 0; ks < 8; ++ks) qf[ks] = v8{};
   }
 
+  TraceAcc tr;  // trace build: column entries and valid keys this thread loaded
+
   // ---- key tokens.  BLOCKTILE (C a multiple of KT): a key tile lies inside one
   // block, whose id and length are uniform scalar loads.  Otherwise each key
   // looks its block up.  Tiles past the end (only ever loaded, never used)
@@ -214,7 +216,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
       __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(pv + (u ^ v_swz(row)) * 8),
                                        (__attribute__((address_space(3))) void*)(st + L::kKBytes + b * 1024), 16, 0,
                                        0);
-      if (u == 0) ktok[row] = tok;
+      if (u == 0) {
+        ktok[row] = tok;
+        if (kTrace && tok >= 0) tr.keys(cb + (kt * KT + row) / C, 1);
+      }
     }
   };
 
@@ -240,6 +245,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
       k8[i] = *reinterpret_cast<const u32x4*>(pk + pc);
       v8r[i] = *reinterpret_cast<const u32x4*>(pv + pc);
       tok8[i] = tok;
+      if (kTrace && (piece & 7) == 0 && tok >= 0) tr.keys(cb + (kt * KT + row) / C, 1);
     }
   };
   auto store8 = [&](unsigned char* st, int* ktok) {
@@ -284,6 +290,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   const unsigned char* vbytes = reinterpret_cast<const unsigned char*>(vbase);
   int dblk = 0, doff = 0;  // block and offset of the next tile to load (FAST)
   auto dma_fast = [&](unsigned char* st) -> int {
+    if (kTrace && tid == 0) tr.keys(cb + dblk, KT);
     const int lo = cols[cb + dblk] * C + doff;
     doff += KT;
     if (doff == C) {
@@ -530,6 +537,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     }
   }
   auto load8_fast = [&]() -> int {
+    if (kTrace && tid == 0) tr.keys(cb + dblk, KT);
     const int lo = cols[cb + dblk] * C + doff;
     doff += KT;
     if (doff == C) {
@@ -593,6 +601,8 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
       }
     }
   }
+
+  trace_flush(a.trace, blockIdx.x, tr, tid == 0, part, kvh, row0, nrows);
 
   // ---- finalize this lane's row
   const float l_tot = l_run + xor_lane32(l_run);

@@ -74,6 +74,45 @@ __device__ __forceinline__ u32x4 fp8x8_widen(u32x2 w) {
                fp8x2_widen<T, true>(w[1])};
 }
 
+// Trace build (BSA_TRACE, a separate library that only tests load): each
+// kernel records per planner tile what its loops did, 8 int32 per tile,
+// {times processed, first column entry loaded, last entry loaded + 1, valid
+// keys loaded, partial offset written (-1: o/lse), kv head, first row, rows};
+// the host fills every record with {0, INT_MAX, 0, 0, ...} before the launch.
+// In the product build every trace statement is dead code.
+#ifdef BSA_TRACE
+constexpr bool kTrace = true;
+#else
+constexpr bool kTrace = false;
+#endif
+struct TraceAcc {
+  int lo = 0x7fffffff, end = 0, n = 0;
+  __device__ __forceinline__ void keys(int entry, int count) {
+    if (kTrace && count > 0) {
+      lo = entry < lo ? entry : lo;
+      end = entry + 1 > end ? entry + 1 : end;
+      n += count;
+    }
+  }
+};
+__device__ __forceinline__ void trace_flush(int32_t* trace, int tile, const TraceAcc& acc, bool owner, int part,
+                                            int kvh, int row0, int nrows) {
+  if (!kTrace) return;
+  int32_t* r = trace + static_cast<int64_t>(tile) * 8;
+  if (acc.n > 0) {
+    atomicMin(r + 1, acc.lo);
+    atomicMax(r + 2, acc.end);
+    atomicAdd(r + 3, acc.n);
+  }
+  if (owner) {
+    atomicAdd(r + 0, 1);
+    r[4] = part;
+    r[5] = kvh;
+    r[6] = row0;
+    r[7] = nrows;
+  }
+}
+
 // v_exp_f32: 2^x, with 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -37,6 +37,7 @@ struct AttnArgs {
   // column-list entry e's row block sees key c of that block; null = none
   const uint32_t* mbits;
   int64_t mask_plane_words;
+  int32_t* trace;          // trace build only: per-tile records (planner.h), else null
 };
 
 struct MergeArgs {

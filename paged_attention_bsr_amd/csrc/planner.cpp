@@ -515,6 +515,10 @@ bsa_status_t build_plan_impl(const bsa_plan_desc_t& desc, int32_t num_cus, Plan&
   P.table_bytes = std::max<int64_t>(o, 256);
   P.partial_bytes = round_up(P.partial_floats * 4, 256);
   P.workspace_bytes = P.table_bytes + P.partial_bytes;
+#ifdef BSA_TRACE
+  // trace build: one record of kTraceInts int32 per tile after the partials
+  P.workspace_bytes += round_up(static_cast<int64_t>(P.tiles.size() / kTileInts) * kTraceInts * 4, 256);
+#endif
   P.table_blob.assign(static_cast<size_t>(P.table_bytes), 0);
   auto put = [&](int64_t at, const std::vector<int32_t>& v) {
     if (!v.empty()) std::copy(reinterpret_cast<const uint8_t*>(v.data()),

@@ -14,6 +14,13 @@ namespace bsa {
 constexpr int kTileInts = 8;
 constexpr int kMergeInts = 8;
 
+// Trace build (BSA_TRACE, a separate library for tests): each kernel records
+// per planner tile what its loops actually did, kTraceInts int32 per tile after
+// the split partials: {times processed, first column entry walked, last entry
+// walked + 1, valid keys counted, partial offset written, kv head, first row,
+// rows}.
+constexpr int kTraceInts = 8;
+
 // Tile record fields.
 enum TileField { T_ROWBLOCK = 0, T_KVHEAD, T_ROW0, T_NROWS, T_COLB, T_COLE, T_PART, T_KEYS };
 // Merge record fields.

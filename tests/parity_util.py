@@ -28,16 +28,17 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
-def plan_for(w, kv_splits=1, num_cus=0) -> Plan:
+def plan_for(w, kv_splits=1, num_cus=0, trace=False) -> Plan:
     """The library plan of a workload; a per-head structure (w.meta["block_mask"], or
     w.meta["q2k"] = (q2k_indices, q2k_num)) replaces the shared BSR rows; element masks
     come from w.meta["packed_mask"] (else w.meta["mask"]); w.meta["variable"] =
-    (block_mask_map, block_row_sz, block_col_sz) plans variable block sizes."""
+    (block_mask_map, block_row_sz, block_col_sz) plans variable block sizes.  ``trace``
+    plans with the trace build of the library (per-tile records)."""
     if "variable" in w.meta:
         bm, rs, cs = w.meta["variable"]
         return Plan.variable(bm, rs, cs, w.num_qo_heads, w.num_kv_heads, w.head_dim, causal=w.causal,
                              sm_scale=w.sm_scale, kv_splits=kv_splits, q_dtype=w.q_dtype, num_cus=num_cus,
-                             **w.meta.get("grid", {}))
+                             trace=trace, **w.meta.get("grid", {}))
     extra = {}
     if "packed_mask" in w.meta:
         extra["packed_mask"] = w.meta["packed_mask"]
@@ -52,7 +53,7 @@ def plan_for(w, kv_splits=1, num_cus=0) -> Plan:
                 kv_splits=kv_splits, kv_block_lens=w.kv_block_lens, q_dtype=w.q_dtype,
                 kv_dtype=w.kv_dtype, o_dtype=w.o_dtype, k_descale=w.k_descale,
                 v_descale=w.v_descale, k_token_stride=w.k_token_stride,
-                v_token_stride=w.v_token_stride, num_cus=num_cus, **extra)
+                v_token_stride=w.v_token_stride, num_cus=num_cus, trace=trace, **extra)
 
 
 def to_device(w, device="cuda"):

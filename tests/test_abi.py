@@ -31,6 +31,51 @@ def test_library_exports_every_declared_function():
     assert set(names) <= exported
 
 
+@pytest.mark.parametrize("path", [L.LIB_PATH, L.TRACE_LIB_PATH], ids=["product", "trace"])
+def test_both_builds_export_the_same_declared_functions(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\b(bsa_[a-z0-9_]+)\b", out))
+    assert set(_declared_functions()) <= exported
+
+
+def _tiny_plan(lib):
+    indptr = np.array([0, 1], np.int32)
+    indices = np.array([0], np.int32)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    d = L.PlanDesc()
+    lib.bsa_plan_desc_init(ctypes.byref(d))
+    d.indptr, d.indices = indptr.ctypes.data_as(i32p), indices.ctypes.data_as(i32p)
+    d.M = d.N = d.R = d.C = 4
+    d.num_qo_heads = d.num_kv_heads = 2
+    d.head_dim_qk = d.head_dim_vo = 128
+    d.num_cus = 256
+    h = ctypes.c_void_p()
+    st = lib.bsa_plan_ex(ctypes.byref(d), ctypes.byref(h))
+    assert st == L.BSA_OK, lib.bsa_last_error()
+    return h
+
+
+def test_trace_records_only_in_the_trace_build():
+    # the product build refuses on the host, before touching any device memory
+    lib = L.lib()
+    h = _tiny_plan(lib)
+    rec = np.zeros(8, np.int32)
+    st = lib.bsa_trace_records(h, ctypes.c_void_p(256), rec.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None)
+    assert st == L.BSA_ERR_UNSUPPORTED and b"BSA_TRACE" in lib.bsa_last_error()
+    assert lib.bsa_trace_records(h, None, rec.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None) == \
+        L.BSA_ERR_INVALID_ARGUMENT
+    lib.bsa_plan_destroy(h)
+    # the trace build reserves one record of 8 int32 per tile after the partials
+    tl = L.trace_lib()
+    ht, hp = _tiny_plan(tl), _tiny_plan(lib)
+    it, ip = L.PlanInfo(), L.PlanInfo()
+    assert tl.bsa_plan_info(ht, ctypes.byref(it)) == 0 and lib.bsa_plan_info(hp, ctypes.byref(ip)) == 0
+    assert it.table_bytes == ip.table_bytes and it.partial_bytes == ip.partial_bytes
+    assert it.workspace_bytes == ip.workspace_bytes + -(-it.num_tiles * 32 // 256) * 256
+    tl.bsa_plan_destroy(ht)
+    lib.bsa_plan_destroy(hp)
+
+
 def test_desc_layout_matches_binding():
     assert L.lib().bsa_plan_desc_sizeof() == ctypes.sizeof(L.PlanDesc)
 
