@@ -52,9 +52,15 @@ constexpr int kVBytes = kKT * kD * 2;   // wave-private V tile
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-// LDS byte offset of 16-byte chunk `c` of key row `k` in a V tile.
+// LDS byte offset of 16-byte chunk `c` of key row `k` in a V tile: chunk
+// c ^ s(k), s(k) = 2 (k & 3) + 9 bit3(k).  A V store writes one chunk of keys
+// {0..3, 8..11} (+ 4) from 8 consecutive lanes, which a ds_write_b128 serves
+// in one pass when the chunks differ mod 8 (measured on gfx950): s(k) mod 8 =
+// 0, 2, 4, 6, 1, 3, 5, 7.  A transposed read takes the aligned chunk pair
+// (2m, 2m + 1) of the same 8 rows: pair m ^ (s(k) >> 1) = m ^ 0..7, all
+// different.
 __device__ __forceinline__ int v_chunk_off(int k, int c) {
-  return k * (kD * 2) + ((c ^ (((k & 3) << 1) | (((k >> 3) & 1) << 3))) << 4);
+  return k * (kD * 2) + ((c ^ (((k & 3) << 1) | (((k >> 3) & 1) * 9))) << 4);
 }
 
 // KV8: K and V are stored as OCP fp8 e4m3 (one byte per value) and widened

@@ -84,18 +84,27 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
-// Unit u of key k's row sits at unit u ^ kx(k), kx(k) = bits 1 and 2 of the
-// key in place plus bit 3 as bit 0, so the XOR stays inside an aligned group
-// of 8 units.  LDS has 64 banks of 4 B; a row is 72 units of 16 B, so even
-// keys start at bank 0 and odd keys at bank 32.  Then
-//   * 16 consecutive keys at one unit (the QK reads and the tile stores, 16
-//     lanes x 16 B per pass) hit 16 different bank units: bit 0 picks the
-//     half, kx (bits 1-3) a distinct unit inside it;
+// Unit u of key k's row sits at unit u ^ kx(k), kx(k) = k & 7, so the XOR
+// stays inside an aligned group of 8 units.  LDS has 64 banks of 4 B; a row is
+// 72 units of 16 B, so even keys start at bank 0 and odd keys at bank 32.
+// Measured on gfx950 (SQ_LDS_BANK_CONFLICT): a ds_write_b128 serves 8
+// consecutive lanes per pass and is conflict-free when their units differ mod
+// 8; a ds_read_b128 serves 16 lanes per pass, lanes 0-7 of one quad (16-lane
+// group) with lanes 8-15 of another, and is conflict-free when their units
+// differ mod 16.  Then
+//   * the tile stores (8 consecutive keys at one unit) hit units U ^ k mod 8:
+//     all different;
+//   * the QK reads (lane (col, quad) at key col, unit B + quad): keys of one
+//     quad hit different units; for keys c < 8 of one quad and d >= 8 of the
+//     quad read with it, both even or both odd (else their rows start in
+//     different bank halves), the units differ because (c ^ d) & 7 is even
+//     while quad ^ quad' is odd (1 or 3 for the quads read together);
 //   * a transposed read (32 lanes x 8 B per pass: 8 consecutive keys 8p ..
 //     8p + 7, each at the two units 2m, 2m + 1 before the XOR) hits 8
-//     different aligned unit pairs: bit 0 picks the half, bits 1 and 2 (kx
-//     bits 1 and 2) the pair; kx bit 0 only swaps the two units of a pair.
-__device__ __forceinline__ int kx(int key) { return (key & 6) | ((key >> 3) & 1); }
+//     different aligned unit pairs: bit 0 of the key picks the bank half,
+//     bits 1 and 2 (kx bits 1 and 2) the pair; kx bit 0 only swaps the two
+//     units of a pair.
+__device__ __forceinline__ int kx(int key) { return key & 7; }
 __device__ __forceinline__ int k_off(int key, int u) { return key * MlaLds::kKRow + ((u ^ kx(key)) << 4); }
 
 // Workgroup -> tile: within each run of 16 workgroups, b and b + 8 (which the

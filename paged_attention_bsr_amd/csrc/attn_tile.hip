@@ -254,10 +254,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
       const int piece = tid + i * NTHR;
       const int row = piece >> 3;
       const int c = (piece & 7) * 2;  // its two 16-bit chunks
-      *reinterpret_cast<u32x4*>(st + k_off(row, c)) = fp8x8_widen<T>(u32x2{k8[i][0], k8[i][1]});
-      *reinterpret_cast<u32x4*>(st + k_off(row, c + 1)) = fp8x8_widen<T>(u32x2{k8[i][2], k8[i][3]});
-      *reinterpret_cast<u32x4*>(st + L::kKBytes + v_off(row, c)) = fp8x8_widen<T>(u32x2{v8r[i][0], v8r[i][1]});
-      *reinterpret_cast<u32x4*>(st + L::kKBytes + v_off(row, c + 1)) = fp8x8_widen<T>(u32x2{v8r[i][2], v8r[i][3]});
+      // pieces 4-7 of a row store their odd chunk first: a ds_write_b128 serves
+      // 8 consecutive lanes per pass, conflict-free when their chunks differ mod
+      // 8 (measured on gfx950), and chunks 2p, p = 0..7, do so only in pairs
+      const bool h = (piece & 4) != 0;
+      const u32x2 k0 = h ? u32x2{k8[i][2], k8[i][3]} : u32x2{k8[i][0], k8[i][1]};
+      const u32x2 k1 = h ? u32x2{k8[i][0], k8[i][1]} : u32x2{k8[i][2], k8[i][3]};
+      const u32x2 v0 = h ? u32x2{v8r[i][2], v8r[i][3]} : u32x2{v8r[i][0], v8r[i][1]};
+      const u32x2 v1 = h ? u32x2{v8r[i][0], v8r[i][1]} : u32x2{v8r[i][2], v8r[i][3]};
+      const int c0 = c + (h ? 1 : 0), c1 = c + (h ? 0 : 1);
+      *reinterpret_cast<u32x4*>(st + k_off(row, c0)) = fp8x8_widen<T>(k0);
+      *reinterpret_cast<u32x4*>(st + k_off(row, c1)) = fp8x8_widen<T>(k1);
+      *reinterpret_cast<u32x4*>(st + L::kKBytes + v_off(row, c0)) = fp8x8_widen<T>(v0);
+      *reinterpret_cast<u32x4*>(st + L::kKBytes + v_off(row, c1)) = fp8x8_widen<T>(v1);
       // the whole-tile path (full blocks, whole key tiles) keeps no token array
       if (!(BLOCKTILE && !LENS))
         if ((piece & 7) == 0) ktok[row] = tok8[i];
