@@ -8,7 +8,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsa.so")
+# BSA_LIBRARY names another build of the same C ABI to load instead (the planner's
+# sanitizer tests use a host-only one that lacks the device entry points)
+LIB_PATH = os.environ.get("BSA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsa.so")
 TRACE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsa_trace.so")
 
 BSA_OK = 0
@@ -140,10 +142,33 @@ def trace_lib() -> ctypes.CDLL:
     return _trace_lib
 
 
+class _Declarer:
+    """Attribute setter that skips functions a host-only build does not export."""
+
+    def __init__(self, lib: ctypes.CDLL, host_only: bool):
+        self._lib, self._host_only = lib, host_only
+
+    def __getattr__(self, name):
+        try:
+            return getattr(self._lib, name)
+        except AttributeError:
+            if not self._host_only:
+                raise
+            return _Sink()
+
+
+class _Sink:
+    """Absorbs argtypes / restype of a function the loaded build does not have."""
+
+    argtypes = restype = None
+
+
 def _load(path: str) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m paged_attention_bsr_amd.build`")
-    L = ctypes.CDLL(path)
+    lib = ctypes.CDLL(path)
+    host_only = not hasattr(lib, "bsa_run")
+    L = _Declarer(lib, host_only)
     vp, st, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
     L.bsa_plan_desc_init.argtypes = [ctypes.POINTER(PlanDesc)]
     L.bsa_plan_desc_init.restype = None
@@ -191,7 +216,7 @@ def _load(path: str) -> ctypes.CDLL:
     L.bsa_trace_records.restype = st
     if L.bsa_plan_desc_sizeof() != ctypes.sizeof(PlanDesc):
         raise RuntimeError("bsa_plan_desc_t layout mismatch between bsa.h and the Python binding")
-    return L
+    return lib
 
 
 class BsaError(RuntimeError):

@@ -232,6 +232,24 @@ class Plan:
         ``phase`` selects bsa_run_phase's attention-only / merge-only halves.
         ``scale_q`` (num_qo_heads,), ``scale_k`` / ``scale_v`` (num_kv_heads,): per-head
         float32 dequant scales on the device (run(): scale_q/k/v), None = 1."""
+        call, out, lse = self._prepare(q, k, v, out, lse, return_lse, workspace, stream, phase,
+                                       scale_q, scale_k, scale_v)
+        call()
+        return (out, lse) if return_lse else out
+
+    def bind(self, q: torch.Tensor, k: torch.Tensor, v: Optional[torch.Tensor] = None,
+             out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+             return_lse: bool = True, workspace: Optional[torch.Tensor] = None, stream=None,
+             phase: int = L.BSA_PHASE_ALL, scale_q: Optional[torch.Tensor] = None,
+             scale_k: Optional[torch.Tensor] = None, scale_v: Optional[torch.Tensor] = None):
+        """Validate the arguments of run() once, pin the tables in the workspace and
+        return (fn, out, lse): fn() runs the attention into out / lse with nothing
+        but the C call (bsa_run_ex), for loops that run the same buffers many
+        times.  fn keeps every tensor it uses alive; the caller must not resize,
+        free or re-pin the workspace to another plan while using it."""
+        return self._prepare(q, k, v, out, lse, return_lse, workspace, stream, phase, scale_q, scale_k, scale_v)
+
+    def _prepare(self, q, k, v, out, lse, return_lse, workspace, stream, phase, scale_q, scale_k, scale_v):
         if v is None:
             v = k
         for name, t, dt in (("q", q, self.q_dtype), ("k", k, self.kv_dtype), ("v", v, self.kv_dtype)):
@@ -265,10 +283,15 @@ class Plan:
             if not t.is_cuda or t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous():
                 raise ValueError(f"{name} must be a contiguous float32 device tensor of {n} entries")
             scales.append(t.data_ptr())
-        self._check(self._lib.bsa_run_ex(self._handle, int(phase), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                   out.data_ptr(), lse.data_ptr() if lse is not None else None, *scales,
-                                   ws.data_ptr(), ws.numel() * ws.element_size(), st))
-        return (out, lse) if return_lse else out
+        fn, args = self._lib.bsa_run_ex, (self._handle, int(phase), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                          out.data_ptr(), lse.data_ptr() if lse is not None else None, *scales,
+                                          ws.data_ptr(), ws.numel() * ws.element_size(), st)
+        keep = (q, k, v, out, lse, ws, scale_q, scale_k, scale_v)  # alive as long as the call
+
+        def call(_keep=keep):
+            self._check(fn(*args))
+
+        return call, out, lse
 
     def trace_records(self, workspace: torch.Tensor, stream=None) -> np.ndarray:
         """(num_tiles, 8) int32 records of the last attention phase run in ``workspace``

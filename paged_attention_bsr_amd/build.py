@@ -37,7 +37,7 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", 
 EXTRA = os.environ.get("BSA_EXTRA_CFLAGS", "").split()
 
 HIP_SOURCES = ["attn_tile.hip", "attn_decode.hip", "attn_mla.hip", "merge.hip", "rope_quant.hip", "api.cpp"]
-HOST_SOURCES = ["planner.cpp"]
+HOST_SOURCES = ["planner.cpp", "abi_host.cpp"]
 
 
 def _run(cmd):

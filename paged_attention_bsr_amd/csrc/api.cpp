@@ -1,4 +1,5 @@
-// C ABI of libbsa.so: validation, plan lifetime, workspace tables, launches.
+// C ABI of libbsa.so, device half: workspace tables, runs, launches (the
+// host half -- planning, plan inspection and lifetime -- is abi_host.cpp).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -9,23 +10,13 @@
 #include <string>
 #include <utility>
 
-#include "bsa.h"
+#include "abi_internal.h"
 #include "kernels.h"
 #include "rope_quant.h"
-#include "planner.h"
-
-struct bsa_plan_s {
-  bsa::Plan p;
-};
 
 namespace {
 
-thread_local std::string g_err;
-
-bsa_status_t set_err(bsa_status_t st, const std::string& msg) {
-  g_err = msg;
-  return st;
-}
+using bsa::set_err;
 
 // Which plan's tables each (device, workspace address) currently holds, and
 // whether the caller pinned them there with bsa_upload.  Only a pinned entry
@@ -105,94 +96,30 @@ bool pinned_here(const bsa::Plan& P, void* ws) {
 
 }  // namespace
 
-extern "C" {
+namespace bsa {
 
-void bsa_plan_desc_init(bsa_plan_desc_t* d) {
-  if (!d) return;
-  std::memset(d, 0, sizeof(*d));
-  d->R = 1;
-  d->C = 1;
-  d->num_qo_heads = 1;
-  d->num_kv_heads = 1;
-  d->head_dim_qk = 128;
-  d->head_dim_vo = 0;
-  d->sm_scale = 0.f;
-  d->kv_splits = 1;
-  d->q_dtype = d->kv_dtype = d->o_dtype = BSA_F16;
-  d->q_descale = d->k_descale = d->v_descale = 1.f;
-}
-
-size_t bsa_plan_desc_sizeof(void) { return sizeof(bsa_plan_desc_t); }
-
-bsa_status_t bsa_plan_ex(const bsa_plan_desc_t* desc, bsa_plan_t* out_plan) {
-  g_err.clear();
-  if (!desc || !out_plan) return set_err(BSA_ERR_INVALID_ARGUMENT, "desc and out_plan must be non-NULL");
-  *out_plan = nullptr;
-  bsa_plan_desc_t d = *desc;
-  if (d.head_dim_vo == 0) d.head_dim_vo = d.head_dim_qk;
-  if (d.q_token_stride == 0) d.q_token_stride = static_cast<int64_t>(d.num_qo_heads) * d.head_dim_qk;
-  if (d.k_token_stride == 0) d.k_token_stride = static_cast<int64_t>(d.num_kv_heads) * d.head_dim_qk;
-  if (d.v_token_stride == 0) d.v_token_stride = static_cast<int64_t>(d.num_kv_heads) * d.head_dim_vo;
-  if (d.o_token_stride == 0) d.o_token_stride = static_cast<int64_t>(d.num_qo_heads) * d.head_dim_vo;
-  if (d.q_token_stride < static_cast<int64_t>(d.num_qo_heads) * d.head_dim_qk ||
-      d.k_token_stride < static_cast<int64_t>(d.num_kv_heads) * d.head_dim_qk ||
-      d.v_token_stride < static_cast<int64_t>(d.num_kv_heads) * d.head_dim_vo ||
-      d.o_token_stride < static_cast<int64_t>(d.num_qo_heads) * d.head_dim_vo)
-    return set_err(BSA_ERR_INVALID_ARGUMENT, "token strides must cover all heads of a token");
-  const int vec = 16 / elt_bytes(d.kv_dtype);
-  if (d.k_token_stride % vec || d.v_token_stride % vec || d.q_token_stride % 8 || d.o_token_stride % 8)
-    return set_err(BSA_ERR_INVALID_ARGUMENT, "token strides must keep every row 16-byte aligned");
-  int32_t cus = d.num_cus;
-  if (cus == 0) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return hip_fail(e, "querying the CU count (pass num_cus > 0 to plan without a GPU)");
-  }
-  bsa_plan_s* plan = nullptr;
-  try {
-    plan = new bsa_plan_s();
-    std::string err;
-    const bsa_status_t st = bsa::build_plan(d, cus, plan->p, err);
-    if (st != BSA_OK) {
-      delete plan;
-      return set_err(st, err);
-    }
-  } catch (const std::bad_alloc&) {
-    delete plan;
-    return set_err(BSA_ERR_HOST_ALLOC, "host allocation failed while planning");
-  }
-  *out_plan = plan;
+bsa_status_t current_device_cus(int32_t* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return hip_fail(e, "querying the CU count (pass num_cus > 0 to plan without a GPU)");
   return BSA_OK;
 }
 
-bsa_status_t bsa_plan(const int32_t* indptr, const int32_t* indices, int64_t M, int64_t N, int32_t R,
-                      int32_t C, int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
-                      int32_t causal, float sm_scale, int32_t kv_splits, bsa_plan_t* out_plan) {
-  bsa_plan_desc_t d;
-  bsa_plan_desc_init(&d);
-  d.indptr = indptr;
-  d.indices = indices;
-  d.M = M;
-  d.N = N;
-  d.R = R;
-  d.C = C;
-  d.num_qo_heads = num_qo_heads;
-  d.num_kv_heads = num_kv_heads;
-  d.head_dim_qk = head_dim;
-  d.head_dim_vo = head_dim;
-  d.causal = causal;
-  d.sm_scale = sm_scale;
-  d.kv_splits = kv_splits;
-  return bsa_plan_ex(&d, out_plan);
+void forget_plan(uint64_t plan_id) {
+  std::lock_guard<std::mutex> lk(g_reg_mu);
+  for (auto it = g_registry.begin(); it != g_registry.end();) {
+    if (it->second.plan_id == plan_id) it = g_registry.erase(it);
+    else ++it;
+  }
 }
 
-size_t bsa_workspace_size(bsa_plan_t plan) {
-  return plan ? static_cast<size_t>(plan->p.workspace_bytes) : 0;
-}
+}  // namespace bsa
+
+extern "C" {
 
 bsa_status_t bsa_upload(bsa_plan_t plan, void* workspace, size_t workspace_bytes, void* stream) {
-  g_err.clear();
+  bsa::clear_err();
   if (!plan || !workspace) return set_err(BSA_ERR_INVALID_ARGUMENT, "plan and workspace must be non-NULL");
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
     return set_err(BSA_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
@@ -202,7 +129,7 @@ bsa_status_t bsa_upload(bsa_plan_t plan, void* workspace, size_t workspace_bytes
 }
 
 bsa_status_t bsa_unpin(bsa_plan_t plan, void* workspace) {
-  g_err.clear();
+  bsa::clear_err();
   if (!plan || !workspace) return set_err(BSA_ERR_INVALID_ARGUMENT, "plan and workspace must be non-NULL");
   int dev = 0;
   const hipError_t e = hipGetDevice(&dev);
@@ -226,7 +153,7 @@ bsa_status_t bsa_run_phase(bsa_plan_t plan, int32_t phase, const void* q, const 
 bsa_status_t bsa_run_ex(bsa_plan_t plan, int32_t phase, const void* q, const void* k, const void* v, void* o,
                         float* lse, const float* scale_q, const float* scale_k, const float* scale_v,
                         void* workspace, size_t workspace_bytes, void* stream) {
-  g_err.clear();
+  bsa::clear_err();
   if (!plan) return set_err(BSA_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (phase < BSA_PHASE_ATTENTION || phase > BSA_PHASE_ALL)
     return set_err(BSA_ERR_INVALID_ARGUMENT, "phase must be BSA_PHASE_ATTENTION, BSA_PHASE_MERGE or BSA_PHASE_ALL");
@@ -339,7 +266,7 @@ bsa_status_t bsa_run_ex(bsa_plan_t plan, int32_t phase, const void* q, const voi
 
 bsa_status_t bsa_run_noalloc(bsa_plan_t plan, const void* q, const void* k, const void* v, void* o, float* lse,
                              void* stream) {
-  g_err.clear();
+  bsa::clear_err();
   if (!plan) return set_err(BSA_ERR_INVALID_ARGUMENT, "plan is NULL");
   if (static_cast<size_t>(plan->p.workspace_bytes) > kScratchBytes)
     return set_err(BSA_ERR_WORKSPACE_TOO_SMALL,
@@ -360,7 +287,7 @@ bsa_status_t bsa_run_noalloc(bsa_plan_t plan, const void* q, const void* k, cons
 bsa_status_t bsa_merge_states(const float* v, const float* s, void* v_out, float* s_out, int64_t seq_len,
                               int32_t num_states, int32_t num_heads, int32_t head_dim, int32_t out_dtype,
                               void* stream) {
-  g_err.clear();
+  bsa::clear_err();
   if (seq_len < 0 || num_states < 1 || num_heads < 1 || head_dim < 4 || head_dim % 4)
     return set_err(BSA_ERR_INVALID_ARGUMENT, "need seq_len >= 0, num_states >= 1, num_heads >= 1, head_dim % 4 == 0");
   if (out_dtype != BSA_F16 && out_dtype != BSA_BF16 && out_dtype != BSA_FP32_OUT)
@@ -375,40 +302,8 @@ bsa_status_t bsa_merge_states(const float* v, const float* s, void* v_out, float
   return BSA_OK;
 }
 
-bsa_status_t bsa_plan_info(bsa_plan_t plan, bsa_plan_info_t* info) {
-  g_err.clear();
-  if (!plan || !info) return set_err(BSA_ERR_INVALID_ARGUMENT, "plan and info must be non-NULL");
-  const bsa::Plan& P = plan->p;
-  info->kernel = P.kernel;
-  info->tile_rows = P.tile_rows;
-  info->key_tile = P.key_tile;
-  info->num_tiles = static_cast<int32_t>(P.tiles.size() / bsa::kTileInts);
-  info->num_merges = static_cast<int32_t>(P.merges.size() / bsa::kMergeInts);
-  info->num_cols = static_cast<int32_t>(P.cols.size());
-  info->max_splits = P.max_splits;
-  info->num_cus = P.num_cus;
-  info->num_workgroups = static_cast<int32_t>(P.wg_ptr.size()) - 1;
-  info->heads_per_wg = P.heads_per_wg;
-  info->table_bytes = P.table_bytes;
-  info->partial_bytes = P.partial_bytes;
-  info->workspace_bytes = P.workspace_bytes;
-  info->valid_pairs = P.valid_pairs;
-  info->R = P.d.R;
-  info->C = P.d.C;
-  info->mask_plane_words = P.mask_plane_words;
-  return BSA_OK;
-}
-
-bsa_status_t bsa_plan_export_mask_bits(bsa_plan_t plan, uint32_t* bits) {
-  g_err.clear();
-  if (!plan || !bits) return set_err(BSA_ERR_INVALID_ARGUMENT, "plan and bits must be non-NULL");
-  const bsa::Plan& P = plan->p;
-  if (!P.mbits.empty()) std::memcpy(bits, P.mbits.data(), P.mbits.size() * 4);
-  return BSA_OK;
-}
-
 bsa_status_t bsa_trace_records(bsa_plan_t plan, const void* workspace, int32_t* records, void* stream) {
-  g_err.clear();
+  bsa::clear_err();
   if (!plan || !workspace || !records)
     return set_err(BSA_ERR_INVALID_ARGUMENT, "plan, workspace and records must be non-NULL");
 #ifdef BSA_TRACE
@@ -427,49 +322,8 @@ bsa_status_t bsa_trace_records(bsa_plan_t plan, const void* workspace, int32_t* 
 #endif
 }
 
-bsa_status_t bsa_plan_export(bsa_plan_t plan, int32_t* tiles, int32_t* merges, int32_t* cols) {
-  g_err.clear();
-  if (!plan) return set_err(BSA_ERR_INVALID_ARGUMENT, "plan is NULL");
-  const bsa::Plan& P = plan->p;
-  if (tiles && !P.tiles.empty()) std::memcpy(tiles, P.tiles.data(), P.tiles.size() * 4);
-  if (merges && !P.merges.empty()) std::memcpy(merges, P.merges.data(), P.merges.size() * 4);
-  if (cols && !P.cols.empty()) std::memcpy(cols, P.cols.data(), P.cols.size() * 4);
-  return BSA_OK;
-}
-
-bsa_status_t bsa_plan_export_workgroups(bsa_plan_t plan, int32_t* wg_ptr) {
-  g_err.clear();
-  if (!plan || !wg_ptr) return set_err(BSA_ERR_INVALID_ARGUMENT, "plan and wg_ptr must be non-NULL");
-  const bsa::Plan& P = plan->p;
-  std::memcpy(wg_ptr, P.wg_ptr.data(), P.wg_ptr.size() * 4);
-  return BSA_OK;
-}
-
-void bsa_plan_destroy(bsa_plan_t plan) {
-  if (!plan) return;
-  {
-    std::lock_guard<std::mutex> lk(g_reg_mu);
-    for (auto it = g_registry.begin(); it != g_registry.end();) {
-      if (it->second.plan_id == plan->p.id) it = g_registry.erase(it);
-      else ++it;
-    }
-  }
-  delete plan;
-}
-
-const char* bsa_last_error(void) { return g_err.c_str(); }
-
-void bsa_rope_quant_init(bsa_rope_quant_t* args) {
-  if (!args) return;
-  std::memset(args, 0, sizeof(*args));
-  args->is_neox = 1;
-  args->quant_scale_q = args->quant_scale_kv = 1.f;
-}
-
-size_t bsa_rope_quant_sizeof(void) { return sizeof(bsa_rope_quant_t); }
-
 bsa_status_t bsa_mla_rope_quantize_fp8(const bsa_rope_quant_t* p, void* stream) {
-  g_err.clear();
+  bsa::clear_err();
   if (!p) return set_err(BSA_ERR_INVALID_ARGUMENT, "args is NULL");
   if (p->nnz < 0 || p->nnz > 0x7fffffff) return set_err(BSA_ERR_INVALID_ARGUMENT, "nnz must lie in [0, 2^31)");
   if (p->num_heads < 1 || p->num_heads > 65535 * 16)

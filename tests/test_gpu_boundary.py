@@ -127,3 +127,27 @@ def test_two_plans_alternating_on_one_workspace():
     for (o, lse), w, what in ((outs[1], wb, "plan B"), (outs[2], wa, "plan A again")):
         o_ref, lse_ref = oracle_result(w)
         compare(o, lse, o_ref, lse_ref, tol_for(w), what)
+
+
+@pytest.mark.parametrize("kv_splits", [1, 0])
+def test_bound_run_matches_run(kv_splits):
+    # Plan.bind validates once and then only calls bsa_run_ex: same bits as run(),
+    # call after call, also for the attention phase alone followed by the merge phase
+    w = W.paged_decode(seed=61, batch=9, min_len=5, max_len=900)
+    say(f"[boundary] bind vs run, splits={kv_splits}")
+    plan = Plan(w.indptr, w.indices, w.M, w.N, w.R, w.C, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                kv_splits=kv_splits, kv_block_lens=w.kv_block_lens, q_dtype=w.q_dtype)
+    dev = torch.device("cuda")
+    q, k, v = (t.to(dev) for t in (w.q, w.k, w.v))
+    o_ref, l_ref = plan.run(q, k, v)
+    fn, o, lse = plan.bind(q, k, v)
+    attn, o2, l2 = plan.bind(q, k, v, phase=L.BSA_PHASE_ATTENTION)
+    merge, _, _ = plan.bind(q, k, v, out=o2, lse=l2, phase=L.BSA_PHASE_MERGE)
+    for _ in range(3):
+        o.zero_(), lse.zero_(), o2.zero_(), l2.zero_()
+        fn()
+        attn()
+        merge()
+        torch.cuda.synchronize()
+        for a, b in ((o, o_ref), (lse, l_ref), (o2, o_ref), (l2, l_ref)):
+            assert torch.equal(a, b)

@@ -504,6 +504,8 @@ def test_run_scales_rejected_for_the_mla_shape():
                      values=False)
     p = _plan(w, 1)
     lib = L.lib()
+    if not hasattr(lib, "bsa_run_ex"):
+        pytest.skip("host-only build of the planner (no device entry points)")
     st = lib.bsa_run_ex(p._handle, L.BSA_PHASE_ALL, None, None, None, None, None, 16, None, None, None, 0, None)
     assert st == L.BSA_ERR_UNSUPPORTED
     assert b"per-head scales" in lib.bsa_last_error()
