@@ -112,6 +112,19 @@ def counters(d: str) -> dict:
     return out
 
 
+def last_dispatch(d: str, kernel: str, counter: str) -> float:
+    """The counter's value on the last dispatch of ``kernel`` in the run (the calibration
+    copy comes after the timed loop; earlier copies of the same blit kernel move the inputs)."""
+    paths = glob.glob(os.path.join(ROOT, d, "**", "*counter_collection.csv"), recursive=True)
+    best, val = -1, None
+    for r in csv.DictReader(open(paths[0])):
+        if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter and int(r["Dispatch_Id"]) > best:
+            best, val = int(r["Dispatch_Id"]), float(r["Counter_Value"])
+    if val is None:
+        raise RuntimeError(f"no {kernel} dispatch with {counter} under {d}")
+    return val
+
+
 def pick(per: dict, kernel: str) -> dict:
     hits = [v for k, v in per.items() if kernel in k]
     if not hits:
@@ -166,7 +179,7 @@ def profile(workload: str, out: str, steps: int, with_counters: bool, execute: b
             sq.update(pick(counters(d), kernel))
         else:
             per = counters(d)
-            copy_kib = pick(per, COPY_KERNEL)[kind]
+            copy_kib = last_dispatch(d, COPY_KERNEL, kind)
             tr[kind] = (pick(per, kernel)[kind], (CALIB_MIB << 10) / copy_kib, copy_kib)
         say(f"[profile] {workload}: {kind} pass done")
     traffic = None
@@ -247,7 +260,7 @@ def write_summary(workload, out, kernel, line, stats, sq, traffic, cmds) -> None
         L += ["", "## HBM traffic of the kernel (rocprofv3 --pmc, one pass per counter)", "",
               f"- FETCH_SIZE: {traffic['fetch_kib_counted']:.0f} KiB counted per dispatch; "
               f"WRITE_SIZE: {traffic['write_kib_counted']:.0f} KiB",
-              f"- calibration: a {CALIB_MIB} MiB device copy ({COPY_KERNEL}) in the same run reads "
+              f"- calibration: a {CALIB_MIB} MiB device copy ({COPY_KERNEL}, the run's last dispatch of it) reads "
               f"{traffic['copy_fetch_kib']:.0f} KiB on FETCH_SIZE and writes {traffic['copy_write_kib']:.0f} KiB "
               f"on WRITE_SIZE, so the counts are scaled by {traffic['fetch_scale']:.3f} and {traffic['write_scale']:.3f}",
               f"- HBM bytes per launch: {traffic['hbm_bytes_per_launch'] / 1e6:.1f} MB; algorithmic bytes "

@@ -180,7 +180,46 @@ FULL_ROWS = {
 def test_full_size_workload(name):
     kv_splits, rows = W.BENCH_KV_SPLITS[name], FULL_ROWS[name]
     w = W.by_name(name)
-    _check(w, kv_splits, rows=rows, what=f"full {name} splits={kv_splits}")
+    if rows is not None:
+        # the fixed rows (edges of tiles and blocks) plus six drawn with a seed per workload
+        rng = np.random.default_rng(sum(map(ord, name)))
+        drawn = rng.choice(np.setdiff1d(np.arange(w.M), rows), 6, replace=False)
+        rows = sorted(set(rows) | set(int(r) for r in drawn))
+    _check(w, kv_splits, rows=rows, what=f"full {name} splits={kv_splits} rows={rows}")
+
+
+DETERMINISM = {
+    # tile kernel with split rows merged by LSE, fixed and automatic splits
+    "bsr_prefill_s3": (lambda: W.bsr_prefill(seed=70, M=1024, density=0.3), 3),
+    "bsr_prefill_auto": (lambda: W.bsr_prefill(seed=71, M=1024, density=0.3), 0),
+    "fp8_prefill_auto": (lambda: W.fp8_kv(W.bsr_prefill(seed=72, M=1024, density=0.3), 72), 0),
+    # decode kernel, balanced partition over the device
+    "paged_decode_auto": (lambda: W.paged_decode(seed=73, batch=12, min_len=1, max_len=900), 0),
+    # sparse MLA, head pairs on one XCD, unsplit and split
+    "sparse_mla": (lambda: W.sparse_mla(seed=74, num_tokens=6, num_heads=128, cache_rows=4096, topk=256,
+                                        min_ctx=512, max_ctx=4096), 1),
+    "sparse_mla_s3": (lambda: W.sparse_mla(seed=75, num_tokens=4, num_heads=64, cache_rows=2048, topk=200,
+                                           min_ctx=300, max_ctx=2048), 3),
+}
+
+
+@pytest.mark.parametrize("name", list(DETERMINISM))
+def test_bitwise_determinism(name):
+    # no atomics and a fixed reduction order: repeated runs give the same bits, also
+    # after other work has run on the device in between
+    make, kv_splits = DETERMINISM[name]
+    w = make()
+    say(f"[determinism] {name} splits={kv_splits}")
+    plan = plan_for(w, kv_splits)
+    q, k, v = to_device(w)
+    o0, l0 = run_gpu(w, kv_splits, plan=plan, dev=(q, k, v))
+    o0, l0 = o0.clone(), l0.clone()
+    for i in range(3):
+        if i == 1:
+            torch.randn(1 << 22, device=q.device).sum()  # unrelated work in between
+        o, lse = run_gpu(w, kv_splits, plan=plan, dev=(q, k, v))
+        assert torch.equal(o.view(torch.int16), o0.view(torch.int16)), f"{name}: output bits differ on run {i + 1}"
+        assert torch.equal(lse.view(torch.int32), l0.view(torch.int32)), f"{name}: lse bits differ on run {i + 1}"
 
 
 # Every launch variant of the generic tile kernel: (rows per tile, keys per
