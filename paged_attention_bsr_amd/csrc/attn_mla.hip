@@ -66,6 +66,8 @@ struct MlaLds {
   static constexpr int kKBytes = kKT * kKRow;
   static constexpr int kTokBytes = kKT * 4;
   static constexpr int kBuf = kKBytes + kTokBytes;
+  // stores of the round past a row's 36 units (waves 2, 3) go here: 2 x 128 lanes x 16 B
+  static constexpr int kDummy = 2 * 128 * 16;
   // partial-score exchange: per wave 4 planes of [64 lanes] x 16 B (a plane
   // per (key block, head block) accumulator), so 16 lanes of a pass touch 256
   // contiguous bytes
@@ -120,9 +122,11 @@ __device__ __forceinline__ int xcd_paired_tile(int b, int num_tiles) {
 template <bool CAUSAL, bool LENS, bool C1>
 __global__ __launch_bounds__(kThreads, 1) void attn_mla_kernel(AttnArgs a) {
   using L = MlaLds;
-  constexpr int NBUF = 2;  // LDS tile buffers: tile kt + 1 is stored while tile kt is computed
-
-  __shared__ __attribute__((aligned(16))) unsigned char lds[NBUF * L::kBuf + L::kXsBytes];
+  // two LDS tile buffers (tile kt + 1 is stored while tile kt is computed) as separate
+  // arrays, so the compiler sees that the stores into one never alias the reads of the other
+  __shared__ __attribute__((aligned(16))) unsigned char lds_b0[L::kBuf + L::kDummy];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_b1[L::kBuf + L::kDummy];
+  __shared__ __attribute__((aligned(16))) unsigned char lds_xs[L::kXsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -230,12 +234,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mla_kernel(AttnArgs a) {
       creg[i] = *reinterpret_cast<const u32x4*>(src + (u < kUnits ? u : kUnits - 1) * 16);
     }
   };
-  auto store_tile = [&](int buf, const u32x4 (&creg)[kLdRounds], int tok) {
-    unsigned char* base = lds + buf * L::kBuf;
+  // widen a tile's rows to bf16 and store them into `base` (no branch: the round
+  // past a row's last unit stores into the buffer's dummy area)
+  auto store_rows = [&](unsigned char* base, const u32x4 (&creg)[kLdRounds]) {
 #pragma unroll
     for (int i = 0; i < kLdRounds; ++i) {
       const int u = unit0 + 8 * i;
-      if (i == kLdRounds - 1 && u >= kUnits) continue;  // uniform per wave
       uint32_t b[8];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -243,10 +247,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mla_kernel(AttnArgs a) {
         b[2 * w + 1] = fp8x2_to_bf16x2<true>(creg[i][w]);
       }
       // bf16 units 2u and 2u + 1 of this key's row
-      *reinterpret_cast<u32x4*>(base + k_off(my_key, 2 * u)) = u32x4{b[0], b[1], b[2], b[3]};
-      *reinterpret_cast<u32x4*>(base + k_off(my_key, 2 * u + 1)) = u32x4{b[4], b[5], b[6], b[7]};
+      const bool real = i < kLdRounds - 1 || u < kUnits;
+      unsigned char* p0 = real ? base + k_off(my_key, 2 * u) : base + L::kBuf + (tid & 127) * 16;
+      unsigned char* p1 = real ? base + k_off(my_key, 2 * u + 1) : base + L::kBuf + (128 + (tid & 127)) * 16;
+      *reinterpret_cast<u32x4*>(p0) = u32x4{b[0], b[1], b[2], b[3]};
+      *reinterpret_cast<u32x4*>(p1) = u32x4{b[4], b[5], b[6], b[7]};
     }
+  };
+  auto store_tok = [&](unsigned char* base, int tok) {
     if (tid < 128 && quad == 0) reinterpret_cast<int*>(base + L::kKBytes)[my_key] = tok;
+  };
+  auto store_tile = [&](unsigned char* base, const u32x4 (&creg)[kLdRounds], int tok) {
+    store_rows(base, creg);
+    store_tok(base, tok);
   };
 
   // this wave's output: O^T for dv in [256 hf, 256 hf + 256) of its 32 heads
@@ -260,8 +273,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mla_kernel(AttnArgs a) {
   bool over = false;            // some tile exceeded its row's reference by more than 2^kOverflowLog2
   const float sl2 = a.scale_log2;
   // this wave's exchange planes and its partner's
-  unsigned char* xs_own = lds + NBUF * L::kBuf + wave * L::kXsWave + lane * 16;
-  const unsigned char* xs_peer = lds + NBUF * L::kBuf + (wave ^ 1) * L::kXsWave + lane * 16;
+  unsigned char* xs_own = lds_xs + wave * L::kXsWave + lane * 16;
+  const unsigned char* xs_peer = lds_xs + (wave ^ 1) * L::kXsWave + lane * 16;
 
   // One tile.  `ld`: registers of tile kt (stored last iteration), refilled
   // with the rows of tile kt + 2; `nx`: registers of tile kt + 1, widened and
@@ -269,8 +282,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mla_kernel(AttnArgs a) {
   // A: tile kt is in LDS and every wave is done with tile kt - 1 (its buffer
   // and the score exchange area are free).  Barrier B: scores exchanged,
   // tile kt + 1 stored.
-  auto tile_step = [&](int kt, u32x4 (&ld)[kLdRounds], int& ld_tok, const u32x4 (&nx)[kLdRounds], int nx_tok) {
-    const int buf = kt & 1;
+  auto tile_step = [&](int kt, unsigned char* kl, unsigned char* knx, u32x4 (&ld)[kLdRounds], int& ld_tok,
+                       const u32x4 (&nx)[kLdRounds], int nx_tok) {
     __syncthreads();
     {
       // index of tile kt + 3 first, then the rows of tile kt + 2 (whose index
@@ -294,49 +307,58 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mla_kernel(AttnArgs a) {
     const bool skip = CAUSAL && tok_lo > static_cast<int64_t>(qtok) + a.causal_off;
     const bool need_mask = LENS || (t0 + kKT > npos) || (CAUSAL && tok_hi > static_cast<int64_t>(qtok) + a.causal_off);
 
-    const unsigned char* kl = lds + buf * L::kBuf;
     const int* ktok = reinterpret_cast<const int*>(kl + L::kKBytes);
 
     // (1) this wave's part of S^T: all 32 keys (key blocks kb) x 32 heads (head
     // blocks hb) over its 288 dims, 9 k-steps; each K fragment is read once for
     // both head blocks
     f32x4 sacc[2][2] = {{f32x4{}, f32x4{}}, {f32x4{}, f32x4{}}};
-    if (group_active && !skip) {
-      // bf16 unit 32 HF + 4 j + quad (j = ks + HF) of key 16 kb + col: the XOR
-      // touches the low three unit bits only, so even and odd j each have one
-      // base per key block and immediate offsets of 128 B per pair of steps
-      auto qk = [&](auto hf_c) {
-        constexpr int HF = decltype(hf_c)::value;
-        constexpr int kRing = 6;
-        const unsigned char* ke[2] = {kl + k_off(col, 32 * HF + quad), kl + k_off(16 + col, 32 * HF + quad)};
-        const unsigned char* ko[2] = {kl + k_off(col, 32 * HF + quad + 4), kl + k_off(16 + col, 32 * HF + quad + 4)};
+    {
+      // bf16 unit 32 hf + 4 j + quad (j = ks + hf) of key 16 kb + col.  The XOR
+      // touches the low three unit bits only, so step ks reads at a per-wave
+      // base plus an immediate offset: even ks at pa + 64 ks, odd ks at
+      // pb + 64 (ks - 1), with pa / pb the units of j = 0 / 1 for hf = 0 and of
+      // j = 1 / 2 for hf = 1.  The products run for every wave and tile (an
+      // inactive head group multiplies zero Q rows, a tile above the causal
+      // diagonal is dropped after the exchange), so the block has no branch and
+      // the next tile's widening and stores interleave with the products.
+      constexpr int kRing = 6;
+      const unsigned char* pa[2];
+      const unsigned char* pb[2];
 #pragma unroll
-        for (int ks = 0; ks < kSteps; ++ks)
+      for (int kb = 0; kb < 2; ++kb) {
+        const unsigned char* ke = kl + k_off(16 * kb + col, 32 * hf + quad);
+        const unsigned char* ko = kl + k_off(16 * kb + col, 32 * hf + quad + 4);
+        pa[kb] = hf ? ko : ke;
+        pb[kb] = hf ? ke + 128 : ko;
+      }
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) {
-            const int j = ks + HF;
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(((j & 1) ? ko[kb] : ke[kb]) + (j >> 1) * 128);
-            sacc[kb][0] = MfmaType<__bf16>::mfma16(kf, qf[0][ks], sacc[kb][0]);
-            sacc[kb][1] = MfmaType<__bf16>::mfma16(kf, qf[1][ks], sacc[kb][1]);
-          }
-        // reads run kRing fragments ahead of the products
-        __builtin_amdgcn_sched_group_barrier(0x100, kRing, 0);
+      for (int ks = 0; ks < kSteps; ++ks)
 #pragma unroll
-        for (int i = 0; i < 2 * kSteps - kRing; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        for (int kb = 0; kb < 2; ++kb) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>((ks & 1) ? pb[kb] + (ks >> 1) * 128
+                                                                      : pa[kb] + (ks >> 1) * 128);
+          sacc[kb][0] = MfmaType<__bf16>::mfma16(kf, qf[0][ks], sacc[kb][0]);
+          sacc[kb][1] = MfmaType<__bf16>::mfma16(kf, qf[1][ks], sacc[kb][1]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2 * kRing, 0);
-      };
-      if (hf == 0) qk(std::integral_constant<int, 0>{});
-      else qk(std::integral_constant<int, 1>{});
+      // the next tile's rows, widened and stored between the products (the
+      // store buffer is another array than the one read here)
+      store_rows(knx, nx);
+      __builtin_amdgcn_sched_group_barrier(0x100, kRing, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * kSteps - kRing; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * kRing, 0);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
           *reinterpret_cast<f32x4*>(xs_own + (kb * 2 + hb) * 1024) = sacc[kb][hb];
     }
-    if (kt + 1 < ntiles) store_tile(buf ^ 1, nx, nx_tok);
+    store_tok(knx, nx_tok);
     __syncthreads();
     if (!group_active || skip) return;
 
@@ -432,11 +454,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mla_kernel(AttnArgs a) {
       trace_key(my_key, tok_a);
       trace_key(kKT + my_key, tok_b);
       blk_next = fetch_blk(2 * kKT + my_key);
-      store_tile(0, creg_a, tok_a);
+      store_tile(lds_b0, creg_a, tok_a);
     }
     for (int kt = 0; kt < ntiles; kt += 2) {
-      tile_step(kt, creg_a, tok_a, creg_b, tok_b);
-      tile_step(kt + 1, creg_b, tok_b, creg_a, tok_a);
+      tile_step(kt, lds_b0, lds_b1, creg_a, tok_a, creg_b, tok_b);
+      tile_step(kt + 1, lds_b1, lds_b0, creg_b, tok_b, creg_a, tok_a);
     }
     // a second pass, against each row's true maximum, only if some row of the
     // workgroup overflowed its first reference (its result is then discarded);
