@@ -263,8 +263,12 @@ def write_summary(workload, out, kernel, line, stats, sq, traffic, cmds) -> None
               f"- calibration: a {CALIB_MIB} MiB device copy ({COPY_KERNEL}, the run's last dispatch of it) reads "
               f"{traffic['copy_fetch_kib']:.0f} KiB on FETCH_SIZE and writes {traffic['copy_write_kib']:.0f} KiB "
               f"on WRITE_SIZE, so the counts are scaled by {traffic['fetch_scale']:.3f} and {traffic['write_scale']:.3f}",
-              f"- HBM bytes per launch: {traffic['hbm_bytes_per_launch'] / 1e6:.1f} MB; algorithmic bytes "
-              f"{alg / 1e6:.1f} MB (ratio {traffic['hbm_bytes_per_launch'] / alg if alg else float('nan'):.3f})",
+              (f"- HBM bytes per launch: {traffic['hbm_bytes_per_launch'] / 1e6:.1f} MB; algorithmic bytes "
+               f"{alg / 1e6:.1f} MB (ratio {traffic['hbm_bytes_per_launch'] / alg if alg else float('nan'):.3f})"
+               if roof["bound"] == "hbm" else
+               f"- HBM bytes per launch: {traffic['hbm_bytes_per_launch'] / 1e6:.1f} MB (the roofline of this "
+               f"kernel is in flops; its byte count, K and V once per query row and kv head, is not a floor for "
+               f"a tiled kernel)"),
               f"- kernel source hash: {traffic['kernel_source_hash']}"]
     path = os.path.join(ROOT, out, f"{kernel}_{workload}.md")
     with open(path, "w") as f:
