@@ -198,7 +198,13 @@ bsa_status_t bsa_plan(const int32_t* indptr, const int32_t* indices, int64_t M, 
                       int32_t head_dim, int32_t causal, float sm_scale, int32_t kv_splits,
                       bsa_plan_t* out_plan);
 
-/* Extended form (partial blocks, other dtypes, fp8 scales, strides, CU count). */
+/* Extended form (partial blocks, other dtypes, fp8 scales, strides, CU count).  *
+ * With the environment variable BSA_LOG set (to anything but "0"), every call
+ * of bsa_plan / bsa_plan_ex that reaches the planner prints one line to
+ * stderr: the plan's kernel, tiles, merges, splits, workgroups, workspace and
+ * planning time, or the error it failed with (the plan() conventions: fail
+ * explicitly, and say why).
+ */
 bsa_status_t bsa_plan_ex(const bsa_plan_desc_t* desc, bsa_plan_t* out_plan);
 
 /* Bytes of device workspace bsa_run needs for this plan (multiple of 256).
@@ -442,15 +448,19 @@ bsa_status_t bsa_plan_export_mask_bits(bsa_plan_t plan, uint32_t* bits);
  * Per-tile trace records of the last attention phase run with `workspace`
  * (a check that the kernels walk exactly the tables bsa_plan_export returns).
  * Only a library built with BSA_TRACE keeps them: there the workspace
- * (bsa_workspace_size) ends with int32[num_tiles][8] records, after the split
+ * (bsa_workspace_size) ends with int32[num_tiles][16] records, after the split
  * partials, which each run's attention phase resets and its kernel fills in,
  * tile t (launch order) =
  *   {times the tile was processed, first column entry whose keys it loaded,
  *    last such entry + 1, keys it loaded that lie inside their block's valid
  *    length (before the causal mask), partial_offset it wrote (-1: o/lse
- *    directly), kv_head, row0, nrows}
- * and a tile with no valid key reads {1, INT32_MAX, 0, 0, ...}.  Waits for
- * `stream`, then copies the records to host `records` (int32[num_tiles * 8]).
+ *    directly), kv_head, row0, nrows, key tokens outside [0, N) it met,
+ *    7 unused}
+ * and a tile with no valid key reads {1, INT32_MAX, 0, 0, ...}.  That build
+ * checks every key token its kernels derive from the tables against [0, N):
+ * one outside is counted in field 8 and read as a masked key, never loaded.
+ * Waits for `stream`, then copies the records to host `records`
+ * (int32[num_tiles * 16]).
  * The product library returns BSA_ERR_UNSUPPORTED; BSA_ERR_INVALID_ARGUMENT
  * for NULL arguments, BSA_ERR_HIP when the copy fails.
  */

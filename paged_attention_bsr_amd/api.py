@@ -294,10 +294,10 @@ class Plan:
         return call, out, lse
 
     def trace_records(self, workspace: torch.Tensor, stream=None) -> np.ndarray:
-        """(num_tiles, 8) int32 records of the last attention phase run in ``workspace``
+        """(num_tiles, 16) int32 records of the last attention phase run in ``workspace``
         (bsa_trace_records; trace=True plans only)."""
         st = torch.cuda.current_stream(workspace.device).cuda_stream if stream is None else stream
-        rec = np.zeros((self.info()["num_tiles"], 8), np.int32)
+        rec = np.zeros((self.info()["num_tiles"], 16), np.int32)
         self._check(self._lib.bsa_trace_records(self._handle, workspace.data_ptr(), _ptr(rec), st))
         return rec
 

@@ -3,6 +3,9 @@
 // device facts planning needs (the current device's CU count, forgetting a
 // destroyed plan's workspace bindings) come through the hooks of
 // abi_internal.h.
+#include <chrono>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <string>
@@ -22,6 +25,39 @@ bsa_status_t set_err(bsa_status_t st, const std::string& msg) {
 }
 
 void clear_err() { g_err.clear(); }
+
+namespace {
+// BSA_LOG set (and not "0"): one line per planning call on stderr -- the plan's
+// statistics, or the error it failed with
+bool log_on() {
+  static const bool on = [] {
+    const char* v = std::getenv("BSA_LOG");
+    return v && *v && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+void log_plan(const bsa_plan_desc_t& d, const Plan* P, bsa_status_t st, double us) {
+  if (!log_on()) return;
+  if (!P) {
+    std::fprintf(stderr, "[bsa] plan M=%lld N=%lld R=%d C=%d Hq=%d Hkv=%d D=%d/%d failed (%d): %s\n",
+                 static_cast<long long>(d.M), static_cast<long long>(d.N), d.R, d.C, d.num_qo_heads,
+                 d.num_kv_heads, d.head_dim_qk, d.head_dim_vo, static_cast<int>(st), g_err.c_str());
+    return;
+  }
+  static const char* kNames[] = {"tile", "mla", "decode"};
+  const int k = P->kernel >= 0 && P->kernel <= 2 ? P->kernel : 0;
+  std::fprintf(stderr,
+               "[bsa] plan M=%lld N=%lld R=%d C=%d Hq=%d Hkv=%d D=%d/%d causal=%d kv_splits=%d: kernel=%s "
+               "tile_rows=%d key_tile=%d tiles=%zu merges=%zu max_splits=%d workgroups=%zu cols=%zu "
+               "valid_pairs=%lld workspace=%lld B (tables %lld) in %.1f us\n",
+               static_cast<long long>(d.M), static_cast<long long>(d.N), P->d.R, P->d.C, d.num_qo_heads,
+               d.num_kv_heads, d.head_dim_qk, d.head_dim_vo, d.causal, d.kv_splits, kNames[k], P->tile_rows,
+               P->key_tile, P->tiles.size() / kTileInts, P->merges.size() / kMergeInts, P->max_splits,
+               P->wg_ptr.size() - 1, P->cols.size(), static_cast<long long>(P->valid_pairs),
+               static_cast<long long>(P->workspace_bytes), static_cast<long long>(P->table_bytes), us);
+}
+}  // namespace
 
 }  // namespace bsa
 
@@ -72,18 +108,27 @@ bsa_status_t bsa_plan_ex(const bsa_plan_desc_t* desc, bsa_plan_t* out_plan) {
     if (s != BSA_OK) return s;
   }
   bsa_plan_s* plan = nullptr;
+  const auto t0 = std::chrono::steady_clock::now();
+  auto elapsed_us = [&] {
+    return std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count();
+  };
   try {
     plan = new bsa_plan_s();
     std::string err;
     const bsa_status_t st = bsa::build_plan(d, cus, plan->p, err);
     if (st != BSA_OK) {
       delete plan;
-      return set_err(st, err);
+      set_err(st, err);
+      bsa::log_plan(d, nullptr, st, elapsed_us());
+      return st;
     }
   } catch (const std::bad_alloc&) {
     delete plan;
-    return set_err(BSA_ERR_HOST_ALLOC, "host allocation failed while planning");
+    set_err(BSA_ERR_HOST_ALLOC, "host allocation failed while planning");
+    bsa::log_plan(d, nullptr, BSA_ERR_HOST_ALLOC, elapsed_us());
+    return BSA_ERR_HOST_ALLOC;
   }
+  bsa::log_plan(d, &plan->p, BSA_OK, elapsed_us());
   *out_plan = plan;
   return BSA_OK;
 }

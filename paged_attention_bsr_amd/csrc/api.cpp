@@ -219,6 +219,7 @@ bsa_status_t bsa_run_ex(bsa_plan_t plan, int32_t phase, const void* q, const voi
 #ifdef BSA_TRACE
   a.trace = reinterpret_cast<int32_t*>(ws + P.table_bytes + P.partial_bytes);
 #endif
+  a.num_keys = d.N;
   a.q_scale = scale_q;
   a.k_scale = scale_k;
   a.v_scale = scale_v;
@@ -226,11 +227,11 @@ bsa_status_t bsa_run_ex(bsa_plan_t plan, int32_t phase, const void* q, const voi
   hipError_t e;
 #ifdef BSA_TRACE
   if (phase & BSA_PHASE_ATTENTION) {
-    // every record starts as {0, INT32_MAX, 0, 0, -2, -2, -2, -2}
+    // every record starts as {0, INT32_MAX, 0, 0, -2, -2, -2, -2, 0, -2 ...}
     std::vector<int32_t> init(static_cast<size_t>(a.num_tiles) * bsa::kTraceInts, -2);
     for (int32_t t = 0; t < a.num_tiles; ++t) {
       int32_t* r = init.data() + static_cast<size_t>(t) * bsa::kTraceInts;
-      r[0] = 0, r[1] = INT32_MAX, r[2] = 0, r[3] = 0;
+      r[0] = 0, r[1] = INT32_MAX, r[2] = 0, r[3] = 0, r[8] = 0;
     }
     e = hipMemcpyAsync(a.trace, init.data(), init.size() * 4, hipMemcpyHostToDevice, st);
     if (e == hipSuccess) e = hipStreamSynchronize(st);

@@ -161,6 +161,7 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
     }
     return s;
   };
+  TraceAcc tr_chk;  // trace build: out-of-range key tokens (counted into each tile's record)
   // branch-free, so every stage issues the same loads and the compiler can
   // wait for exactly the older stage
   auto key_token = [&](const Src& b, int t) -> int {
@@ -178,7 +179,8 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
     bool ok = t < b.npos;
     if (LENS) ok = ok && off < len;
     if (CAUSAL) ok = ok && tok <= b.qlim;
-    return ok ? tok : -1;
+    // trace build: tokens outside [0, N) are counted (by quad 0, one lane per key) and masked
+    return tr_chk.check(ok ? tok : -1, a.num_keys, quad == 0);
   };
 
   // per-key-tile registers: K fragments and V chunks, both indexed (kb, ks):
@@ -468,7 +470,11 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
       }
       p += NS;
     } while (p < nTe);
-    if constexpr (kTrace) trace_flush(a.trace, gn - HG + hw, tr, sub == 0 && lane == 0, cur.part, cur.kvh, cur.row0, cur.nrows);
+    if constexpr (kTrace) {
+      tr.bad = tr_chk.bad;  // met while loading this group's keys (and the next group's first ones)
+      tr_chk.bad = 0;
+      trace_flush(a.trace, gn - HG + hw, tr, sub == 0 && lane == 0, cur.part, cur.kvh, cur.row0, cur.nrows);
+    }
     finish_tile(cur);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qf[ks] = qn[ks];

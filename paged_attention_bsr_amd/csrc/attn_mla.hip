@@ -180,6 +180,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mla_kernel(AttnArgs a) {
     }
   }
 
+  // trace build: one thread per key (waves 0, 1, lanes 0-15) counts the keys
+  // and column entries of every tile it loads, in the last pass
+  TraceAcc tr;
   // token of key position t (-1 past the range or past a block's valid
   // length), in two steps: fetch_blk issues the (unconditional, clamped)
   // table loads, finish_tok uses them -- a tile later for the prefetched
@@ -200,12 +203,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mla_kernel(AttnArgs a) {
     const int off = C1 ? 0 : t - (t / C) * C;
     bool ok = t < npos;
     if (LENS) ok = ok && off < r.len;
-    return ok ? r.J * C + off : -1;
+    // trace build: tokens outside [0, N) are counted (by the key's counting lane) and masked
+    return tr.check(ok ? r.J * C + off : -1, a.num_keys, tid < 128 && quad == 0);
   };
   auto key_tok = [&](int t) -> int { return finish_tok(t, fetch_blk(t)); };
-  // trace build: one thread per key (waves 0, 1, lanes 0-15) counts the keys
-  // and column entries of every tile it loads, in the last pass
-  TraceAcc tr;
   auto trace_key = [&](int t, int tok) {
     if (kTrace && tid < 128 && quad == 0 && tok >= 0) tr.keys(cb + (C1 ? t : t / C), 1);
   };

@@ -172,18 +172,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     ti.len = LENS ? lens[cb + blk] : C;
     return ti;
   };
-  auto key_tok = [&](int kt, const TileInfo& ti, int key) -> int {
+  // (trace build: tokens outside [0, N) are masked, and counted where `count`: one
+  // lane per key)
+  auto key_tok = [&](int kt, const TileInfo& ti, int key, bool count = false) -> int {
     const int t = kt * KT + key;
     if (BLOCKTILE) {
       bool ok = t < npos;
       if (LENS) ok = ok && ti.off0 + key < ti.len;
-      return ok ? ti.base + key : -1;
+      return tr.check(ok ? ti.base + key : -1, a.num_keys, count);
     } else {
       if (t >= npos) return -1;
       const int blk = t / C;
       const int off = t - blk * C;
       if (LENS && off >= lens[cb + blk]) return -1;
-      return cols[cb + blk] * C + off;
+      return tr.check(cols[cb + blk] * C + off, a.num_keys, count);
     }
   };
 
@@ -208,7 +210,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     for (int j = 0; j < BPW; ++j) {
       const int b = wave * BPW + j;
       const int row = 4 * b + (lane >> 4);
-      const int tok = key_tok(kt, ti, row);
+      const int tok = key_tok(kt, ti, row, u == 0);
       const T* pk = tok >= 0 ? kbase + static_cast<int64_t>(tok) * a.k_stride : zrow;
       const T* pv = tok >= 0 ? vbase + static_cast<int64_t>(tok) * a.v_stride : zrow;
       __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(pk + (u ^ k_swz(row)) * 8),
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
       const int piece = tid + i * NTHR;
       const int row = piece >> 3;
       const int pc = (piece & 7) * 16;
-      const int tok = key_tok(kt, ti, row);
+      const int tok = key_tok(kt, ti, row, (piece & 7) == 0);
       const unsigned char* pk = tok >= 0 ? kbase8 + static_cast<int64_t>(tok) * a.k_stride : zrow8;
       const unsigned char* pv = tok >= 0 ? vbase8 + static_cast<int64_t>(tok) * a.v_stride : zrow8;
       k8[i] = *reinterpret_cast<const u32x4*>(pk + pc);
@@ -298,9 +300,18 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   const unsigned char* kbytes = reinterpret_cast<const unsigned char*>(kbase);
   const unsigned char* vbytes = reinterpret_cast<const unsigned char*>(vbase);
   int dblk = 0, doff = 0;  // block and offset of the next tile to load (FAST)
+  // (trace build: a tile whose tokens leave [0, N) counts its KT keys and loads tile 0's
+  // rows instead, so no load leaves the cache; this path has no per-key mask)
+  auto fast_check = [&](int lo) -> int {
+    if (kTrace && (lo < 0 || static_cast<int64_t>(lo) + KT > a.num_keys)) {
+      if (tid == 0) tr.bad += KT;
+      return 0;
+    }
+    return lo;
+  };
   auto dma_fast = [&](unsigned char* st) -> int {
     if (kTrace && tid == 0) tr.keys(cb + dblk, KT);
-    const int lo = cols[cb + dblk] * C + doff;
+    const int lo = fast_check(cols[cb + dblk] * C + doff);
     doff += KT;
     if (doff == C) {
       doff = 0;
@@ -547,7 +558,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   }
   auto load8_fast = [&]() -> int {
     if (kTrace && tid == 0) tr.keys(cb + dblk, KT);
-    const int lo = cols[cb + dblk] * C + doff;
+    const int lo = fast_check(cols[cb + dblk] * C + doff);
     doff += KT;
     if (doff == C) {
       doff = 0;

@@ -75,18 +75,32 @@ __device__ __forceinline__ u32x4 fp8x8_widen(u32x2 w) {
 }
 
 // Trace build (BSA_TRACE, a separate library that only tests load): each
-// kernel records per planner tile what its loops did, 8 int32 per tile,
+// kernel records per planner tile what its loops did, 16 int32 per tile,
 // {times processed, first column entry loaded, last entry loaded + 1, valid
-// keys loaded, partial offset written (-1: o/lse), kv head, first row, rows};
-// the host fills every record with {0, INT_MAX, 0, 0, ...} before the launch.
-// In the product build every trace statement is dead code.
+// keys loaded, partial offset written (-1: o/lse), kv head, first row, rows,
+// key tokens outside [0, N) met, unused...}; the host fills every record with
+// {0, INT_MAX, 0, 0, ..., 0 at 8} before the launch.  The build also checks
+// every key token a kernel derives from the tables against [0, N): one
+// outside is counted and replaced by a masked key (the zero row), so a
+// corrupted table never makes a load leave the cache.  In the product build
+// every trace statement is dead code.
 #ifdef BSA_TRACE
 constexpr bool kTrace = true;
 #else
 constexpr bool kTrace = false;
 #endif
 struct TraceAcc {
-  int lo = 0x7fffffff, end = 0, n = 0;
+  int lo = 0x7fffffff, end = 0, n = 0, bad = 0;
+  // a key token (-1 = masked) checked against [0, num_keys): outside -> masked,
+  // and counted when `count` (one of the lanes that derive the same token)
+  __device__ __forceinline__ int check(int tok, int64_t num_keys, bool count) {
+    if (!kTrace) return tok;
+    if (tok < -1 || static_cast<int64_t>(tok) >= num_keys) {
+      if (count) ++bad;
+      return -1;
+    }
+    return tok;
+  }
   __device__ __forceinline__ void keys(int entry, int count) {
     if (kTrace && count > 0) {
       lo = entry < lo ? entry : lo;
@@ -98,12 +112,13 @@ struct TraceAcc {
 __device__ __forceinline__ void trace_flush(int32_t* trace, int tile, const TraceAcc& acc, bool owner, int part,
                                             int kvh, int row0, int nrows) {
   if (!kTrace) return;
-  int32_t* r = trace + static_cast<int64_t>(tile) * 8;
+  int32_t* r = trace + static_cast<int64_t>(tile) * 16;
   if (acc.n > 0) {
     atomicMin(r + 1, acc.lo);
     atomicMax(r + 2, acc.end);
     atomicAdd(r + 3, acc.n);
   }
+  if (acc.bad > 0) atomicAdd(r + 8, acc.bad);
   if (owner) {
     atomicAdd(r + 0, 1);
     r[4] = part;

@@ -38,6 +38,7 @@ struct AttnArgs {
   const uint32_t* mbits;
   int64_t mask_plane_words;
   int32_t* trace;          // trace build only: per-tile records (planner.h), else null
+  int64_t num_keys;        // N: key tokens are in [0, N) (checked by the trace build)
 };
 
 struct MergeArgs {

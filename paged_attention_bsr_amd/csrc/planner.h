@@ -18,8 +18,8 @@ constexpr int kMergeInts = 8;
 // per planner tile what its loops actually did, kTraceInts int32 per tile after
 // the split partials: {times processed, first column entry walked, last entry
 // walked + 1, valid keys counted, partial offset written, kv head, first row,
-// rows}.
-constexpr int kTraceInts = 8;
+// rows, key tokens outside [0, N) met (and masked), 7 x unused}.
+constexpr int kTraceInts = 16;
 
 // Tile record fields.
 enum TileField { T_ROWBLOCK = 0, T_KVHEAD, T_ROW0, T_NROWS, T_COLB, T_COLE, T_PART, T_KEYS };

@@ -220,3 +220,33 @@ def test_noalloc_limit_matches_header_and_refuses_large_plans_on_the_host():
     assert st == L.BSA_ERR_WORKSPACE_TOO_SMALL and "bsa_run_noalloc" in lib.bsa_last_error().decode()
     lib.bsa_plan_destroy(h)
     assert lib.bsa_run_noalloc(None, fake, fake, fake, fake, None, None) == L.BSA_ERR_INVALID_ARGUMENT
+
+
+def test_bsa_log_prints_plan_statistics():
+    # BSA_LOG=1: one line per planning call on stderr, with the plan's statistics or the error
+    code = (
+        "import ctypes, numpy as np\n"
+        "from paged_attention_bsr_amd import _lib as L\n"
+        "lib = L.lib()\n"
+        "d = L.PlanDesc(); lib.bsa_plan_desc_init(ctypes.byref(d))\n"
+        "ip = np.array([0, 2], np.int32); ix = np.array([0, 1], np.int32)\n"
+        "P = ctypes.POINTER(ctypes.c_int32)\n"
+        "d.indptr, d.indices = ip.ctypes.data_as(P), ix.ctypes.data_as(P)\n"
+        "d.M, d.N, d.R, d.C, d.num_cus = 4, 8, 4, 4, 8\n"
+        "h = ctypes.c_void_p()\n"
+        "assert lib.bsa_plan_ex(ctypes.byref(d), ctypes.byref(h)) == 0\n"
+        "d.N = 6\n"
+        "assert lib.bsa_plan_ex(ctypes.byref(d), ctypes.byref(h)) != 0\n"
+    )
+    env = dict(os.environ, BSA_LOG="1")
+    r = subprocess.run([__import__("sys").executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    lines = [l for l in r.stderr.splitlines() if l.startswith("[bsa] plan")]
+    assert len(lines) == 2, r.stderr
+    assert "kernel=tile" in lines[0] and "tiles=" in lines[0] and "workspace=" in lines[0]
+    assert "failed" in lines[1]
+    env["BSA_LOG"] = "0"
+    r = subprocess.run([__import__("sys").executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 0 and "[bsa] plan" not in r.stderr
