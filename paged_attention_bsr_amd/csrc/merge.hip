@@ -31,9 +31,10 @@ __device__ __forceinline__ void store4<float>(float* p, f32x4 v) {
 // Merge `n` states of one row: lse of state s at lse_p[s * lse_step], its
 // 4-vector at o_p[s * o_step].  Returns the merged 4-vector, *lse_out the
 // merged lse.  One pass with a running maximum (the accumulator is rescaled
-// when it grows), four states per step so that their loads are in flight
-// together; a state with lse = -inf is skipped by a select, so whatever its
-// values hold never reaches the sum.
+// when it grows); the loads of up to eight states are issued together before
+// any of them is merged (a split row has at most a few partitions, so this is
+// usually a single memory round trip), and a state with lse = -inf is skipped
+// by a select, so whatever its values hold never reaches the sum.
 __device__ __forceinline__ void merge_one(float l, f32x4 o, float& mx, float& tot, f32x4& acc) {
   const bool live = l != -INFINITY;
   const float m_new = live ? fmaxf(mx, l) : mx;
@@ -46,22 +47,22 @@ __device__ __forceinline__ void merge_one(float l, f32x4 o, float& mx, float& to
 
 __device__ __forceinline__ f32x4 merge_row4(const float* lse_p, int64_t lse_step, const float* o_p,
                                             int64_t o_step, int n, float* lse_out) {
+  constexpr int kBatch = 8;
   float mx = -INFINITY, tot = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  int s = 0;
-  for (; s + 4 <= n; s += 4) {
-    float l[4];
-    f32x4 o[4];
+  for (int s0 = 0; s0 < n; s0 += kBatch) {
+    float l[kBatch];
+    f32x4 o[kBatch];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      l[j] = lse_p[(s + j) * lse_step];
-      o[j] = *reinterpret_cast<const f32x4*>(o_p + (s + j) * o_step);
+    for (int j = 0; j < kBatch; ++j) {
+      // states past n read state s0 (in bounds) and are dropped below
+      const int s = s0 + j < n ? s0 + j : s0;
+      l[j] = lse_p[s * lse_step];
+      o[j] = *reinterpret_cast<const f32x4*>(o_p + s * o_step);
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) merge_one(l[j], o[j], mx, tot, acc);
+    for (int j = 0; j < kBatch; ++j) merge_one(s0 + j < n ? l[j] : -INFINITY, o[j], mx, tot, acc);
   }
-  for (; s < n; ++s)
-    merge_one(lse_p[s * lse_step], *reinterpret_cast<const f32x4*>(o_p + s * o_step), mx, tot, acc);
   if (mx == -INFINITY) {
     *lse_out = -INFINITY;
     return f32x4{0.f, 0.f, 0.f, 0.f};
