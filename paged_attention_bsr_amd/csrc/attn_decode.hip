@@ -290,8 +290,7 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
   auto accumulate = [&](const f32x4 (&sc)[2]) {
     float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
                      fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = max_rows4(mx);
     const float m_new = fmaxf(m_run, mx * sl2);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
     const float alpha = fast_exp2(m_run - m_use);
@@ -330,8 +329,7 @@ __global__ __launch_bounds__(NW * 64, BSA_DECODE_MIN_WAVES) void attn_decode_ker
   // for the finished group and write each head's output (or split partial);
   // c is this wave's tile of the group.
   auto finish_tile = [&](const Ctx& c) {
-    float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
+    const float l_tot = sum_rows4(l_run);
     if (WPH == 1) {
       // the wave owns its head: normalise and store straight from the
       // accumulators (lane (col, quad) holds dims db*16 + 4*quad .. +3 of

@@ -391,8 +391,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mla_kernel(AttnArgs a) {
       float mx = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = max_rows4(mx);
       const float mt = mx * sl2;
       m_max[hb] = fmaxf(m_max[hb], mt);
       // the first tile with a visible key sets the reference (O and l are
@@ -480,8 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_mla_kernel(AttnArgs a) {
   const int dv0 = hf * (kDv / 2);
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
-    float l_tot = l_run[hb] + __shfl_xor(l_run[hb], 16, 64);
-    l_tot += __shfl_xor(l_tot, 32, 64);
+    const float l_tot = sum_rows4(l_run[hb]);
     const float inv = l_tot > 0.f ? a.out_scale / l_tot : 0.f;
     const float lse_v = l_tot > 0.f ? (m_ref[hb] + __log2f(l_tot)) * kLn2 : -INFINITY;
     const int rloc = hg * 32 + hb * 16 + col;

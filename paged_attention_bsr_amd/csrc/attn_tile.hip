@@ -435,7 +435,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
-    mx = fmaxf(mx, xor_lane32(mx));
+    mx = max_xor32(mx);
     const float mt = mx * sl2;
     upd = live && mt > m_run + kRescaleSlack;
     const float m_new = upd ? mt : m_run;
@@ -625,7 +625,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
   trace_flush(a.trace, blockIdx.x, tr, tid == 0, part, kvh, row0, nrows);
 
   // ---- finalize this lane's row
-  const float l_tot = l_run + xor_lane32(l_run);
+  const float l_tot = sum_xor32(l_run);
   const float inv = l_tot > 0.f ? out_scale / l_tot : 0.f;
   const float lse_v = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   if (!row_ok) return;

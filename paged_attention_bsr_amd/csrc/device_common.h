@@ -131,6 +131,42 @@ __device__ __forceinline__ void trace_flush(int32_t* trace, int tile, const Trac
 // v_exp_f32: 2^x, with 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float xor_lane32(float x) { return __shfl_xor(x, 32, 64); }
+// Cross-lane reductions on the VALU (gfx950's lane swaps) instead of LDS
+// permutes: v_permlane32_swap a, b exchanges the upper 32 lanes of a with the
+// lower 32 of b, v_permlane16_swap a, b the odd 16-lane rows of a with the
+// even rows of b.  With b a copy of a, the two registers then hold, per lane,
+// its own value and its partner's (lane ^ 32, resp. ^ 16); max / sum are
+// commutative, so the results equal x op (x of the partner) bit for bit.
+// The swaps are written as inline asm with both registers tied in and out
+// (through the compiler builtins, this toolchain combined the two results as
+// if they were one value, x op x, in some kernels).  The hazard checks do not
+// look inside inline asm, so each swap is preceded by the two wait states the
+// compiler itself puts between a VALU write and a swap reading that register
+// (without them the swap read stale values).
+template <typename Op>
+__device__ __forceinline__ float reduce_xor32(float x, Op op) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return op(a, b);
+}
+template <typename Op>
+__device__ __forceinline__ float reduce_xor16(float x, Op op) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return op(a, b);
+}
+struct MaxOp {
+  __device__ float operator()(float a, float b) const { return fmaxf(a, b); }
+};
+struct AddOp {
+  __device__ float operator()(float a, float b) const { return a + b; }
+};
+// x combined with the lane l ^ 32
+__device__ __forceinline__ float max_xor32(float x) { return reduce_xor32(x, MaxOp{}); }
+__device__ __forceinline__ float sum_xor32(float x) { return reduce_xor32(x, AddOp{}); }
+// x combined over the four 16-lane rows (lanes l, l ^ 16, l ^ 32, l ^ 48):
+// (x op x^16) op (that)^32
+__device__ __forceinline__ float max_rows4(float x) { return max_xor32(reduce_xor16(x, MaxOp{})); }
+__device__ __forceinline__ float sum_rows4(float x) { return sum_xor32(reduce_xor16(x, AddOp{})); }
 
 }  // namespace bsa
