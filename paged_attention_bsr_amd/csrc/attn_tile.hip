@@ -340,25 +340,33 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_tile_kernel(AttnArgs a) {
     hi = static_cast<int64_t>(cols[cb + blk1]) * C + (t1 - blk1 * C);
   };
 
-  // all eight K fragments of a 32-key block are read before its products,
-  // so the LDS latency is paid once per block rather than per k-step
+  // the eight K fragments of the first 32-key block are read before its
+  // products; those of block kb + 1 are read one by one between the products
+  // of block kb (each into the register the product before it consumed), so
+  // the LDS latency is paid once per tile
   auto qk = [&](const unsigned char* kl, f32x16 (&sacc)[NKB]) {
+    v8 kf[NKB][8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kf[0][ks] = *reinterpret_cast<const v8*>(kl + k_off(swap23(ql), 2 * ks + half));
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const int key = kb * 32 + swap23(ql);
-      v8 kf[8];
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) kf[ks] = *reinterpret_cast<const v8*>(kl + k_off(key, 2 * ks + half));
       sacc[kb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) sacc[kb] = Ops::mfma32(kf[ks], qf[ks], sacc[kb]);
+      for (int ks = 0; ks < 8; ++ks) {
+        sacc[kb] = Ops::mfma32(kf[kb][ks], qf[ks], sacc[kb]);
+        if (kb + 1 < NKB)
+          kf[kb + 1][ks] = *reinterpret_cast<const v8*>(kl + k_off((kb + 1) * 32 + swap23(ql), 2 * ks + half));
+      }
     }
-    // keep that order: the scheduler would otherwise pair each read with its product
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // block 0's reads
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // 8 LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // 8 MFMAs
-    }
+    for (int kb = 0; kb + 1 < NKB; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // a product of block kb
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // a read of block kb + 1
+      }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // the last block's products
   };
 
   f32x16 oacc[4];
