@@ -413,7 +413,7 @@ def cpu_entry(w, unit: str, budget_s: float) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100, help="timed steps (rounded up to a multiple of 5)")
+    ap.add_argument("--steps", type=int, default=500, help="timed steps (rounded up to a multiple of 5)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="all",
                     choices=["all", "worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla",
