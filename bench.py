@@ -242,9 +242,10 @@ def host_cores():
 
 
 # Steps per pair of timing events: a HIP event pair costs a few microseconds of GPU
-# time on this part, so each pair brackets CHUNK consecutive steps and the step's GPU
-# time is the pair's elapsed time / CHUNK (one sample per chunk).
-CHUNK = 5
+# time on this part (outside the pair's own window, so the wall clock of the timed
+# region carries it), so each pair brackets CHUNK consecutive steps and the step's
+# GPU time is the pair's elapsed time / CHUNK (one sample per chunk).
+CHUNK = 25
 # Default seconds of warm-up work (at least --warmup steps) before a workload's timed region.
 WARM_S = 0.25
 
@@ -413,7 +414,7 @@ def cpu_entry(w, unit: str, budget_s: float) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500, help="timed steps (rounded up to a multiple of 5)")
+    ap.add_argument("--steps", type=int, default=500, help="timed steps (rounded up to a multiple of 25)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="all",
                     choices=["all", "worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla",

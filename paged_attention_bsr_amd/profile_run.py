@@ -281,7 +281,7 @@ def main() -> int:
     ap.add_argument("workloads", nargs="+")
     ap.add_argument("--out", default=os.path.join("gpurun_out", "prof"))
     ap.add_argument("--counters", action="store_true")
-    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=150)
     ap.add_argument("--summarize-only", action="store_true",
                     help="write the summaries from what an earlier run left in --out (no GPU work)")
     args = ap.parse_args()
