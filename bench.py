@@ -323,16 +323,23 @@ def measure(name: str, args, dev):
 
     # W warm-up steps, continued until the GPU has been busy for WARM_S (its clocks come up
     # from idle, e.g. after the previous workload's host work)
-    warm_steps, t_w = 0, time.perf_counter()
-    while warm_steps < args.warmup or time.perf_counter() - t_w < args.warm_s:
-        step()
-        warm_steps += 1
-        if warm_steps % 8 == 0:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
+    def warm_up(fn, min_calls):
+        calls, t_w = 0, time.perf_counter()
+        while calls < min_calls or time.perf_counter() - t_w < args.warm_s:
+            fn()
+            calls += 1
+            if calls % 8 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        return calls
+
+    warm_steps = warm_up(step, args.warmup)
     wall, step_ms = timed_chunks(step, args.steps)
     ms_per_step = wall * 1e3 / len(step_ms) / CHUNK
     gpu_ms = float(np.median(step_ms))
+    # the attention-only loop gets a warm-up of its own: after the synchronisation that
+    # ends the timed steps the clocks may have dropped again
+    warm_up(attention_only, args.warmup)
     _, attn_ms = timed_chunks(attention_only, args.steps)
     attn_med = float(np.median(attn_ms))
     step()   # leave a complete result behind
