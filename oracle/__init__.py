@@ -26,3 +26,9 @@ from .rope_quantize import (  # noqa: F401
     rope_fp32,
     mla_rope_quantize_fp8,
 )
+from .indexer import (  # noqa: F401
+    key_slots,
+    indexer_scores,
+    topk_positions,
+    indexer_topk,
+)
