@@ -380,6 +380,62 @@ void bsa_rope_quant_init(bsa_rope_quant_t* args);
 size_t bsa_rope_quant_sizeof(void);
 bsa_status_t bsa_mla_rope_quantize_fp8(const bsa_rope_quant_t* args, void* stream);
 
+/*
+ * Sparse-attention indexer: FP32 scores and each query row's exact Top-K keys
+ * (flashinfer.sparse 0.7.4 API page, "SDSA Indexer": indexer_scores computes
+ * FP32 scores of query rows against their request's paged keys;
+ * top_k_from_candidates writes each row's exact Top-K keys; one query head,
+ * no head weights).  The output, int32 physical cache rows, is the index list
+ * of index-selected sparse MLA decode.
+ *
+ *   score(row, p) = sum_d q[row][d] * key_cache[slot(r, p)][d], accumulated in float32,
+ *   slot(r, p)    = block_table[r][p / page_size] * page_size + p % page_size,
+ * for the positions p = 0 .. n - 1 of the row's request r, n = min(ctx_len[row],
+ * req_kv_len[r], max_ctx).  A row keeps the K = topk positions of highest score;
+ * among equal scores the lower position wins (-0 and +0 are equal).  out[row] holds
+ * their slots in ascending position order; a row with n <= K keeps all n and pads
+ * with -1.  A position whose page index reaches max_pages or whose page id lies
+ * outside [0, num_slots / page_size) is scored as a zero key and, if kept, written
+ * as -1 (no read leaves the arrays).
+ *
+ *   q            device [num_rows][head_dim] fp16 or bf16 (dtype = BSA_F16 / BSA_BF16),
+ *                row stride q_stride elements (0 = head_dim), 16-byte aligned rows
+ *   key_cache    device [num_slots][head_dim], the same type, row stride k_stride (0 = dense)
+ *   block_table  device int32 [num_reqs][max_pages]
+ *   req_row_ptr  device int32 [num_reqs + 1], ascending in [0, num_rows]: the rows of
+ *                request r are req_row_ptr[r] .. req_row_ptr[r + 1] - 1, at most
+ *                max_rows_per_req of them (rows beyond it are not scored)
+ *   ctx_len      device int32 [num_rows]; req_kv_len device int32 [num_reqs]
+ *   scores       device float32 [num_rows][max_ctx], caller-owned workspace; afterwards
+ *                scores[row][p] holds score(row, p) for p < n
+ *   out          device int32 [num_rows][topk]
+ *   scores_only  non-zero: compute the scores only
+ * Sizes: num_reqs >= 1, head_dim in {64, 128, 256}, page_size >= 1, max_pages >= 1,
+ * topk >= 1, 1 <= num_slots < 2^31, max_ctx >= 1, strides multiples of 8 and >= head_dim.
+ * Runs two kernels on `stream` (scores, then Top-K); num_rows = 0 launches nothing.
+ * BSA_ERR_INVALID_ARGUMENT for a NULL argument struct or array, a bad size, stride,
+ * type or alignment.
+ */
+typedef struct {
+  const void* q;
+  const void* key_cache;
+  const int32_t* block_table;
+  const int32_t* req_row_ptr;
+  const int32_t* ctx_len;
+  const int32_t* req_kv_len;
+  float* scores;
+  int32_t* out;
+  int64_t num_slots, max_ctx, q_stride, k_stride;
+  int32_t num_rows, num_reqs, max_rows_per_req, max_pages, page_size, head_dim, topk, dtype;
+  int32_t scores_only;
+} bsa_indexer_t;
+
+/* Defaults: everything zero / NULL (dense strides), dtype BSA_BF16. */
+void bsa_indexer_init(bsa_indexer_t* args);
+/* sizeof(bsa_indexer_t) as compiled into the library. */
+size_t bsa_indexer_sizeof(void);
+bsa_status_t bsa_indexer_topk(const bsa_indexer_t* args, void* stream);
+
 /* Plan statistics, and the tables themselves, for inspection and tests. */
 typedef struct {
   int32_t kernel;          /* bsa_kernel_t */

@@ -4,6 +4,6 @@ The compute path is libbsa.so (hand-written HIP kernels behind the C ABI in
 include/bsa.h); this package is its thin Python binding plus seeded
 synthetic workloads.
 """
-from .api import Plan, merge_states, mla_rope_quantize_fp8  # noqa: F401
+from .api import Plan, indexer_topk, merge_states, mla_rope_quantize_fp8  # noqa: F401
 
-__all__ = ["Plan", "merge_states", "mla_rope_quantize_fp8"]
+__all__ = ["Plan", "indexer_topk", "merge_states", "mla_rope_quantize_fp8"]

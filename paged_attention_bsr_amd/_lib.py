@@ -122,6 +122,33 @@ class RopeQuant(ctypes.Structure):
     ]
 
 
+
+class Indexer(ctypes.Structure):
+    _fields_ = [
+        ("q", ctypes.c_void_p),
+        ("key_cache", ctypes.c_void_p),
+        ("block_table", ctypes.c_void_p),
+        ("req_row_ptr", ctypes.c_void_p),
+        ("ctx_len", ctypes.c_void_p),
+        ("req_kv_len", ctypes.c_void_p),
+        ("scores", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
+        ("num_slots", ctypes.c_int64),
+        ("max_ctx", ctypes.c_int64),
+        ("q_stride", ctypes.c_int64),
+        ("k_stride", ctypes.c_int64),
+        ("num_rows", ctypes.c_int32),
+        ("num_reqs", ctypes.c_int32),
+        ("max_rows_per_req", ctypes.c_int32),
+        ("max_pages", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("scores_only", ctypes.c_int32),
+    ]
+
+
 _lib = None
 _trace_lib = None
 
@@ -208,6 +235,12 @@ def _load(path: str) -> ctypes.CDLL:
     L.bsa_rope_quant_sizeof.restype = sz
     L.bsa_mla_rope_quantize_fp8.argtypes = [ctypes.POINTER(RopeQuant), vp]
     L.bsa_mla_rope_quantize_fp8.restype = st
+    L.bsa_indexer_init.argtypes = [ctypes.POINTER(Indexer)]
+    L.bsa_indexer_init.restype = None
+    L.bsa_indexer_sizeof.argtypes = []
+    L.bsa_indexer_sizeof.restype = sz
+    L.bsa_indexer_topk.argtypes = [ctypes.POINTER(Indexer), vp]
+    L.bsa_indexer_topk.restype = st
     L.bsa_plan_destroy.argtypes = [vp]
     L.bsa_plan_destroy.restype = None
     L.bsa_last_error.argtypes = []

@@ -332,6 +332,63 @@ def merge_states(v: torch.Tensor, s: torch.Tensor, out_dtype: torch.dtype = torc
     return v_out, s_out
 
 
+def indexer_topk(q: torch.Tensor, key_cache: torch.Tensor, block_table: torch.Tensor, req_row_ptr: torch.Tensor,
+                 ctx_len: torch.Tensor, req_kv_len: torch.Tensor, topk: int, page_size: int,
+                 max_rows_per_req: Optional[int] = None, max_ctx: Optional[int] = None,
+                 scores: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                 scores_only: bool = False, stream=None):
+    """Sparse-attention indexer (bsa_indexer_topk; flashinfer.sparse "SDSA Indexer":
+    indexer_scores, top_k_from_candidates): FP32 scores of each query row against its
+    request's paged keys, and the row's exact Top-K keys (ties to the lower position) as
+    int32 physical cache rows in ascending position order, padded with -1.
+
+    q (num_rows, head_dim) and key_cache (num_slots, head_dim): fp16 or bf16 device
+    tensors with contiguous rows; block_table (num_reqs, max_pages), req_row_ptr
+    (num_reqs + 1,), ctx_len (num_rows,), req_kv_len (num_reqs,): int32 device tensors.
+    max_rows_per_req and max_ctx default to values read back from the device (a
+    synchronising copy); pass them to avoid it.  Returns (out, scores)."""
+    for name, t in (("q", q), ("key_cache", key_cache)):
+        if not t.is_cuda or t.dim() != 2 or t.stride(1) != 1 or t.dtype not in (torch.float16, torch.bfloat16):
+            raise ValueError(f"{name} must be a 2-D fp16 / bf16 device tensor with contiguous rows")
+    if q.dtype != key_cache.dtype or q.shape[1] != key_cache.shape[1]:
+        raise ValueError("q and key_cache must share dtype and head_dim")
+    for name, t, nd in (("block_table", block_table, 2), ("req_row_ptr", req_row_ptr, 1), ("ctx_len", ctx_len, 1),
+                        ("req_kv_len", req_kv_len, 1)):
+        if not t.is_cuda or t.dtype != torch.int32 or t.dim() != nd or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {nd}-D int32 device tensor")
+    num_rows, num_reqs = q.shape[0], block_table.shape[0]
+    if req_row_ptr.shape[0] != num_reqs + 1 or ctx_len.shape[0] != num_rows or req_kv_len.shape[0] != num_reqs:
+        raise ValueError("req_row_ptr, ctx_len and req_kv_len do not match num_reqs / num_rows")
+    if max_rows_per_req is None:
+        max_rows_per_req = max(1, int(torch.diff(req_row_ptr).max().item())) if num_reqs else 1
+    if max_ctx is None:
+        max_ctx = max(1, int(ctx_len.max().item())) if num_rows else 1
+    if scores is None:
+        scores = torch.empty((num_rows, max_ctx), dtype=torch.float32, device=q.device)
+    elif scores.dtype != torch.float32 or scores.shape != (num_rows, max_ctx) or not scores.is_contiguous():
+        raise ValueError(f"scores must be a contiguous ({num_rows}, {max_ctx}) float32 tensor")
+    if out is None:
+        out = torch.empty((num_rows, topk), dtype=torch.int32, device=q.device)
+    elif out.dtype != torch.int32 or out.shape != (num_rows, topk) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous ({num_rows}, {topk}) int32 tensor")
+    lib = L.lib()
+    a = L.Indexer()
+    lib.bsa_indexer_init(ctypes.byref(a))
+    a.q, a.key_cache = q.data_ptr(), key_cache.data_ptr()
+    a.block_table, a.req_row_ptr = block_table.data_ptr(), req_row_ptr.data_ptr()
+    a.ctx_len, a.req_kv_len = ctx_len.data_ptr(), req_kv_len.data_ptr()
+    a.scores, a.out = scores.data_ptr(), out.data_ptr()
+    a.num_slots, a.max_ctx = key_cache.shape[0], max_ctx
+    a.q_stride, a.k_stride = q.stride(0), key_cache.stride(0)
+    a.num_rows, a.num_reqs, a.max_rows_per_req = num_rows, num_reqs, max_rows_per_req
+    a.max_pages, a.page_size, a.head_dim, a.topk = block_table.shape[1], page_size, q.shape[1], topk
+    a.dtype = L.BSA_BF16 if q.dtype == torch.bfloat16 else L.BSA_F16
+    a.scores_only = 1 if scores_only else 0
+    st = torch.cuda.current_stream(q.device).cuda_stream if stream is None else stream
+    L.check(lib.bsa_indexer_topk(ctypes.byref(a), st))
+    return out, scores
+
+
 def mla_rope_quantize_fp8(q_rope: torch.Tensor, k_rope: torch.Tensor, q_nope: torch.Tensor, k_nope: torch.Tensor,
                           cos_sin_cache: torch.Tensor, pos_ids: torch.Tensor, is_neox: bool = True,
                           quant_scale_q: float = 1.0, quant_scale_kv: float = 1.0,

@@ -36,7 +36,8 @@ HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", 
 # Extra -D definitions for tuning builds (e.g. "-DBSA_DECODE_NW=2"); empty for the product build.
 EXTRA = os.environ.get("BSA_EXTRA_CFLAGS", "").split()
 
-HIP_SOURCES = ["attn_tile.hip", "attn_decode.hip", "attn_mla.hip", "merge.hip", "rope_quant.hip", "api.cpp"]
+HIP_SOURCES = ["attn_tile.hip", "attn_decode.hip", "attn_mla.hip", "merge.hip", "rope_quant.hip", "indexer.hip",
+               "api.cpp"]
 HOST_SOURCES = ["planner.cpp", "abi_host.cpp"]
 
 

@@ -225,4 +225,12 @@ void bsa_rope_quant_init(bsa_rope_quant_t* args) {
 
 size_t bsa_rope_quant_sizeof(void) { return sizeof(bsa_rope_quant_t); }
 
+void bsa_indexer_init(bsa_indexer_t* args) {
+  if (!args) return;
+  std::memset(args, 0, sizeof(*args));
+  args->dtype = BSA_BF16;
+}
+
+size_t bsa_indexer_sizeof(void) { return sizeof(bsa_indexer_t); }
+
 }  // extern "C"

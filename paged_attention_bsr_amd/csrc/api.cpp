@@ -12,6 +12,7 @@
 
 #include "abi_internal.h"
 #include "kernels.h"
+#include "indexer.h"
 #include "rope_quant.h"
 
 namespace {
@@ -384,4 +385,60 @@ bsa_status_t bsa_mla_rope_quantize_fp8(const bsa_rope_quant_t* p, void* stream) 
   return BSA_OK;
 }
 
+
+bsa_status_t bsa_indexer_topk(const bsa_indexer_t* p, void* stream) {
+  bsa::clear_err();
+  if (!p) return set_err(BSA_ERR_INVALID_ARGUMENT, "args is NULL");
+  if (p->num_rows < 0) return set_err(BSA_ERR_INVALID_ARGUMENT, "num_rows must be >= 0");
+  if (p->num_reqs < 1) return set_err(BSA_ERR_INVALID_ARGUMENT, "num_reqs must be >= 1");
+  if (p->max_rows_per_req < 1) return set_err(BSA_ERR_INVALID_ARGUMENT, "max_rows_per_req must be >= 1");
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "head_dim must be 64, 128 or 256");
+  if (p->page_size < 1 || p->max_pages < 1)
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "page_size and max_pages must be >= 1");
+  if (p->topk < 1) return set_err(BSA_ERR_INVALID_ARGUMENT, "topk must be >= 1");
+  if (p->num_slots < 1 || p->num_slots > 0x7fffffff)
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "num_slots must lie in [1, 2^31)");
+  if (p->max_ctx < 1) return set_err(BSA_ERR_INVALID_ARGUMENT, "max_ctx must be >= 1");
+  if (p->dtype != BSA_F16 && p->dtype != BSA_BF16)
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "dtype must be BSA_F16 or BSA_BF16");
+  const int64_t qs = p->q_stride != 0 ? p->q_stride : p->head_dim;
+  const int64_t ks = p->k_stride != 0 ? p->k_stride : p->head_dim;
+  if (qs < p->head_dim || ks < p->head_dim || qs % 8 != 0 || ks % 8 != 0)
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "strides must be multiples of 8 and at least head_dim");
+  const int64_t groups = (p->max_rows_per_req + 15) / 16;
+  if (static_cast<int64_t>(p->num_reqs) * groups > 0x7fffffff || (p->max_ctx + 255) / 256 > 65535)
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "too many request row groups, or max_ctx above 16776960");
+  if (p->num_rows == 0) return BSA_OK;
+  if (!p->q || !p->key_cache || reinterpret_cast<uintptr_t>(p->q) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(p->key_cache) % 16 != 0)
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "q and key_cache must be non-NULL and 16-byte aligned");
+  const void* ints[] = {p->block_table, p->req_row_ptr, p->ctx_len, p->req_kv_len, p->scores, p->out};
+  for (const void* x : ints)
+    if (!x || reinterpret_cast<uintptr_t>(x) % 4 != 0)
+      return set_err(BSA_ERR_INVALID_ARGUMENT, "table, score and output arrays must be non-NULL and 4-byte aligned");
+  bsa::IndexerArgs a{};
+  a.q = p->q;
+  a.key_cache = p->key_cache;
+  a.block_table = p->block_table;
+  a.req_row_ptr = p->req_row_ptr;
+  a.ctx_len = p->ctx_len;
+  a.req_kv_len = p->req_kv_len;
+  a.scores = p->scores;
+  a.out = p->out;
+  a.num_slots = p->num_slots;
+  a.max_ctx = p->max_ctx;
+  a.q_stride = qs;
+  a.k_stride = ks;
+  a.num_rows = p->num_rows;
+  a.num_reqs = p->num_reqs;
+  a.max_rows_per_req = p->max_rows_per_req;
+  a.max_pages = p->max_pages;
+  a.page_size = p->page_size;
+  a.head_dim = p->head_dim;
+  a.topk = p->topk;
+  const hipError_t e = bsa::launch_indexer(a, p->dtype == BSA_BF16, p->scores_only != 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "indexer kernel launch");
+  return BSA_OK;
+}
 }  // extern "C"

@@ -1,0 +1,28 @@
+// Launch interface of the sparse-attention indexer (scores + exact Top-K).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace bsa {
+
+// Pointers are device addresses; strides in elements.
+struct IndexerArgs {
+  const void* q;               // [num_rows][head_dim] fp16 / bf16
+  const void* key_cache;       // [num_slots][head_dim], same type
+  const int32_t* block_table;  // [num_reqs][max_pages]
+  const int32_t* req_row_ptr;  // [num_reqs + 1]
+  const int32_t* ctx_len;      // [num_rows]
+  const int32_t* req_kv_len;   // [num_reqs]
+  float* scores;               // [num_rows][max_ctx]
+  int32_t* out;                // [num_rows][topk]
+  int64_t num_slots, max_ctx, q_stride, k_stride;
+  int32_t num_rows, num_reqs, max_rows_per_req, max_pages, page_size, head_dim, topk;
+};
+
+// The scores kernel (unless there are no rows), then, unless scores_only, the
+// Top-K kernel.  head_dim in {64, 128, 256}.
+hipError_t launch_indexer(const IndexerArgs& a, bool bf16, bool scores_only, hipStream_t stream);
+
+}  // namespace bsa

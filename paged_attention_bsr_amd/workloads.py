@@ -481,6 +481,41 @@ def rope_quantize(seed: int = 10, nnz: int = 4096, num_heads: int = 128, max_seq
     return w
 
 
+def indexer(seed: int = 5, num_tokens: int = 128, cache_rows: int = 65536, head_dim: int = 128,
+            topk: int = 2048, page_size: int = 64, min_ctx: int = 4096, max_ctx: int = 65536,
+            num_reqs: int = 1, dtype: torch.dtype = torch.bfloat16, integer: bool = False,
+            values: bool = True) -> dict:
+    """The indexer upstream of sparse MLA decode: ``num_tokens`` query rows (one index head of
+    ``head_dim``) split evenly over ``num_reqs`` requests, each request owning
+    cache_rows / num_reqs keys laid out over pages of ``page_size`` in a random page order.  Row t
+    scores positions [0, ctx_t) of its request, ctx_t uniform in [min_ctx, max_ctx] (capped at the
+    request's keys) and drawn first from the seed as in sparse_mla, and keeps ``topk`` of them.
+    Values: standard normals in ``dtype``, or (``integer``) integers in [-4, 4], whose float32
+    dot products are exact in any summation order."""
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(min_ctx, max_ctx + 1, size=num_tokens).astype(np.int64)
+    per_req = cache_rows // num_reqs
+    pages_per_req = (per_req + page_size - 1) // page_size
+    num_pages = pages_per_req * num_reqs
+    table = rng.permutation(num_pages).astype(np.int32).reshape(num_reqs, pages_per_req)
+    bounds = np.linspace(0, num_tokens, num_reqs + 1).round().astype(np.int32)
+    ctx = np.minimum(ctx, per_req).astype(np.int32)
+    w = {"name": "indexer", "num_rows": num_tokens, "num_reqs": num_reqs, "head_dim": head_dim, "topk": topk,
+         "page_size": page_size, "num_slots": num_pages * page_size, "block_table": table,
+         "req_row_ptr": bounds, "ctx_len": ctx, "req_kv_len": np.full(num_reqs, per_req, np.int32),
+         "max_ctx": int(ctx.max()) if num_tokens else 1,
+         "max_rows_per_req": int(np.diff(bounds).max()) if num_reqs else 1}
+    if values:
+        g = torch.Generator().manual_seed(seed)
+        if integer:
+            w["q"] = torch.randint(-4, 5, (num_tokens, head_dim), generator=g).to(dtype)
+            w["key_cache"] = torch.randint(-4, 5, (num_pages * page_size, head_dim), generator=g).to(dtype)
+        else:
+            w["q"] = torch.randn(num_tokens, head_dim, generator=g).to(dtype)
+            w["key_cache"] = torch.randn(num_pages * page_size, head_dim, generator=g).to(dtype)
+    return w
+
+
 # Split-KV setting each workload is timed (and parity-checked at full size) with:
 # 0 = automatic, 1 = no split.
 BENCH_KV_SPLITS = {"worked_example": 1, "paged_decode": 0, "bsr_prefill": 1, "window_prefill": 1,

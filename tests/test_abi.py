@@ -184,6 +184,41 @@ def test_rope_quant_layout_matches_binding():
     assert (a.is_neox, a.quant_scale_q, a.quant_scale_kv, a.nnz) == (1, 1.0, 1.0, 0)
 
 
+def test_indexer_layout_matches_binding():
+    import ctypes
+    from paged_attention_bsr_amd import _lib as L
+    assert L.lib().bsa_indexer_sizeof() == ctypes.sizeof(L.Indexer)
+    a = L.Indexer()
+    L.lib().bsa_indexer_init(ctypes.byref(a))
+    assert (a.dtype, a.num_rows, a.topk, a.q_stride, a.scores_only) == (L.BSA_BF16, 0, 0, 0, 0)
+
+
+def test_indexer_validates_before_touching_the_gpu():
+    import ctypes
+    from paged_attention_bsr_amd import _lib as L
+    lib = L.lib()
+
+    def base():
+        a = L.Indexer()
+        lib.bsa_indexer_init(ctypes.byref(a))
+        a.num_rows, a.num_reqs, a.max_rows_per_req, a.max_pages, a.page_size = 0, 1, 1, 4, 16
+        a.head_dim, a.topk, a.num_slots, a.max_ctx = 128, 8, 64, 64
+        return a
+
+    a = base()
+    assert lib.bsa_indexer_topk(ctypes.byref(a), None) == L.BSA_OK          # no rows: nothing to do
+    a.num_rows = 2
+    assert lib.bsa_indexer_topk(ctypes.byref(a), None) == L.BSA_ERR_INVALID_ARGUMENT  # NULL arrays
+    assert b"16-byte aligned" in lib.bsa_last_error()
+    assert lib.bsa_indexer_topk(None, None) == L.BSA_ERR_INVALID_ARGUMENT
+    for field, value in (("head_dim", 96), ("topk", 0), ("num_reqs", 0), ("page_size", 0), ("max_pages", 0),
+                         ("num_slots", 0), ("max_ctx", 0), ("dtype", L.BSA_FP8_E4M3), ("q_stride", 100),
+                         ("k_stride", 64), ("max_rows_per_req", 0)):
+        a = base()
+        setattr(a, field, value)
+        assert lib.bsa_indexer_topk(ctypes.byref(a), None) == L.BSA_ERR_INVALID_ARGUMENT, field
+
+
 def test_rope_quant_validates_before_touching_the_gpu():
     import ctypes
     from paged_attention_bsr_amd import _lib as L
