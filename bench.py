@@ -41,6 +41,7 @@ KERNEL_SOURCES = {
     "attn_decode_kernel": ["attn_decode.hip", "device_common.h", "kernels.h"],
     "attn_mla_kernel": ["attn_mla.hip", "device_common.h", "kernels.h"],
     "rope_quant_kernel": ["rope_quant.hip", "rope_quant.h", "device_common.h"],
+    "indexer_topk_kernel": ["indexer.hip", "indexer.h", "device_common.h"],
 }
 
 
@@ -426,7 +427,7 @@ def main() -> int:
     ap.add_argument("--workload", default="all",
                     choices=["all", "worked_example", "paged_decode", "bsr_prefill", "window_prefill", "sparse_mla",
                              "head_sparse_prefill", "paged_decode_fp8", "element_mask_prefill",
-                             "variable_block_prefill", "bsr_prefill_fp8", "rope_quantize"],
+                             "variable_block_prefill", "bsr_prefill_fp8", "rope_quantize", "indexer"],
                     help="all = the five configurations (headline: paged_decode); otherwise one workload")
     ap.add_argument("--warm-s", type=float, default=WARM_S,
                     help="keep warming up (beyond --warmup steps) until the GPU has worked this many seconds")
@@ -459,6 +460,8 @@ def main() -> int:
 
     if args.workload == "rope_quantize":
         return run_rope_quantize(args, dev)
+    if args.workload == "indexer":
+        return run_indexer(args, dev)
 
     names = CONFIGS if args.workload == "all" else [args.workload]
     # every GPU measurement first (back to back, the GPU kept busy), then the host baselines
@@ -561,6 +564,101 @@ def run_rope_quantize(args, dev) -> int:
     line = {"metric": METRIC, "value": alg / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in, fp8 e4m3 out (f32 arithmetic)",
+            "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def indexer_bytes(w: dict) -> int:
+    """Algorithmic bytes of one indexer step: each request's keys read once (up to its longest
+    row's context), the query rows read and the int32 index lists written.  The float32 score
+    rows are an intermediate of this implementation, not part of the floor."""
+    rp, ctx, D = w["req_row_ptr"], w["ctx_len"], w["head_dim"]
+    keys = sum(int(ctx[rp[r]:rp[r + 1]].max()) for r in range(w["num_reqs"]) if rp[r + 1] > rp[r])
+    return keys * D * 2 + w["num_rows"] * D * 2 + w["num_rows"] * w["topk"] * 4
+
+
+def run_indexer(args, dev) -> int:
+    """One step = one bsa_indexer_topk (scores kernel, then Top-K kernel) over the workload's
+    query rows: the indexer upstream of the sparse-MLA configuration."""
+    import numpy as np
+    import torch
+    from paged_attention_bsr_amd import indexer_topk
+    from paged_attention_bsr_amd import workloads as W
+    w = W.indexer()
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    q, kc = w["q"].to(dev), w["key_cache"].to(dev)
+    bt, rp, ctx, kv = t(w["block_table"]), t(w["req_row_ptr"]), t(w["ctx_len"]), t(w["req_kv_len"])
+    rows, K = w["num_rows"], w["topk"]
+    scores = torch.empty((rows, (w["max_ctx"] + 63) // 64 * 64), dtype=torch.float32, device=dev)
+    out = torch.empty((rows, K), dtype=torch.int32, device=dev)
+
+    def run(scores_only):
+        return lambda: indexer_topk(q, kc, bt, rp, ctx, kv, K, w["page_size"], max_ctx=w["max_ctx"], scores=scores, out=out, scores_only=scores_only)
+
+    step, scores_step = run(False), run(True)
+    for fn in (step, scores_step):
+        n, t_w = 0, time.perf_counter()
+        while n < args.warmup or time.perf_counter() - t_w < args.warm_s:
+            fn()
+            n += 1
+        torch.cuda.synchronize()
+    wall, step_ms = timed_chunks(step, args.steps)
+    ms_per_step = wall * 1e3 / len(step_ms) / CHUNK
+    gpu_ms = float(np.median(step_ms))
+    n, t_w = 0, time.perf_counter()
+    while n < args.warmup or time.perf_counter() - t_w < args.warm_s:
+        scores_step()
+        n += 1
+    torch.cuda.synchronize()
+    _, sc_ms = timed_chunks(scores_step, args.steps)
+    sc_med = float(np.median(sc_ms))
+    step()
+    torch.cuda.synchronize()
+    log(f"[bench] indexer: {len(step_ms) * CHUNK} steps: {ms_per_step:.4f} ms/step wall; GPU step median "
+        f"{gpu_ms:.4f} ms (scores kernel {sc_med:.4f} ms, Top-K kernel {gpu_ms - sc_med:.4f} ms)")
+    if args.calibration_copy > 0:
+        n = args.calibration_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    alg = indexer_bytes(w)
+    flops = 2 * w["head_dim"] * int(np.asarray(w["ctx_len"], np.int64).sum())
+    achieved = alg / (gpu_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+            "kernel": "indexer_topk_kernel",
+            "traffic": measured_traffic("indexer", kernel_source_hash("indexer_topk_kernel")),
+            "alg_bytes_per_launch": alg, "alg_flops_per_launch": flops, "step_gpu_ms_median": gpu_ms,
+            "scores_kernel_ms_median": sc_med, "topk_kernel_ms": gpu_ms - sc_med,
+            "timing": f"median over {len(step_ms)} chunks of {CHUNK} steps of the HIP-event GPU time per step "
+                      "(scores + Top-K kernels)"}
+    cpu = None
+    if args.cpu_budget > 0:
+        import oracle
+        log(f"[bench] indexer: CPU oracle baseline (~{args.cpu_budget:.0f} s budget)")
+        n_cpu, n_aff, threads = host_cores()
+        qn, kn = w["q"].float().numpy(), w["key_cache"].float().numpy()
+        done, used, done_bytes = 0, 0.0, 0
+        while done < rows and used < args.cpu_budget:
+            t1 = time.perf_counter()
+            oracle.indexer_topk(qn[done:done + 1], kn, w["block_table"], w["page_size"], np.array([0, 1], np.int32),
+                                w["ctx_len"][done:done + 1], K)
+            used += time.perf_counter() - t1
+            done_bytes += int(w["ctx_len"][done]) * w["head_dim"] * 2 + w["head_dim"] * 2 + K * 4
+            done += 1
+        cpu = {"value": done_bytes / used / 1e9, "unit": "GB/s", "cores": threads, "os_cpu_count": n_cpu,
+               "affinity_cores": n_aff, "blas_threads": threads, "kind": "oracle",
+               "sample": f"{done} of {rows} query rows, each reading its own keys, float64 scores + sort, "
+                         f"{used:.1f} s"}
+    cfg = {"workload": "indexer", "num_rows": rows, "num_reqs": w["num_reqs"], "head_dim": w["head_dim"],
+           "topk": K, "page_size": w["page_size"], "num_slots": w["num_slots"], "max_ctx": w["max_ctx"],
+           "alg_bytes": alg, "alg_flops": flops}
+    line = {"metric": METRIC, "value": alg / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in, f32 scores, int32 out",
             "data": "synthetic", "config": cfg, "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
     return 0

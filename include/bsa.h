@@ -403,15 +403,16 @@ bsa_status_t bsa_mla_rope_quantize_fp8(const bsa_rope_quant_t* args, void* strea
  *   key_cache    device [num_slots][head_dim], the same type, row stride k_stride (0 = dense)
  *   block_table  device int32 [num_reqs][max_pages]
  *   req_row_ptr  device int32 [num_reqs + 1], ascending in [0, num_rows]: the rows of
- *                request r are req_row_ptr[r] .. req_row_ptr[r + 1] - 1, at most
- *                max_rows_per_req of them (rows beyond it are not scored)
+ *                request r are req_row_ptr[r] .. req_row_ptr[r + 1] - 1
  *   ctx_len      device int32 [num_rows]; req_kv_len device int32 [num_reqs]
- *   scores       device float32 [num_rows][max_ctx], caller-owned workspace; afterwards
- *                scores[row][p] holds score(row, p) for p < n
+ *   scores       device float32 [num_rows][ld], ld = max_ctx rounded up to a multiple of 64,
+ *                16-byte aligned, caller-owned workspace; afterwards scores[row][p] holds
+ *                score(row, p) for p < n
  *   out          device int32 [num_rows][topk]
  *   scores_only  non-zero: compute the scores only
  * Sizes: num_reqs >= 1, head_dim in {64, 128, 256}, page_size >= 1, max_pages >= 1,
- * topk >= 1, 1 <= num_slots < 2^31, max_ctx >= 1, strides multiples of 8 and >= head_dim.
+ * topk >= 1, 1 <= num_slots < 2^31, 1 <= max_ctx <= 16776960, strides multiples of 8 and
+ * >= head_dim.
  * Runs two kernels on `stream` (scores, then Top-K); num_rows = 0 launches nothing.
  * BSA_ERR_INVALID_ARGUMENT for a NULL argument struct or array, a bad size, stride,
  * type or alignment.
@@ -426,7 +427,7 @@ typedef struct {
   float* scores;
   int32_t* out;
   int64_t num_slots, max_ctx, q_stride, k_stride;
-  int32_t num_rows, num_reqs, max_rows_per_req, max_pages, page_size, head_dim, topk, dtype;
+  int32_t num_rows, num_reqs, max_pages, page_size, head_dim, topk, dtype;
   int32_t scores_only;
 } bsa_indexer_t;
 

@@ -139,7 +139,6 @@ class Indexer(ctypes.Structure):
         ("k_stride", ctypes.c_int64),
         ("num_rows", ctypes.c_int32),
         ("num_reqs", ctypes.c_int32),
-        ("max_rows_per_req", ctypes.c_int32),
         ("max_pages", ctypes.c_int32),
         ("page_size", ctypes.c_int32),
         ("head_dim", ctypes.c_int32),

@@ -334,7 +334,7 @@ def merge_states(v: torch.Tensor, s: torch.Tensor, out_dtype: torch.dtype = torc
 
 def indexer_topk(q: torch.Tensor, key_cache: torch.Tensor, block_table: torch.Tensor, req_row_ptr: torch.Tensor,
                  ctx_len: torch.Tensor, req_kv_len: torch.Tensor, topk: int, page_size: int,
-                 max_rows_per_req: Optional[int] = None, max_ctx: Optional[int] = None,
+                 max_ctx: Optional[int] = None,
                  scores: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                  scores_only: bool = False, stream=None):
     """Sparse-attention indexer (bsa_indexer_topk; flashinfer.sparse "SDSA Indexer":
@@ -345,8 +345,9 @@ def indexer_topk(q: torch.Tensor, key_cache: torch.Tensor, block_table: torch.Te
     q (num_rows, head_dim) and key_cache (num_slots, head_dim): fp16 or bf16 device
     tensors with contiguous rows; block_table (num_reqs, max_pages), req_row_ptr
     (num_reqs + 1,), ctx_len (num_rows,), req_kv_len (num_reqs,): int32 device tensors.
-    max_rows_per_req and max_ctx default to values read back from the device (a
-    synchronising copy); pass them to avoid it.  Returns (out, scores)."""
+    max_ctx defaults to the largest ctx_len, read back from the device (a synchronising
+    copy); pass it to avoid that.  Returns (out, scores); scores has
+    max_ctx rounded up to a multiple of 64 columns (row i's scores are scores[i, :n])."""
     for name, t in (("q", q), ("key_cache", key_cache)):
         if not t.is_cuda or t.dim() != 2 or t.stride(1) != 1 or t.dtype not in (torch.float16, torch.bfloat16):
             raise ValueError(f"{name} must be a 2-D fp16 / bf16 device tensor with contiguous rows")
@@ -359,14 +360,13 @@ def indexer_topk(q: torch.Tensor, key_cache: torch.Tensor, block_table: torch.Te
     num_rows, num_reqs = q.shape[0], block_table.shape[0]
     if req_row_ptr.shape[0] != num_reqs + 1 or ctx_len.shape[0] != num_rows or req_kv_len.shape[0] != num_reqs:
         raise ValueError("req_row_ptr, ctx_len and req_kv_len do not match num_reqs / num_rows")
-    if max_rows_per_req is None:
-        max_rows_per_req = max(1, int(torch.diff(req_row_ptr).max().item())) if num_reqs else 1
     if max_ctx is None:
         max_ctx = max(1, int(ctx_len.max().item())) if num_rows else 1
+    ld = (max_ctx + 63) // 64 * 64  # score rows are padded to a multiple of 64 floats
     if scores is None:
-        scores = torch.empty((num_rows, max_ctx), dtype=torch.float32, device=q.device)
-    elif scores.dtype != torch.float32 or scores.shape != (num_rows, max_ctx) or not scores.is_contiguous():
-        raise ValueError(f"scores must be a contiguous ({num_rows}, {max_ctx}) float32 tensor")
+        scores = torch.empty((num_rows, ld), dtype=torch.float32, device=q.device)
+    elif scores.dtype != torch.float32 or scores.shape != (num_rows, ld) or not scores.is_contiguous():
+        raise ValueError(f"scores must be a contiguous ({num_rows}, {ld}) float32 tensor")
     if out is None:
         out = torch.empty((num_rows, topk), dtype=torch.int32, device=q.device)
     elif out.dtype != torch.int32 or out.shape != (num_rows, topk) or not out.is_contiguous():
@@ -380,7 +380,7 @@ def indexer_topk(q: torch.Tensor, key_cache: torch.Tensor, block_table: torch.Te
     a.scores, a.out = scores.data_ptr(), out.data_ptr()
     a.num_slots, a.max_ctx = key_cache.shape[0], max_ctx
     a.q_stride, a.k_stride = q.stride(0), key_cache.stride(0)
-    a.num_rows, a.num_reqs, a.max_rows_per_req = num_rows, num_reqs, max_rows_per_req
+    a.num_rows, a.num_reqs = num_rows, num_reqs
     a.max_pages, a.page_size, a.head_dim, a.topk = block_table.shape[1], page_size, q.shape[1], topk
     a.dtype = L.BSA_BF16 if q.dtype == torch.bfloat16 else L.BSA_F16
     a.scores_only = 1 if scores_only else 0

@@ -391,7 +391,6 @@ bsa_status_t bsa_indexer_topk(const bsa_indexer_t* p, void* stream) {
   if (!p) return set_err(BSA_ERR_INVALID_ARGUMENT, "args is NULL");
   if (p->num_rows < 0) return set_err(BSA_ERR_INVALID_ARGUMENT, "num_rows must be >= 0");
   if (p->num_reqs < 1) return set_err(BSA_ERR_INVALID_ARGUMENT, "num_reqs must be >= 1");
-  if (p->max_rows_per_req < 1) return set_err(BSA_ERR_INVALID_ARGUMENT, "max_rows_per_req must be >= 1");
   if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 256)
     return set_err(BSA_ERR_INVALID_ARGUMENT, "head_dim must be 64, 128 or 256");
   if (p->page_size < 1 || p->max_pages < 1)
@@ -406,17 +405,17 @@ bsa_status_t bsa_indexer_topk(const bsa_indexer_t* p, void* stream) {
   const int64_t ks = p->k_stride != 0 ? p->k_stride : p->head_dim;
   if (qs < p->head_dim || ks < p->head_dim || qs % 8 != 0 || ks % 8 != 0)
     return set_err(BSA_ERR_INVALID_ARGUMENT, "strides must be multiples of 8 and at least head_dim");
-  const int64_t groups = (p->max_rows_per_req + 15) / 16;
-  if (static_cast<int64_t>(p->num_reqs) * groups > 0x7fffffff || (p->max_ctx + 255) / 256 > 65535)
-    return set_err(BSA_ERR_INVALID_ARGUMENT, "too many request row groups, or max_ctx above 16776960");
+  if ((p->max_ctx + 255) / 256 > 65535) return set_err(BSA_ERR_INVALID_ARGUMENT, "max_ctx must be at most 16776960");
   if (p->num_rows == 0) return BSA_OK;
   if (!p->q || !p->key_cache || reinterpret_cast<uintptr_t>(p->q) % 16 != 0 ||
       reinterpret_cast<uintptr_t>(p->key_cache) % 16 != 0)
     return set_err(BSA_ERR_INVALID_ARGUMENT, "q and key_cache must be non-NULL and 16-byte aligned");
-  const void* ints[] = {p->block_table, p->req_row_ptr, p->ctx_len, p->req_kv_len, p->scores, p->out};
+  if (!p->scores || reinterpret_cast<uintptr_t>(p->scores) % 16 != 0)
+    return set_err(BSA_ERR_INVALID_ARGUMENT, "scores must be non-NULL and 16-byte aligned");
+  const void* ints[] = {p->block_table, p->req_row_ptr, p->ctx_len, p->req_kv_len, p->out};
   for (const void* x : ints)
     if (!x || reinterpret_cast<uintptr_t>(x) % 4 != 0)
-      return set_err(BSA_ERR_INVALID_ARGUMENT, "table, score and output arrays must be non-NULL and 4-byte aligned");
+      return set_err(BSA_ERR_INVALID_ARGUMENT, "table and output arrays must be non-NULL and 4-byte aligned");
   bsa::IndexerArgs a{};
   a.q = p->q;
   a.key_cache = p->key_cache;
@@ -428,13 +427,14 @@ bsa_status_t bsa_indexer_topk(const bsa_indexer_t* p, void* stream) {
   a.out = p->out;
   a.num_slots = p->num_slots;
   a.max_ctx = p->max_ctx;
+  a.ld_scores = (p->max_ctx + 63) / 64 * 64;
   a.q_stride = qs;
   a.k_stride = ks;
   a.num_rows = p->num_rows;
   a.num_reqs = p->num_reqs;
-  a.max_rows_per_req = p->max_rows_per_req;
   a.max_pages = p->max_pages;
   a.page_size = p->page_size;
+  a.page_shift = (p->page_size & (p->page_size - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(p->page_size)) : -1;
   a.head_dim = p->head_dim;
   a.topk = p->topk;
   const hipError_t e = bsa::launch_indexer(a, p->dtype == BSA_BF16, p->scores_only != 0, static_cast<hipStream_t>(stream));

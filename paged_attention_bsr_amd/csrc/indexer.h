@@ -15,10 +15,11 @@ struct IndexerArgs {
   const int32_t* req_row_ptr;  // [num_reqs + 1]
   const int32_t* ctx_len;      // [num_rows]
   const int32_t* req_kv_len;   // [num_reqs]
-  float* scores;               // [num_rows][max_ctx]
+  float* scores;               // [num_rows][ld_scores]
   int32_t* out;                // [num_rows][topk]
-  int64_t num_slots, max_ctx, q_stride, k_stride;
-  int32_t num_rows, num_reqs, max_rows_per_req, max_pages, page_size, head_dim, topk;
+  int64_t num_slots, max_ctx, ld_scores, q_stride, k_stride;  // ld_scores: max_ctx rounded up to 64
+  int32_t num_rows, num_reqs, max_pages, page_size, head_dim, topk;
+  int32_t page_shift;          // log2(page_size) when it is a power of two, else -1
 };
 
 // The scores kernel (unless there are no rows), then, unless scores_only, the

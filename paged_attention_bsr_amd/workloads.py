@@ -503,8 +503,7 @@ def indexer(seed: int = 5, num_tokens: int = 128, cache_rows: int = 65536, head_
     w = {"name": "indexer", "num_rows": num_tokens, "num_reqs": num_reqs, "head_dim": head_dim, "topk": topk,
          "page_size": page_size, "num_slots": num_pages * page_size, "block_table": table,
          "req_row_ptr": bounds, "ctx_len": ctx, "req_kv_len": np.full(num_reqs, per_req, np.int32),
-         "max_ctx": int(ctx.max()) if num_tokens else 1,
-         "max_rows_per_req": int(np.diff(bounds).max()) if num_reqs else 1}
+         "max_ctx": int(ctx.max()) if num_tokens else 1}
     if values:
         g = torch.Generator().manual_seed(seed)
         if integer:

@@ -201,7 +201,7 @@ def test_indexer_validates_before_touching_the_gpu():
     def base():
         a = L.Indexer()
         lib.bsa_indexer_init(ctypes.byref(a))
-        a.num_rows, a.num_reqs, a.max_rows_per_req, a.max_pages, a.page_size = 0, 1, 1, 4, 16
+        a.num_rows, a.num_reqs, a.max_pages, a.page_size = 0, 1, 4, 16
         a.head_dim, a.topk, a.num_slots, a.max_ctx = 128, 8, 64, 64
         return a
 
@@ -213,7 +213,7 @@ def test_indexer_validates_before_touching_the_gpu():
     assert lib.bsa_indexer_topk(None, None) == L.BSA_ERR_INVALID_ARGUMENT
     for field, value in (("head_dim", 96), ("topk", 0), ("num_reqs", 0), ("page_size", 0), ("max_pages", 0),
                          ("num_slots", 0), ("max_ctx", 0), ("dtype", L.BSA_FP8_E4M3), ("q_stride", 100),
-                         ("k_stride", 64), ("max_rows_per_req", 0)):
+                         ("k_stride", 64), ("max_ctx", 1 << 25)):
         a = base()
         setattr(a, field, value)
         assert lib.bsa_indexer_topk(ctypes.byref(a), None) == L.BSA_ERR_INVALID_ARGUMENT, field

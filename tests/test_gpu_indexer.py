@@ -24,7 +24,7 @@ def _run(w, **kw):
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
     out, scores = indexer_topk(w["q"].to(DEV), w["key_cache"].to(DEV), t(w["block_table"]), t(w["req_row_ptr"]),
                                t(w["ctx_len"]), t(w["req_kv_len"]), w["topk"], w["page_size"],
-                               max_rows_per_req=w["max_rows_per_req"], max_ctx=w["max_ctx"], **kw)
+                               max_ctx=w["max_ctx"], **kw)
     torch.cuda.synchronize()
     return out.cpu().numpy().astype(np.int64), scores.cpu().numpy()
 
