@@ -144,3 +144,44 @@ def test_invalid_pages_score_zero_and_are_written_as_minus_one():
         assert np.all(scores[row, 48:64] == 0) and np.all(scores[row, 160:176] == 0)
         assert np.all(scores[row, :48] == -1)
         assert out[row].tolist()[:16] == [-1] * 16 and out[row].tolist()[16:] == [-1] * 4
+
+
+@pytest.mark.parametrize("k", [100, 5000])
+def test_heavy_ties_take_the_slow_path(k):
+    # every score equal: the K-th key's bin holds all n > 4096 keys, more than the candidate
+    # buffer, so the row is done by radix passes over the whole row
+    w = W.indexer(seed=7, num_tokens=3, cache_rows=16384, num_reqs=1, page_size=64, head_dim=128, topk=k,
+                  min_ctx=9000, max_ctx=16000, integer=True)
+    w["key_cache"] = torch.ones_like(w["key_cache"])
+    say(f"[indexer] heavy ties, top {k}")
+    out, _ = _run(w)
+    for row in range(3):
+        assert np.array_equal(out[row], oracle.key_slots(w["block_table"], 64, 0, k))
+
+
+def test_workspace_counters_are_reset_and_calls_are_independent():
+    """Per row the workspace holds a fixed block: state words, a 4096-bin histogram, candidates
+    and per-chunk counts.  Only the arrival counters (state words 0, 1), the candidate count
+    (word 5) and the histogram must start at zero; each call resets them.  Everything else is
+    written before it is read, so garbage there changes nothing."""
+    from paged_attention_bsr_amd import _lib as L
+    a = W.indexer(seed=21, num_tokens=24, cache_rows=20000, num_reqs=2, page_size=16, head_dim=64, topk=300,
+                  min_ctx=5000, max_ctx=20000, integer=True)
+    b = W.indexer(seed=22, num_tokens=9, cache_rows=9000, num_reqs=3, page_size=32, head_dim=128, topk=64,
+                  min_ctx=100, max_ctx=9000, integer=True)
+    block = int(L.lib().bsa_indexer_workspace_size(1))
+    ws = torch.zeros(24 * block, dtype=torch.uint8, device=DEV)
+    words = ws.view(torch.int32).view(24, block // 4)
+    zero_cols = torch.tensor([0, 1, 5] + list(range(64, 64 + 4096)), device=DEV)
+    garbage = torch.ones(block // 4, dtype=torch.bool, device=DEV)
+    garbage[zero_cols] = False
+    words[:, garbage] = -1234567
+    say("[indexer] own workspace: A, B, A")
+    out_a, _ = _run(a, workspace=ws)
+    assert int(torch.count_nonzero(words[:, zero_cols]).item()) == 0
+    out_b, _ = _run(b, workspace=ws)
+    assert int(torch.count_nonzero(words[:, zero_cols]).item()) == 0
+    again, _ = _run(a, workspace=ws)
+    assert np.array_equal(out_a, again)
+    assert np.array_equal(out_a, oracle.indexer_topk(*_oracle_inputs(a), 300))
+    assert np.array_equal(out_b, oracle.indexer_topk(*_oracle_inputs(b), 64))
