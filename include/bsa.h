@@ -382,10 +382,10 @@ bsa_status_t bsa_mla_rope_quantize_fp8(const bsa_rope_quant_t* args, void* strea
 
 /*
  * Sparse-attention indexer: FP32 scores and each query row's exact Top-K keys
- * (flashinfer.sparse 0.7.4 API page, "SDSA Indexer": indexer_scores computes
- * FP32 scores of query rows against their request's paged keys;
- * top_k_from_candidates writes each row's exact Top-K keys; one query head,
- * no head weights).  The output, int32 physical cache rows, is the index list
+ * (flashinfer.sparse 0.7.4 API page, "SDSA Indexer": indexer_scores gives a
+ * float32 score per query row and key position of the row's request in the
+ * paged cache; top_k_from_candidates keeps the row's exact Top-K; one query
+ * head, no head weights).  The output, int32 physical cache rows, is the index list
  * of index-selected sparse MLA decode.
  *
  *   score(row, p) = sum_d q[row][d] * key_cache[slot(r, p)][d], accumulated in float32,

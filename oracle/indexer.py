@@ -12,8 +12,9 @@ sparse MLA decode (whose int32 physical-token index lists it produces):
       keys.  The indexer has one query head and no head weights, so a score
       is the dot product of the row's query vector with the key vector;
   I2  exact Top-K: each query row keeps the K keys of highest score
-      (top_k_from_candidates writes "each query row's exact Top-K keys ...
-      and ties", so a tie at the K-th score has to be resolved by a rule).
+      (top_k_from_candidates writes every row's exact Top-K from the
+      candidates and the tied keys the selection stored, so a tie at the
+      K-th score has to be resolved by a rule).
 
 Readings taken where the pages are silent:
   * a request's key position p lives in cache row

@@ -353,8 +353,8 @@ def indexer_topk(q: torch.Tensor, key_cache: torch.Tensor, block_table: torch.Te
                  scores: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                  scores_only: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
     """Sparse-attention indexer (bsa_indexer_topk; flashinfer.sparse "SDSA Indexer":
-    indexer_scores, top_k_from_candidates): FP32 scores of each query row against its
-    request's paged keys, and the row's exact Top-K keys (ties to the lower position) as
+    indexer_scores, top_k_from_candidates): a float32 score for each key position a query row
+    sees in its request's paged cache, and the row's exact Top-K keys (ties to the lower position) as
     int32 physical cache rows in ascending position order, padded with -1.
 
     q (num_rows, head_dim) and key_cache (num_slots, head_dim): fp16 or bf16 device

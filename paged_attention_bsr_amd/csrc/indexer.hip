@@ -1,8 +1,9 @@
-// Sparse-attention indexer on gfx950: FP32 scores of query rows against their
-// request's paged keys, then each row's exact Top-K keys (flashinfer.sparse
-// 0.7.4, "SDSA Indexer": indexer_scores, top_k_from_candidates; one query
-// head, no head weights).  Its output -- int32 physical cache rows -- is the
-// index list that index-selected sparse MLA decode consumes.
+// Sparse-attention indexer on gfx950: a float32 score for every key position
+// a query row sees in its request's paged cache, then the row's exact Top-K
+// keys (flashinfer.sparse 0.7.4, "SDSA Indexer": indexer_scores,
+// top_k_from_candidates; one query head, no head weights).  Its output --
+// int32 physical cache rows -- is the index list that index-selected sparse
+// MLA decode consumes.
 //
 // Scores: a workgroup takes one request (grid x) and 256 of its key positions
 // (grid y; four waves of 64): it loads the keys once into registers, stages

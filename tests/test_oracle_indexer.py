@@ -1,5 +1,5 @@
-"""Pins of the indexer oracle (oracle/indexer.py): FP32 scores of query rows
-against their request's paged keys and the exact Top-K with ties to the
+"""Pins of the indexer oracle (oracle/indexer.py): float32 scores of each query
+row over the key positions of its request's paged cache and the exact Top-K with ties to the
 lower position (flashinfer.sparse 0.7.4, "SDSA Indexer": indexer_scores,
 top_k_from_candidates).
 
