@@ -332,26 +332,11 @@ def merge_states(v: torch.Tensor, s: torch.Tensor, out_dtype: torch.dtype = torc
     return v_out, s_out
 
 
-_INDEXER_WORKSPACE = {}  # device -> zero-filled uint8 tensor (every completed call leaves it zeroed)
-
-
-def indexer_workspace(num_rows: int, device) -> torch.Tensor:
-    """A zero-filled workspace of at least bsa_indexer_workspace_size(num_rows) bytes on
-    `device`, shared by every call on that device that does not pass its own."""
-    need = int(L.lib().bsa_indexer_workspace_size(num_rows))
-    dev = torch.device(device)
-    ws = _INDEXER_WORKSPACE.get(dev)
-    if ws is None or ws.numel() < need:
-        ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
-        _INDEXER_WORKSPACE[dev] = ws
-    return ws
-
-
 def indexer_topk(q: torch.Tensor, key_cache: torch.Tensor, block_table: torch.Tensor, req_row_ptr: torch.Tensor,
                  ctx_len: torch.Tensor, req_kv_len: torch.Tensor, topk: int, page_size: int,
                  max_ctx: Optional[int] = None,
                  scores: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                 scores_only: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
+                 scores_only: bool = False, stream=None):
     """Sparse-attention indexer (bsa_indexer_topk; flashinfer.sparse "SDSA Indexer":
     indexer_scores, top_k_from_candidates): a float32 score for each key position a query row
     sees in its request's paged cache, and the row's exact Top-K keys (ties to the lower position) as
@@ -361,9 +346,7 @@ def indexer_topk(q: torch.Tensor, key_cache: torch.Tensor, block_table: torch.Te
     tensors with contiguous rows; block_table (num_reqs, max_pages), req_row_ptr
     (num_reqs + 1,), ctx_len (num_rows,), req_kv_len (num_reqs,): int32 device tensors.
     max_ctx defaults to the largest ctx_len, read back from the device (a synchronising
-    copy); pass it to avoid that.  workspace: a zero-filled device uint8 tensor of at least
-    bsa_indexer_workspace_size bytes that calls leave zeroed (default: one shared per device;
-    calls that share a workspace must not overlap).  Returns (out, scores); scores has
+    copy); pass it to avoid that.  Returns (out, scores); scores has
     max_ctx rounded up to a multiple of 64 columns (row i's scores are scores[i, :n])."""
     for name, t in (("q", q), ("key_cache", key_cache)):
         if not t.is_cuda or t.dim() != 2 or t.stride(1) != 1 or t.dtype not in (torch.float16, torch.bfloat16):
@@ -389,15 +372,8 @@ def indexer_topk(q: torch.Tensor, key_cache: torch.Tensor, block_table: torch.Te
     elif out.dtype != torch.int32 or out.shape != (num_rows, topk) or not out.is_contiguous():
         raise ValueError(f"out must be a contiguous ({num_rows}, {topk}) int32 tensor")
     lib = L.lib()
-    if not scores_only:
-        if workspace is None:
-            workspace = indexer_workspace(num_rows, q.device)
-        elif not workspace.is_cuda or not workspace.is_contiguous():
-            raise ValueError("workspace must be a contiguous device tensor")
     a = L.Indexer()
     lib.bsa_indexer_init(ctypes.byref(a))
-    if workspace is not None:
-        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     a.q, a.key_cache = q.data_ptr(), key_cache.data_ptr()
     a.block_table, a.req_row_ptr = block_table.data_ptr(), req_row_ptr.data_ptr()
     a.ctx_len, a.req_kv_len = ctx_len.data_ptr(), req_kv_len.data_ptr()

@@ -17,27 +17,13 @@
 // outside the cache reads as a zero key.
 //
 // Top-K: a score maps to an unsigned key that orders like the float (sign bit
-// flipped for positives, all bits for negatives; -0 becomes +0).  Each row is
-// cut into chunks of 16384 positions, one 1024-thread workgroup per (row,
-// chunk), in three kernels:
-//   (1) histogram of the keys' top 12 bits in LDS, added to the row's
-//       histogram in the workspace; the row's last workgroup to finish finds
-//       the bin of the K-th largest key;
-//   (2) each chunk counts its keys in the bins above (kept outright) and
-//       appends that bin's keys with their positions to the row's candidates;
-//       the last workgroup selects among the candidates the exact K-th largest
-//       key T (radix passes over the remaining bits) and, when not every key
-//       equal to T is kept, the last kept position among them (ties to the
-//       lower position), then turns the chunks' kept counts into output
-//       offsets;
-//   (3) each chunk writes its kept positions' cache rows in position order
-//       from its offset (ballots within a wave, wave totals through LDS).
-// "Last workgroup" is decided by a per-row arrival counter; the data it reads
-// from the others goes through device-scope atomics (see last_to_arrive), and
-// it resets the counters and the histogram, so the workspace is ready for the
-// next call.  A bin with more keys than the candidate buffer holds (heavy
-// ties) sends the row down a slower path: its first chunk's workgroup in (3)
-// does the whole row by four 8-bit radix passes and per-thread segments.
+// flipped for positives, all bits for negatives; -0 becomes +0).  One
+// 1024-thread workgroup per row takes a threshold from a sample of the row's
+// scores, moves the keys at or above it into LDS in position order, finds the
+// exact K-th largest key among them and writes the kept keys' cache rows in
+// position order (see indexer_topk_kernel).  A row whose sample misses (fewer
+// than K keys reach the threshold, or more than the LDS holds, as with heavy
+// ties) is done by four 8-bit radix passes over the whole row.
 #include <algorithm>
 
 #include "device_common.h"
@@ -279,43 +265,6 @@ __device__ __forceinline__ int64_t row_keys(const IndexerArgs& a, int row, int* 
   return n;
 }
 
-// the row's block of the workspace and its parts
-__device__ __forceinline__ char* row_ws(const IndexerArgs& a, int row) { return a.ws + static_cast<int64_t>(row) * kIdxRowBytes; }
-__device__ __forceinline__ uint32_t* row_state(const IndexerArgs& a, int row) {
-  return reinterpret_cast<uint32_t*>(row_ws(a, row) + kIdxRowState);
-}
-
-// Workgroups of one row pass data to the row's last workgroup only through
-// device-scope atomics: read-modify-writes whose returned value each thread
-// waits for (an atomic returns after it has been performed at the device's
-// coherence point), and atomic loads in the reader.  No fence is needed, and
-// none is taken: a device-scope fence writes back and invalidates the L2 of
-// the caller's XCD.
-__device__ __forceinline__ uint32_t dev_add(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t dev_xchg(uint32_t* p, uint32_t v) {
-  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t dev_xchg(uint64_t* p, uint64_t v) {
-  return __hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ T dev_load(const T* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// True in the one workgroup that completes a row's step.  `sink` folds the
-// values the thread's device atomics returned: using it makes the thread wait
-// for them, so when the workgroup counts itself in, its atomics are performed.
-__device__ __forceinline__ bool last_to_arrive(uint32_t* counter, int count, uint32_t sink, int* flag) {
-  asm volatile("" ::"v"(sink));
-  __syncthreads();
-  if (threadIdx.x == 0) *flag = dev_add(counter, 1u) == static_cast<uint32_t>(count - 1) ? 1 : 0;
-  __syncthreads();
-  return *flag != 0;
-}
-
 // Top-K of one row by four 8-bit radix passes over the scores in global
 // memory and per-thread contiguous segments for the ordered output: one
 // workgroup does the whole row (the path for a row whose bin of the K-th
@@ -369,247 +318,61 @@ __device__ void topk_by_radix_passes(const IndexerArgs& a, int r, const float* s
   }
 }
 
-constexpr int kHistShift = 32 - kIdxHistBits;  // a key's histogram bin is key >> kHistShift
-constexpr int kChunkShift = 14;                 // log2(kIdxChunk)
-constexpr int kPer = kIdxChunk / (4 * kTopkThreads);  // 16-byte groups per thread and chunk
-constexpr int kWaveSpan = kIdxChunk / (kTopkThreads / 64);  // positions per wave and chunk
-static_assert(kQRows * 8 % kScoreThreads == 0, "whole 16-byte pieces per thread");
-static_assert((1 << kChunkShift) == kIdxChunk && kPer == 4 && kWaveSpan == 4 * 64 * kPer, "chunk layout");
-static_assert(kIdxHistBits == 12, "candidates are resolved by two 10-bit passes over the low 20 bits");
+constexpr int kSegSteps = 8;                                   // 16-byte groups per thread per segment
+constexpr int kWaveSpan = kSegSteps * 256;                      // positions per wave per segment
+constexpr int kSeg = (kTopkThreads / 64) * kWaveSpan;           // positions per segment: 32768
+static_assert(kIdxSample % kTopkThreads == 0 && kIdxSample <= kIdxCandCap, "sample layout");
 
-// first of the four positions that thread tid takes in step j of chunk c: wave w owns
-// the chunk's positions kWaveSpan w .. + kWaveSpan - 1, 256 of them per step
-__device__ __forceinline__ int64_t chunk_pos(int c, int tid, int j) {
-  return (static_cast<int64_t>(c) << kChunkShift) + (tid >> 6) * kWaveSpan + j * 256 + 4 * (tid & 63);
-}
-
-// the thread's kPer 16-byte groups of the chunk (zeros past n; score rows are padded
-// to 64 floats, so a group that starts below n lies in the row)
-__device__ __forceinline__ void load_chunk(const float* srow, int c, int tid, int64_t n, f32x4 (&v)[kPer]) {
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int64_t p = chunk_pos(c, tid, j);
-    v[j] = p < n ? *reinterpret_cast<const f32x4*>(srow + p) : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-}
-
-// (1) per chunk: a histogram of the keys' top 12 bits in LDS, added to the
-// row's histogram in the workspace; the last chunk to finish locates the bin
-// of the K-th largest key and clears the histogram for the next call
-__global__ __launch_bounds__(kTopkThreads) void topk_hist_kernel(IndexerArgs a) {
-  __shared__ int hist[kIdxHistBins];
-  __shared__ int scan[kTopkThreads / 64];
-  __shared__ int flag;
-  const int row = blockIdx.x;
-  const int c = blockIdx.y;
+// The key that `rank` keys of keys[0 .. S) reach (the rank-th largest): four 8-bit
+// radix passes from the top.  Requires 1 <= rank <= S.
+__device__ __forceinline__ uint32_t select_rank(const uint32_t* keys, int S, int rank, int* hist, int* scan,
+                                                int* pick) {
   const int tid = threadIdx.x;
-  int r;
-  const int64_t n = row_keys(a, row, &r);
-  const int K = a.topk;
-  if (n <= K) return;
-  const int nch = static_cast<int>((n + kIdxChunk - 1) >> kChunkShift);
-  if (c >= nch) return;
-  f32x4 v[kPer];
-  load_chunk(a.scores + static_cast<int64_t>(row) * a.ld_scores, c, tid, n, v);
-  for (int i = tid; i < kIdxHistBins; i += kTopkThreads) hist[i] = 0;
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int64_t p = chunk_pos(c, tid, j);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (p + e < n) atomicAdd(&hist[score_key(v[j][e]) >> kHistShift], 1);
-  }
-  __syncthreads();
-  uint32_t* gh = reinterpret_cast<uint32_t*>(row_ws(a, row) + kIdxRowHist);
-  uint32_t sink = 0;
-  for (int i = tid; i < kIdxHistBins; i += kTopkThreads) {
-    const int h = hist[i];
-    if (h != 0) sink ^= dev_add(&gh[i], static_cast<uint32_t>(h));
-  }
-  uint32_t* st = row_state(a, row);
-  if (!last_to_arrive(&st[kStArrive0], nch, sink, &flag)) return;
-  // the row's last chunk: thread t takes bins 4095 - 4t .. 4092 - 4t (from the top)
-  constexpr int BPT = kIdxHistBins / kTopkThreads;
-  int h[BPT], sum = 0;
-#pragma unroll
-  for (int j = 0; j < BPT; ++j) {
-    h[j] = static_cast<int>(dev_load(&gh[kIdxHistBins - 1 - (tid * BPT + j)]));
-    sum += h[j];
-  }
-  int tot;
-  int above = block_exclusive_scan(sum, scan, &tot);
-#pragma unroll
-  for (int j = 0; j < BPT; ++j) {
-    if (above < K && above + h[j] >= K) {
-      st[kStBin] = static_cast<uint32_t>(kIdxHistBins - 1 - (tid * BPT + j));
-      st[kStNeed] = static_cast<uint32_t>(K - above);  // keys to take from that bin
-      st[kStInBin] = static_cast<uint32_t>(h[j]);      // keys in that bin
-      st[kStFallback] = h[j] > kIdxCandCap ? 1u : 0u;
+  uint32_t pre = 0, msk = 0;
+  int need = rank, cnt;
+#pragma unroll 1
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < S; i += kTopkThreads) {
+      const uint32_t u = keys[i];
+      if ((u & msk) == pre) atomicAdd(&hist[(u >> shift) & 255], 1);
     }
-    above += h[j];
+    __syncthreads();
+    const int d = pick_bin(tid < 256 ? hist[255 - tid] : 0, 255 - tid, need, &cnt, scan, pick);
+    pre |= static_cast<uint32_t>(d) << shift;
+    msk |= 0xFFu << shift;
   }
-#pragma unroll
-  for (int j = 0; j < BPT; ++j) gh[kIdxHistBins - 1 - (tid * BPT + j)] = 0;
-  if (tid == 0) st[kStArrive0] = 0;
+  return pre;
 }
 
-// (2) per chunk: the count of keys in the bins above the K-th key's bin (all
-// kept) and that bin's keys appended, with their positions, to the row's
-// candidates (one reservation per workgroup).  The last chunk to finish
-// selects among the candidates the exact K-th largest key T (two 10-bit radix
-// passes over the bits below the bin's) and, when not every key equal to T is
-// kept, the position of the last one kept (ties to the lower position: 10-,
-// 10- and 4-bit passes over the tied keys' positions, lowest first); it then
-// turns each chunk's kept count into the chunk's offset in the row's output.
-__global__ __launch_bounds__(kTopkThreads) void topk_collect_kernel(IndexerArgs a) {
-  __shared__ uint32_t cu[kIdxCandCap];
-  __shared__ int32_t cp[kIdxCandCap];
-  __shared__ int kc[kIdxMaxChunks];
-  __shared__ int h[kTopkThreads];
-  __shared__ int scan[kTopkThreads / 64];
-  __shared__ int pick[3];
-  __shared__ int flag;
-  __shared__ uint32_t base_lds;
-  const int row = blockIdx.x;
-  const int c = blockIdx.y;
-  const int tid = threadIdx.x;
-  int r;
-  const int64_t n = row_keys(a, row, &r);
-  const int K = a.topk;
-  if (n <= K) return;
-  const int nch = static_cast<int>((n + kIdxChunk - 1) >> kChunkShift);
-  if (c >= nch) return;
-  f32x4 v[kPer];
-  load_chunk(a.scores + static_cast<int64_t>(row) * a.ld_scores, c, tid, n, v);
-  uint32_t* st = row_state(a, row);
-  const uint32_t bin = st[kStBin];
-  const bool collect = st[kStFallback] == 0;
-  int above = 0, mine = 0;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int64_t p = chunk_pos(c, tid, j);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t hb = score_key(v[j][e]) >> kHistShift;
-      if (p + e < n) {
-        above += hb > bin ? 1 : 0;
-        mine += hb == bin ? 1 : 0;
-      }
-    }
-  }
-  // one scan for both counts: a chunk holds at most 2^14 keys, so the low 16 bits never carry
-  int tot;
-  const int pre = block_exclusive_scan(above | mine << 16, scan, &tot);
-  const int above_c = tot & 0xffff;
-  const int mine_c = tot >> 16;
-  uint64_t* cand = reinterpret_cast<uint64_t*>(row_ws(a, row) + kIdxRowCand);  // key | position << 32
-  uint32_t sink = 0;
-  if (collect && mine_c > 0) {
-    if (tid == 0) base_lds = dev_add(&st[kStNcand], static_cast<uint32_t>(mine_c));
-    __syncthreads();
-    // the bin holds at most kIdxCandCap keys, so every append fits
-    uint32_t idx = base_lds + static_cast<uint32_t>(pre >> 16);
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int64_t p = chunk_pos(c, tid, j);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t u = score_key(v[j][e]);
-        if (p + e < n && (u >> kHistShift) == bin) {
-          if (idx < static_cast<uint32_t>(kIdxCandCap))
-            sink ^= static_cast<uint32_t>(dev_xchg(&cand[idx], u | static_cast<uint64_t>(p + e) << 32));
-          ++idx;
-        }
-      }
-    }
-  }
-  uint32_t* chunk = reinterpret_cast<uint32_t*>(row_ws(a, row) + kIdxRowChunk);
-  if (tid == 0) sink ^= dev_xchg(&chunk[c], static_cast<uint32_t>(above_c));
-  if (!last_to_arrive(&st[kStArrive1], nch, sink, &flag)) return;
-  if (!collect) {  // the output kernel takes the whole row by radix passes
-    if (tid == 0) st[kStArrive1] = 0;
-    return;
-  }
-  const int m = min(static_cast<int>(st[kStInBin]), kIdxCandCap);
-  for (int j = tid; j < m; j += kTopkThreads) {
-    const uint64_t x = dev_load(&cand[j]);
-    cu[j] = static_cast<uint32_t>(x);
-    cp[j] = static_cast<int32_t>(x >> 32);
-  }
-  // each chunk's keys above the bin: its kept count before the candidates
-  if (tid < nch) kc[tid] = static_cast<int>(dev_load(&chunk[tid]));
-  int need = static_cast<int>(st[kStNeed]);
-  uint32_t T = bin << kHistShift;
-  int ties = 0;
-#pragma unroll 1
-  for (int pass = 0; pass < 2; ++pass) {
-    const int shift = 10 - 10 * pass;
-    const uint32_t msk = ~0u << (shift + 10);
-    h[tid] = 0;
-    __syncthreads();
-    for (int j = tid; j < m; j += kTopkThreads) {
-      const uint32_t u = cu[j];
-      if ((u & msk) == T) atomicAdd(&h[(u >> shift) & 1023], 1);
-    }
-    __syncthreads();
-    const int d = pick_bin(h[1023 - tid], 1023 - tid, need, &ties, scan, pick);
-    T |= static_cast<uint32_t>(d) << shift;
-  }
-  // `ties` keys equal T; the `need` of them with the lowest positions are kept
-  int32_t p_last = 0x7fffffff;
-  if (need < ties) {
-    uint32_t ppre = 0, pmsk = 0;
-#pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = pass == 0 ? 14 : (pass == 1 ? 4 : 0);
-      const uint32_t dm = pass < 2 ? 1023u : 15u;
-      h[tid] = 0;
-      __syncthreads();
-      for (int j = tid; j < m; j += kTopkThreads) {
-        const uint32_t pj = static_cast<uint32_t>(cp[j]);
-        if (cu[j] == T && (pj & pmsk) == ppre) atomicAdd(&h[(pj >> shift) & dm], 1);
-      }
-      __syncthreads();
-      int cnt;
-      const int d = pick_bin(h[tid], tid, need, &cnt, scan, pick);
-      ppre |= static_cast<uint32_t>(d) << shift;
-      pmsk |= dm << shift;
-    }
-    p_last = static_cast<int32_t>(ppre);
-  }
-  // kept keys per chunk: those above the bin plus the kept candidates
-  static_assert(kIdxMaxChunks == kTopkThreads, "one chunk per thread");
-  for (int j = tid; j < m; j += kTopkThreads) {
-    const uint32_t u = cu[j];
-    const int32_t pj = cp[j];
-    if (u > T || (u == T && pj <= p_last)) atomicAdd(&kc[pj >> kChunkShift], 1);
-  }
-  __syncthreads();
-  const int mine_k = tid < nch ? kc[tid] : 0;
-  const int off = block_exclusive_scan(mine_k, scan, &tot);
-  if (tid < nch) chunk[tid] = static_cast<uint32_t>(off);
-  if (tid == 0) {
-    st[kStT] = T;
-    st[kStPLast] = static_cast<uint32_t>(p_last);
-    st[kStNcand] = 0;
-    st[kStArrive1] = 0;
-  }
-}
-
-// (3) per chunk: the kept keys' cache rows, in position order, from the
-// chunk's offset.  A wave's keys rank after the kept keys of the waves
-// before it; inside a wave, step j's keys after those of steps j' < j, and
-// lane l's four keys after the kept keys of lanes below it (one ballot per
-// key of the group).  A row with n <= K writes its n slots and the -1 padding
-// here; a row on the slow path is done whole by its first chunk's workgroup.
-__global__ __launch_bounds__(kTopkThreads) void topk_out_kernel(IndexerArgs a) {
-  __shared__ int wc[kTopkThreads / 64];
+// One 1024-thread workgroup per row.
+//  (1) The row's first 32768 scores are requested into registers (wave w takes
+//      positions 2048 w .. 2048 w + 2047 of a segment, 256 per step: lane l the
+//      four from 4 l), and with them a sample of the row: 256 runs of 16
+//      consecutive scores spread evenly over it (the whole row when n <= 4096).
+//  (2) A threshold from the sample: with the whole row as the sample, the K-th
+//      largest key itself; otherwise the key that K's share of the sample plus
+//      four standard deviations and 8 reach, so that at least K keys of the row
+//      lie at or above it unless the sample is far from typical.
+//  (3) One pass over the row moves the keys at or above the threshold, with
+//      their positions, into LDS in position order (per-wave counts, then
+//      ballot ranks inside each step).
+//  (4) Among these candidates the exact K-th largest key T (four 8-bit radix
+//      passes); the keys above T are kept, and of those equal to T the
+//      lowest-positioned ones; each thread writes the cache rows of a run of
+//      consecutive candidates from its offset.
+// A row with fewer than K or more than kIdxCandCap candidates is done instead by
+// radix passes over the whole row.
+__global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerArgs a) {
+  __shared__ uint32_t ck[kIdxCandCap];  // candidates' keys in position order; the sample before them
+  __shared__ int32_t cpos[kIdxCandCap];
   __shared__ int hist[256];
   __shared__ int scan[kTopkThreads / 64];
+  __shared__ int wcnt[kTopkThreads / 64];
   __shared__ int pick[3];
   const int row = blockIdx.x;
-  const int c = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -618,58 +381,124 @@ __global__ __launch_bounds__(kTopkThreads) void topk_out_kernel(IndexerArgs a) {
   const int K = a.topk;
   int32_t* out = a.out + static_cast<int64_t>(row) * K;
   if (n <= K) {
-    const int64_t i0 = static_cast<int64_t>(c) << kChunkShift;
-    for (int64_t i = i0 + tid; i < i0 + kIdxChunk && i < K; i += kTopkThreads)
-      out[i] = i < n ? static_cast<int32_t>(idx_slot(a, r, i)) : -1;
+    for (int i = tid; i < K; i += kTopkThreads) out[i] = i < n ? static_cast<int32_t>(idx_slot(a, r, i)) : -1;
     return;
   }
-  const int nch = static_cast<int>((n + kIdxChunk - 1) >> kChunkShift);
-  if (c >= nch) return;
   const float* s = a.scores + static_cast<int64_t>(row) * a.ld_scores;
-  f32x4 v[kPer];
-  load_chunk(s, c, tid, n, v);
-  const uint32_t* st = row_state(a, row);
-  if (st[kStFallback] != 0) {
-    if (c == 0) topk_by_radix_passes(a, r, s, n, K, out, hist, scan, pick);
+  // (1) score rows are padded to 64 floats, so a 16-byte group that starts below n lies in the row
+  f32x4 v[kSegSteps];
+  auto load_seg = [&](int64_t base) {
+#pragma unroll
+    for (int j = 0; j < kSegSteps; ++j) {
+      const int64_t p = base + wave * kWaveSpan + j * 256 + 4 * lane;
+      v[j] = p < n ? *reinterpret_cast<const f32x4*>(s + p) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  load_seg(0);
+  const int S = n < kIdxSample ? static_cast<int>(n) : kIdxSample;
+  uint32_t smp[kIdxSample / kTopkThreads];
+#pragma unroll
+  for (int j = 0; j < kIdxSample / kTopkThreads; ++j) {
+    const int i = tid + j * kTopkThreads;
+    // 256 runs of 16 consecutive positions, the runs n / 256 apart (n > 4096 here, so the
+    // runs do not overlap); the whole row when it is no longer than the sample
+    const int64_t p = S < n ? (i >> 4) * (n >> 8) + (i & 15) : i;
+    smp[j] = i < S ? score_key(s[p]) : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < kIdxSample / kTopkThreads; ++j) {
+    const int i = tid + j * kTopkThreads;
+    if (i < S) ck[i] = smp[j];
+  }
+  // (2)
+  int rank = K;
+  if (S < n) {
+    const double f = static_cast<double>(K) / static_cast<double>(n);
+    const double m = S * f;
+    rank = min(S, static_cast<int>(ceil(m + 4.0 * sqrt(m * (1.0 - f)) + 8.0)));
+  }
+  __syncthreads();
+  const uint32_t thr = select_rank(ck, S, rank, hist, scan, pick);  // ends with a barrier
+  // (3)
+  int total = 0;
+#pragma unroll 1
+  for (int64_t base = 0; base < n; base += kSeg) {
+    if (base > 0) load_seg(base);
+    int w_cnt = 0;
+#pragma unroll
+    for (int j = 0; j < kSegSteps; ++j) {
+      const int64_t p = base + wave * kWaveSpan + j * 256 + 4 * lane;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w_cnt += __popcll(__ballot(p + e < n && score_key(v[j][e]) >= thr));
+    }
+    if (lane == 0) wcnt[wave] = w_cnt;
+    __syncthreads();
+    int o = total, seg_total = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkThreads / 64; ++w) {
+      const int c = wcnt[w];
+      o += w < wave ? c : 0;
+      seg_total += c;
+    }
+#pragma unroll
+    for (int j = 0; j < kSegSteps; ++j) {
+      const int64_t p = base + wave * kWaveSpan + j * 256 + 4 * lane;
+      bool k[4];
+      int below = 0, step = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        k[e] = p + e < n && score_key(v[j][e]) >= thr;
+        const uint64_t bal = __ballot(k[e]);
+        below += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                           __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
+        step += __popcll(bal);
+      }
+      int idx = o + below;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (k[e]) {
+          if (idx < kIdxCandCap) {
+            ck[idx] = score_key(v[j][e]);
+            cpos[idx] = static_cast<int32_t>(p + e);
+          }
+          ++idx;
+        }
+      }
+      o += step;
+    }
+    total += seg_total;
+    __syncthreads();  // wcnt is rewritten by the next segment; the candidates are complete
+  }
+  if (total < K || total > kIdxCandCap) {
+    topk_by_radix_passes(a, r, s, n, K, out, hist, scan, pick);
     return;
   }
-  const uint32_t T = st[kStT];
-  const int64_t p_last = static_cast<int32_t>(st[kStPLast]);
-  const int base = static_cast<int>(reinterpret_cast<const uint32_t*>(row_ws(a, row) + kIdxRowChunk)[c]);
-  uint32_t keep = 0;  // bit 4 j + e: key e of step j is kept
-  int rank[kPer];     // kept keys of the wave before lane's group in step j
-  int w_total = 0;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int64_t p = chunk_pos(c, tid, j);
-    int below = 0, step = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t u = score_key(v[j][e]);
-      const bool k = p + e < n && (u > T || (u == T && p + e <= p_last));
-      keep |= k ? 1u << (4 * j + e) : 0u;
-      const uint64_t bal = __ballot(k);
-      below += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
-                                         __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
-      step += __popcll(bal);
-    }
-    rank[j] = w_total + below;
-    w_total += step;
+  // (4)
+  const uint32_t T = select_rank(ck, total, K, hist, scan, pick);
+  const int R = (total + kTopkThreads - 1) / kTopkThreads;
+  const int j0 = min(tid * R, total), j1 = min(j0 + R, total);
+  int gt = 0, eq = 0;
+  for (int j = j0; j < j1; ++j) {
+    gt += ck[j] > T ? 1 : 0;
+    eq += ck[j] == T ? 1 : 0;
   }
-  if (lane == 0) wc[wave] = w_total;
-  __syncthreads();
-  int o0 = base;
-  for (int w = 0; w < wave; ++w) o0 += wc[w];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int64_t p = chunk_pos(c, tid, j);
-    int o = o0 + rank[j];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (keep & (1u << (4 * j + e))) {
-        if (o < K) out[o] = static_cast<int32_t>(idx_slot(a, r, p + e));
-        ++o;
-      }
+  int gt_all, t3;
+  block_exclusive_scan(gt, scan, &gt_all);
+  const int eq_before = block_exclusive_scan(eq, scan, &t3);
+  const int need_eq = K - gt_all;  // tied keys to keep, lowest positions first
+  const int take_eq = min(max(need_eq - eq_before, 0), eq);
+  int o = block_exclusive_scan(gt + take_eq, scan, &t3);
+  int taken = 0;
+  for (int j = j0; j < j1; ++j) {
+    const uint32_t u = ck[j];
+    bool keep = u > T;
+    if (u == T) {
+      keep = taken < take_eq;
+      ++taken;
+    }
+    if (keep) {
+      if (o < K) out[o] = static_cast<int32_t>(idx_slot(a, r, cpos[j]));
+      ++o;
     }
   }
 }
@@ -695,11 +524,7 @@ hipError_t launch_indexer(const IndexerArgs& a, bool bf16, bool scores_only, hip
     if (e != hipSuccess) return e;
   }
   if (scores_only) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(a.num_rows), static_cast<unsigned>(a.nch_max));
-  topk_hist_kernel<<<grid, kTopkThreads, 0, st>>>(a);
-  topk_collect_kernel<<<grid, kTopkThreads, 0, st>>>(a);
-  const int64_t out_chunks = std::max<int64_t>(a.nch_max, (a.topk + kIdxChunk - 1) / kIdxChunk);
-  topk_out_kernel<<<dim3(static_cast<unsigned>(a.num_rows), static_cast<unsigned>(out_chunks)), kTopkThreads, 0, st>>>(a);
+  indexer_topk_kernel<<<static_cast<unsigned>(a.num_rows), kTopkThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

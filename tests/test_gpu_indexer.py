@@ -159,29 +159,48 @@ def test_heavy_ties_take_the_slow_path(k):
         assert np.array_equal(out[row], oracle.key_slots(w["block_table"], 64, 0, k))
 
 
-def test_workspace_counters_are_reset_and_calls_are_independent():
-    """Per row the workspace holds a fixed block: state words, a 4096-bin histogram, candidates
-    and per-chunk counts.  Only the arrival counters (state words 0, 1), the candidate count
-    (word 5) and the histogram must start at zero; each call resets them.  Everything else is
-    written before it is read, so garbage there changes nothing."""
-    from paged_attention_bsr_amd import _lib as L
+def test_calls_are_independent():
+    # two shapes in a row, then the first again
     a = W.indexer(seed=21, num_tokens=24, cache_rows=20000, num_reqs=2, page_size=16, head_dim=64, topk=300,
                   min_ctx=5000, max_ctx=20000, integer=True)
     b = W.indexer(seed=22, num_tokens=9, cache_rows=9000, num_reqs=3, page_size=32, head_dim=128, topk=64,
                   min_ctx=100, max_ctx=9000, integer=True)
-    block = int(L.lib().bsa_indexer_workspace_size(1))
-    ws = torch.zeros(24 * block, dtype=torch.uint8, device=DEV)
-    words = ws.view(torch.int32).view(24, block // 4)
-    zero_cols = torch.tensor([0, 1, 5] + list(range(64, 64 + 4096)), device=DEV)
-    garbage = torch.ones(block // 4, dtype=torch.bool, device=DEV)
-    garbage[zero_cols] = False
-    words[:, garbage] = -1234567
-    say("[indexer] own workspace: A, B, A")
-    out_a, _ = _run(a, workspace=ws)
-    assert int(torch.count_nonzero(words[:, zero_cols]).item()) == 0
-    out_b, _ = _run(b, workspace=ws)
-    assert int(torch.count_nonzero(words[:, zero_cols]).item()) == 0
-    again, _ = _run(a, workspace=ws)
+    say("[indexer] A, B, A")
+    out_a, _ = _run(a)
+    out_b, _ = _run(b)
+    again, _ = _run(a)
     assert np.array_equal(out_a, again)
     assert np.array_equal(out_a, oracle.indexer_topk(*_oracle_inputs(a), 300))
     assert np.array_equal(out_b, oracle.indexer_topk(*_oracle_inputs(b), 64))
+
+
+def test_rows_longer_than_one_segment():
+    # 32768 positions per step of the pass over the row: rows of up to 150000 keys take five
+    w = W.indexer(seed=23, num_tokens=6, cache_rows=150000, num_reqs=1, page_size=64, head_dim=64, topk=1000,
+                  min_ctx=60000, max_ctx=150000, integer=True)
+    say("[indexer] rows over several segments")
+    out, _ = _run(w)
+    assert np.array_equal(out, oracle.indexer_topk(*_oracle_inputs(w), 1000))
+
+
+def test_sample_that_misses_takes_the_slow_path():
+    # the sampled positions (256 runs of 16, n / 256 apart) hold the row's only high scores, all
+    # distinct, so the threshold from the sample is met by fewer than K keys of the row: the
+    # selection must notice and do the row by radix passes
+    n, S, k, D = 20000, 4096, 2000, 64
+    w = W.indexer(seed=9, num_tokens=1, cache_rows=n, num_reqs=1, page_size=16, head_dim=D, topk=k,
+                  min_ctx=n, max_ctx=n, integer=True)
+    q = torch.zeros(1, D)
+    q[0, 0], q[0, 1] = 256.0, 1.0
+    slots = oracle.key_slots(w["block_table"], 16, 0, n)
+    kc = torch.zeros(n, D)
+    kc[:, 0] = -1.0
+    for i in range(S):
+        v, p = S - i, (i >> 4) * (n >> 8) + (i & 15)
+        kc[slots[p], 0], kc[slots[p], 1] = v // 256, v % 256
+    w["q"], w["key_cache"] = q.to(torch.bfloat16), kc.to(torch.bfloat16)
+    say("[indexer] sample that misses")
+    out, scores = _run(w)
+    args = _oracle_inputs(w)
+    assert np.array_equal(scores[0, :n], oracle.indexer_scores(*args)[0])
+    assert np.array_equal(out, oracle.indexer_topk(*args, k))
