@@ -409,12 +409,18 @@ bsa_status_t bsa_mla_rope_quantize_fp8(const bsa_rope_quant_t* args, void* strea
  *                16-byte aligned, caller-owned workspace; afterwards scores[row][p] holds
  *                score(row, p) for p < n
  *   out          device int32 [num_rows][topk]
+ *   workspace    device, >= bsa_indexer_workspace_size(num_rows, max_ctx) bytes, 256-byte
+ *                aligned, caller-owned scratch of the Top-K step (per chunk of 16384
+ *                positions a candidate count and up to 8192 candidates); no initial
+ *                contents are needed.  Calls that share a workspace must not overlap.
+ *                Not read when scores_only is set (may then be NULL).
  *   scores_only  non-zero: compute the scores only
  * Sizes: num_reqs >= 1, head_dim in {64, 128, 256}, page_size >= 1, max_pages >= 1,
  * 1 <= topk <= 2^24, 1 <= num_slots < 2^31, 1 <= max_ctx <= 16776960, strides multiples of
  * 8 and >= head_dim.
- * Runs two kernels on `stream` (scores, then one Top-K workgroup per row); num_rows = 0
- * launches nothing.
+ * Runs three kernels on `stream` (scores; candidates per chunk of 16384 positions above a
+ * threshold taken from a sample of the row's scores; the exact selection per row);
+ * num_rows = 0 launches nothing.
  * BSA_ERR_INVALID_ARGUMENT for a NULL argument struct or array, a bad size, stride,
  * type or alignment.
  */
@@ -427,6 +433,8 @@ typedef struct {
   const int32_t* req_kv_len;
   float* scores;
   int32_t* out;
+  void* workspace;
+  size_t workspace_bytes;
   int64_t num_slots, max_ctx, q_stride, k_stride;
   int32_t num_rows, num_reqs, max_pages, page_size, head_dim, topk, dtype;
   int32_t scores_only;
@@ -436,6 +444,9 @@ typedef struct {
 void bsa_indexer_init(bsa_indexer_t* args);
 /* sizeof(bsa_indexer_t) as compiled into the library. */
 size_t bsa_indexer_sizeof(void);
+/* Bytes of workspace bsa_indexer_topk needs for num_rows rows of at most max_ctx keys
+ * (0 when either is <= 0). */
+size_t bsa_indexer_workspace_size(int32_t num_rows, int64_t max_ctx);
 bsa_status_t bsa_indexer_topk(const bsa_indexer_t* args, void* stream);
 
 /* Plan statistics, and the tables themselves, for inspection and tests. */

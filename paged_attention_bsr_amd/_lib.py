@@ -133,6 +133,8 @@ class Indexer(ctypes.Structure):
         ("req_kv_len", ctypes.c_void_p),
         ("scores", ctypes.c_void_p),
         ("out", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
         ("num_slots", ctypes.c_int64),
         ("max_ctx", ctypes.c_int64),
         ("q_stride", ctypes.c_int64),
@@ -238,6 +240,8 @@ def _load(path: str) -> ctypes.CDLL:
     L.bsa_indexer_init.restype = None
     L.bsa_indexer_sizeof.argtypes = []
     L.bsa_indexer_sizeof.restype = sz
+    L.bsa_indexer_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int64]
+    L.bsa_indexer_workspace_size.restype = sz
     L.bsa_indexer_topk.argtypes = [ctypes.POINTER(Indexer), vp]
     L.bsa_indexer_topk.restype = st
     L.bsa_plan_destroy.argtypes = [vp]

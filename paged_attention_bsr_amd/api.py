@@ -336,7 +336,7 @@ def indexer_topk(q: torch.Tensor, key_cache: torch.Tensor, block_table: torch.Te
                  ctx_len: torch.Tensor, req_kv_len: torch.Tensor, topk: int, page_size: int,
                  max_ctx: Optional[int] = None,
                  scores: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                 scores_only: bool = False, stream=None):
+                 scores_only: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
     """Sparse-attention indexer (bsa_indexer_topk; flashinfer.sparse "SDSA Indexer":
     indexer_scores, top_k_from_candidates): a float32 score for each key position a query row
     sees in its request's paged cache, and the row's exact Top-K keys (ties to the lower position) as
@@ -346,7 +346,9 @@ def indexer_topk(q: torch.Tensor, key_cache: torch.Tensor, block_table: torch.Te
     tensors with contiguous rows; block_table (num_reqs, max_pages), req_row_ptr
     (num_reqs + 1,), ctx_len (num_rows,), req_kv_len (num_reqs,): int32 device tensors.
     max_ctx defaults to the largest ctx_len, read back from the device (a synchronising
-    copy); pass it to avoid that.  Returns (out, scores); scores has
+    copy); pass it to avoid that.  workspace: a device tensor of at least
+    bsa_indexer_workspace_size(num_rows, max_ctx) bytes (default: a fresh one from torch's
+    allocator).  Returns (out, scores); scores has
     max_ctx rounded up to a multiple of 64 columns (row i's scores are scores[i, :n])."""
     for name, t in (("q", q), ("key_cache", key_cache)):
         if not t.is_cuda or t.dim() != 2 or t.stride(1) != 1 or t.dtype not in (torch.float16, torch.bfloat16):
@@ -372,8 +374,17 @@ def indexer_topk(q: torch.Tensor, key_cache: torch.Tensor, block_table: torch.Te
     elif out.dtype != torch.int32 or out.shape != (num_rows, topk) or not out.is_contiguous():
         raise ValueError(f"out must be a contiguous ({num_rows}, {topk}) int32 tensor")
     lib = L.lib()
+    if not scores_only:
+        need = int(lib.bsa_indexer_workspace_size(num_rows, max_ctx))
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+        elif (not workspace.is_cuda or not workspace.is_contiguous()
+              or workspace.numel() * workspace.element_size() < need):
+            raise ValueError(f"workspace must be a contiguous device tensor of at least {need} bytes")
     a = L.Indexer()
     lib.bsa_indexer_init(ctypes.byref(a))
+    if workspace is not None:
+        a.workspace, a.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     a.q, a.key_cache = q.data_ptr(), key_cache.data_ptr()
     a.block_table, a.req_row_ptr = block_table.data_ptr(), req_row_ptr.data_ptr()
     a.ctx_len, a.req_kv_len = ctx_len.data_ptr(), req_kv_len.data_ptr()

@@ -386,6 +386,10 @@ bsa_status_t bsa_mla_rope_quantize_fp8(const bsa_rope_quant_t* p, void* stream) 
 }
 
 
+size_t bsa_indexer_workspace_size(int32_t num_rows, int64_t max_ctx) {
+  return bsa::indexer_workspace_bytes(num_rows, max_ctx);
+}
+
 bsa_status_t bsa_indexer_topk(const bsa_indexer_t* p, void* stream) {
   bsa::clear_err();
   if (!p) return set_err(BSA_ERR_INVALID_ARGUMENT, "args is NULL");
@@ -416,6 +420,13 @@ bsa_status_t bsa_indexer_topk(const bsa_indexer_t* p, void* stream) {
   for (const void* x : ints)
     if (!x || reinterpret_cast<uintptr_t>(x) % 4 != 0)
       return set_err(BSA_ERR_INVALID_ARGUMENT, "table and output arrays must be non-NULL and 4-byte aligned");
+  const size_t ws_need = bsa::indexer_workspace_bytes(p->num_rows, p->max_ctx);
+  if (!p->scores_only) {
+    if (!p->workspace || reinterpret_cast<uintptr_t>(p->workspace) % 256 != 0)
+      return set_err(BSA_ERR_INVALID_ARGUMENT, "workspace must be non-NULL and 256-byte aligned");
+    if (p->workspace_bytes < ws_need)
+      return set_err(BSA_ERR_INVALID_ARGUMENT, "workspace is smaller than bsa_indexer_workspace_size");
+  }
   bsa::IndexerArgs a{};
   a.q = p->q;
   a.key_cache = p->key_cache;
@@ -437,6 +448,12 @@ bsa_status_t bsa_indexer_topk(const bsa_indexer_t* p, void* stream) {
   a.page_shift = (p->page_size & (p->page_size - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(p->page_size)) : -1;
   a.head_dim = p->head_dim;
   a.topk = p->topk;
+  a.nch_max = static_cast<int32_t>((p->max_ctx + bsa::kIdxChunk - 1) / bsa::kIdxChunk);
+  if (!p->scores_only) {
+    const size_t chunks = static_cast<size_t>(p->num_rows) * static_cast<size_t>(a.nch_max);
+    a.ws_count = static_cast<int32_t*>(p->workspace);
+    a.ws_cand = reinterpret_cast<uint2*>(static_cast<char*>(p->workspace) + (chunks * 4 + 255) / 256 * 256);
+  }
   const hipError_t e = bsa::launch_indexer(a, p->dtype == BSA_BF16, p->scores_only != 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "indexer kernel launch");
   return BSA_OK;

@@ -17,13 +17,15 @@
 // outside the cache reads as a zero key.
 //
 // Top-K: a score maps to an unsigned key that orders like the float (sign bit
-// flipped for positives, all bits for negatives; -0 becomes +0).  One
-// 1024-thread workgroup per row takes a threshold from a sample of the row's
-// scores, moves the keys at or above it into LDS in position order, finds the
-// exact K-th largest key among them and writes the kept keys' cache rows in
-// position order (see indexer_topk_kernel).  A row whose sample misses (fewer
-// than K keys reach the threshold, or more than the LDS holds, as with heavy
-// ties) is done by four 8-bit radix passes over the whole row.
+// flipped for positives, all bits for negatives; -0 becomes +0).  Every
+// workgroup of a row takes the same threshold from a sample of the row's
+// scores; one workgroup per (row, chunk of 16384 positions) writes the chunk's
+// keys at or above it, in position order, to the chunk's region of the
+// workspace; then one workgroup per row gathers them, finds the exact K-th
+// largest key among them and writes the kept keys' cache rows in position
+// order.  A row whose sample misses (fewer than K keys reach the threshold, or
+// more than the candidate buffer holds, as with heavy ties) is done by four
+// 8-bit radix passes over the whole row.
 #include <algorithm>
 
 #include "device_common.h"
@@ -318,10 +320,12 @@ __device__ void topk_by_radix_passes(const IndexerArgs& a, int r, const float* s
   }
 }
 
-constexpr int kSegSteps = 8;                                   // 16-byte groups per thread per segment
-constexpr int kWaveSpan = kSegSteps * 256;                      // positions per wave per segment
-constexpr int kSeg = (kTopkThreads / 64) * kWaveSpan;           // positions per segment: 32768
-static_assert(kIdxSample % kTopkThreads == 0 && kIdxSample <= kIdxCandCap, "sample layout");
+constexpr int kChunkShift = 14;                                // log2(kIdxChunk)
+constexpr int kCSteps = kIdxChunk / (4 * kTopkThreads);        // 16-byte groups per thread per chunk
+constexpr int kCWaveSpan = kIdxChunk / (kTopkThreads / 64);    // positions per wave per chunk
+static_assert((1 << kChunkShift) == kIdxChunk && kCSteps == 4 && kCWaveSpan == 256 * kCSteps, "chunk layout");
+static_assert(kIdxSample == 4 * kTopkThreads && kIdxMaxChunks <= kTopkThreads, "one chunk per thread");
+static_assert(kIdxCandCap % kTopkThreads == 0, "whole candidates per thread");
 
 // The key that `rank` keys of keys[0 .. S) reach (the rank-th largest): four 8-bit
 // radix passes from the top.  Requires 1 <= rank <= S.
@@ -347,35 +351,145 @@ __device__ __forceinline__ uint32_t select_rank(const uint32_t* keys, int S, int
   return pre;
 }
 
-// One 1024-thread workgroup per row.
-//  (1) The row's first 32768 scores are requested into registers (wave w takes
-//      positions 2048 w .. 2048 w + 2047 of a segment, 256 per step: lane l the
-//      four from 4 l), and with them a sample of the row: 256 runs of 16
-//      consecutive scores spread evenly over it (the whole row when n <= 4096).
-//  (2) A threshold from the sample: with the whole row as the sample, the K-th
-//      largest key itself; otherwise the key that K's share of the sample plus
-//      four standard deviations and 8 reach, so that at least K keys of the row
-//      lie at or above it unless the sample is far from typical.
-//  (3) One pass over the row moves the keys at or above the threshold, with
-//      their positions, into LDS in position order (per-wave counts, then
-//      ballot ranks inside each step).
-//  (4) Among these candidates the exact K-th largest key T (four 8-bit radix
-//      passes); the keys above T are kept, and of those equal to T the
-//      lowest-positioned ones; each thread writes the cache rows of a run of
-//      consecutive candidates from its offset.
-// A row with fewer than K or more than kIdxCandCap candidates is done instead by
-// radix passes over the whole row.
-__global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerArgs a) {
-  __shared__ uint32_t ck[kIdxCandCap];  // candidates' keys in position order; the sample before them
-  __shared__ int32_t cpos[kIdxCandCap];
-  __shared__ int hist[256];
+// The row's threshold key, the same in every workgroup of the row: from a sample of
+// S = min(n, 4096) scores (the whole row when n <= 4096, else 256 runs of 16
+// consecutive scores spread evenly over the row), the lower edge of the 12-bit key bin
+// that holds the sample's rank-th largest key.  With the whole row as the sample,
+// rank = K; otherwise K's share of the sample plus four standard deviations and 8, so
+// that at least K keys of the row reach the threshold unless the sample is far from
+// typical.  hist holds 4096 ints.
+__device__ __forceinline__ uint32_t sample_threshold(const float* s, int64_t n, int K, int* hist, int* scan,
+                                                     int* pick) {
+  const int tid = threadIdx.x;
+  const int S = n < kIdxSample ? static_cast<int>(n) : kIdxSample;
+  uint32_t smp[kIdxSample / kTopkThreads];
+#pragma unroll
+  for (int j = 0; j < kIdxSample / kTopkThreads; ++j) {
+    const int i = tid + j * kTopkThreads;
+    const int64_t p = S < n ? (i >> 4) * (n >> 8) + (i & 15) : i;  // n > 4096: the runs are n / 256 apart
+    smp[j] = i < S ? score_key(s[p]) : 0u;
+  }
+  int rank = K;
+  if (S < n) {
+    const double f = static_cast<double>(K) / static_cast<double>(n);
+    const double m = S * f;
+    rank = min(S, static_cast<int>(ceil(m + 4.0 * sqrt(m * (1.0 - f)) + 8.0)));
+  }
+#pragma unroll
+  for (int j = 0; j < kIdxSample / kTopkThreads; ++j) hist[tid * 4 + j] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kIdxSample / kTopkThreads; ++j)
+    if (tid + j * kTopkThreads < S) atomicAdd(&hist[smp[j] >> 20], 1);
+  __syncthreads();
+  // thread t takes bins 4095 - 4t .. 4092 - 4t (from the top)
+  int h[4], sum = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    h[j] = hist[4095 - (tid * 4 + j)];
+    sum += h[j];
+  }
+  int tot;
+  int above = block_exclusive_scan(sum, scan, &tot);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (above < rank && above + h[j] >= rank) pick[0] = 4095 - (tid * 4 + j);
+    above += h[j];
+  }
+  __syncthreads();
+  const uint32_t thr = static_cast<uint32_t>(pick[0]) << 20;
+  __syncthreads();
+  return thr;
+}
+
+// (1) One 1024-thread workgroup per (row, chunk of 16384 positions): wave w takes
+// positions 1024 w .. 1024 w + 1023 of the chunk, 256 per step (lane l the four from
+// 4 l).  It writes the chunk's keys at or above the row's threshold, with their
+// positions, in position order (per-wave counts, then ballot ranks inside each step)
+// into the chunk's own region of the workspace, and their number beside it.
+__global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexerArgs a) {
+  __shared__ int hist[kIdxSample];
   __shared__ int scan[kTopkThreads / 64];
   __shared__ int wcnt[kTopkThreads / 64];
   __shared__ int pick[3];
   const int row = blockIdx.x;
+  const int c = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  int r;
+  const int64_t n = row_keys(a, row, &r);
+  if (n <= a.topk) return;
+  const int nch = static_cast<int>((n + kIdxChunk - 1) >> kChunkShift);
+  if (c >= nch) return;
+  const float* s = a.scores + static_cast<int64_t>(row) * a.ld_scores;
+  const int64_t p0 = (static_cast<int64_t>(c) << kChunkShift) + wave * kCWaveSpan + 4 * lane;
+  // score rows are padded to 64 floats, so a 16-byte group that starts below n lies in the row
+  f32x4 v[kCSteps];
+#pragma unroll
+  for (int j = 0; j < kCSteps; ++j)
+    v[j] = p0 + j * 256 < n ? *reinterpret_cast<const f32x4*>(s + p0 + j * 256) : f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t thr = sample_threshold(s, n, a.topk, hist, scan, pick);
+  uint32_t sel = 0;  // bit 4 j + e: position p0 + 256 j + e is a candidate
+#pragma unroll
+  for (int j = 0; j < kCSteps; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      sel |= p0 + j * 256 + e < n && score_key(v[j][e]) >= thr ? 1u << (4 * j + e) : 0u;
+  int w_cnt = 0;
+#pragma unroll
+  for (int b = 0; b < 4 * kCSteps; ++b) w_cnt += __popcll(__ballot((sel >> b) & 1u));
+  if (lane == 0) wcnt[wave] = w_cnt;
+  __syncthreads();
+  int o = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kTopkThreads / 64; ++w) {
+    const int cw = wcnt[w];
+    o += w < wave ? cw : 0;
+    tot += cw;
+  }
+  const int64_t chunk_id = static_cast<int64_t>(row) * a.nch_max + c;
+  uint2* reg = a.ws_cand + chunk_id * kIdxCandCap;
+#pragma unroll
+  for (int j = 0; j < kCSteps; ++j) {
+    int below = 0, step = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint64_t bal = __ballot((sel >> (4 * j + e)) & 1u);
+      below += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                         __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
+      step += __popcll(bal);
+    }
+    int idx = o + below;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if ((sel >> (4 * j + e)) & 1u) {
+        if (idx < kIdxCandCap)
+          reg[idx] = make_uint2(score_key(v[j][e]), static_cast<uint32_t>(p0 + j * 256 + e));
+        ++idx;
+      }
+    }
+    o += step;
+  }
+  if (tid == 0) a.ws_count[chunk_id] = tot;
+}
+
+// (2) One 1024-thread workgroup per row: the chunks' candidates in position order
+// into LDS (each chunk's count, then an exclusive scan over the chunks gives where
+// its candidates start), the exact K-th largest key T among them (four 8-bit radix
+// passes), and the kept keys' cache rows in position order: the keys above T, and of
+// those equal to T the lowest-positioned ones.  A row whose candidates number fewer
+// than K or more than kIdxCandCap (in total or in one chunk) is done by radix passes
+// over the whole row.  Rows with n <= K write their n slots and the -1 padding.
+__global__ __launch_bounds__(kTopkThreads) void topk_finish_kernel(IndexerArgs a) {
+  __shared__ uint32_t ck[kIdxCandCap];
+  __shared__ int32_t cpos[kIdxCandCap];
+  __shared__ int coff[kIdxMaxChunks];
+  __shared__ int hist[256];
+  __shared__ int scan[kTopkThreads / 64];
+  __shared__ int pick[3];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
   int r;
   const int64_t n = row_keys(a, row, &r);
   const int K = a.topk;
@@ -385,96 +499,45 @@ __global__ __launch_bounds__(kTopkThreads) void indexer_topk_kernel(IndexerArgs 
     return;
   }
   const float* s = a.scores + static_cast<int64_t>(row) * a.ld_scores;
-  // (1) score rows are padded to 64 floats, so a 16-byte group that starts below n lies in the row
-  f32x4 v[kSegSteps];
-  auto load_seg = [&](int64_t base) {
-#pragma unroll
-    for (int j = 0; j < kSegSteps; ++j) {
-      const int64_t p = base + wave * kWaveSpan + j * 256 + 4 * lane;
-      v[j] = p < n ? *reinterpret_cast<const f32x4*>(s + p) : f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  };
-  load_seg(0);
-  const int S = n < kIdxSample ? static_cast<int>(n) : kIdxSample;
-  uint32_t smp[kIdxSample / kTopkThreads];
-#pragma unroll
-  for (int j = 0; j < kIdxSample / kTopkThreads; ++j) {
-    const int i = tid + j * kTopkThreads;
-    // 256 runs of 16 consecutive positions, the runs n / 256 apart (n > 4096 here, so the
-    // runs do not overlap); the whole row when it is no longer than the sample
-    const int64_t p = S < n ? (i >> 4) * (n >> 8) + (i & 15) : i;
-    smp[j] = i < S ? score_key(s[p]) : 0u;
-  }
-#pragma unroll
-  for (int j = 0; j < kIdxSample / kTopkThreads; ++j) {
-    const int i = tid + j * kTopkThreads;
-    if (i < S) ck[i] = smp[j];
-  }
-  // (2)
-  int rank = K;
-  if (S < n) {
-    const double f = static_cast<double>(K) / static_cast<double>(n);
-    const double m = S * f;
-    rank = min(S, static_cast<int>(ceil(m + 4.0 * sqrt(m * (1.0 - f)) + 8.0)));
-  }
-  __syncthreads();
-  const uint32_t thr = select_rank(ck, S, rank, hist, scan, pick);  // ends with a barrier
-  // (3)
-  int total = 0;
-#pragma unroll 1
-  for (int64_t base = 0; base < n; base += kSeg) {
-    if (base > 0) load_seg(base);
-    int w_cnt = 0;
-#pragma unroll
-    for (int j = 0; j < kSegSteps; ++j) {
-      const int64_t p = base + wave * kWaveSpan + j * 256 + 4 * lane;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) w_cnt += __popcll(__ballot(p + e < n && score_key(v[j][e]) >= thr));
-    }
-    if (lane == 0) wcnt[wave] = w_cnt;
-    __syncthreads();
-    int o = total, seg_total = 0;
-#pragma unroll
-    for (int w = 0; w < kTopkThreads / 64; ++w) {
-      const int c = wcnt[w];
-      o += w < wave ? c : 0;
-      seg_total += c;
-    }
-#pragma unroll
-    for (int j = 0; j < kSegSteps; ++j) {
-      const int64_t p = base + wave * kWaveSpan + j * 256 + 4 * lane;
-      bool k[4];
-      int below = 0, step = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        k[e] = p + e < n && score_key(v[j][e]) >= thr;
-        const uint64_t bal = __ballot(k[e]);
-        below += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
-                                           __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
-        step += __popcll(bal);
-      }
-      int idx = o + below;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (k[e]) {
-          if (idx < kIdxCandCap) {
-            ck[idx] = score_key(v[j][e]);
-            cpos[idx] = static_cast<int32_t>(p + e);
-          }
-          ++idx;
-        }
-      }
-      o += step;
-    }
-    total += seg_total;
-    __syncthreads();  // wcnt is rewritten by the next segment; the candidates are complete
-  }
-  if (total < K || total > kIdxCandCap) {
+  const int nch = static_cast<int>((n + kIdxChunk - 1) >> kChunkShift);
+  const int64_t chunk0 = static_cast<int64_t>(row) * a.nch_max;
+  const int cnt = tid < nch ? a.ws_count[chunk0 + tid] : 0;
+  int total;
+  const int off = block_exclusive_scan(cnt, scan, &total);
+  const bool over = __syncthreads_or(cnt > kIdxCandCap);
+  if (over || total < K || total > kIdxCandCap) {
     topk_by_radix_passes(a, r, s, n, K, out, hist, scan, pick);
     return;
   }
-  // (4)
+  if (tid < nch) coff[tid] = off;
+  __syncthreads();
+  // candidate j (position order) is entry j - coff[c] of chunk c, the last chunk with coff[c] <= j
+  constexpr int PER = kIdxCandCap / kTopkThreads;
+  uint2 x[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int j = tid + u * kTopkThreads;
+    if (j < total) {
+      int lo = 0, hi = nch;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (coff[mid] <= j) lo = mid;
+        else hi = mid;
+      }
+      x[u] = a.ws_cand[(chunk0 + lo) * kIdxCandCap + (j - coff[lo])];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int j = tid + u * kTopkThreads;
+    if (j < total) {
+      ck[j] = x[u].x;
+      cpos[j] = static_cast<int32_t>(x[u].y);
+    }
+  }
+  __syncthreads();
   const uint32_t T = select_rank(ck, total, K, hist, scan, pick);
+  // thread t takes the candidates t R .. t R + R - 1
   const int R = (total + kTopkThreads - 1) / kTopkThreads;
   const int j0 = min(tid * R, total), j1 = min(j0 + R, total);
   int gt = 0, eq = 0;
@@ -524,7 +587,9 @@ hipError_t launch_indexer(const IndexerArgs& a, bool bf16, bool scores_only, hip
     if (e != hipSuccess) return e;
   }
   if (scores_only) return hipSuccess;
-  indexer_topk_kernel<<<static_cast<unsigned>(a.num_rows), kTopkThreads, 0, st>>>(a);
+  topk_candidates_kernel<<<dim3(static_cast<unsigned>(a.num_rows), static_cast<unsigned>(a.nch_max)), kTopkThreads, 0,
+                           st>>>(a);
+  topk_finish_kernel<<<static_cast<unsigned>(a.num_rows), kTopkThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -211,6 +211,20 @@ def test_indexer_validates_before_touching_the_gpu():
     assert lib.bsa_indexer_topk(ctypes.byref(a), None) == L.BSA_ERR_INVALID_ARGUMENT  # NULL arrays
     assert b"16-byte aligned" in lib.bsa_last_error()
     assert lib.bsa_indexer_topk(None, None) == L.BSA_ERR_INVALID_ARGUMENT
+    # the workspace: per (row, chunk of 16384 positions) a count and 8192 candidates
+    ws = lib.bsa_indexer_workspace_size
+    assert ws(0, 100) == 0 and ws(3, 0) == 0
+    assert ws(1, 16384) == 256 + 8192 * 8 and ws(2, 16385) == 256 + 4 * 8192 * 8
+    a = base()
+    a.num_rows = 2
+    # host-side checks up to the workspace (16-byte aligned fake device addresses, never dereferenced)
+    for f in ("q", "key_cache", "scores", "block_table", "req_row_ptr", "ctx_len", "req_kv_len", "out"):
+        setattr(a, f, 1 << 20)
+    assert lib.bsa_indexer_topk(ctypes.byref(a), None) == L.BSA_ERR_INVALID_ARGUMENT
+    assert b"workspace" in lib.bsa_last_error()
+    a.workspace, a.workspace_bytes = 1 << 20, ws(2, 64) - 1
+    assert lib.bsa_indexer_topk(ctypes.byref(a), None) == L.BSA_ERR_INVALID_ARGUMENT
+    assert b"workspace" in lib.bsa_last_error()
     for field, value in (("head_dim", 96), ("topk", 0), ("topk", (1 << 24) + 1), ("num_reqs", 0), ("page_size", 0), ("max_pages", 0),
                          ("num_slots", 0), ("max_ctx", 0), ("dtype", L.BSA_FP8_E4M3), ("q_stride", 100),
                          ("k_stride", 64), ("max_ctx", 1 << 25)):
