@@ -626,7 +626,7 @@ def run_indexer(args, dev) -> int:
     step()
     torch.cuda.synchronize()
     log(f"[bench] indexer: {len(step_ms) * CHUNK} steps: {ms_per_step:.4f} ms/step wall; GPU step median "
-        f"{gpu_ms:.4f} ms (scores kernel {sc_med:.4f} ms, the three Top-K kernels {gpu_ms - sc_med:.4f} ms)")
+        f"{gpu_ms:.4f} ms (scores kernel {sc_med:.4f} ms, the two Top-K kernels {gpu_ms - sc_med:.4f} ms)")
     if args.calibration_copy > 0:
         n = args.calibration_copy << 20
         src = torch.ones(n, dtype=torch.uint8, device=dev)
