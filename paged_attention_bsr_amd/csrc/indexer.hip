@@ -327,26 +327,58 @@ static_assert((1 << kChunkShift) == kIdxChunk && kCSteps == 4 && kCWaveSpan == 2
 static_assert(kIdxSample == 4 * kTopkThreads && kIdxMaxChunks <= kTopkThreads, "one chunk per thread");
 static_assert(kIdxCandCap % kTopkThreads == 0, "whole candidates per thread");
 
-// The key that `rank` keys of keys[0 .. S) reach (the rank-th largest): four 8-bit
-// radix passes from the top.  Requires 1 <= rank <= S.
+// The key that `rank` keys of keys[0 .. S) reach (the rank-th largest).  The bits all
+// keys share (above the highest bit where the smallest and the largest differ) are
+// fixed first; the rest are resolved by 8-bit radix passes from the top (so the first
+// histogram spreads over its bins even when the keys lie close together, as the
+// candidates above a threshold do).  Requires 1 <= rank <= S.
 __device__ __forceinline__ uint32_t select_rank(const uint32_t* keys, int S, int rank, int* hist, int* scan,
                                                 int* pick) {
   const int tid = threadIdx.x;
-  uint32_t pre = 0, msk = 0;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int i = tid; i < S; i += kTopkThreads) {
+    lo = min(lo, keys[i]);
+    hi = max(hi, keys[i]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), off)));
+    hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), off)));
+  }
+  if (lane == 0) {
+    hist[2 * wave] = static_cast<int>(lo);
+    hist[2 * wave + 1] = static_cast<int>(hi);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kTopkThreads / 64; ++w) {
+    lo = min(lo, static_cast<uint32_t>(hist[2 * w]));
+    hi = max(hi, static_cast<uint32_t>(hist[2 * w + 1]));
+  }
+  __syncthreads();
+  if (lo == hi) return lo;
+  int bits = 32 - __clz(static_cast<int>(lo ^ hi));  // bits [0, bits) still to decide
+  const uint32_t low_mask = bits == 32 ? 0xFFFFFFFFu : (1u << bits) - 1u;
+  uint32_t pre = lo & ~low_mask, msk = ~low_mask;
   int need = rank, cnt;
 #pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
+  while (bits > 0) {
+    const int w = bits < 8 ? bits : 8;
+    const int shift = bits - w;
+    const int nb = 1 << w;
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
     for (int i = tid; i < S; i += kTopkThreads) {
       const uint32_t u = keys[i];
-      if ((u & msk) == pre) atomicAdd(&hist[(u >> shift) & 255], 1);
+      if ((u & msk) == pre) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1);
     }
     __syncthreads();
-    const int d = pick_bin(tid < 256 ? hist[255 - tid] : 0, 255 - tid, need, &cnt, scan, pick);
+    const int d = pick_bin(tid < nb ? hist[nb - 1 - tid] : 0, nb - 1 - tid, need, &cnt, scan, pick);
     pre |= static_cast<uint32_t>(d) << shift;
-    msk |= 0xFFu << shift;
+    msk |= static_cast<uint32_t>(nb - 1) << shift;
+    bits = shift;
   }
   return pre;
 }
