@@ -8,13 +8,13 @@
 // Scores: a workgroup takes one request (grid x) and 256 of its key positions
 // (grid y; four waves of 64): it loads the keys once into registers, stages
 // the request's query rows in LDS 64 at a time, and runs them against the
-// keys 16 at a time.  The dot products run on
-// v_mfma_f32_16x16x32 with the query rows as the A operand (lane l: row
-// l % 16, dims 8 (l / 16) .. + 7 of the k-step) and the keys as B (the same
-// dims of key l % 16), so lane l ends with rows 4 (l / 16) + v of key l % 16
-// and the 16 lanes of a group store 16 consecutive scores of one row.  Key
-// rows are fetched through the block table with 16-byte loads; a page id
-// outside the cache reads as a zero key.
+// keys 16 at a time.  The dot products run on v_mfma_f32_16x16x32 with the
+// query rows as the A operand (lane l: row l % 16, dims 8 (l / 16) .. + 7 of
+// the k-step) and the keys as B (the same dims of key l % 16), so lane l ends
+// with rows 4 (l / 16) + v of key l % 16 and the 16 lanes of a group store 16
+// consecutive scores of one row.  Key rows are fetched through the block
+// table with 16-byte loads; a position whose page is missing or outside the
+// cache scores as a zero key.
 //
 // Top-K: a score maps to an unsigned key that orders like the float (sign bit
 // flipped for positives, all bits for negatives; -0 becomes +0).  Every
