@@ -416,7 +416,7 @@ bsa_status_t bsa_mla_rope_quantize_fp8(const bsa_rope_quant_t* args, void* strea
  *                Not read when scores_only is set (may then be NULL).
  *   scores_only  non-zero: compute the scores only
  * Sizes: num_reqs >= 1, head_dim in {64, 128, 256}, page_size >= 1, max_pages >= 1,
- * 1 <= topk <= 2^24, 1 <= num_slots < 2^31, 1 <= max_ctx <= 16776960, strides multiples of
+ * 1 <= topk <= 2^24, 1 <= num_slots < 2^31, 1 <= max_ctx <= 8388480, strides multiples of
  * 8 and >= head_dim.
  * Runs three kernels on `stream` (scores; candidates per chunk of 16384 positions above a
  * threshold taken from a sample of the row's scores; the exact selection per row);

@@ -409,7 +409,7 @@ bsa_status_t bsa_indexer_topk(const bsa_indexer_t* p, void* stream) {
   const int64_t ks = p->k_stride != 0 ? p->k_stride : p->head_dim;
   if (qs < p->head_dim || ks < p->head_dim || qs % 8 != 0 || ks % 8 != 0)
     return set_err(BSA_ERR_INVALID_ARGUMENT, "strides must be multiples of 8 and at least head_dim");
-  if (p->max_ctx > 16776960) return set_err(BSA_ERR_INVALID_ARGUMENT, "max_ctx must be at most 16776960");
+  if (p->max_ctx > 8388480) return set_err(BSA_ERR_INVALID_ARGUMENT, "max_ctx must be at most 8388480");
   if (p->num_rows == 0) return BSA_OK;
   if (!p->q || !p->key_cache || reinterpret_cast<uintptr_t>(p->q) % 16 != 0 ||
       reinterpret_cast<uintptr_t>(p->key_cache) % 16 != 0)

@@ -14,7 +14,7 @@ namespace bsa {
 constexpr int kIdxChunk = 16384;
 constexpr int kIdxSample = 4096;
 constexpr int kIdxCandCap = 8192;
-constexpr int kIdxMaxChunks = 1024;  // max_ctx <= 16776960 spans at most 1024 chunks
+constexpr int kIdxMaxChunks = 1024;  // max_ctx <= 8388480 (65535 score workgroups of 128 keys) spans at most 512 chunks
 
 // Workspace: per (row, chunk) a candidate count, then per (row, chunk) a region of
 // kIdxCandCap (key, position) pairs.  Nothing in it needs initialising.

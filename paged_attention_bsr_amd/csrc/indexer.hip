@@ -5,8 +5,8 @@
 // int32 physical cache rows -- is the index list that index-selected sparse
 // MLA decode consumes.
 //
-// Scores: a workgroup takes one request (grid x) and 256 of its key positions
-// (grid y; four waves of 64): it loads the keys once into registers, stages
+// Scores: a workgroup takes one request (grid x) and 128 of its key positions
+// (grid y; four waves of 32): it loads the keys once into registers, stages
 // the request's query rows in LDS 64 at a time, and runs them against the
 // keys 16 at a time.  The dot products run on v_mfma_f32_16x16x32 with the
 // query rows as the A operand (lane l: row l % 16, dims 8 (l / 16) .. + 7 of
@@ -36,7 +36,7 @@ namespace bsa {
 namespace {
 
 constexpr int kRowsPerGroup = 16;
-constexpr int kKeyBlocks = 4;               // 16-key blocks per wave
+constexpr int kKeyBlocks = 2;               // 16-key blocks per wave
 constexpr int kQRows = 64;                  // query rows staged in LDS at a time
 constexpr int kKeysPerWg = 4 * 16 * kKeyBlocks;
 constexpr int kScoreThreads = 256;
