@@ -24,8 +24,8 @@
 // workspace; then one workgroup per row gathers them, finds the exact K-th
 // largest key among them and writes the kept keys' cache rows in position
 // order.  A row whose sample misses (fewer than K keys reach the threshold, or
-// more than the candidate buffer holds, as with heavy ties) is done by four
-// 8-bit radix passes over the whole row.
+// more than the candidate buffer holds, as with heavy ties) is done by radix
+// passes over the whole row in one workgroup.
 #include <algorithm>
 
 #include "device_common.h"
@@ -267,31 +267,61 @@ __device__ __forceinline__ int64_t row_keys(const IndexerArgs& a, int row, int* 
   return n;
 }
 
-// Top-K of one row by four 8-bit radix passes over the scores in global
-// memory and per-thread contiguous segments for the ordered output: one
-// workgroup does the whole row (the path for a row whose bin of the K-th
-// largest key holds more keys than the candidate buffer, i.e. heavy ties).
+// Top-K of one row by radix passes over the scores in global memory and
+// per-thread contiguous segments for the ordered output: one workgroup does the
+// whole row (the path for a row whose sample misses, e.g. heavy ties).  The
+// bits that all the row's keys share (above the highest bit where the smallest
+// and the largest differ) are fixed by one pass first, so a row of equal scores
+// needs no radix pass; the rest are resolved 8 bits at a time from the top.
 __device__ void topk_by_radix_passes(const IndexerArgs& a, int r, const float* s, int64_t n, int K, int32_t* out,
                                      int* hist, int* scan, int* pick) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0, mask = 0;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int64_t i = tid; i < n; i += kTopkThreads) {
+    const uint32_t u = score_key(s[i]);
+    lo = min(lo, u);
+    hi = max(hi, u);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), off)));
+    hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), off)));
+  }
+  if (lane == 0) {
+    hist[2 * wave] = static_cast<int>(lo);
+    hist[2 * wave + 1] = static_cast<int>(hi);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kTopkThreads / 64; ++w) {
+    lo = min(lo, static_cast<uint32_t>(hist[2 * w]));
+    hi = max(hi, static_cast<uint32_t>(hist[2 * w + 1]));
+  }
+  __syncthreads();
+  int bits = lo == hi ? 0 : 32 - __clz(static_cast<int>(lo ^ hi));  // bits [0, bits) still to decide
+  const uint32_t low_mask = bits == 32 ? 0xFFFFFFFFu : (1u << bits) - 1u;
+  uint32_t prefix = lo & ~low_mask, mask = ~low_mask;
   int need = K;  // keys still to take among those matching prefix
 #pragma unroll 1
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
+  while (bits > 0) {
+    const int w = bits < 8 ? bits : 8;
+    const int shift = bits - w;
+    const int nb = 1 << w;
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
     for (int64_t i = tid; i < n; i += kTopkThreads) {
       const uint32_t u = score_key(s[i]);
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1);
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1);
     }
     __syncthreads();
     // the digit whose bin holds the need-th largest key, bins taken from the top
-    const int d = 255 - tid;
     int cnt;
-    const int digit = pick_bin(tid < 256 ? hist[d] : 0, d, need, &cnt, scan, pick);
+    const int digit = pick_bin(tid < nb ? hist[nb - 1 - tid] : 0, nb - 1 - tid, need, &cnt, scan, pick);
     prefix |= static_cast<uint32_t>(digit) << shift;
-    mask |= 0xFFu << shift;
+    mask |= static_cast<uint32_t>(nb - 1) << shift;
+    bits = shift;
   }
   const uint32_t T = prefix;  // the K-th largest key; `need` keys equal to it are kept
   const int64_t seg = (n + kTopkThreads - 1) / kTopkThreads;
