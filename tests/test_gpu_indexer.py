@@ -204,3 +204,28 @@ def test_sample_that_misses_takes_the_slow_path():
     args = _oracle_inputs(w)
     assert np.array_equal(scores[0, :n], oracle.indexer_scores(*args)[0])
     assert np.array_equal(out, oracle.indexer_topk(*args, k))
+
+
+# the sampled threshold across K / n: tiny K on long rows (the margin's +8 dominates), K near n
+# (the threshold admits most of the row), and K so close to n that the candidates overflow the
+# buffer (the row takes the slow path)
+REGIMES = {
+    "k16_long_rows": (31, 4, 70000, 16, 60000, 70000),
+    "k6000_of_8000": (32, 3, 8000, 6000, 8000, 8000),
+    "k8000_of_9000": (33, 2, 9000, 8000, 9000, 9000),
+    "k2048_mixed": (34, 24, 40000, 2048, 100, 40000),
+}
+
+
+@pytest.mark.parametrize("name", sorted(REGIMES))
+def test_sampled_threshold_regimes(name):
+    seed, rows, cache, k, lo, hi = REGIMES[name]
+    w = W.indexer(seed=seed, num_tokens=rows, cache_rows=cache, num_reqs=1, page_size=32, head_dim=128, topk=k,
+                  min_ctx=lo, max_ctx=hi, integer=True)
+    say(f"[indexer] threshold regime {name}")
+    out, _ = _run(w)
+    assert np.array_equal(out, oracle.indexer_topk(*_oracle_inputs(w), k))
+    wn = W.indexer(seed=seed, num_tokens=rows, cache_rows=cache, num_reqs=1, page_size=32, head_dim=128, topk=k,
+                   min_ctx=lo, max_ctx=hi)
+    out_n, scores_n = _run(wn)
+    _check_within_bound(wn, out_n, scores_n, range(rows))
