@@ -406,8 +406,8 @@ bsa_status_t bsa_mla_rope_quantize_fp8(const bsa_rope_quant_t* args, void* strea
  *                request r are req_row_ptr[r] .. req_row_ptr[r + 1] - 1
  *   ctx_len      device int32 [num_rows]; req_kv_len device int32 [num_reqs]
  *   scores       device float32 [num_rows][ld], ld = max_ctx rounded up to a multiple of 64,
- *                16-byte aligned, caller-owned workspace; afterwards scores[row][p] holds
- *                score(row, p) for p < n
+ *                16-byte aligned, caller-owned output: afterwards scores[row][p] holds
+ *                score(row, p) for p < n (the rest of the row is unspecified)
  *   out          device int32 [num_rows][topk]
  *   workspace    device, >= bsa_indexer_workspace_size(num_rows, max_ctx) bytes, 256-byte
  *                aligned, caller-owned scratch of the Top-K step (per chunk of 16384
