@@ -229,3 +229,13 @@ def test_sampled_threshold_regimes(name):
                    min_ctx=lo, max_ctx=hi)
     out_n, scores_n = _run(wn)
     _check_within_bound(wn, out_n, scores_n, range(rows))
+
+
+def test_many_requests_short_rows():
+    # a decode-like batch: 2048 rows over 512 requests, contexts up to 3000, top 256 (many rows
+    # keep all their keys and pad, the others select from one chunk)
+    w = W.indexer(seed=41, num_tokens=2048, cache_rows=512 * 3072, num_reqs=512, page_size=64, head_dim=64,
+                  topk=256, min_ctx=1, max_ctx=3000, integer=True)
+    say("[indexer] 2048 rows over 512 requests")
+    out, _ = _run(w)
+    assert np.array_equal(out, oracle.indexer_topk(*_oracle_inputs(w), 256))
