@@ -239,3 +239,16 @@ def test_many_requests_short_rows():
     say("[indexer] 2048 rows over 512 requests")
     out, _ = _run(w)
     assert np.array_equal(out, oracle.indexer_topk(*_oracle_inputs(w), 256))
+
+
+def test_rows_outside_every_request_keep_nothing():
+    # req_row_ptr ends before num_rows: rows 7..9 belong to no request and come back as -1
+    w = W.indexer(seed=43, num_tokens=10, cache_rows=4000, num_reqs=2, page_size=16, head_dim=64, topk=50,
+                  min_ctx=20, max_ctx=2000, integer=True)
+    w["req_row_ptr"] = np.array([0, 3, 7], np.int32)
+    out, _ = _run(w)
+    assert np.all(out[7:] == -1)
+    ctx = np.minimum(w["ctx_len"][:7], np.repeat(w["req_kv_len"], np.diff(w["req_row_ptr"])))
+    ref = oracle.indexer_topk(w["q"].float().numpy()[:7], w["key_cache"].float().numpy(), w["block_table"],
+                              w["page_size"], w["req_row_ptr"], ctx, 50)
+    assert np.array_equal(out[:7], ref)
