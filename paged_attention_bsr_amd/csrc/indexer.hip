@@ -267,22 +267,43 @@ __device__ __forceinline__ int64_t row_keys(const IndexerArgs& a, int row, int* 
   return n;
 }
 
-// Top-K of one row by radix passes over the scores in global memory and
-// per-thread contiguous segments for the ordered output: one workgroup does the
-// whole row (the path for a row whose sample misses, e.g. heavy ties).  The
-// bits that all the row's keys share (above the highest bit where the smallest
-// and the largest differ) are fixed by one pass first, so a row of equal scores
-// needs no radix pass; the rest are resolved 8 bits at a time from the top.
+// Top-K of one row in one workgroup, for a row whose sample misses (e.g.
+// heavy ties).  Every pass reads the row in steps of 4096 positions: wave w
+// takes positions 256 w .. 256 w + 255 of a step (lane l the four from 4 l),
+// with 16-byte loads.  The bits that all the row's keys share (above the
+// highest bit where the smallest and the largest differ) are fixed by a first
+// pass, so a row of equal scores needs no radix pass; the rest are resolved 8
+// bits at a time from the top, giving the K-th largest key T and the number of
+// keys equal to T to keep.  The output pass ranks the keys equal to T in
+// position order (ballots inside a wave, wave totals through LDS, a running
+// count across steps), keeps the lowest ones, and writes every kept key's
+// cache row at its rank among the kept keys.
 __device__ void topk_by_radix_passes(const IndexerArgs& a, int r, const float* s, int64_t n, int K, int32_t* out,
                                      int* hist, int* scan, int* pick) {
+  constexpr int kStep = 4096;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  // thread's 4 keys of the step at `base` (positions p0 + e); keys past n read as 0
+  auto load_step = [&](int64_t base, uint32_t (&u)[4], int64_t& p0) {
+    p0 = base + wave * 256 + 4 * lane;
+    // score rows are padded to 64 floats: a 16-byte group that starts below n lies in the row
+    const f32x4 v = p0 < n ? *reinterpret_cast<const f32x4*>(s + p0) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = score_key(v[e]);
+  };
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  for (int64_t i = tid; i < n; i += kTopkThreads) {
-    const uint32_t u = score_key(s[i]);
-    lo = min(lo, u);
-    hi = max(hi, u);
+#pragma unroll 1
+  for (int64_t base = 0; base < n; base += kStep) {
+    uint32_t u[4];
+    int64_t p0;
+    load_step(base, u, p0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (p0 + i < n) {
+        lo = min(lo, u[i]);
+        hi = max(hi, u[i]);
+      }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -311,9 +332,14 @@ __device__ void topk_by_radix_passes(const IndexerArgs& a, int r, const float* s
     const int nb = 1 << w;
     if (tid < 256) hist[tid] = 0;
     __syncthreads();
-    for (int64_t i = tid; i < n; i += kTopkThreads) {
-      const uint32_t u = score_key(s[i]);
-      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1);
+#pragma unroll 1
+    for (int64_t base = 0; base < n; base += kStep) {
+      uint32_t u[4];
+      int64_t p0;
+      load_step(base, u, p0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (p0 + i < n && (u[i] & mask) == prefix) atomicAdd(&hist[(u[i] >> shift) & (nb - 1)], 1);
     }
     __syncthreads();
     // the digit whose bin holds the need-th largest key, bins taken from the top
@@ -323,30 +349,73 @@ __device__ void topk_by_radix_passes(const IndexerArgs& a, int r, const float* s
     mask |= static_cast<uint32_t>(nb - 1) << shift;
     bits = shift;
   }
-  const uint32_t T = prefix;  // the K-th largest key; `need` keys equal to it are kept
-  const int64_t seg = (n + kTopkThreads - 1) / kTopkThreads;
-  const int64_t b = tid * seg < n ? tid * seg : n;
-  const int64_t e = b + seg < n ? b + seg : n;
-  int gt = 0, eq = 0;
-  for (int64_t i = b; i < e; ++i) {
-    const uint32_t u = score_key(s[i]);
-    gt += u > T;
-    eq += u == T;
-  }
-  int tot;
-  const int eq_before = block_exclusive_scan(eq, scan, &tot);
-  int eq_take = need - eq_before;
-  eq_take = eq_take < 0 ? 0 : (eq_take > eq ? eq : eq_take);
-  const int out0 = block_exclusive_scan(gt + eq_take, scan, &tot);
-  int o = out0, taken = 0;
-  for (int64_t i = b; i < e; ++i) {
-    const uint32_t u = score_key(s[i]);
-    bool keep = u > T;
-    if (u == T) {
-      keep = taken < eq_take;
-      taken += 1;
+  const uint32_t T = prefix;  // the K-th largest key; the `need` lowest-positioned keys equal to it are kept
+  int* w_eq = hist;           // per wave: keys equal to T in this step
+  int* w_keep = hist + 32;    // per wave: keys kept in this step
+  int eq_base = 0, out_base = 0;  // over the steps before
+#pragma unroll 1
+  for (int64_t base = 0; base < n; base += kStep) {
+    uint32_t u[4];
+    int64_t p0;
+    load_step(base, u, p0);
+    // ranks of the keys equal to T: lanes below, then this lane's earlier keys
+    uint32_t eqm = 0, gtm = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool in = p0 + i < n;
+      eqm |= in && u[i] == T ? 1u << i : 0u;
+      gtm |= in && u[i] > T ? 1u << i : 0u;
     }
-    if (keep && o < K) out[o++] = static_cast<int32_t>(idx_slot(a, r, i));
+    int below = 0, eq_w = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint64_t bal = __ballot((eqm >> e) & 1u);
+      below += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                         __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
+      eq_w += __popcll(bal);
+    }
+    if (lane == 0) w_eq[wave] = eq_w;
+    __syncthreads();
+    int eq_off = eq_base, eq_step = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkThreads / 64; ++w) {
+      eq_off += w < wave ? w_eq[w] : 0;
+      eq_step += w_eq[w];
+    }
+    uint32_t keepm = gtm;
+    int rk = eq_off + below;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((eqm >> e) & 1u) {
+        keepm |= rk < need ? 1u << e : 0u;
+        ++rk;
+      }
+    // output ranks of the kept keys, in the same order
+    int kbelow = 0, keep_w = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint64_t bal = __ballot((keepm >> e) & 1u);
+      kbelow += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                          __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), 0));
+      keep_w += __popcll(bal);
+    }
+    if (lane == 0) w_keep[wave] = keep_w;
+    __syncthreads();
+    int o = out_base + kbelow, keep_step = 0;
+#pragma unroll
+    for (int w = 0; w < kTopkThreads / 64; ++w) {
+      o += w < wave ? w_keep[w] : 0;
+      keep_step += w_keep[w];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if ((keepm >> e) & 1u) {
+        if (o < K) out[o] = static_cast<int32_t>(idx_slot(a, r, p0 + e));
+        ++o;
+      }
+    eq_base += eq_step;
+    out_base += keep_step;
+    __syncthreads();  // w_eq / w_keep are rewritten by the next step
   }
 }
 
