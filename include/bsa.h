@@ -411,7 +411,7 @@ bsa_status_t bsa_mla_rope_quantize_fp8(const bsa_rope_quant_t* args, void* strea
  *   out          device int32 [num_rows][topk]
  *   workspace    device, >= bsa_indexer_workspace_size(num_rows, max_ctx) bytes, 256-byte
  *                aligned, caller-owned scratch of the Top-K step (per chunk of 16384
- *                positions a candidate count and up to 8192 candidates); no initial
+ *                positions a candidate count and up to 12288 candidates); no initial
  *                contents are needed.  Calls that share a workspace must not overlap.
  *                Not read when scores_only is set (may then be NULL).
  *   scores_only  non-zero: compute the scores only

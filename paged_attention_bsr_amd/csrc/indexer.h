@@ -13,7 +13,7 @@ namespace bsa {
 // or above the threshold) per chunk and per row.
 constexpr int kIdxChunk = 16384;
 constexpr int kIdxSample = 4096;
-constexpr int kIdxCandCap = 8192;
+constexpr int kIdxCandCap = 12288;
 constexpr int kIdxMaxChunks = 1024;  // max_ctx <= 8388480 (65535 score workgroups of 128 keys) spans at most 512 chunks
 
 // Workspace: per (row, chunk) a candidate count, then per (row, chunk) a region of

@@ -211,10 +211,10 @@ def test_indexer_validates_before_touching_the_gpu():
     assert lib.bsa_indexer_topk(ctypes.byref(a), None) == L.BSA_ERR_INVALID_ARGUMENT  # NULL arrays
     assert b"16-byte aligned" in lib.bsa_last_error()
     assert lib.bsa_indexer_topk(None, None) == L.BSA_ERR_INVALID_ARGUMENT
-    # the workspace: per (row, chunk of 16384 positions) a count and 8192 candidates
+    # the workspace: per (row, chunk of 16384 positions) a count and 12288 candidates
     ws = lib.bsa_indexer_workspace_size
     assert ws(0, 100) == 0 and ws(3, 0) == 0
-    assert ws(1, 16384) == 256 + 8192 * 8 and ws(2, 16385) == 256 + 4 * 8192 * 8
+    assert ws(1, 16384) == 256 + 12288 * 8 and ws(2, 16385) == 256 + 4 * 12288 * 8
     a = base()
     a.num_rows = 2
     # host-side checks up to the workspace (16-byte aligned fake device addresses, never dereferenced)

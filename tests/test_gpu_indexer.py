@@ -252,3 +252,16 @@ def test_rows_outside_every_request_keep_nothing():
     ref = oracle.indexer_topk(w["q"].float().numpy()[:7], w["key_cache"].float().numpy(), w["block_table"],
                               w["page_size"], w["req_row_ptr"], ctx, 50)
     assert np.array_equal(out[:7], ref)
+
+
+def test_full_size_large_k():
+    # K = 7000 of up to 65536 keys: the candidates above the sampled threshold exceed 8192 and
+    # stay within the buffer
+    w = W.indexer(integer=True, topk=7000)
+    say("[indexer] full size, top 7000")
+    out, _ = _run(w)
+    args = _oracle_inputs(w)
+    rows = [0, 17, 64, 127]
+    ref = oracle.indexer_topk(args[0][rows], args[1], args[2], args[3], np.array([0, len(rows)], np.int32),
+                              args[5][rows], 7000)
+    assert np.array_equal(out[rows], ref)
