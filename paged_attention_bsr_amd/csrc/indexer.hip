@@ -83,13 +83,7 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_scores_kernel(IndexerAr
   __shared__ __attribute__((aligned(16))) T qs[kQRows * LDQ];
   __shared__ int lens[kQRows];
   const int r = blockIdx.x;
-  const int rb = a.req_row_ptr[r];
-  const int re = min(a.req_row_ptr[r + 1], a.num_rows);
-  if (rb >= re) return;
-  const int64_t kv_len = a.req_kv_len[r];
   const int64_t p_wg = static_cast<int64_t>(blockIdx.y) * kKeysPerWg;
-  if (p_wg >= kv_len || p_wg >= a.max_ctx) return;
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -97,27 +91,32 @@ __global__ __launch_bounds__(kScoreThreads) void indexer_scores_kernel(IndexerAr
   const int quad = lane >> 4;
 
   // B: this wave's kKeyBlocks 16-key blocks, loaded once for every query row of the request.
-  // A key past the request or outside the cache loads cache row 0 and its scores are
-  // stored as 0 (a zero key), so nothing waits on the loads before the first product.
-  // All block-table entries are read before any key row is requested (a position
-  // without a page reads entry 0 and is marked as a zero key).
-  v8 kf[kKeyBlocks][KSTEPS];
+  // The block-table entries depend only on the grid position, so they are requested
+  // together with the request's bounds (a position without a page reads entry 0); then
+  // every key row.  A key past the request or outside the cache loads cache row 0 and its
+  // scores are stored as 0 (a zero key), so nothing waits on the key loads before the
+  // first product.
   int32_t page[kKeyBlocks];
   uint32_t pidx[kKeyBlocks];
   uint32_t zero_key = 0;  // bit kb: this lane's key of block kb counts as zeros
 #pragma unroll
   for (int kb = 0; kb < kKeyBlocks; ++kb) {
     const int64_t p = p_wg + wave * (16 * kKeyBlocks) + kb * 16 + c16;
-    pidx[kb] = page_of(a, static_cast<uint32_t>(p));
-    const bool has_page = p < kv_len && static_cast<int32_t>(pidx[kb]) < a.max_pages;
+    pidx[kb] = page_of(a, static_cast<uint32_t>(p < a.max_ctx ? p : 0));
+    const bool has_page = p < a.max_ctx && static_cast<int32_t>(pidx[kb]) < a.max_pages;
     zero_key |= has_page ? 0u : 1u << kb;
     page[kb] = a.block_table[static_cast<int64_t>(r) * a.max_pages + (has_page ? pidx[kb] : 0)];
   }
+  const int rb = a.req_row_ptr[r];
+  const int re = min(a.req_row_ptr[r + 1], a.num_rows);
+  const int64_t kv_len = a.req_kv_len[r];
+  if (rb >= re || p_wg >= kv_len || p_wg >= a.max_ctx) return;
+  v8 kf[kKeyBlocks][KSTEPS];
 #pragma unroll
   for (int kb = 0; kb < kKeyBlocks; ++kb) {
     const int64_t p = p_wg + wave * (16 * kKeyBlocks) + kb * 16 + c16;
     const int64_t slot = static_cast<int64_t>(page[kb]) * a.page_size + (p - static_cast<int64_t>(pidx[kb]) * a.page_size);
-    const bool ok = !((zero_key >> kb) & 1u) && page[kb] >= 0 && slot < a.num_slots;
+    const bool ok = !((zero_key >> kb) & 1u) && p < kv_len && page[kb] >= 0 && slot < a.num_slots;
     zero_key |= ok ? 0u : 1u << kb;
     const T* kp = static_cast<const T*>(a.key_cache) + (ok ? slot : 0) * a.k_stride + quad * 8;
 #pragma unroll
