@@ -12,7 +12,7 @@ namespace bsa {
 // of at most kIdxSample scores per row; at most kIdxCandCap candidates (keys at
 // or above the threshold) per chunk and per row.
 constexpr int kIdxChunk = 16384;
-constexpr int kIdxSample = 4096;
+constexpr int kIdxSample = 2048;
 constexpr int kIdxCandCap = 12288;
 constexpr int kIdxMaxChunks = 1024;  // max_ctx <= 8388480 (65535 score workgroups of 128 keys) spans at most 512 chunks
 

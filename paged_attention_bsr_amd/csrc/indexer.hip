@@ -422,7 +422,7 @@ constexpr int kChunkShift = 14;                                // log2(kIdxChunk
 constexpr int kCSteps = kIdxChunk / (4 * kTopkThreads);        // 16-byte groups per thread per chunk
 constexpr int kCWaveSpan = kIdxChunk / (kTopkThreads / 64);    // positions per wave per chunk
 static_assert((1 << kChunkShift) == kIdxChunk && kCSteps == 4 && kCWaveSpan == 256 * kCSteps, "chunk layout");
-static_assert(kIdxSample == 4 * kTopkThreads && kIdxMaxChunks <= kTopkThreads, "one chunk per thread");
+static_assert(kIdxSample % kTopkThreads == 0 && kIdxMaxChunks <= kTopkThreads, "one chunk per thread");
 static_assert(kIdxCandCap % kTopkThreads == 0, "whole candidates per thread");
 
 // The key that `rank` keys of keys[0 .. S) reach (the rank-th largest).  The bits all
@@ -482,7 +482,7 @@ __device__ __forceinline__ uint32_t select_rank(const uint32_t* keys, int S, int
 }
 
 // The row's threshold key, the same in every workgroup of the row: from a sample of
-// S = min(n, 4096) scores (the whole row when n <= 4096, else 256 runs of 16
+// S = min(n, 2048) scores (the whole row when n <= 2048, else 128 runs of 16
 // consecutive scores spread evenly over the row), the lower edge of the 12-bit key bin
 // that holds the sample's rank-th largest key.  With the whole row as the sample,
 // rank = K; otherwise K's share of the sample plus four standard deviations and 8, so
@@ -496,7 +496,7 @@ __device__ __forceinline__ uint32_t sample_threshold(const float* s, int64_t n, 
 #pragma unroll
   for (int j = 0; j < kIdxSample / kTopkThreads; ++j) {
     const int i = tid + j * kTopkThreads;
-    const int64_t p = S < n ? (i >> 4) * (n >> 8) + (i & 15) : i;  // n > 4096: the runs are n / 256 apart
+    const int64_t p = S < n ? (i >> 4) * (n >> 7) + (i & 15) : i;  // n > 2048: the runs are n / 128 apart
     smp[j] = i < S ? score_key(s[p]) : 0u;
   }
   int rank = K;
@@ -506,7 +506,7 @@ __device__ __forceinline__ uint32_t sample_threshold(const float* s, int64_t n, 
     rank = min(S, static_cast<int>(ceil(m + 4.0 * sqrt(m * (1.0 - f)) + 8.0)));
   }
 #pragma unroll
-  for (int j = 0; j < kIdxSample / kTopkThreads; ++j) hist[tid * 4 + j] = 0;
+  for (int j = 0; j < 4; ++j) hist[tid * 4 + j] = 0;
   __syncthreads();
 #pragma unroll
   for (int j = 0; j < kIdxSample / kTopkThreads; ++j)
@@ -538,7 +538,7 @@ __device__ __forceinline__ uint32_t sample_threshold(const float* s, int64_t n, 
 // positions, in position order (per-wave counts, then ballot ranks inside each step)
 // into the chunk's own region of the workspace, and their number beside it.
 __global__ __launch_bounds__(kTopkThreads) void topk_candidates_kernel(IndexerArgs a) {
-  __shared__ int hist[kIdxSample];
+  __shared__ int hist[4096];
   __shared__ int scan[kTopkThreads / 64];
   __shared__ int wcnt[kTopkThreads / 64];
   __shared__ int pick[3];

@@ -184,10 +184,10 @@ def test_rows_longer_than_one_segment():
 
 
 def test_sample_that_misses_takes_the_slow_path():
-    # the sampled positions (256 runs of 16, n / 256 apart) hold the row's only high scores, all
+    # the sampled positions (128 runs of 16, n / 128 apart) hold the row's only high scores, all
     # distinct, so the threshold from the sample is met by fewer than K keys of the row: the
     # selection must notice and do the row by radix passes
-    n, S, k, D = 20000, 4096, 2000, 64
+    n, S, k, D = 20000, 2048, 2000, 64
     w = W.indexer(seed=9, num_tokens=1, cache_rows=n, num_reqs=1, page_size=16, head_dim=D, topk=k,
                   min_ctx=n, max_ctx=n, integer=True)
     q = torch.zeros(1, D)
@@ -196,7 +196,7 @@ def test_sample_that_misses_takes_the_slow_path():
     kc = torch.zeros(n, D)
     kc[:, 0] = -1.0
     for i in range(S):
-        v, p = S - i, (i >> 4) * (n >> 8) + (i & 15)
+        v, p = S - i, (i >> 4) * (n >> 7) + (i & 15)
         kc[slots[p], 0], kc[slots[p], 1] = v // 256, v % 256
     w["q"], w["key_cache"] = q.to(torch.bfloat16), kc.to(torch.bfloat16)
     say("[indexer] sample that misses")
